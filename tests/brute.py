@@ -1,0 +1,52 @@
+"""Brute-force attention in plain Python scalar loops, for tiny inputs.
+
+Independent of the oracle: contiguous (unpaged) keys and values given as Python lists,
+its own masking loop, math.fsum for every sum, and exp with the row maximum subtracted
+(the same real number as exp(s)/sum exp(s), written so large logits stay finite).
+"""
+import math
+
+
+def attention_row(q_vec, keys, vals, scale):
+    """One head: q_vec [D], keys [N][D], vals [N][Dv] -> (out [Dv], lse)."""
+    if not keys:
+        return [0.0] * (len(vals[0]) if vals else 0), -math.inf
+    logits = [scale * math.fsum(a * b for a, b in zip(q_vec, k)) for k in keys]
+    top = max(logits)
+    w = [math.exp(x - top) for x in logits]
+    tot = math.fsum(w)
+    dv = len(vals[0])
+    out = [math.fsum(w[r] * vals[r][c] for r in range(len(keys))) / tot for c in range(dv)]
+    return out, top + math.log(tot)
+
+
+def decode_contiguous(q_rows, seq_keys, n_tokens, scale, mask, window=-1, value_width=512):
+    """q_rows[t][h][d]; seq_keys[b] = contiguous list of that sequence's cache rows.
+
+    Query token j of the n tokens of sequence b sits at position len(keys) - n + j.
+    Returns out[t][h][c] and lse[t][h].
+    """
+    out, lse = [], []
+    t = 0
+    for b, keys in enumerate(seq_keys):
+        L = len(keys)
+        for j in range(n_tokens[b]):
+            pos = L - n_tokens[b] + j
+            vis = []
+            for r in range(L):
+                if mask == "causal" and r > pos:
+                    continue
+                if mask == "sliding_window_causal" and (r > pos or r <= pos - window):
+                    continue
+                vis.append(r)
+            ks = [keys[r] for r in vis]
+            vs = [keys[r][:value_width] for r in vis]
+            o_t, l_t = [], []
+            for h in range(len(q_rows[t])):
+                o, l = attention_row(q_rows[t][h], ks, vs, scale)
+                o_t.append(o)
+                l_t.append(l)
+            out.append(o_t)
+            lse.append(l_t)
+            t += 1
+    return out, lse

@@ -1,0 +1,489 @@
+"""Pins for the CPU oracle: each function checks the oracle against something other than
+itself (brute force on tiny inputs, closed forms, invariants, format definitions) and
+raises AssertionError on failure.  They are collected as tests by test_oracle_pins.py
+and re-run under planted mistakes by test_oracle_mutants.py.
+
+Every oracle call goes through the module object ``O`` so that a patched function is
+the one that runs.
+"""
+import math
+import os
+
+import numpy as np
+
+import oracle.mla_oracle as O
+from brute import attention_row, decode_contiguous
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+D = 576
+DV = 512
+SCALE = float(np.float32(1.0 / math.sqrt(192.0)))
+
+
+# --------------------------------------------------------------------------------------
+# tiny-input builders (layout only)
+# --------------------------------------------------------------------------------------
+
+def page_up(seq_keys, page_size, rng, spare=2, fill=np.nan):
+    """Scatter contiguous per-sequence rows into a shuffled page pool; unused slots = fill."""
+    npages = [-(-len(k) // page_size) for k in seq_keys]
+    total = sum(npages) + spare
+    perm = rng.permutation(total)
+    width = max(1, max(npages))
+    cache = np.full((total, page_size, seq_keys[0].shape[1]), fill)
+    table = np.full((len(seq_keys), width), -1, dtype=np.int32)
+    cur = 0
+    for b, keys in enumerate(seq_keys):
+        for j in range(npages[b]):
+            pid = int(perm[cur])
+            cur += 1
+            table[b, j] = pid
+            chunk = keys[j * page_size:(j + 1) * page_size]
+            cache[pid, :len(chunk)] = chunk
+    lens = np.array([len(k) for k in seq_keys], dtype=np.int32)
+    return cache, table, lens
+
+
+def offsets_of(n_tokens):
+    off = np.zeros(len(n_tokens) + 1, dtype=np.uint32)
+    off[1:] = np.cumsum(n_tokens)
+    return off
+
+
+def tiny_decode(seed=1, lens=(5, 37, 20), n_tokens=(1, 3, 2), H=2, page_size=16, q_std=1.0):
+    rng = np.random.default_rng(seed)
+    seq_keys = [rng.standard_normal((L, D)) for L in lens]
+    T = sum(n_tokens)
+    q = rng.standard_normal((T, H, D)) * q_std
+    cache, table, lens_arr = page_up(seq_keys, page_size, rng)
+    return dict(q=q, seq_keys=seq_keys, cache=cache, table=table, lens=lens_arr,
+                off=offsets_of(n_tokens), n_tokens=list(n_tokens), page_size=page_size)
+
+
+def run_dense(c, mask="causal", window=-1, scale=SCALE, table=None, cache=None):
+    return O.decode_paged_f64(c["q"], c["off"], c["table"] if table is None else table,
+                              c["lens"], c["cache"] if cache is None else cache,
+                              c["page_size"], scale, mask, window)
+
+
+def close(a, b, tol):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    diff = np.where(same_inf, 0.0, np.abs(a - b))
+    assert np.all(np.isfinite(diff)), "non-finite mismatch"
+    assert diff.max(initial=0.0) <= tol, f"max diff {diff.max()} > {tol}"
+
+
+# --------------------------------------------------------------------------------------
+# P1: brute force on contiguous (unpaged) keys
+# --------------------------------------------------------------------------------------
+
+def pin_p1_dense_causal():
+    c = tiny_decode()
+    out, lse = run_dense(c, "causal")
+    bo, bl = decode_contiguous(c["q"].tolist(), [k.tolist() for k in c["seq_keys"]],
+                               c["n_tokens"], SCALE, "causal")
+    close(out, bo, 1e-12)
+    close(lse, bl, 1e-12)
+
+
+def pin_p1_dense_null():
+    c = tiny_decode(seed=2, lens=(9, 17), n_tokens=(2, 1), page_size=4)
+    out, lse = run_dense(c, "null")
+    bo, bl = decode_contiguous(c["q"].tolist(), [k.tolist() for k in c["seq_keys"]],
+                               c["n_tokens"], SCALE, "null")
+    close(out, bo, 1e-12)
+    close(lse, bl, 1e-12)
+
+
+def pin_p1_dense_sliding():
+    c = tiny_decode(seed=3, lens=(12, 30), n_tokens=(3, 2), page_size=8)
+    out, lse = run_dense(c, "sliding_window_causal", window=5)
+    bo, bl = decode_contiguous(c["q"].tolist(), [k.tolist() for k in c["seq_keys"]],
+                               c["n_tokens"], SCALE, "sliding_window_causal", window=5)
+    close(out, bo, 1e-12)
+    close(lse, bl, 1e-12)
+
+
+def _torch_e4m3(codes):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float32).numpy().astype(np.float64)
+
+
+def tiny_sparse(seed=4, H=2, page_size=8, pages=5, T=3, stride=9):
+    rng = np.random.default_rng(seed)
+    # finite E4M3 codes only (exclude the two NaN codes)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    cache8 = rng.choice(finite, size=(pages, page_size, D)).astype(np.uint8)
+    q8 = rng.choice(finite[(finite & 0x78) < 0x50], size=(T, H, D)).astype(np.uint8)  # |q| <= 8
+    q_scale = rng.uniform(0.001, 0.01, size=T).astype(np.float32)
+    c_scale = rng.uniform(0.001, 0.01, size=(pages, page_size)).astype(np.float32)
+    rows = pages * page_size
+    idx = np.full((T, stride), -1, dtype=np.int32)
+    topk = np.array([7, 1, 9], dtype=np.int32)[:T]
+    for t in range(T):
+        idx[t] = rng.integers(0, rows, size=stride)
+    idx[0, 2] = -1            # a pad inside the counted prefix is skipped
+    idx[2, 3] = idx[2, 5]     # a duplicate counts twice
+    return dict(q8=q8, q_scale=q_scale, cache8=cache8, c_scale=c_scale, idx=idx, topk=topk,
+                page_size=page_size, off=np.arange(T + 1, dtype=np.uint32))
+
+
+def pin_p1_sparse():
+    s = tiny_sparse()
+    out, lse = O.decode_sparse(s["q8"], s["q_scale"], s["off"], s["cache8"], s["c_scale"],
+                               s["idx"], s["topk"], s["page_size"], SCALE)
+    ps = s["page_size"]
+    qv = _torch_e4m3(s["q8"]) * s["q_scale"].astype(np.float64)[:, None, None]
+    cv = _torch_e4m3(s["cache8"]) * s["c_scale"].astype(np.float64)[:, :, None]
+    for t in range(len(s["topk"])):
+        keys = []
+        for i in range(int(s["topk"][t])):
+            r = int(s["idx"][t, i])
+            if r < 0:
+                continue
+            keys.append(cv[r // ps, r % ps].tolist())
+        for h in range(qv.shape[1]):
+            o, l = attention_row(qv[t, h].tolist(), keys, [k[:DV] for k in keys], SCALE)
+            close(out[t, h], o, 1e-12)
+            close(lse[t, h], l, 1e-12)
+
+
+def tiny_prefill(seed=5, new=(3, 4), prefix=(0, 2), H=2, page_size=4):
+    rng = np.random.default_rng(seed)
+    total = [a + b for a, b in zip(new, prefix)]
+    seq_cache = [rng.standard_normal((L, D)) for L in total]
+    cache, table, lens = page_up(seq_cache, page_size, rng)
+    Tq, Tk = sum(new), sum(total)
+    q = rng.standard_normal((Tq, H, 192))
+    k = rng.standard_normal((Tk, H, 128))
+    v = rng.standard_normal((Tk, H, 128))
+    return dict(q=q, k=k, v=v, bro=offsets_of(total), cofs=np.zeros(len(new), dtype=np.uint32),
+                ino=offsets_of(new), table=table, lens=lens, cache=cache, seq_cache=seq_cache,
+                page_size=page_size, new=list(new), total=total)
+
+
+def run_prefill(p, mask="causal", **kw):
+    return O.prefill_paged_f64(p["q"], p["k"], p["v"], p["bro"], p["cofs"], p["ino"], p["table"],
+                               p["lens"], p["cache"], p["page_size"], SCALE, mask, **kw)
+
+
+def pin_p1_prefill():
+    p = tiny_prefill()
+    out = run_prefill(p)
+    H = p["q"].shape[1]
+    t = 0
+    for b, n in enumerate(p["new"]):
+        L = p["total"][b]
+        k0 = int(p["bro"][b])
+        for j in range(n):
+            pos = L - n + j
+            for h in range(H):
+                keys, vals = [], []
+                for i in range(L):
+                    if i > pos:
+                        continue
+                    keys.append(list(p["k"][k0 + i, h]) + list(p["seq_cache"][b][i, 512:576]))
+                    vals.append(list(p["v"][k0 + i, h]))
+                o, _ = attention_row(list(p["q"][t, h]), keys, vals, SCALE)
+                close(out[t, h], o, 1e-12)
+            t += 1
+
+
+# --------------------------------------------------------------------------------------
+# P2, P14: layout invariances
+# --------------------------------------------------------------------------------------
+
+def pin_p2_page_permutation():
+    c = tiny_decode(seed=6)
+    out1, lse1 = run_dense(c)
+    cache2, table2, _ = page_up(c["seq_keys"], c["page_size"], np.random.default_rng(99), spare=5)
+    out2, lse2 = run_dense(c, table=table2, cache=cache2)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def pin_p14_batch_permutation():
+    c = tiny_decode(seed=7, lens=(5, 37, 20, 11), n_tokens=(1, 1, 1, 1))
+    out, lse = run_dense(c)
+    perm = [2, 0, 3, 1]
+    keys2 = [c["seq_keys"][i] for i in perm]
+    cache2, table2, lens2 = page_up(keys2, c["page_size"], np.random.default_rng(5))
+    out2, lse2 = O.decode_paged_f64(c["q"][perm], c["off"], table2, lens2, cache2,
+                                    c["page_size"], SCALE, "causal")
+    assert np.array_equal(out2, out[perm]) and np.array_equal(lse2, lse[perm])
+
+
+# --------------------------------------------------------------------------------------
+# P3 - P7: closed forms
+# --------------------------------------------------------------------------------------
+
+def pin_p3_one_key():
+    c = tiny_decode(seed=8, lens=(1, 1), n_tokens=(1, 1), page_size=16)
+    out, lse = run_dense(c)
+    for b in range(2):
+        assert np.array_equal(out[b], np.broadcast_to(c["seq_keys"][b][0, :DV], out[b].shape))
+        s = SCALE * (c["q"][b] @ c["seq_keys"][b][0])
+        close(lse[b], s, 1e-12)
+
+
+def pin_p4_normalisation():
+    rng = np.random.default_rng(9)
+    qh = rng.standard_normal((3, D))
+    keys = rng.standard_normal((40, D))
+    _, _, p = O.attend(qh, keys, O.value_columns(keys), SCALE, return_probs=True)
+    close(p.sum(axis=1), np.ones(3), 1e-14)
+    assert np.all(p >= 0)
+    const = keys.copy()
+    const[:, :DV] = 0.625
+    out, _ = O.attend(qh, const, O.value_columns(const), SCALE)
+    close(out, np.full((3, DV), 0.625), 1e-14)
+
+
+def pin_p5_zero_scale_is_mean():
+    c = tiny_decode(seed=10, lens=(5, 37, 20), n_tokens=(1, 3, 2))
+    out, _ = run_dense(c, scale=0.0)
+    t = 0
+    for b, keys in enumerate(c["seq_keys"]):
+        n = c["n_tokens"][b]
+        for j in range(n):
+            vis = keys[:len(keys) - n + j + 1, :DV]
+            close(out[t], np.broadcast_to(vis.mean(axis=0), out[t].shape), 1e-13)
+            t += 1
+    c["q"] = np.zeros_like(c["q"])
+    out0, _ = run_dense(c)
+    close(out0[0], np.broadcast_to(c["seq_keys"][0][:, :DV].mean(axis=0), out0[0].shape), 1e-13)
+
+
+def _golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()[:2]
+                vals[k] = v
+    return vals
+
+
+def pin_p6_two_keys():
+    g = _golden("two_key_example.txt")
+    q = np.zeros((1, D))
+    q[0, 0] = 1.0
+    keys = np.zeros((2, D))
+    keys[0, 0], keys[1, 0] = 2.0, 1.0
+    vals = np.zeros((2, DV))
+    vals[0, 0], vals[1, 1] = 1.0, 1.0
+    out, lse = O.attend(q, keys, vals, 1.0)
+    close(out[0, 0], float(g["p0"]), 1e-15)
+    close(out[0, 1], float(g["p1"]), 1e-15)
+    close(out[0, 2:], np.zeros(DV - 2), 0.0)
+    close(lse[0], float(g["lse"]), 1e-15)
+    # random two-key case against the logistic closed form
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((2, D))
+    keys = rng.standard_normal((2, D))
+    out, _ = O.attend(q, keys, O.value_columns(keys), SCALE)
+    for h in range(2):
+        s0 = SCALE * math.fsum(q[h] * keys[0])
+        s1 = SCALE * math.fsum(q[h] * keys[1])
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        close(out[h], w0 * keys[0, :DV] + (1.0 - w0) * keys[1, :DV], 1e-13)
+
+
+def pin_p7_rope_shift():
+    c = tiny_decode(seed=12, lens=(13, 21), n_tokens=(1, 2))
+    j = 512 + 17
+    for keys in c["seq_keys"]:
+        keys[:, j] = 1.5
+    cache, table, _ = page_up(c["seq_keys"], c["page_size"], np.random.default_rng(3))
+    outs, lses = [], []
+    for a in (0.0, 2.5):
+        q = c["q"].copy()
+        q[:, :, j] = a
+        o, l = O.decode_paged_f64(q, c["off"], table, c["lens"], cache, c["page_size"], SCALE)
+        outs.append(o)
+        lses.append(l)
+    close(outs[0], outs[1], 1e-12)
+    close(lses[1] - lses[0], np.full(lses[0].shape, SCALE * 2.5 * 1.5), 1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# P8: split-KV algebra
+# --------------------------------------------------------------------------------------
+
+def pin_p8_split_combine():
+    rng = np.random.default_rng(13)
+    qh = rng.standard_normal((4, D))
+    keys = rng.standard_normal((70, D))
+    full_o, full_l = O.attend(qh, keys, O.value_columns(keys), SCALE)
+    for cuts in ([0, 70], [0, 1, 70], [0, 23, 23, 50, 70], [0, 5, 9, 64, 69, 70]):
+        parts = [O.attend(qh, keys[a:b], O.value_columns(keys[a:b]), SCALE)
+                 for a, b in zip(cuts[:-1], cuts[1:])]
+        o, l = O.combine(parts)
+        close(o, full_o, 1e-12)
+        close(l, full_l, 1e-12)
+    o, l = O.combine([O.attend(qh, keys[:0], O.value_columns(keys[:0]), SCALE)] * 2)
+    close(o, np.zeros_like(full_o), 0.0)
+    assert np.all(np.isneginf(l))
+
+
+# --------------------------------------------------------------------------------------
+# P9: absorbed decode equals un-absorbed prefill
+# --------------------------------------------------------------------------------------
+
+def pin_p9_absorption():
+    """Projecting q's no-rope part through w_uk and the latent output through w_uv turns
+    MLA decode over the latent cache into ordinary attention with per-head k = w_uk^T c
+    and v = w_uv c (mla_decode_branch_fp8 summary and Args w_uk / w_uv)."""
+    rng = np.random.default_rng(14)
+    H, N = 3, 11
+    latent = rng.standard_normal((N, 512))
+    rope = rng.standard_normal((N, 64))
+    w_uk = rng.standard_normal((H, 512, 128)) / math.sqrt(512)
+    w_uv = rng.standard_normal((H, 128, 512)) / math.sqrt(512)
+    q_nope = rng.standard_normal((H, 128))
+    q_rope = rng.standard_normal((H, 64))
+    rows = np.concatenate([latent, rope], axis=1)
+    cache, table, lens = page_up([rows], 4, rng)
+    q_abs = np.concatenate([np.einsum("hln,hn->hl", w_uk, q_nope), q_rope], axis=1)[None]
+    raw, _ = O.decode_paged_f64(q_abs, offsets_of([1]), table, lens, cache, 4, SCALE, "causal")
+    dec = np.einsum("hvl,hl->hv", w_uv, raw[0])
+    k = np.einsum("hln,il->ihn", w_uk, latent)
+    v = np.einsum("hvl,il->ihv", w_uv, latent)
+    q_pre = np.concatenate([q_nope, q_rope], axis=1)[None]
+    pre = O.prefill_paged_f64(q_pre, k, v, offsets_of([N]), np.zeros(1, np.uint32), offsets_of([1]),
+                              table, lens, cache, 4, SCALE, "causal")
+    close(pre[0], dec, 1e-10)
+
+
+# --------------------------------------------------------------------------------------
+# P10: masks
+# --------------------------------------------------------------------------------------
+
+def pin_p10_masks():
+    c = tiny_decode(seed=15, lens=(5, 37, 20), n_tokens=(1, 1, 1))
+    oc, lc = run_dense(c, "causal")
+    on, ln = run_dense(c, "null")
+    assert np.array_equal(oc, on) and np.array_equal(lc, ln)
+    p = tiny_prefill(seed=16, new=(4, 3), prefix=(0, 2))
+    out = run_prefill(p, "causal")
+    assert np.array_equal(out[0], p["v"][0])                 # first query of a fresh sequence
+    out_null = run_prefill(p, "null")
+    last = [int(p["ino"][b + 1]) - 1 for b in range(2)]
+    close(out[last], out_null[last], 1e-14)
+
+
+# --------------------------------------------------------------------------------------
+# P11, P12: sparse semantics
+# --------------------------------------------------------------------------------------
+
+def pin_p11_sparse_is_dense():
+    c = tiny_decode(seed=17, lens=(37, 20), n_tokens=(1, 1), page_size=8)
+    ps = c["page_size"]
+    stride = 40
+    idx = np.full((2, stride), -1, dtype=np.int32)
+    topk = np.zeros(2, dtype=np.int32)
+    for b in range(2):
+        L = int(c["lens"][b])
+        pos = np.arange(L)
+        idx[b, :L] = c["table"][b, pos // ps] * ps + pos % ps
+        topk[b] = L
+    so, sl = O.decode_sparse_f64(c["q"], c["off"], c["cache"], idx, topk, ps, SCALE)
+    do, dl = run_dense(c, "null")
+    assert np.array_equal(so, do) and np.array_equal(sl, dl)
+    # a subset equals dense attention over a cache holding only those rows, listed order
+    rng = np.random.default_rng(18)
+    sub = [rng.choice(int(c["lens"][b]), size=7, replace=False) for b in range(2)]
+    idx2 = np.full((2, 9), -1, dtype=np.int32)
+    for b in range(2):
+        idx2[b, :7] = c["table"][b, sub[b] // ps] * ps + sub[b] % ps
+    so2, _ = O.decode_sparse_f64(c["q"], c["off"], c["cache"], idx2, np.array([7, 7]), ps, SCALE)
+    packed = [c["seq_keys"][b][sub[b]] for b in range(2)]
+    cache3, table3, lens3 = page_up(packed, 4, rng)
+    do2, _ = O.decode_paged_f64(c["q"], c["off"], table3, lens3, cache3, 4, SCALE, "null")
+    close(so2, do2, 1e-13)
+
+
+def pin_p12_sparse_poison():
+    s = tiny_sparse(seed=19)
+    args = (s["off"],)
+    out, lse = O.decode_sparse(s["q8"], s["q_scale"], s["off"], s["cache8"], s["c_scale"],
+                               s["idx"], s["topk"], s["page_size"], SCALE)
+    assert np.all(np.isfinite(out))
+    ps = s["page_size"]
+    listed = np.zeros(s["cache8"].shape[0] * ps, dtype=bool)
+    for t in range(len(s["topk"])):
+        r = s["idx"][t, :s["topk"][t]]
+        listed[r[r >= 0]] = True
+    c8 = s["cache8"].copy().reshape(-1, D)
+    cs = s["c_scale"].copy().reshape(-1)
+    c8[~listed] = 0x7F
+    cs[~listed] = np.nan
+    out2, lse2 = O.decode_sparse(s["q8"], s["q_scale"], *args, c8.reshape(s["cache8"].shape),
+                                 cs.reshape(s["c_scale"].shape), s["idx"], s["topk"], ps, SCALE)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    idx3 = s["idx"].copy()
+    for t in range(len(s["topk"])):
+        idx3[t, s["topk"][t]:] = np.flatnonzero(~listed)[:idx3.shape[1] - s["topk"][t]]
+    out3, _ = O.decode_sparse(s["q8"], s["q_scale"], *args, s["cache8"], s["c_scale"], idx3,
+                              s["topk"], ps, SCALE)
+    assert np.array_equal(out, out3)
+
+
+# --------------------------------------------------------------------------------------
+# P13: storage formats
+# --------------------------------------------------------------------------------------
+
+def pin_p13_e4m3():
+    import torch
+    g = _golden("e4m3_ocp_points.txt")
+    for code, val in g.items():
+        got = O.e4m3_to_f64(np.array([int(code, 16)], dtype=np.uint8))[0]
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), code
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = O.e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(mine))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], mine[ok])
+
+
+def pin_p13_bf16():
+    import torch
+    g = _golden("bf16_points.txt")
+    for bits, val in g.items():
+        got = O.bf16_to_f64(np.array([int(bits, 16)], dtype=np.uint16))[0]
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val), (bits, got, val)
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    mine = O.bf16_to_f64(allbits)
+    assert np.array_equal(np.isnan(ref), np.isnan(mine))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], mine[ok])
+
+
+# --------------------------------------------------------------------------------------
+# numerics: large logits stay finite and exact
+# --------------------------------------------------------------------------------------
+
+def pin_large_logits():
+    c = tiny_decode(seed=20, lens=(9, 14), n_tokens=(1, 1), q_std=400.0)
+    out, lse = run_dense(c)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    assert np.max(lse) > 800.0  # exp of such logits overflows float64
+    bo, bl = decode_contiguous(c["q"].tolist(), [k.tolist() for k in c["seq_keys"]],
+                               c["n_tokens"], SCALE, "causal")
+    close(out, bo, 1e-11)
+    close(lse, bl, 1e-11)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
