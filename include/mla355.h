@@ -1,0 +1,191 @@
+/*
+ * libmla355 -- multi-head latent attention (MLA) over a paged latent KV cache on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: tensors are described by mla_tensor
+ * (a device pointer plus element type, shape and element strides); nothing here
+ * depends on any framework's types.
+ *
+ * The operations follow the Modular MAX kernel-library pages, cited by title and
+ * section:
+ *   generic_flare_mla_decode_kv_cache_ragged  (summary; Parameters mask_str,
+ *       local_window_size, sparse_mla; Args q, input_row_offsets, scale, output,
+ *       q_scale_ptr, d_indices, indices_stride, topk_lengths, num_partitions_in)
+ *   generic_flare_mla_prefill_kv_cache_ragged (summary; Args q, k, v,
+ *       buffer_row_offsets, cache_offsets, input_row_offsets, scale, output)
+ *   mla_decode_branch_fp8 (summary: the 576-wide query is the projected no-rope part
+ *       followed by the rope part; the decode output is in the 512-wide latent space)
+ *
+ * Common conventions
+ *   - Every tensor pointer is a device pointer on the current HIP device and is owned
+ *     by the caller, outputs included; the library never frees or reallocates it.
+ *   - Strides are in elements.  The innermost dimension must be contiguous (stride 1),
+ *     every other stride and every base pointer must be a multiple of 16 bytes.
+ *   - A latent cache row is 576 values: columns 0..511 are the latent part (which is
+ *     also V), columns 512..575 the rope part.
+ *   - cache_lens[b] counts the valid cache rows of sequence b, the rows written for
+ *     its current query tokens included; query token j of the n_b tokens of sequence
+ *     b sits at cache position cache_lens[b] - n_b + j.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
+ *     return as soon as the work is queued.  Validation uses only the descriptors and
+ *     scalars: the library never reads device data on the host.  On any error nothing
+ *     is launched and the call returns a status; mla_last_error_message() gives the
+ *     detail (per host thread).  Device faults surface at the caller's next
+ *     synchronisation.  Out-of-range device data (a page id outside the pool, an index
+ *     outside the pool, non-monotone offsets) never causes an out-of-bounds access:
+ *     the offending rows contribute nothing and a bit is set in the device error word
+ *     read by mla_check_device_errors().
+ *   - Workspace (split-KV partial results and per-row metadata) is owned by the
+ *     library, one grow-only buffer per (device, stream).  It is allocated on first
+ *     use; a call issued while `stream` is capturing a graph must find it already large
+ *     enough (see mla_reserve_workspace), else it returns MLA_ERR_WORKSPACE.  Calls on
+ *     one stream are ordered, so they may share that stream's workspace.
+ */
+#ifndef MLA355_H_
+#define MLA355_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL_ARG = 1,    /* a required pointer or descriptor is NULL */
+  MLA_ERR_SHAPE = 2,       /* shapes or strides disagree with each other */
+  MLA_ERR_DTYPE = 3,       /* a tensor has the wrong element type */
+  MLA_ERR_ALIGNMENT = 4,   /* a base pointer or stride is not 16-byte aligned */
+  MLA_ERR_UNSUPPORTED = 5, /* a well-formed request outside what this build implements */
+  MLA_ERR_WORKSPACE = 6,   /* workspace could not be allocated, or is too small while capturing */
+  MLA_ERR_HIP = 7,         /* a HIP runtime call failed */
+  MLA_ERR_VALUE = 8        /* a scalar argument is out of range */
+} mla_status;
+
+/* Masking strategy (generic_flare_mla_decode_kv_cache_ragged, Parameters mask_str). */
+typedef enum mla_mask {
+  MLA_MASK_NULL = 0,                 /* every cache row 0..L-1 is visible */
+  MLA_MASK_CAUSAL = 1,               /* rows 0..pos are visible */
+  MLA_MASK_SLIDING_WINDOW_CAUSAL = 2 /* rows pos-W+1..pos, W = local_window_size > 0 */
+} mla_mask;
+
+typedef enum mla_dtype {
+  MLA_DTYPE_BF16 = 0,
+  MLA_DTYPE_FP8_E4M3 = 1, /* OCP E4M3 (finite-only "fn" variant), the gfx950 native FP8 */
+  MLA_DTYPE_F32 = 2,
+  MLA_DTYPE_I32 = 3,
+  MLA_DTYPE_U32 = 4
+} mla_dtype;
+
+typedef struct mla_tensor {
+  void* data;        /* device pointer, caller-owned */
+  int32_t dtype;     /* an mla_dtype */
+  int32_t ndim;      /* 1..4 */
+  int64_t shape[4];  /* entries past ndim are ignored */
+  int64_t stride[4]; /* element strides; entries past ndim are ignored */
+} mla_tensor;
+
+/*
+ * Dense MLA decode over a ragged batch against a paged latent cache
+ * (generic_flare_mla_decode_kv_cache_ragged: summary; Args q, input_row_offsets,
+ * scale, output, num_partitions_in; Parameters mask_str, local_window_size).
+ *
+ * For every query row t of sequence b and every head h:
+ *   s_r = scale * <q[t,h,:], C_b[r,:]> over the visible cache rows r,
+ *   out[t,h,:] = sum_r softmax(s)_r * C_b[r, 0:512],
+ * where C_b[r] = latent_cache[page_table[b, r / PS], r % PS, :].
+ *
+ *   q                  bf16 [T, H, 576]; H in {16, 32, 64, 128}
+ *   input_row_offsets  u32 [B + 1], off[0] = 0, non-decreasing, off[B] = T
+ *   page_table         i32 [B, max_pages]; entries past a sequence's pages are not read
+ *   cache_lens         i32 [B]
+ *   latent_cache       bf16 [num_pages, PS, 576], PS >= 1, rows contiguous
+ *   scale              finite float (usually 1/sqrt(qk head width))
+ *   mask, local_window_size   see mla_mask; the window is ignored unless sliding
+ *   num_partitions     <= 0: the library balances the work over the whole GPU,
+ *                      splitting long rows (split-KV) and merging the pieces by their
+ *                      log-sum-exp; >= 1: every query row is split into exactly that
+ *                      many key ranges (the graph-capture override), at most 4096
+ *   out                bf16 [T, H, 512], written in full (rows with no visible key
+ *                      become 0)
+ */
+mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_offsets,
+                            const mla_tensor* page_table, const mla_tensor* cache_lens,
+                            const mla_tensor* latent_cache, float scale, int32_t mask,
+                            int32_t local_window_size, int32_t num_partitions,
+                            mla_tensor* out, void* stream);
+
+/*
+ * Sparse MLA decode (generic_flare_mla_decode_kv_cache_ragged: Parameters sparse_mla;
+ * Args q_scale_ptr, d_indices, indices_stride, topk_lengths, num_partitions_in).
+ * Query row t attends only to the cache rows listed in d_indices[t, :], in listed
+ * order, with no positional mask: the first topk_lengths[t] entries count, negative
+ * entries (the -1 fill) are skipped, duplicates count as often as they are listed.
+ * A listed value is a physical row of the pool: page * PS + slot.
+ *
+ *   q             fp8 e4m3 [T, H, 576] (or bf16, then q_scale must be NULL)
+ *   q_scale       f32 [T] (one scale per query token, shared by its heads) or NULL = 1
+ *   input_row_offsets  u32 [B + 1] (only its shape is checked: index lists are per row)
+ *   latent_cache  fp8 e4m3 [num_pages, PS, 576] (or bf16, then cache_scale must be NULL)
+ *   cache_scale   f32 [num_pages, PS] (one scale per cache row) or NULL = 1
+ *   d_indices     i32 [T, indices_stride] (row stride = stride[0] >= shape[1])
+ *   topk_lengths  i32 [T], values above shape[1] of d_indices are clamped to it
+ *   scale, num_partitions, out   as for mla_decode_paged; out is bf16 [T, H, 512]
+ */
+mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scale,
+                                   const mla_tensor* input_row_offsets,
+                                   const mla_tensor* latent_cache, const mla_tensor* cache_scale,
+                                   const mla_tensor* d_indices, const mla_tensor* topk_lengths,
+                                   float scale, int32_t num_partitions, mla_tensor* out,
+                                   void* stream);
+
+/*
+ * Ragged MLA prefill with per-head keys (generic_flare_mla_prefill_kv_cache_ragged:
+ * summary; Args q, k, v, buffer_row_offsets, cache_offsets, input_row_offsets, scale,
+ * output).  Key i of sequence b is row buffer_row_offsets[b] + i of k / v at cache
+ * position cache_offsets[b] + i; its 192-wide key is [k[row, h, 0:128] | the rope
+ * columns 512..575 of its latent cache row], shared rope across heads.
+ *
+ *   q                   bf16 [Tq, H, 192] = [no-rope 128 | rope 64]; H in {16,...,128}
+ *   k, v                bf16 [Tk, H, 128]
+ *   buffer_row_offsets  u32 [B + 1] rows of k / v per sequence
+ *   cache_offsets       u32 [B]
+ *   input_row_offsets   u32 [B + 1] rows of q / out per sequence
+ *   page_table, cache_lens, latent_cache   as for mla_decode_paged
+ *   mask                MLA_MASK_CAUSAL or MLA_MASK_NULL
+ *   out                 bf16 [Tq, H, 128]
+ */
+mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla_tensor* v,
+                             const mla_tensor* buffer_row_offsets, const mla_tensor* cache_offsets,
+                             const mla_tensor* input_row_offsets, const mla_tensor* page_table,
+                             const mla_tensor* cache_lens, const mla_tensor* latent_cache,
+                             float scale, int32_t mask, mla_tensor* out, void* stream);
+
+/* Workspace bytes a decode call with these sizes needs (host only, no device access).
+ * num_partitions as in mla_decode_paged; device selects the CU count (-1 = current). */
+size_t mla_decode_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t num_partitions,
+                                  int32_t device);
+
+/* Grow the workspace of (device, stream) to at least `bytes` (allocates and clears it;
+ * not allowed while `stream` is capturing).  device -1 = the current device. */
+mla_status mla_reserve_workspace(int32_t device, void* stream, size_t bytes);
+
+/* Synchronise `stream`, read and clear the device error word of (device, stream):
+ * bit 0 a page id outside [0, num_pages) was met, bit 1 a sparse index outside the
+ * pool, bit 2 offsets that decrease or exceed the q rows, bit 3 a cache length above
+ * max_pages * PS.  *flags receives the word (0 = clean). */
+mla_status mla_check_device_errors(int32_t device, void* stream, uint32_t* flags);
+
+/* Free every workspace the library holds (all devices, all streams). */
+void mla_shutdown(void);
+
+const char* mla_status_string(mla_status s);
+/* Detail of the last failed call on this host thread ("" if none). */
+const char* mla_last_error_message(void);
+/* Library version string. */
+const char* mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA355_H_ */

@@ -1,0 +1,194 @@
+"""Python binding of libmla355 (MLA attention over a paged latent KV cache on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+libmla355.so.  PyTorch supplies device memory and the current stream; the functions
+build plain C descriptors (pointer, element type, shape, strides) from tensors without
+copying them and call the C ABI declared in include/mla355.h.  If the shared library is
+missing or fails to load, every call raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LIBRARY_PATH", "MlaError", "library", "decode_paged", "decode_paged_sparse",
+    "prefill_paged", "decode_workspace_bytes", "reserve_workspace", "check_device_errors",
+    "shutdown", "version", "MASKS", "STATUS",
+]
+
+LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla355.so")
+
+MASKS = {"null": 0, "causal": 1, "sliding_window_causal": 2}
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL_ARG", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE",
+          4: "MLA_ERR_ALIGNMENT", 5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_WORKSPACE",
+          7: "MLA_ERR_HIP", 8: "MLA_ERR_VALUE"}
+DT_BF16, DT_FP8, DT_F32, DT_I32, DT_U32 = 0, 1, 2, 3, 4
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class MlaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+_LIB = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libmla355.so from this package directory (raises if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY_PATH):
+            raise MlaError(5, f"{LIBRARY_PATH} is not built (run __graft_entry__.build())")
+        lib = ctypes.CDLL(LIBRARY_PATH)
+        P = ctypes.POINTER(MlaTensor)
+        i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+        lib.mla_decode_paged.argtypes = [P, P, P, P, P, f32, i32, i32, i32, P, vp]
+        lib.mla_decode_paged_sparse.argtypes = [P, P, P, P, P, P, P, f32, i32, P, vp]
+        lib.mla_prefill_paged.argtypes = [P, P, P, P, P, P, P, P, P, f32, i32, P, vp]
+        for fn in ("mla_decode_paged", "mla_decode_paged_sparse", "mla_prefill_paged",
+                   "mla_reserve_workspace", "mla_check_device_errors"):
+            getattr(lib, fn).restype = ctypes.c_int
+        lib.mla_decode_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32, i32]
+        lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.mla_reserve_workspace.argtypes = [i32, vp, ctypes.c_size_t]
+        lib.mla_check_device_errors.argtypes = [i32, vp, ctypes.POINTER(ctypes.c_uint32)]
+        lib.mla_shutdown.argtypes = []
+        lib.mla_shutdown.restype = None
+        lib.mla_status_string.argtypes = [ctypes.c_int]
+        lib.mla_status_string.restype = ctypes.c_char_p
+        lib.mla_last_error_message.argtypes = []
+        lib.mla_last_error_message.restype = ctypes.c_char_p
+        lib.mla_version.argtypes = []
+        lib.mla_version.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = library().mla_last_error_message().decode()
+        raise MlaError(status, msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    table = {torch.bfloat16: DT_BF16, torch.float8_e4m3fn: DT_FP8, torch.uint8: DT_FP8,
+             torch.float32: DT_F32, torch.int32: DT_I32}
+    if hasattr(torch, "uint32"):
+        table[torch.uint32] = DT_U32
+    if t.dtype not in table:
+        raise MlaError(3, f"unsupported tensor dtype {t.dtype}")
+    return table[t.dtype]
+
+
+def _desc(t, as_dtype: int | None = None):
+    """A descriptor of tensor ``t`` (None -> NULL).  ``as_dtype`` reinterprets the element
+    type with the same width (int32 offsets passed as uint32)."""
+    if t is None:
+        return None
+    if t.dim() > 4:
+        raise MlaError(2, "at most 4 dimensions")
+    d = MlaTensor()
+    d.data = t.data_ptr() if t.numel() else None
+    d.dtype = _dtype_code(t) if as_dtype is None else as_dtype
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return ctypes.byref(d)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _on_gpu(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise MlaError(2, "tensors must be on the GPU")
+
+
+def _offsets(t):
+    import torch
+    if t.dtype == torch.int32:
+        return _desc(t, DT_U32)
+    return _desc(t)
+
+
+def decode_paged(q, input_row_offsets, page_table, cache_lens, latent_cache, scale,
+                 mask="causal", local_window_size=-1, num_partitions=0, out=None, stream=None):
+    """Dense MLA decode (mla_decode_paged).  q bf16 [T, H, 576]; latent_cache bf16
+    [num_pages, PS, 576]; returns out bf16 [T, H, 512] (allocated if not given)."""
+    import torch
+    _on_gpu(q, input_row_offsets, page_table, cache_lens, latent_cache, out)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
+    _check(library().mla_decode_paged(
+        _desc(q), _offsets(input_row_offsets), _desc(page_table), _desc(cache_lens),
+        _desc(latent_cache), float(scale), MASKS[mask] if isinstance(mask, str) else int(mask),
+        int(local_window_size), int(num_partitions), _desc(out), _stream(stream)))
+    return out
+
+
+def decode_paged_sparse(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices,
+                        topk_lengths, scale, num_partitions=0, out=None, stream=None):
+    """Sparse MLA decode (mla_decode_paged_sparse).  q / latent_cache fp8 e4m3 (torch
+    float8_e4m3fn or uint8 codes) or bf16; returns out bf16 [T, H, 512]."""
+    import torch
+    _on_gpu(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices, topk_lengths, out)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
+    _check(library().mla_decode_paged_sparse(
+        _desc(q), _desc(q_scale), _offsets(input_row_offsets), _desc(latent_cache),
+        _desc(cache_scale), _desc(d_indices), _desc(topk_lengths), float(scale),
+        int(num_partitions), _desc(out), _stream(stream)))
+    return out
+
+
+def prefill_paged(q, k, v, buffer_row_offsets, cache_offsets, input_row_offsets, page_table,
+                  cache_lens, latent_cache, scale, mask="causal", out=None, stream=None):
+    """Ragged MLA prefill (mla_prefill_paged); returns out bf16 [Tq, H, 128]."""
+    import torch
+    _on_gpu(q, k, v, buffer_row_offsets, cache_offsets, input_row_offsets, page_table,
+            cache_lens, latent_cache, out)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], 128), dtype=torch.bfloat16, device=q.device)
+    _check(library().mla_prefill_paged(
+        _desc(q), _desc(k), _desc(v), _offsets(buffer_row_offsets), _offsets(cache_offsets),
+        _offsets(input_row_offsets), _desc(page_table), _desc(cache_lens), _desc(latent_cache),
+        float(scale), MASKS[mask] if isinstance(mask, str) else int(mask), _desc(out),
+        _stream(stream)))
+    return out
+
+
+def decode_workspace_bytes(total_q, num_heads, num_partitions=0, device=-1) -> int:
+    return int(library().mla_decode_workspace_bytes(int(total_q), int(num_heads),
+                                                    int(num_partitions), int(device)))
+
+
+def reserve_workspace(nbytes, device=-1, stream=None) -> None:
+    _check(library().mla_reserve_workspace(int(device), _stream(stream), int(nbytes)))
+
+
+def check_device_errors(device=-1, stream=None) -> int:
+    flags = ctypes.c_uint32(0)
+    _check(library().mla_check_device_errors(int(device), _stream(stream), ctypes.byref(flags)))
+    return int(flags.value)
+
+
+def shutdown() -> None:
+    library().mla_shutdown()
+
+
+def version() -> str:
+    return library().mla_version().decode()

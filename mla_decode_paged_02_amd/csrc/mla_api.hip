@@ -1,0 +1,353 @@
+// C-ABI layer of libmla355: descriptor validation (host only, before any HIP call),
+// per-(device, stream) workspace, and kernel launches.  See include/mla355.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/mla355.h"
+#include "mla_kernels.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mla_status ok() {
+  g_msg[0] = 0;
+  return MLA_OK;
+}
+
+size_t dtype_size(int32_t d) {
+  switch (d) {
+    case MLA_DTYPE_BF16: return 2;
+    case MLA_DTYPE_FP8_E4M3: return 1;
+    case MLA_DTYPE_F32:
+    case MLA_DTYPE_I32:
+    case MLA_DTYPE_U32: return 4;
+    default: return 0;
+  }
+}
+
+// Checks a descriptor: non-null, dtype, rank, inner stride 1, outer strides and base
+// 16-byte aligned when `aligned16`.
+mla_status check_tensor(const mla_tensor* t, const char* name, int32_t dtype, int32_t ndim,
+                        bool aligned16) {
+  if (!t) return fail(MLA_ERR_NULL_ARG, "%s: descriptor is NULL", name);
+  if (t->dtype != dtype) return fail(MLA_ERR_DTYPE, "%s: dtype %d, expected %d", name, t->dtype, dtype);
+  if (t->ndim != ndim) return fail(MLA_ERR_SHAPE, "%s: rank %d, expected %d", name, t->ndim, ndim);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(MLA_ERR_SHAPE, "%s: negative extent in dim %d", name, i);
+  bool empty = false;
+  for (int i = 0; i < ndim; ++i) empty |= t->shape[i] == 0;
+  if (!t->data && !empty) return fail(MLA_ERR_NULL_ARG, "%s: data pointer is NULL", name);
+  if (t->shape[ndim - 1] > 1 && t->stride[ndim - 1] != 1)
+    return fail(MLA_ERR_SHAPE, "%s: innermost dimension must be contiguous", name);
+  const size_t es = dtype_size(dtype);
+  if (aligned16) {
+    if ((uintptr_t)t->data % 16) return fail(MLA_ERR_ALIGNMENT, "%s: base pointer not 16-byte aligned", name);
+    for (int i = 0; i < ndim - 1; ++i)
+      if (t->shape[i] > 1 && ((size_t)t->stride[i] * es) % 16)
+        return fail(MLA_ERR_ALIGNMENT, "%s: stride of dim %d not a multiple of 16 bytes", name, i);
+  } else if ((uintptr_t)t->data % es) {
+    return fail(MLA_ERR_ALIGNMENT, "%s: base pointer not element aligned", name);
+  }
+  for (int i = 0; i < ndim - 1; ++i)
+    if (t->shape[i] > 1 && t->stride[i] < 0) return fail(MLA_ERR_SHAPE, "%s: negative stride", name);
+  return MLA_OK;
+}
+
+mla_status check_1d(const mla_tensor* t, const char* name, int32_t dtype, int64_t n) {
+  mla_status s = check_tensor(t, name, dtype, 1, false);
+  if (s != MLA_OK) return s;
+  if (t->shape[0] != n) return fail(MLA_ERR_SHAPE, "%s: length %lld, expected %lld", name, (long long)t->shape[0], (long long)n);
+  return MLA_OK;
+}
+
+bool supported_heads(int64_t h) { return h == 16 || h == 32 || h == 64 || h == 128; }
+
+// ---------------------------------------------------------------------------------------
+// workspace: one grow-only buffer per (device, stream)
+// ---------------------------------------------------------------------------------------
+constexpr size_t kZeroRowBytes = 4096;  // the zero row (>= 1152 bytes) and the error word
+constexpr size_t kErrOffset = 2048;
+
+struct Workspace {
+  void* base = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+std::map<int, int> g_cu_count;
+
+int current_device() {
+  int d = 0;
+  (void)hipGetDevice(&d);
+  return d;
+}
+
+int cu_count(int device) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = g_cu_count.find(device);
+  if (it != g_cu_count.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0) n = 256;
+  g_cu_count[device] = n;
+  return n;
+}
+
+mla_status grow_workspace(int device, void* stream, size_t need, bool capturing, void** out_base) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace& w = g_ws[{device, stream}];
+  need += kZeroRowBytes;
+  if (w.bytes >= need) {
+    *out_base = w.base;
+    return MLA_OK;
+  }
+  if (capturing)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed while the stream is capturing; reserve it first", need);
+  if (w.base) {
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess || hipFree(w.base) != hipSuccess)
+      return fail(MLA_ERR_HIP, "could not release the old workspace");
+    w.base = nullptr;
+    w.bytes = 0;
+  }
+  size_t bytes = need + need / 4;  // headroom so slowly growing calls do not reallocate
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) return fail(MLA_ERR_WORKSPACE, "hipMalloc(%zu) failed", bytes);
+  // the zero row and the error word must start cleared; the rest needs no initial value
+  if (hipMemset(p, 0, kZeroRowBytes) != hipSuccess) {
+    (void)hipFree(p);
+    return fail(MLA_ERR_HIP, "hipMemset of the workspace header failed");
+  }
+  w.base = p;
+  w.bytes = bytes;
+  *out_base = p;
+  return MLA_OK;
+}
+
+mla_status stream_capturing(void* stream, bool* capturing) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing((hipStream_t)stream, &st) != hipSuccess)
+    return fail(MLA_ERR_HIP, "hipStreamIsCapturing failed");
+  *capturing = st != hipStreamCaptureStatusNone;
+  return MLA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct DecodeLayout {
+  size_t part_o, part_lse, meta, total;
+};
+
+DecodeLayout decode_layout(int64_t T, int32_t H, int32_t nparts, int32_t grid) {
+  const size_t slots = mla::decode_slots(T, nparts, grid);
+  DecodeLayout L;
+  L.part_o = 0;
+  L.part_lse = align256(slots * (size_t)H * 512 * sizeof(float));
+  L.meta = L.part_lse + align256(slots * (size_t)H * sizeof(float));
+  L.total = L.meta + align256((2 + 2 * (size_t)T) * sizeof(int32_t));
+  return L;
+}
+
+}  // namespace
+
+namespace mla {
+size_t decode_workspace_bytes(int64_t T, int32_t H, int32_t nparts, int32_t grid) {
+  return decode_layout(T, H, nparts, grid).total;
+}
+}  // namespace mla
+
+extern "C" {
+
+const char* mla_version(void) { return "libmla355 0.1 (gfx950)"; }
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL_ARG: return "null argument";
+    case MLA_ERR_SHAPE: return "shape mismatch";
+    case MLA_ERR_DTYPE: return "wrong element type";
+    case MLA_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_WORKSPACE: return "workspace unavailable";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_VALUE: return "scalar argument out of range";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_error_message(void) { return g_msg; }
+
+size_t mla_decode_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t num_partitions, int32_t device) {
+  const int dev = device < 0 ? current_device() : device;
+  const int grid = cu_count(dev);
+  return decode_layout(total_q, num_heads, num_partitions > 0 ? num_partitions : 0, grid).total + kZeroRowBytes;
+}
+
+mla_status mla_reserve_workspace(int32_t device, void* stream, size_t bytes) {
+  const int dev = device < 0 ? current_device() : device;
+  bool cap = false;
+  mla_status s = stream_capturing(stream, &cap);
+  if (s != MLA_OK) return s;
+  if (cap) return fail(MLA_ERR_WORKSPACE, "cannot reserve workspace while the stream is capturing");
+  void* base = nullptr;
+  const size_t need = bytes > kZeroRowBytes ? bytes - kZeroRowBytes : 0;
+  s = grow_workspace(dev, stream, need, false, &base);
+  return s == MLA_OK ? ok() : s;
+}
+
+mla_status mla_check_device_errors(int32_t device, void* stream, uint32_t* flags) {
+  if (!flags) return fail(MLA_ERR_NULL_ARG, "flags is NULL");
+  *flags = 0;
+  const int dev = device < 0 ? current_device() : device;
+  void* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end()) return ok();
+    base = it->second.base;
+  }
+  uint32_t v = 0;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
+      hipMemcpy(&v, (char*)base + kErrOffset, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset((char*)base + kErrOffset, 0, 4) != hipSuccess)
+    return fail(MLA_ERR_HIP, "reading the device error word failed");
+  *flags = v;
+  return ok();
+}
+
+void mla_shutdown(void) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (auto& kv : g_ws) {
+    if (kv.second.base) {
+      int cur = 0;
+      (void)hipGetDevice(&cur);
+      (void)hipSetDevice(kv.first.first);
+      (void)hipDeviceSynchronize();
+      (void)hipFree(kv.second.base);
+      (void)hipSetDevice(cur);
+    }
+  }
+  g_ws.clear();
+}
+
+mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_offsets,
+                            const mla_tensor* page_table, const mla_tensor* cache_lens,
+                            const mla_tensor* latent_cache, float scale, int32_t mask,
+                            int32_t local_window_size, int32_t num_partitions, mla_tensor* out,
+                            void* stream) {
+  mla_status s;
+  if ((s = check_tensor(q, "q", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  const int64_t T = q->shape[0], H = q->shape[1];
+  if (q->shape[2] != 576) return fail(MLA_ERR_SHAPE, "q: head width %lld, expected 576", (long long)q->shape[2]);
+  if ((s = check_tensor(input_row_offsets, "input_row_offsets", MLA_DTYPE_U32, 1, false)) != MLA_OK) return s;
+  const int64_t B = input_row_offsets->shape[0] - 1;
+  if (B < 1) return fail(MLA_ERR_SHAPE, "input_row_offsets: needs batch + 1 >= 2 entries");
+  if ((s = check_tensor(page_table, "page_table", MLA_DTYPE_I32, 2, false)) != MLA_OK) return s;
+  if (page_table->shape[0] != B) return fail(MLA_ERR_SHAPE, "page_table: %lld rows, expected batch %lld", (long long)page_table->shape[0], (long long)B);
+  if ((s = check_1d(cache_lens, "cache_lens", MLA_DTYPE_I32, B)) != MLA_OK) return s;
+  if ((s = check_tensor(latent_cache, "latent_cache", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  if (latent_cache->shape[2] != 576) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576", (long long)latent_cache->shape[2]);
+  const int64_t PS = latent_cache->shape[1];
+  if (PS < 1) return fail(MLA_ERR_SHAPE, "latent_cache: page size must be >= 1");
+  if (latent_cache->shape[1] > 1 && latent_cache->stride[1] != 576)
+    return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride 576)");
+  if (latent_cache->shape[0] > 1 && latent_cache->stride[0] < PS * 576)
+    return fail(MLA_ERR_SHAPE, "latent_cache: pages overlap (page stride below page_size * 576)");
+  if ((s = check_tensor(out, "out", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  if (out->shape[0] != T || out->shape[1] != H || out->shape[2] != 512)
+    return fail(MLA_ERR_SHAPE, "out: shape must be [%lld, %lld, 512]", (long long)T, (long long)H);
+  if (!supported_heads(H)) return fail(MLA_ERR_UNSUPPORTED, "num_heads %lld not in {16, 32, 64, 128}", (long long)H);
+  if (mask < MLA_MASK_NULL || mask > MLA_MASK_SLIDING_WINDOW_CAUSAL) return fail(MLA_ERR_VALUE, "mask %d unknown", mask);
+  if (mask == MLA_MASK_SLIDING_WINDOW_CAUSAL && local_window_size <= 0)
+    return fail(MLA_ERR_VALUE, "sliding-window mask needs local_window_size > 0");
+  if (!std::isfinite(scale)) return fail(MLA_ERR_VALUE, "scale must be finite");
+  if (num_partitions > 4096) return fail(MLA_ERR_VALUE, "num_partitions %d above 4096", num_partitions);
+  if (page_table->shape[1] * PS > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "max_pages * page_size above 2^30");
+  if (T > (int64_t)1 << 24) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 query rows");
+  if (T == 0) return ok();
+
+  bool cap = false;
+  if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
+  const int dev = current_device();
+  const int grid = cu_count(dev);
+  const int32_t nparts = num_partitions > 0 ? num_partitions : 0;
+  const DecodeLayout L = decode_layout(T, (int32_t)H, nparts, grid);
+  void* ws = nullptr;
+  if ((s = grow_workspace(dev, stream, L.total, cap, &ws)) != MLA_OK) return s;
+  char* w = (char*)ws + kZeroRowBytes;
+
+  mla::DecodeArgs a{};
+  a.q = (const uint16_t*)q->data;
+  a.q_tok = q->stride[0];
+  a.q_head = q->stride[1];
+  a.offsets = (const uint32_t*)input_row_offsets->data;
+  a.page_table = (const int32_t*)page_table->data;
+  a.pt_row = page_table->stride[0];
+  a.cache_lens = (const int32_t*)cache_lens->data;
+  a.cache = (const uint8_t*)latent_cache->data;
+  a.page_bytes = latent_cache->stride[0] * 2;
+  a.num_pages = latent_cache->shape[0];
+  a.B = (int32_t)B;
+  a.T = (int32_t)T;
+  a.H = (int32_t)H;
+  a.PS = (int32_t)PS;
+  a.max_pages = (int32_t)page_table->shape[1];
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.mask = mask;
+  a.window = local_window_size;
+  a.nparts = nparts;
+  a.grid = grid;
+  a.out = (uint16_t*)out->data;
+  a.o_tok = out->stride[0];
+  a.o_head = out->stride[1];
+  a.part_o = (float*)(w + L.part_o);
+  a.part_lse = (float*)(w + L.part_lse);
+  a.row_meta = (int32_t*)(w + L.meta);
+  a.zero_row = (const uint8_t*)ws;
+  a.err = (uint32_t*)((char*)ws + kErrOffset);
+  const hipError_t e = mla::launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scale,
+                                   const mla_tensor* input_row_offsets,
+                                   const mla_tensor* latent_cache, const mla_tensor* cache_scale,
+                                   const mla_tensor* d_indices, const mla_tensor* topk_lengths,
+                                   float scale, int32_t num_partitions, mla_tensor* out,
+                                   void* stream) {
+  (void)q; (void)q_scale; (void)input_row_offsets; (void)latent_cache; (void)cache_scale;
+  (void)d_indices; (void)topk_lengths; (void)scale; (void)num_partitions; (void)out; (void)stream;
+  return fail(MLA_ERR_UNSUPPORTED, "sparse decode not built yet");
+}
+
+mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla_tensor* v,
+                             const mla_tensor* buffer_row_offsets, const mla_tensor* cache_offsets,
+                             const mla_tensor* input_row_offsets, const mla_tensor* page_table,
+                             const mla_tensor* cache_lens, const mla_tensor* latent_cache,
+                             float scale, int32_t mask, mla_tensor* out, void* stream) {
+  (void)q; (void)k; (void)v; (void)buffer_row_offsets; (void)cache_offsets; (void)input_row_offsets;
+  (void)page_table; (void)cache_lens; (void)latent_cache; (void)scale; (void)mask; (void)out; (void)stream;
+  return fail(MLA_ERR_UNSUPPORTED, "prefill not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// Device-side building blocks shared by the MLA kernels (gfx950 / CDNA4 only).
+//
+// Layout facts the kernels rely on (checked on the device by an in-bounds probe of the
+// builtins' lane layouts):
+//   * v_mfma_f32_16x16x32_bf16: lane l = 16*g + n holds A[n][8g..8g+7], B[8g..8g+7][n]
+//     and returns D[4g + i][n], i = 0..3.
+//   * ds_read_b64_tr_b16: within each 16-lane group, lane 16g + 4r + q supplies four
+//     16-bit values M[r][4q..4q+3]; lane 16g + j receives M[0..3][j].
+//   * global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr int kHeadDim = 576;    // latent 512 + rope 64
+constexpr int kLatentDim = 512;
+constexpr int kRowBytes = 1152;  // one bf16 cache row
+constexpr int kRowChunks = 72;   // 16-byte chunks per cache row
+constexpr int kStageKeys = 32;   // keys per pipeline stage
+constexpr int kTileKeys = 64;    // keys per scheduling tile (work-split granularity)
+constexpr int kStageBytes = kStageKeys * kRowBytes;  // 36864
+constexpr int kDmaPerStage = kStageBytes / 1024;     // 36 wave-wide 16-byte loads
+constexpr int kNumBuf = 4;       // stage buffers in LDS
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag behind
+
+enum : uint32_t {
+  kErrPageId = 1u,
+  kErrSparseIndex = 2u,
+  kErrOffsets = 4u,
+  kErrCacheLen = 8u,
+};
+
+enum : int { kMaskNull = 0, kMaskCausal = 1, kMaskSliding = 2 };
+
+// ---------------------------------------------------------------------------------------
+// LDS tile layout: stage rows of 72 16-byte chunks; chunk c of row r is stored at chunk
+// c ^ f(r) (c < 64) or c ^ (f(r) & 7) (the 8 rope chunks), which keeps the 16-byte reads
+// of the score step and the transposing reads of the value step free of bank conflicts
+// for both 32- and 64-bank LDS models.  The map is an involution.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int swz_mask(int row) {
+  int f = 0;
+  f ^= (row & 1) ? 10 : 0;
+  f ^= (row & 2) ? 4 : 0;
+  f ^= (row & 4) ? 8 : 0;
+  f ^= (row & 8) ? 15 : 0;
+  f ^= (row & 16) ? 14 : 0;
+  return f;
+}
+__device__ __forceinline__ int swz_chunk(int row, int c) {
+  const int f = swz_mask(row);
+  return c ^ (c < 64 ? f : (f & 7));
+}
+
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).  n is
+// clamped to the counter's 6-bit range; waiting for fewer outstanding loads than asked
+// is always safe.
+template <int N>
+__device__ __forceinline__ void vm_wait_imm() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void vm_wait(int n) {
+  switch (n) {
+#define MLA_VMW(k) case k: vm_wait_imm<k>(); break;
+    MLA_VMW(1) MLA_VMW(2) MLA_VMW(3) MLA_VMW(4) MLA_VMW(5) MLA_VMW(6) MLA_VMW(7) MLA_VMW(8)
+    MLA_VMW(9) MLA_VMW(10) MLA_VMW(11) MLA_VMW(12) MLA_VMW(13) MLA_VMW(14) MLA_VMW(15)
+    MLA_VMW(16) MLA_VMW(17) MLA_VMW(18) MLA_VMW(19) MLA_VMW(20) MLA_VMW(21) MLA_VMW(22)
+    MLA_VMW(23) MLA_VMW(24) MLA_VMW(25) MLA_VMW(26) MLA_VMW(27) MLA_VMW(28) MLA_VMW(29)
+    MLA_VMW(30) MLA_VMW(31) MLA_VMW(32) MLA_VMW(33) MLA_VMW(34) MLA_VMW(35) MLA_VMW(36)
+    MLA_VMW(37) MLA_VMW(38) MLA_VMW(39) MLA_VMW(40) MLA_VMW(41) MLA_VMW(42) MLA_VMW(43)
+    MLA_VMW(44) MLA_VMW(45) MLA_VMW(46) MLA_VMW(47) MLA_VMW(48) MLA_VMW(49) MLA_VMW(50)
+    MLA_VMW(51) MLA_VMW(52) MLA_VMW(53) MLA_VMW(54) MLA_VMW(55) MLA_VMW(56) MLA_VMW(57)
+    MLA_VMW(58) MLA_VMW(59) MLA_VMW(60) MLA_VMW(61) MLA_VMW(62) MLA_VMW(63)
+#undef MLA_VMW
+    default:
+      if (n >= 64) vm_wait_imm<63>(); else vm_wait_imm<0>();
+      break;
+  }
+}
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((63 & 15) | (3 << 14) | (7 << 4)); }
+__device__ __forceinline__ void all_wait0() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Barrier without the compiler's implicit memory fence (the caller states the waits).
+__device__ __forceinline__ void block_barrier() { __builtin_amdgcn_s_barrier(); }
+
+// Direct global->LDS load of 16 bytes per lane (lane l lands at dst + 16*l).  Issued as
+// inline assembly so that the compiler does not treat every later LDS read as a possible
+// alias of it (it would then wait for all outstanding loads); the kernels state the
+// vmcnt waits these loads need themselves.  m0 must be set one wait state before use.
+// m0 is named as clobbered so that nothing the compiler keeps in it is assumed to survive.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, MLA_LDS void* dst_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 ds_read_tr16(const MLA_LDS void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p);
+}
+
+// Load through the constant address space: a wave-uniform address becomes a scalar
+// (SMEM) load, counted by lgkmcnt instead of vmcnt.  Only for data the kernel never
+// writes (page tables, offsets, lengths, index lists).
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max_xor16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+}  // namespace mla

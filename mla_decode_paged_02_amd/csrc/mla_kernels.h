@@ -1,0 +1,98 @@
+// Host-visible kernel argument blocks and launch entry points of libmla355.
+// Included by the C-ABI layer (validation, workspace) and by the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Dense decode over a paged bf16 latent cache.
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [T, H, 576]
+  int64_t q_tok, q_head;      // element strides
+  const uint32_t* offsets;    // [B + 1]
+  const int32_t* page_table;  // [B, max_pages]
+  int64_t pt_row;             // element stride between page-table rows
+  const int32_t* cache_lens;  // [B]
+  const uint8_t* cache;       // bf16 [num_pages, PS, 576], rows contiguous
+  int64_t page_bytes;         // byte stride between pages
+  int64_t num_pages;
+  int32_t B, T, H, PS, max_pages;
+  float scale_log2;           // scale * log2(e): logits are kept in base-2 units
+  int32_t mask, window;
+  int32_t nparts;             // 0: balanced split over `grid` work-groups; >= 1: fixed
+  int32_t grid;
+  uint16_t* out;              // bf16 [T, H, 512]
+  int64_t o_tok, o_head;
+  float* part_o;              // [slots, H, 512] partial outputs (normalised)
+  float* part_lse;            // [slots, H] log2-sum-exp of the partials
+  int32_t* row_meta;          // [2 + 2T]: total tiles, tiles per group, (start, count)/row
+  const uint8_t* zero_row;    // >= 1152 zero bytes
+  uint32_t* err;              // device error word
+};
+
+// Sparse decode: each q row lists physical cache rows to attend to.
+struct SparseArgs {
+  const uint8_t* q;           // fp8 [T, H, 576] or bf16 (q_bf16)
+  int64_t q_tok, q_head;      // element strides
+  const float* q_scale;       // [T] or null
+  const uint8_t* cache;       // fp8 or bf16 [num_pages, PS, 576]
+  int64_t page_elems;         // element stride between pages
+  const float* cache_scale;   // [num_pages, PS] (page stride cs_page) or null
+  int64_t cs_page;
+  int64_t num_pages;
+  int32_t PS;
+  const int32_t* idx;         // [T, stride]
+  int64_t idx_row;            // element stride between index rows
+  int32_t idx_cols;           // shape[1] of d_indices
+  const int32_t* topk;        // [T]
+  int32_t T, H;
+  int32_t q_bf16, c_bf16;     // element types (1 = bf16, 0 = fp8 e4m3)
+  float scale_log2;
+  int32_t nparts;             // 0: balanced; >= 1 fixed
+  int32_t grid;
+  uint16_t* out;
+  int64_t o_tok, o_head;
+  float* part_o;
+  float* part_lse;
+  int32_t* row_meta;
+  uint32_t* err;
+};
+
+// Ragged prefill with per-head keys and values.
+struct PrefillArgs {
+  const uint16_t* q;          // bf16 [Tq, H, 192]
+  int64_t q_tok, q_head;
+  const uint16_t* k;          // bf16 [Tk, H, 128]
+  int64_t k_tok, k_head;
+  const uint16_t* v;          // bf16 [Tk, H, 128]
+  int64_t v_tok, v_head;
+  const uint32_t* buf_off;    // [B + 1]
+  const uint32_t* cache_off;  // [B]
+  const uint32_t* in_off;     // [B + 1]
+  const int32_t* page_table;
+  int64_t pt_row;
+  const int32_t* cache_lens;
+  const uint8_t* cache;       // bf16 latent cache (rope columns 512..575 used)
+  int64_t page_bytes;
+  int64_t num_pages;
+  int32_t B, Tq, Tk, H, PS, max_pages;
+  float scale_log2;
+  int32_t mask;
+  uint16_t* out;              // bf16 [Tq, H, 128]
+  int64_t o_tok, o_head;
+  uint32_t* err;
+};
+
+// Workspace needs of the split-KV paths.
+size_t decode_slots(int64_t T, int32_t nparts, int32_t grid);
+size_t decode_workspace_bytes(int64_t T, int32_t H, int32_t nparts, int32_t grid);
+
+// Launchers (return the HIP status of the launches).
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,114 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and rejects
+malformed descriptors before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_decode_paged_02_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla355.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m.library()
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in m.version()
+    lib = m.library()
+    assert lib.mla_status_string(0) == b"ok"
+    assert lib.mla_status_string(5) == b"unsupported configuration"
+
+
+def _t(data=None, dtype=0, shape=(), stride=None):
+    d = m.MlaTensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if stride is None:
+        stride, acc = [], 1
+        for s in reversed(shape):
+            stride.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, stride)):
+        d.shape[i] = s
+        d.stride[i] = st
+    return d
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced by validation
+
+
+def decode_args(**over):
+    T, H, B, PS = 4, 16, 2, 64
+    a = dict(q=_t(FAKE, 0, (T, H, 576)), off=_t(FAKE, 4, (B + 1,)), pt=_t(FAKE, 3, (B, 8)),
+             lens=_t(FAKE, 3, (B,)), cache=_t(FAKE, 0, (10, PS, 576)),
+             out=_t(FAKE, 0, (T, H, 512)), scale=0.07, mask=1, window=-1, parts=0)
+    a.update(over)
+    return a
+
+
+def call_decode(a):
+    lib = m.library()
+    ref = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    st = lib.mla_decode_paged(ref(a["q"]), ref(a["off"]), ref(a["pt"]), ref(a["lens"]),
+                              ref(a["cache"]), a["scale"], a["mask"], a["window"], a["parts"],
+                              ref(a["out"]), None)
+    return st, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1),
+    (dict(q=_t(None, 0, (4, 16, 576))), 1),
+    (dict(q=_t(FAKE, 2, (4, 16, 576))), 3),
+    (dict(q=_t(FAKE, 0, (4, 16, 512))), 2),
+    (dict(q=_t(FAKE + 2, 0, (4, 16, 576))), 4),
+    (dict(q=_t(FAKE, 0, (4, 24, 576)), out=_t(FAKE, 0, (4, 24, 512))), 5),
+    (dict(off=_t(FAKE, 4, (1,))), 2),
+    (dict(pt=_t(FAKE, 3, (3, 8))), 2),
+    (dict(lens=_t(FAKE, 3, (5,))), 2),
+    (dict(cache=_t(FAKE, 0, (10, 64, 512))), 2),
+    (dict(cache=_t(FAKE, 0, (10, 64, 576), stride=(64 * 584, 584, 1))), 2),
+    (dict(cache=_t(FAKE, 0, (10, 64, 576), stride=(32 * 576, 576, 1))), 2),
+    (dict(out=_t(FAKE, 0, (4, 16, 576))), 2),
+    (dict(mask=7), 8),
+    (dict(mask=2, window=0), 8),
+    (dict(scale=float("nan")), 8),
+    (dict(parts=5000), 8),
+])
+def test_decode_validation_errors(over, status):
+    st, msg = call_decode(decode_args(**over))
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_decode_empty_batch_is_ok_without_gpu():
+    st, msg = call_decode(decode_args(q=_t(FAKE, 0, (0, 16, 576)), out=_t(FAKE, 0, (0, 16, 512))))
+    assert st == 0, msg
+
+
+def test_workspace_size_grows_with_partitions():
+    small = m.decode_workspace_bytes(64, 128, 1)
+    big = m.decode_workspace_bytes(64, 128, 8)
+    assert big > small > 0
+    assert m.decode_workspace_bytes(64, 128, 0) >= 2 * 256 * 128 * 512 * 4
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros((1, 16, 576), dtype=torch.bfloat16)
+    with pytest.raises(m.MlaError):
+        m.decode_paged(q, q, q, q, q, 0.1)
