@@ -175,6 +175,14 @@ mla_status mla_reserve_workspace(int32_t device, void* stream, size_t bytes);
  * max_pages * PS.  *flags receives the word (0 = clean). */
 mla_status mla_check_device_errors(int32_t device, void* stream, uint32_t* flags);
 
+/* Kernel timing for measurement tools.  While enabled, every call brackets its main
+ * kernel (the attention kernel, not the combine) with two HIP events recorded on the
+ * call's stream; mla_profile_read synchronises those events, returns the summed
+ * milliseconds and the number of bracketed launches, and forgets them.  Leave it
+ * disabled (the default) in graph-captured code.  Host-side bookkeeping only. */
+mla_status mla_profile_enable(int32_t enable);
+mla_status mla_profile_read(double* total_ms, int64_t* launches);
+
 /* Free every workspace the library holds (all devices, all streams). */
 void mla_shutdown(void);
 

@@ -14,7 +14,7 @@ import os
 __all__ = [
     "LIBRARY_PATH", "MlaError", "library", "decode_paged", "decode_paged_sparse",
     "prefill_paged", "decode_workspace_bytes", "reserve_workspace", "check_device_errors",
-    "shutdown", "version", "MASKS", "STATUS",
+    "shutdown", "version", "profile_enable", "profile_read", "MASKS", "STATUS",
 ]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla355.so")
@@ -59,6 +59,10 @@ def library() -> ctypes.CDLL:
         lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.mla_reserve_workspace.argtypes = [i32, vp, ctypes.c_size_t]
         lib.mla_check_device_errors.argtypes = [i32, vp, ctypes.POINTER(ctypes.c_uint32)]
+        lib.mla_profile_enable.argtypes = [i32]
+        lib.mla_profile_enable.restype = ctypes.c_int
+        lib.mla_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        lib.mla_profile_read.restype = ctypes.c_int
         lib.mla_shutdown.argtypes = []
         lib.mla_shutdown.restype = None
         lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -184,6 +188,18 @@ def check_device_errors(device=-1, stream=None) -> int:
     flags = ctypes.c_uint32(0)
     _check(library().mla_check_device_errors(int(device), _stream(stream), ctypes.byref(flags)))
     return int(flags.value)
+
+
+def profile_enable(enable: bool = True) -> None:
+    """Bracket each call's main kernel with HIP events on the call's stream."""
+    _check(library().mla_profile_enable(1 if enable else 0))
+
+
+def profile_read() -> tuple[float, int]:
+    """(summed milliseconds, launches) of the bracketed kernels since the last read."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(library().mla_profile_read(ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)
 
 
 def shutdown() -> None:

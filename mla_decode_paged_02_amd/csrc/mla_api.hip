@@ -9,6 +9,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/mla355.h"
 #include "mla_kernels.h"
@@ -149,6 +150,36 @@ mla_status stream_capturing(void* stream, bool* capturing) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// ---------------------------------------------------------------------------------------
+// optional kernel timing
+// ---------------------------------------------------------------------------------------
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<mla::KernelTimer> g_prof_events;
+
+// Returns a timer to pass to a launcher, or null when timing is off.
+mla::KernelTimer* profile_timer(mla::KernelTimer* slot) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return nullptr;
+  if (hipEventCreate(&slot->start) != hipSuccess) return nullptr;
+  if (hipEventCreate(&slot->stop) != hipSuccess) {
+    (void)hipEventDestroy(slot->start);
+    return nullptr;
+  }
+  return slot;
+}
+
+void profile_keep(mla::KernelTimer* t, bool launched) {
+  if (!t) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (launched) {
+    g_prof_events.push_back(*t);
+  } else {
+    (void)hipEventDestroy(t->start);
+    (void)hipEventDestroy(t->stop);
+  }
+}
+
 struct DecodeLayout {
   size_t part_o, part_lse, meta, total;
 };
@@ -227,6 +258,35 @@ mla_status mla_check_device_errors(int32_t device, void* stream, uint32_t* flags
       hipMemset((char*)base + kErrOffset, 0, 4) != hipSuccess)
     return fail(MLA_ERR_HIP, "reading the device error word failed");
   *flags = v;
+  return ok();
+}
+
+mla_status mla_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+  return ok();
+}
+
+mla_status mla_profile_read(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(MLA_ERR_NULL_ARG, "output pointers are NULL");
+  std::vector<mla::KernelTimer> ev;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    ev.swap(g_prof_events);
+  }
+  double sum = 0.0;
+  bool bad = false;
+  for (auto& t : ev) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess)
+      bad = true;
+    sum += ms;
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  *total_ms = sum;
+  *launches = (int64_t)ev.size();
+  if (bad) return fail(MLA_ERR_HIP, "reading kernel timing events failed");
   return ok();
 }
 
@@ -320,7 +380,10 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
   a.row_meta = (int32_t*)(w + L.meta);
   a.zero_row = (const uint8_t*)ws;
   a.err = (uint32_t*)((char*)ws + kErrOffset);
-  const hipError_t e = mla::launch_decode(a, (hipStream_t)stream);
+  mla::KernelTimer tslot;
+  mla::KernelTimer* timer = profile_timer(&tslot);
+  const hipError_t e = mla::launch_decode(a, (hipStream_t)stream, timer);
+  profile_keep(timer, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -554,8 +554,9 @@ static hipError_t launch_decode_h(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const KernelTimer* timer) {
   hipError_t e;
+  if (timer && (e = hipEventRecord(timer->start, stream)) != hipSuccess) return e;
   switch (a.H) {
     case 128: e = launch_decode_h<2, 4>(a, stream); break;
     case 64: e = launch_decode_h<1, 4>(a, stream); break;
@@ -564,6 +565,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  if (timer && (e = hipEventRecord(timer->stop, stream)) != hipSuccess) return e;
   if (a.nparts == 0 || a.nparts > 1) {
     hipLaunchKernelGGL(mla_combine_kernel, dim3(a.T * (a.H / 4)), dim3(256), 0, stream, a);
     e = hipGetLastError();

@@ -90,9 +90,14 @@ struct PrefillArgs {
 size_t decode_slots(int64_t T, int32_t nparts, int32_t grid);
 size_t decode_workspace_bytes(int64_t T, int32_t H, int32_t nparts, int32_t grid);
 
+// Optional events bracketing the main kernel of a launch (null = none).
+struct KernelTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Launchers (return the HIP status of the launches).
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const KernelTimer* timer);
+hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream, const KernelTimer* timer);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, const KernelTimer* timer);
 
 }  // namespace mla
