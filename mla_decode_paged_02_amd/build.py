@@ -23,12 +23,8 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  The decode kernel keeps its 256 accumulator registers per lane
-# in the accumulation file and everything else in ordinary registers; selecting the
-# VGPR form of MFMA lets the register allocator place the score accumulators there.
-EXTRA = {
-    "mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-}
+# Per-source extra flags (none at present).
+EXTRA = {}
 
 
 def sources():

@@ -90,8 +90,9 @@ __device__ __forceinline__ void vm_wait(int n) {
 __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((63 & 15) | (3 << 14) | (7 << 4)); }
 __device__ __forceinline__ void all_wait0() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Barrier without the compiler's implicit memory fence (the caller states the waits).
-__device__ __forceinline__ void block_barrier() { __builtin_amdgcn_s_barrier(); }
+// Barrier that also keeps the compiler from moving memory accesses across it, without
+// the hardware fence __syncthreads adds (the caller states the waits it needs).
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Direct global->LDS load of 16 bytes per lane (lane l lands at dst + 16*l).  Issued as
 // inline assembly so that the compiler does not treat every later LDS read as a possible

@@ -86,6 +86,18 @@ struct PrefillArgs {
   uint32_t* err;
 };
 
+// Where the decode kernels put split rows' partial results (see mla_plan.h).
+struct SplitPlan {
+  int32_t T, H;
+  int32_t nparts;     // 0 = balanced, >= 1 fixed
+  int32_t grid;       // work-groups of the balanced mode
+  uint16_t* out;      // bf16 [T, H, 512]
+  int64_t o_tok, o_head;
+  float* part_o;      // [slots, H, 512]
+  float* part_lse;    // [slots, H]
+  int32_t* row_meta;  // [2 + 2T]: total tiles, tiles per work-group, (first tile, count) per row
+};
+
 // Workspace needs of the split-KV paths.
 size_t decode_slots(int64_t T, int32_t nparts, int32_t grid);
 size_t decode_workspace_bytes(int64_t T, int32_t H, int32_t nparts, int32_t grid);
@@ -97,6 +109,7 @@ struct KernelTimer {
 
 // Launchers (return the HIP status of the launches).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const KernelTimer* timer);
+hipError_t launch_combine(const SplitPlan& p, hipStream_t stream);
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream, const KernelTimer* timer);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, const KernelTimer* timer);
 

@@ -1,0 +1,416 @@
+// Per-wave compute of one 32-key stage held in LDS, shared by the decode kernels.
+//
+// A wave owns 16*HB heads of one query row.  With the stage's keys in LDS as bf16 rows of
+// 576 (swizzled 16-byte chunks, see swz_chunk):
+//   S^T = K Q^T   (16 keys x 16 heads MFMA tiles, 18 k-steps over the 576 columns).  The
+//                 keys of each 16-row tile are permuted -- tile u, row m reads key
+//                 8*(m/4) + 4u + m%4 -- so that the accumulator layout of S^T (lane 16g+n
+//                 holds rows 4g..4g+3, column n) is exactly the operand layout P^T needs:
+//                 lane 16g+n holds head n, keys 8g..8g+7;
+//   softmax       base-2 online softmax; the running max m is raised only when a stage's
+//                 max exceeds it by more than kRescaleSlack, so O and l are rescaled rarely
+//                 (the result is the same real number: any offset cancels in O / l);
+//   O^T += V^T P^T (512 columns x 16*HB heads, V = the first 512 columns of the same rows),
+//                 V^T fragments read with the transposing LDS load.
+#pragma once
+
+#include "mla_device.h"
+
+namespace mla {
+
+template <int HB>
+struct WaveAcc {
+  f32x4 o[32][HB];  // lane 16g+n: O^T[16cb + 4g + i][head 16hb + n]
+  float m[HB];      // running max (log2 units)
+  float l[HB];      // this lane's share of the softmax denominator
+};
+
+// Per-lane constants of the LDS access patterns.
+struct LaneGeo {
+  int gq, rowA0, rowA1, xa0, xa1, rowV0, rowV1, xv0, xv1, vhalf;
+};
+
+__device__ __forceinline__ LaneGeo make_lane_geo(int lane) {
+  LaneGeo g;
+  g.gq = lane >> 4;
+  const int ln = lane & 15;
+  g.rowA0 = 8 * (ln >> 2) + (ln & 3);  // score tile u = 0 reads this key row; u = 1 adds 4
+  g.rowA1 = g.rowA0 + 4;
+  g.xa0 = g.gq ^ swz_mask(g.rowA0);
+  g.xa1 = g.gq ^ swz_mask(g.rowA1);
+  const int vr = ln >> 2, vq = lane & 3;  // transposing-read coordinates
+  g.rowV0 = 8 * g.gq + vr;
+  g.rowV1 = g.rowV0 + 4;
+  g.xv0 = (vq >> 1) ^ swz_mask(g.rowV0);
+  g.xv1 = (vq >> 1) ^ swz_mask(g.rowV1);
+  g.vhalf = (vq & 1) * 8;
+  return g;
+}
+
+template <int HB>
+__device__ __forceinline__ void wave_acc_init(WaveAcc<HB>& acc) {
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb)
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) acc.o[cb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    acc.m[hb] = -INFINITY;
+    acc.l[hb] = 0.f;
+  }
+}
+
+// valid: bit j set when key j of the stage is visible (block-uniform).  kscale (KSCALE
+// only): per-key factors of the stage in LDS, applied to the logit and to the value row.
+template <int HB, bool KSCALE>
+__device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const bf16x8 (&qf)[HB][18],
+                                              WaveAcc<HB>& acc, uint32_t valid, float scale_log2,
+                                              const MLA_LDS float* kscale, const LaneGeo& g) {
+  // ---- S^T = K Q^T, fragments prefetched one k-step ahead
+  f32x4 sacc[2][HB];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) sacc[u][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    // Two waves share each SIMD, so each wave issues its LDS reads just before use and
+    // the other wave covers the latency.  Swizzled addresses are formed per read (one
+    // xor and one add) rather than kept in registers.
+    const MLA_LDS uint8_t* r0 = buf + g.rowA0 * kRowBytes;
+    const MLA_LDS uint8_t* r1 = buf + g.rowA1 * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      int c0, c1;
+      if (ks < 16) {
+        c0 = (4 * ks) ^ g.xa0;
+        c1 = (4 * ks) ^ g.xa1;
+      } else {
+        c0 = 64 + ((4 * (ks - 16)) ^ (g.xa0 & 7));
+        c1 = 64 + ((4 * (ks - 16)) ^ (g.xa1 & 7));
+      }
+      const bf16x8 k0 = *(const MLA_LDS bf16x8*)(r0 + c0 * 16);
+      const bf16x8 k1 = *(const MLA_LDS bf16x8*)(r1 + c1 * 16);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        sacc[0][hb] = mfma16x16x32(k0, qf[hb][ks], sacc[0][hb]);
+        sacc[1][hb] = mfma16x16x32(k1, qf[hb][ks], sacc[1][hb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- online softmax.  Lane 16g+n holds keys 8g + 4u + i for sacc[u][hb][i].
+  const bool all_valid = valid == 0xFFFFFFFFu;
+  float ks8[2][4];
+  if (KSCALE) {
+    const f32x4 a = *(const MLA_LDS f32x4*)(kscale + 8 * g.gq);
+    const f32x4 b = *(const MLA_LDS f32x4*)(kscale + 8 * g.gq + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ks8[0][i] = a[i];
+      ks8[1][i] = b[i];
+    }
+  }
+  bf16x8 pf[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    float x[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = sacc[u][hb][i] * scale_log2;
+        if (KSCALE) v *= ks8[u][i];
+        if (!all_valid) v = ((valid >> (8 * g.gq + 4 * u + i)) & 1u) ? v : -INFINITY;
+        x[u][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = wave_max_xor16_32(mx);
+    const bool need = mx > acc.m[hb] + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? mx : acc.m[hb];
+      const float alpha = fast_exp2(acc.m[hb] - m_new);  // 0 while m is -inf
+      acc.l[hb] *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) acc.o[cb][hb] *= alpha;
+      acc.m[hb] = m_new;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = x[u][i] == -INFINITY ? 0.f : fast_exp2(x[u][i] - acc.m[hb]);
+        if (KSCALE) {
+          // the value row is code * scale: fold the scale into the weight
+          pf[hb][4 * u + i] = (__bf16)(p * ks8[u][i]);
+          lsum += p;
+        } else {
+          // sum the weights as rounded for the MFMA, so a constant V column is reproduced
+          const __bf16 pb = (__bf16)p;
+          pf[hb][4 * u + i] = pb;
+          lsum += (float)pb;
+        }
+      }
+    acc.l[hb] += lsum;
+  }
+
+  // ---- O^T += V^T P^T over the stage's 32 keys
+  {
+    const MLA_LDS uint8_t* v0b = buf + g.rowV0 * kRowBytes + g.vhalf;
+    const MLA_LDS uint8_t* v1b = buf + g.rowV1 * kRowBytes + g.vhalf;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) {
+      const bf16x4 a0 = ds_read_tr16(v0b + (((2 * cb) ^ g.xv0) * 16));
+      const bf16x4 a1 = ds_read_tr16(v1b + (((2 * cb) ^ g.xv1) * 16));
+      const bf16x8 vf = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc.o[cb][hb] = mfma16x16x32(vf, pf[hb], acc.o[cb][hb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Writes the wave's heads h0 + 16hb + n of row t: final bf16 output, or the normalised
+// partial and its log2-sum-exp into `slot`.
+template <int HB>
+__device__ __forceinline__ void stage_epilogue(const WaveAcc<HB>& acc, int lane, int h0, int t, bool full,
+                                               int slot, int H, uint16_t* out, int64_t o_tok, int64_t o_head,
+                                               float* part_o, float* part_lse) {
+  const int gq = lane >> 4, ln = lane & 15;
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const float l_tot = wave_sum_xor16_32(acc.l[hb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int h = h0 + 16 * hb + ln;
+    if (full) {
+      uint16_t* orow = out + (int64_t)t * o_tok + (int64_t)h * o_head + 4 * gq;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) {
+        const uint32_t lo = (uint32_t)bf16_bits_rne(acc.o[cb][hb][0] * inv) |
+                            ((uint32_t)bf16_bits_rne(acc.o[cb][hb][1] * inv) << 16);
+        const uint32_t hi = (uint32_t)bf16_bits_rne(acc.o[cb][hb][2] * inv) |
+                            ((uint32_t)bf16_bits_rne(acc.o[cb][hb][3] * inv) << 16);
+        *(uint2*)(orow + 16 * cb) = make_uint2(lo, hi);
+      }
+    } else {
+      float* prow = part_o + ((int64_t)slot * H + h) * kLatentDim + 4 * gq;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) *(f32x4*)(prow + 16 * cb) = acc.o[cb][hb] * inv;
+      if (gq == 0) part_lse[(int64_t)slot * H + h] = l_tot > 0.f ? acc.m[hb] + __log2f(l_tot) : -INFINITY;
+    }
+  }
+}
+
+// Bits j (0..31) set for keys base + j that lie in [lo, hi).
+__device__ __forceinline__ uint32_t range_bits(int base, int lo, int hi) {
+  const int a = max(0, lo - base), b = min(32, hi - base);
+  if (b <= a) return 0u;
+  const uint32_t upto = b >= 32 ? 0xFFFFFFFFu : ((1u << b) - 1u);
+  const uint32_t from = a >= 32 ? 0u : ~((1u << a) - 1u);
+  return upto & from;
+}
+
+
+// ---------------------------------------------------------------------------------------
+// Wide variant: a wave owns 32 heads (HB = 2), one wave per SIMD.  Each K fragment read
+// from LDS then feeds two MFMAs, halving LDS traffic per MFMA compared with 16-head waves.
+// O (32 heads x 512 columns, 256 registers per lane) must live in the accumulation
+// registers while the score accumulators, Q and the fragments use ordinary ones, so the
+// MFMAs are issued through inline assembly with explicit register-file constraints.  The
+// compiler does not see inside these statements, so the wait states an MFMA result needs
+// before other instructions read it are inserted explicitly (mfma_fence_*): 16 wait
+// states cover the longest MFMA-write -> VALU-read distance of the 16x16x32 shapes, and
+// ordinary-register inputs written by VALU get two wait states before an MFMA reads them.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ void mfma_v_first(f32x4& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x4& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_a(f32x4& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// Orders all later reads of the four score accumulators after enough wait states.
+__device__ __forceinline__ void mfma_fence_v4(f32x4& a, f32x4& b, f32x4& c, f32x4& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+// Two wait states between VALU writes of MFMA inputs and the MFMA reading them.
+__device__ __forceinline__ void valu_fence_v2(bf16x8& a, bf16x8& b) {
+  asm volatile("s_nop 1" : "+v"(a), "+v"(b));
+}
+// Orders later reads of accumulation registers after the MFMAs that wrote them.
+template <int N>
+__device__ __forceinline__ void mfma_fence_acc(f32x4 (&o)[N]) {
+  static_assert(N % 8 == 0, "fenced in groups of eight");
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]),
+               "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
+#pragma unroll
+  for (int i = 8; i < N; i += 8)
+    asm volatile("" : "+a"(o[i]), "+a"(o[i + 1]), "+a"(o[i + 2]), "+a"(o[i + 3]), "+a"(o[i + 4]),
+                 "+a"(o[i + 5]), "+a"(o[i + 6]), "+a"(o[i + 7]));
+}
+
+struct WaveAcc2 {
+  f32x4 o[64];  // o[2*cb + hb], lane 16g+n: O^T[16cb + 4g + i][head 16hb + n]
+  float m[2], l[2];
+};
+
+__device__ __forceinline__ void wave_acc2_init(WaveAcc2& acc) {
+#pragma unroll
+  for (int i = 0; i < 64; ++i) acc.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc.m[0] = acc.m[1] = -INFINITY;
+  acc.l[0] = acc.l[1] = 0.f;
+}
+
+template <bool KSCALE>
+__device__ __forceinline__ void stage_compute2(const MLA_LDS uint8_t* buf, const bf16x8 (&qf)[2][18],
+                                               WaveAcc2& acc, uint32_t valid, float scale_log2,
+                                               const MLA_LDS float* kscale, const LaneGeo& g) {
+  // ---- S^T = K Q^T: 2 key tiles x 2 head blocks, K fragments prefetched one k-step ahead
+  f32x4 s00, s01, s10, s11;  // s<u><hb>
+  {
+    const MLA_LDS uint8_t* r0 = buf + g.rowA0 * kRowBytes;
+    const MLA_LDS uint8_t* r1 = buf + g.rowA1 * kRowBytes;
+    auto chunk = [&](int ks, int xa) {
+      return ks < 16 ? ((4 * ks) ^ xa) : 64 + ((4 * (ks - 16)) ^ (xa & 7));
+    };
+    bf16x8 k0 = *(const MLA_LDS bf16x8*)(r0 + chunk(0, g.xa0) * 16);
+    bf16x8 k1 = *(const MLA_LDS bf16x8*)(r1 + chunk(0, g.xa1) * 16);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      bf16x8 n0 = k0, n1 = k1;
+      if (ks + 1 < 18) {
+        n0 = *(const MLA_LDS bf16x8*)(r0 + chunk(ks + 1, g.xa0) * 16);
+        n1 = *(const MLA_LDS bf16x8*)(r1 + chunk(ks + 1, g.xa1) * 16);
+      }
+      if (ks == 0) {
+        mfma_v_first(s00, k0, qf[0][0]);
+        mfma_v_first(s10, k1, qf[0][0]);
+        mfma_v_first(s01, k0, qf[1][0]);
+        mfma_v_first(s11, k1, qf[1][0]);
+      } else {
+        mfma_v(s00, k0, qf[0][ks]);
+        mfma_v(s10, k1, qf[0][ks]);
+        mfma_v(s01, k0, qf[1][ks]);
+        mfma_v(s11, k1, qf[1][ks]);
+      }
+      k0 = n0;
+      k1 = n1;
+    }
+    mfma_fence_v4(s00, s01, s10, s11);
+  }
+
+  // ---- online softmax.  Lane 16g+n holds keys 8g + 4u + i.
+  const bool all_valid = valid == 0xFFFFFFFFu;
+  float ks8[2][4];
+  if (KSCALE) {
+    const f32x4 a = *(const MLA_LDS f32x4*)(kscale + 8 * g.gq);
+    const f32x4 b = *(const MLA_LDS f32x4*)(kscale + 8 * g.gq + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ks8[0][i] = a[i];
+      ks8[1][i] = b[i];
+    }
+  }
+  bf16x8 pf[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const f32x4 su[2] = {hb == 0 ? s00 : s01, hb == 0 ? s10 : s11};
+    float x[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = su[u][i] * scale_log2;
+        if (KSCALE) v *= ks8[u][i];
+        if (!all_valid) v = ((valid >> (8 * g.gq + 4 * u + i)) & 1u) ? v : -INFINITY;
+        x[u][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = wave_max_xor16_32(mx);
+    const bool need = mx > acc.m[hb] + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      // the previous stage's last writes of O were followed by this stage's score MFMAs,
+      // far more than the wait states a read needs
+      const float m_new = need ? mx : acc.m[hb];
+      const float alpha = fast_exp2(acc.m[hb] - m_new);  // 0 while m is -inf
+      acc.l[hb] *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) acc.o[2 * cb + hb] *= alpha;
+      acc.m[hb] = m_new;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = x[u][i] == -INFINITY ? 0.f : fast_exp2(x[u][i] - acc.m[hb]);
+        if (KSCALE) {
+          pf[hb][4 * u + i] = (__bf16)(p * ks8[u][i]);
+          lsum += p;
+        } else {
+          const __bf16 pb = (__bf16)p;
+          pf[hb][4 * u + i] = pb;
+          lsum += (float)pb;
+        }
+      }
+    acc.l[hb] += lsum;
+  }
+  valu_fence_v2(pf[0], pf[1]);
+
+  // ---- O^T += V^T P^T, V fragments prefetched one column block ahead
+  {
+    const MLA_LDS uint8_t* v0b = buf + g.rowV0 * kRowBytes + g.vhalf;
+    const MLA_LDS uint8_t* v1b = buf + g.rowV1 * kRowBytes + g.vhalf;
+    bf16x4 a0 = ds_read_tr16(v0b + ((0 ^ g.xv0) * 16));
+    bf16x4 a1 = ds_read_tr16(v1b + ((0 ^ g.xv1) * 16));
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) {
+      bf16x4 n0 = a0, n1 = a1;
+      if (cb + 1 < 32) {
+        const int cc = 2 * (cb + 1);
+        n0 = ds_read_tr16(v0b + ((cc ^ g.xv0) * 16));
+        n1 = ds_read_tr16(v1b + ((cc ^ g.xv1) * 16));
+      }
+      const bf16x8 vf = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      mfma_a(acc.o[2 * cb], vf, pf[0]);
+      mfma_a(acc.o[2 * cb + 1], vf, pf[1]);
+      a0 = n0;
+      a1 = n1;
+    }
+  }
+}
+
+__device__ __forceinline__ void stage_epilogue2(WaveAcc2& acc, int lane, int h0, int t, bool full, int slot,
+                                                int H, uint16_t* out, int64_t o_tok, int64_t o_head,
+                                                float* part_o, float* part_lse) {
+  mfma_fence_acc(acc.o);
+  const int gq = lane >> 4, ln = lane & 15;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const float l_tot = wave_sum_xor16_32(acc.l[hb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int h = h0 + 16 * hb + ln;
+    if (full) {
+      uint16_t* orow = out + (int64_t)t * o_tok + (int64_t)h * o_head + 4 * gq;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) {
+        const f32x4 v = acc.o[2 * cb + hb];
+        const uint32_t lo = (uint32_t)bf16_bits_rne(v[0] * inv) | ((uint32_t)bf16_bits_rne(v[1] * inv) << 16);
+        const uint32_t hi = (uint32_t)bf16_bits_rne(v[2] * inv) | ((uint32_t)bf16_bits_rne(v[3] * inv) << 16);
+        *(uint2*)(orow + 16 * cb) = make_uint2(lo, hi);
+      }
+    } else {
+      float* prow = part_o + ((int64_t)slot * H + h) * kLatentDim + 4 * gq;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) *(f32x4*)(prow + 16 * cb) = acc.o[2 * cb + hb] * inv;
+      if (gq == 0) part_lse[(int64_t)slot * H + h] = l_tot > 0.f ? acc.m[hb] + __log2f(l_tot) : -INFINITY;
+    }
+  }
+}
+
+}  // namespace mla
