@@ -33,11 +33,12 @@
  *     outside the pool, non-monotone offsets) never causes an out-of-bounds access:
  *     the offending rows contribute nothing and a bit is set in the device error word
  *     read by mla_check_device_errors().
- *   - Workspace (split-KV partial results and per-row metadata) is owned by the
+ *   - Workspace (split-KV partial results and the split table) is owned by the
  *     library, one grow-only buffer per (device, stream).  It is allocated on first
  *     use; a call issued while `stream` is capturing a graph must find it already large
  *     enough (see mla_reserve_workspace), else it returns MLA_ERR_WORKSPACE.  Calls on
  *     one stream are ordered, so they may share that stream's workspace.
+ *   - At most 2^24 query rows per call.
  */
 #ifndef MLA355_H_
 #define MLA355_H_

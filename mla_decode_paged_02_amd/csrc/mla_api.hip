@@ -84,6 +84,8 @@ bool supported_heads(int64_t h) { return h == 16 || h == 32 || h == 64 || h == 1
 // ---------------------------------------------------------------------------------------
 constexpr size_t kZeroRowBytes = 4096;  // the zero row (>= 1152 bytes) and the error word
 constexpr size_t kErrOffset = 2048;
+constexpr size_t kHeaderBytes = kZeroRowBytes;
+constexpr int64_t kMaxRows = (int64_t)1 << 24;
 
 struct Workspace {
   void* base = nullptr;
@@ -113,7 +115,7 @@ int cu_count(int device) {
 mla_status grow_workspace(int device, void* stream, size_t need, bool capturing, void** out_base) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Workspace& w = g_ws[{device, stream}];
-  need += kZeroRowBytes;
+  need += kHeaderBytes;
   if (w.bytes >= need) {
     *out_base = w.base;
     return MLA_OK;
@@ -130,7 +132,7 @@ mla_status grow_workspace(int device, void* stream, size_t need, bool capturing,
   void* p = nullptr;
   if (hipMalloc(&p, bytes) != hipSuccess) return fail(MLA_ERR_WORKSPACE, "hipMalloc(%zu) failed", bytes);
   // the zero row and the error word must start cleared; the rest needs no initial value
-  if (hipMemset(p, 0, kZeroRowBytes) != hipSuccess) {
+  if (hipMemset(p, 0, kHeaderBytes) != hipSuccess) {
     (void)hipFree(p);
     return fail(MLA_ERR_HIP, "hipMemset of the workspace header failed");
   }
@@ -180,6 +182,7 @@ void profile_keep(mla::KernelTimer* t, bool launched) {
   }
 }
 
+// Past the header: the split rows' parts (bf16), their log2-sum-exps and the split table.
 struct DecodeLayout {
   size_t part_o, part_lse, meta, total;
 };
@@ -188,7 +191,7 @@ DecodeLayout decode_layout(int64_t T, int32_t H, int32_t nparts, int32_t grid) {
   const size_t slots = mla::decode_slots(T, nparts, grid);
   DecodeLayout L;
   L.part_o = 0;
-  L.part_lse = align256(slots * (size_t)H * 512 * sizeof(float));
+  L.part_lse = align256(slots * (size_t)H * 512 * sizeof(uint16_t));
   L.meta = L.part_lse + align256(slots * (size_t)H * sizeof(float));
   L.total = L.meta + align256((2 + 2 * (size_t)T) * sizeof(int32_t));
   return L;
@@ -226,7 +229,7 @@ const char* mla_last_error_message(void) { return g_msg; }
 size_t mla_decode_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t num_partitions, int32_t device) {
   const int dev = device < 0 ? current_device() : device;
   const int grid = cu_count(dev);
-  return decode_layout(total_q, num_heads, num_partitions > 0 ? num_partitions : 0, grid).total + kZeroRowBytes;
+  return decode_layout(total_q, num_heads, num_partitions > 0 ? num_partitions : 0, grid).total + kHeaderBytes;
 }
 
 mla_status mla_reserve_workspace(int32_t device, void* stream, size_t bytes) {
@@ -236,7 +239,7 @@ mla_status mla_reserve_workspace(int32_t device, void* stream, size_t bytes) {
   if (s != MLA_OK) return s;
   if (cap) return fail(MLA_ERR_WORKSPACE, "cannot reserve workspace while the stream is capturing");
   void* base = nullptr;
-  const size_t need = bytes > kZeroRowBytes ? bytes - kZeroRowBytes : 0;
+  const size_t need = bytes > kHeaderBytes ? bytes - kHeaderBytes : 0;
   s = grow_workspace(dev, stream, need, false, &base);
   return s == MLA_OK ? ok() : s;
 }
@@ -338,7 +341,7 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
   if (!std::isfinite(scale)) return fail(MLA_ERR_VALUE, "scale must be finite");
   if (num_partitions > 4096) return fail(MLA_ERR_VALUE, "num_partitions %d above 4096", num_partitions);
   if (page_table->shape[1] * PS > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "max_pages * page_size above 2^30");
-  if (T > (int64_t)1 << 24) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 query rows");
+  if (T > kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 query rows");
   if (T == 0) return ok();
 
   bool cap = false;
@@ -349,7 +352,7 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
   const DecodeLayout L = decode_layout(T, (int32_t)H, nparts, grid);
   void* ws = nullptr;
   if ((s = grow_workspace(dev, stream, L.total, cap, &ws)) != MLA_OK) return s;
-  char* w = (char*)ws + kZeroRowBytes;
+  char* w = (char*)ws + kHeaderBytes;
 
   mla::DecodeArgs a{};
   a.q = (const uint16_t*)q->data;
@@ -375,7 +378,7 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
   a.out = (uint16_t*)out->data;
   a.o_tok = out->stride[0];
   a.o_head = out->stride[1];
-  a.part_o = (float*)(w + L.part_o);
+  a.part_o = (uint16_t*)(w + L.part_o);
   a.part_lse = (float*)(w + L.part_lse);
   a.row_meta = (int32_t*)(w + L.meta);
   a.zero_row = (const uint8_t*)ws;

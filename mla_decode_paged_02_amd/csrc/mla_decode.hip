@@ -1,5 +1,5 @@
-// Dense MLA decode over a paged bf16 latent cache, and the log-sum-exp combine of
-// split-KV partial results (gfx950).
+// Dense MLA decode over a paged bf16 latent cache, and the log-sum-exp combine of rows
+// split over several work-groups (split-KV) (gfx950).
 //
 // What is computed follows generic_flare_mla_decode_kv_cache_ragged (summary; Args q,
 // input_row_offsets, scale, output, num_partitions_in; Parameters mask_str,
@@ -12,6 +12,8 @@
 // (4 buffers, 3 in flight) by direct global->LDS loads; the stage's page id is fetched
 // with a scalar load one stage ahead.  The work split is in mla_plan.h, the per-stage
 // MFMA / softmax work in mla_stage.h.
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "mla_plan.h"
@@ -91,13 +93,21 @@ __device__ __forceinline__ void decode_fill(const DecodeArgs& a, PlanLds& L) {
 
 // ---------------------------------------------------------------------------------------
 // One row segment: tiles [ta, tc) (relative to the row's first visible tile) of row t.
-// KPAGES = 1: PS is a multiple of 32, so a stage lies in one page whose id is fetched with
-// a scalar load one stage ahead; KPAGES = 0: any other page size (page ids fetched per
-// lane, which serialises the stage loads).
+//
+// Page ids reach the stage loop through an LDS window of kPidWindow consecutive page-table
+// entries (refilled, after draining the loads in flight, when a segment outruns it).  A
+// scalar load would be cheaper to issue, but scalar loads complete out of order, so one in
+// flight turns every LDS-read wait of the stage compute into a full wait for it.
+// KPAGES = 1: PS is a multiple of 32, so a stage lies in one page, read one stage ahead;
+// KPAGES = 0: any other page size, each lane looks up the page of its own key.
 // ---------------------------------------------------------------------------------------
+constexpr int kPidWindow = 1024;
+static_assert(sizeof(PlanLds::scan) == kPidWindow * sizeof(int), "the window lives in the planning scratch");
+
 template <int HB, int NW, int KPAGES>
-__device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint8_t* tiles, int t,
-                                               const RowGeo& g, int ta, int tc, bool full, int slot) {
+__device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint8_t* tiles, MLA_LDS int* pids,
+                                               int t, const RowGeo& g, int ta, int tc, bool full, int slot) {
+  constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int gq = lane >> 4, ln = lane & 15;
@@ -114,16 +124,95 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
   const int nst = (khi - 1) / kStageKeys - s_first + 1;
   const int32_t* pt = a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.pt_row;
 
-  // every wave must be done with the previous segment's buffers
+  const int p_last = (khi - 1) / a.PS;  // last logical page of the segment
+
+  // every wave must be done with the previous segment's buffers and page window
   all_wait0();
   stage_barrier();
 
+  // ---- page-id window [pbase, pbase + kPidWindow): loads issued here, stored to LDS by
+  // the caller once they have landed (entries past the segment read as -1)
+  int pbase = klo / a.PS;
+  int pv[kPidWindow / NT];
+  auto window_load = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPidWindow / NT; ++i) {
+      const int p = pbase + tid + i * NT;
+      pv[i] = p <= p_last ? pt[p] : -1;
+    }
+  };
+  auto window_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPidWindow / NT; ++i) pids[tid + i * NT] = pv[i];
+  };
+  // moves the window to start at page `base` (block-uniform call; drains the stage loads)
+  auto window_move = [&](int base) {
+    all_wait0();
+    stage_barrier();
+    pbase = base;
+    window_load();
+    all_wait0();
+    window_store();
+    lgkm_wait0();
+    stage_barrier();
+  };
+  if (KPAGES == 0) {
+    // the per-lane lookups of the prologue's stages need the window already
+    window_load();
+    all_wait0();
+    window_store();
+    lgkm_wait0();
+    stage_barrier();
+  }
+
+  // Byte offset of each of this lane's stage loads within a block of 32 consecutive cache
+  // rows: fixed per lane, so a stage that lies wholly inside one valid page costs one
+  // scalar base and one load instruction per 1 KB.
+  constexpr int kDmaMax = (kDmaPerStage + NW - 1) / NW;
+  uint32_t dma_off[kDmaMax];
+#pragma unroll
+  for (int jj = 0; jj < kDmaMax; ++jj) {
+    const int sl = (jj * NW + wave) * 64 + lane;
+    const int row = sl / kRowChunks;
+    dma_off[jj] = (uint32_t)(row * kRowBytes + swz_chunk(row, sl - row * kRowChunks) * 16);
+  }
+
   bool bad_page = false;
-  auto stage_page = [&](int st) { return ld_const(pt + st * kStageKeys / a.PS); };
+  // page of stage st from the window (KPAGES = 1)
+  auto stage_page = [&](int st) {
+    const int lp = st * kStageKeys / a.PS;
+    if (lp >= pbase + kPidWindow) window_move(lp);
+    return __builtin_amdgcn_readfirstlane(pids[lp - pbase]);
+  };
+  // A stage whose keys are all visible and lie in one valid page is loaded from a scalar
+  // base: fast_base() returns it, or null when the stage needs the general path.
+  auto fast_base = [&](int st, int pa) -> const uint8_t* {
+    const int kbase = st * kStageKeys;
+    if (KPAGES != 0 && kbase >= klo && kbase + kStageKeys <= khi && pa >= 0 && (int64_t)pa < a.num_pages)
+      return a.cache + (int64_t)pa * a.page_bytes + (int64_t)(kbase - (kbase / a.PS) * a.PS) * kRowBytes;
+    return nullptr;
+  };
+  // load jj of this wave for a fast stage (no-op past the wave's share)
+  auto fast_load = [&](const uint8_t* base, MLA_LDS uint8_t* dst, int jj) {
+    const int J = jj * NW + wave;
+    if (J < kDmaPerStage) dma16_base(base, dma_off[jj], dst + J * 1024);
+  };
   auto issue = [&](int st, int bi, int pa) {
     MLA_LDS uint8_t* dst = tiles + bi * kStageBytes;
+    const uint8_t* fb = fast_base(st, pa);
+    if (fb != nullptr) {
+#pragma unroll
+      for (int jj = 0; jj < kDmaMax; ++jj) fast_load(fb, dst, jj);
+      return;
+    }
+    // general case: per-lane keys, pages and bounds (segment edges, invalid pages, page
+    // sizes that are not a multiple of the stage)
     const int kbase = st * kStageKeys;
     const int lpa = kbase / a.PS;
+    if (KPAGES == 0) {
+      const int lp_hi = (min(kbase + kStageKeys, khi) - 1) / a.PS;
+      if (lp_hi >= pbase + kPidWindow) window_move(max(kbase, klo) / a.PS);
+    }
     // the lane's slot arithmetic is redone per call (opaque copy of the lane id) rather
     // than hoisted out of the stage loop into registers
     int lane_v = lane;
@@ -141,7 +230,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
         int pid, lp;
         if (KPAGES == 0) {
           lp = key / a.PS;
-          pid = pt[lp];
+          pid = pids[lp - pbase];
         } else {
           lp = lpa;
           pid = pa;
@@ -155,10 +244,14 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
     }
   };
 
+  // ---- prologue: the first stages (KPAGES = 1: their page ids by scalar loads, which the
+  // full wait below covers), then the window for the loop
   int pa_n = 0;
   const int npro = nst < kNumBuf - 1 ? nst : kNumBuf - 1;
-  for (int k = 0; k < npro; ++k) issue(s_first + k, k, KPAGES != 0 ? stage_page(s_first + k) : 0);
-  if (KPAGES != 0 && kNumBuf - 1 < nst) pa_n = stage_page(s_first + kNumBuf - 1);
+  auto direct_page = [&](int st) { return ld_const(pt + st * kStageKeys / a.PS); };
+  for (int k = 0; k < npro; ++k) issue(s_first + k, k, KPAGES != 0 ? direct_page(s_first + k) : 0);
+  if (KPAGES != 0 && kNumBuf - 1 < nst) pa_n = direct_page(s_first + kNumBuf - 1);
+  if (KPAGES != 0) window_load();
 
   // ---- query fragments: B operand of S^T = K Q^T (lane holds q[h][32ks + 8gq .. +8]).
   // They are loaded after the prologue's LDS loads and waited for completely: the stage
@@ -175,9 +268,15 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
     }
   }
   all_wait0();
+  if (KPAGES != 0) {
+    window_store();
+    lgkm_wait0();  // made visible to the other waves by the barrier at the loop top
+  }
 
-  WaveAcc<HB> acc;
-  wave_acc_init(acc);
+  // HB = 2: one 32-head wave per SIMD with O in the accumulation registers
+  using Acc = std::conditional_t<HB == 2, WaveAcc2, WaveAcc<HB>>;
+  Acc acc;
+  if constexpr (HB == 2) wave_acc2_init(acc); else wave_acc_init(acc);
   const LaneGeo lg = make_lane_geo(lane);
 
 #pragma unroll 1
@@ -195,19 +294,37 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
         if (younger >= 2) vm_wait_imm<2 * kDlo>(); else vm_wait_imm<kDlo>();
       }
       stage_barrier();
-      const int kn = k + kNumBuf - 1;
-      if (kn < nst) {
-        issue(s_first + kn, kn % kNumBuf, pa_n);
-        if (KPAGES != 0 && kn + 1 < nst) pa_n = stage_page(s_first + kn + 1);
-      }
     }
+    // Refill the buffer stage k-1 used with stage k + kNumBuf - 1: a fast stage's loads are
+    // spread over the score k-steps of this stage's compute, any other is issued here.
+    const int kn = k + kNumBuf - 1;
+    const uint8_t* fb = nullptr;
+    MLA_LDS uint8_t* fdst = tiles + (kn % kNumBuf) * kStageBytes;
+    if (kn < nst) {
+      fb = fast_base(s_first + kn, pa_n);
+      if (fb == nullptr) issue(s_first + kn, kn % kNumBuf, pa_n);
+      if (KPAGES != 0 && kn + 1 < nst) pa_n = stage_page(s_first + kn + 1);
+    }
+    auto hook = [&](int ks) {
+      if (fb == nullptr) return;
+#pragma unroll
+      for (int jj = 0; jj < kDmaMax; ++jj)
+        if (jj * 18 / kDmaMax == ks) fast_load(fb, fdst, jj);
+    };
     const int kbase = (s_first + k) * kStageKeys;
-    stage_compute<HB, false>(tiles + (k % kNumBuf) * kStageBytes, qf, acc,
-                             range_bits(kbase, klo, khi), a.scale_log2, nullptr, lg);
+    if constexpr (HB == 2)
+      stage_compute2<false>(tiles + (k % kNumBuf) * kStageBytes, qf, acc, range_bits(kbase, klo, khi),
+                            a.scale_log2, nullptr, lg, hook);
+    else
+      stage_compute<HB, false>(tiles + (k % kNumBuf) * kStageBytes, qf, acc, range_bits(kbase, klo, khi),
+                               a.scale_log2, nullptr, lg, hook);
   }
 
   if (bad_page) atomicOr(a.err, kErrPageId);
-  stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
+  if constexpr (HB == 2)
+    stage_epilogue2(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
+  else
+    stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
 }
 
 template <int HB, int NW, int KPAGES>
@@ -219,64 +336,49 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode_kernel(const DecodeArgs
       plan, L, [&](PlanLds& l) { decode_fill<NW * 64>(a, l); },
       [&](int t) { return decode_row_geo(a, t); },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
-        decode_segment<HB, NW, KPAGES>(a, tiles, r, g, ta, tc, full, slot);
+        decode_segment<HB, NW, KPAGES>(a, tiles, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
       });
 }
 
 // ---------------------------------------------------------------------------------------
-// Combine: out = sum_c 2^(lse_c - M) O_c / sum_c 2^(lse_c - M), pieces in a fixed order.
-// Block = (row, 4 heads); thread = (head, 8 columns).
+// Combine: out = sum_c 2^(lse_c - M) O_c / sum_c 2^(lse_c - M) over the parts of a split
+// row, in a fixed order.  Block = (row, 4 heads); thread = (head, 8 columns).
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mla_combine_kernel(const SplitPlan p) {
   const int groups = p.H / 4;
   const int t = blockIdx.x / groups, hg = blockIdx.x - t * groups;
   const int h = hg * 4 + (threadIdx.x >> 6), col = (threadIdx.x & 63) * 8;
-  int c0, c1, W = 0, pre = 0;
-  if (p.nparts == 0) {
-    W = p.row_meta[1];
-    pre = p.row_meta[2 + 2 * t];
-    const int nt = p.row_meta[3 + 2 * t];
-    if (nt == 0 || W == 0) return;
-    c0 = pre / W;
-    c1 = (pre + nt - 1) / W;
-    if (c0 == c1) return;  // one work-group covered the whole row and wrote it
-  } else {
-    if (p.nparts == 1) return;
-    c0 = 0;
-    c1 = p.nparts - 1;
-  }
-  auto slot_of = [&](int c) {
-    if (p.nparts == 0) return c == c0 ? (pre == c0 * W ? 2 * c0 : 2 * c0 + 1) : 2 * c;
-    return t * p.nparts + c;
-  };
+  int n;
+  const RowSplit rs = row_split(p, t, n);
+  if (n == 0) return;  // the row was written whole (or cleared)
   float M = -INFINITY;
-  for (int c = c0; c <= c1; ++c) M = fmaxf(M, p.part_lse[(int64_t)slot_of(c) * p.H + h]);
+  for (int c = 0; c < n; ++c) M = fmaxf(M, p.part_lse[(int64_t)split_slot(rs, c) * p.H + h]);
   uint16_t* dst = p.out + (int64_t)t * p.o_tok + (int64_t)h * p.o_head + col;
-  if (M == -INFINITY) {
+  if (M == -INFINITY) {  // no part saw a key (an empty row split by a fixed count)
     *(uint4*)dst = make_uint4(0, 0, 0, 0);
     return;
   }
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float den = 0.f;
-  for (int c = c0; c <= c1; ++c) {
-    const int sl = slot_of(c);
+  for (int c = 0; c < n; ++c) {
+    const int sl = split_slot(rs, c);
     const float l = p.part_lse[(int64_t)sl * p.H + h];
     if (l == -INFINITY) continue;
     const float w = fast_exp2(l - M);
     den += w;
-    const float* src = p.part_o + ((int64_t)sl * p.H + h) * kLatentDim + col;
-    const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+    const uint4 x = *(const uint4*)(p.part_o + ((int64_t)sl * p.H + h) * kLatentDim + col);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] += w * x0[i];
-      acc[4 + i] += w * x1[i];
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += w * __builtin_bit_cast(float, xw[j] << 16);
+      acc[2 * j + 1] += w * __builtin_bit_cast(float, xw[j] & 0xFFFF0000u);
     }
   }
   const float inv = 1.f / den;
   uint32_t wd[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    wd[i] = (uint32_t)bf16_bits_rne(acc[2 * i] * inv) | ((uint32_t)bf16_bits_rne(acc[2 * i + 1] * inv) << 16);
+  for (int j = 0; j < 4; ++j)
+    wd[j] = (uint32_t)bf16_bits_rne(acc[2 * j] * inv) | ((uint32_t)bf16_bits_rne(acc[2 * j + 1] * inv) << 16);
   *(uint4*)dst = make_uint4(wd[0], wd[1], wd[2], wd[3]);
 }
 
@@ -323,8 +425,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const KernelTi
   hipError_t e;
   if (timer && (e = hipEventRecord(timer->start, stream)) != hipSuccess) return e;
   switch (a.H) {
-    case 128: e = launch_decode_h<1, 8>(a, p, stream); break;
-    case 64: e = launch_decode_h<1, 4>(a, p, stream); break;
+    case 128: e = launch_decode_h<2, 4>(a, p, stream); break;
+    case 64: e = launch_decode_h<2, 2>(a, p, stream); break;
     case 32: e = launch_decode_h<1, 2>(a, p, stream); break;
     case 16: e = launch_decode_h<1, 1>(a, p, stream); break;
     default: return hipErrorInvalidValue;

@@ -108,6 +108,16 @@ __device__ __forceinline__ void dma16(const void* src, MLA_LDS void* dst_wave_ba
                : "s"(lds), "v"(src)
                : "memory", "m0");
 }
+
+// The same load with the source split into a wave-uniform 64-bit base (scalar registers)
+// and a per-lane 32-bit byte offset, which needs no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16_base(const void* base, uint32_t off, MLA_LDS void* dst_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -128,16 +138,21 @@ __device__ __forceinline__ T ld_const(const T* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_max_xor16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Max / sum over the four lanes l, l^16, l^32, l^48, left in all four.  The lane swaps are
+// VALU instructions of gfx950: with both operands equal, permlane32_swap returns the lower
+// and the upper half of the wave in each half, permlane16_swap the even and the odd rows.
+__device__ __forceinline__ float xor16_32_pair_max(float v, bool sum) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto h = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  const float h0 = __builtin_bit_cast(float, (uint32_t)h[0]), h1 = __builtin_bit_cast(float, (uint32_t)h[1]);
+  v = sum ? h0 + h1 : fmaxf(h0, h1);
+  const uint32_t c = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+  const float r0 = __builtin_bit_cast(float, (uint32_t)r[0]), r1 = __builtin_bit_cast(float, (uint32_t)r[1]);
+  return sum ? r0 + r1 : fmaxf(r0, r1);
 }
-__device__ __forceinline__ float wave_sum_xor16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
+__device__ __forceinline__ float wave_max_xor16_32(float v) { return xor16_32_pair_max(v, false); }
+__device__ __forceinline__ float wave_sum_xor16_32(float v) { return xor16_32_pair_max(v, true); }
 
 __device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
   __bf16 b = (__bf16)f;

@@ -26,9 +26,9 @@ struct DecodeArgs {
   int32_t grid;
   uint16_t* out;              // bf16 [T, H, 512]
   int64_t o_tok, o_head;
-  float* part_o;              // [slots, H, 512] partial outputs (normalised)
+  uint16_t* part_o;           // bf16 [slots, H, 512] partial outputs (normalised)
   float* part_lse;            // [slots, H] log2-sum-exp of the partials
-  int32_t* row_meta;          // [2 + 2T]: total tiles, tiles per group, (start, count)/row
+  int32_t* row_meta;          // [2 + 2T]: the split rows' layout for the combine (mla_plan.h)
   const uint8_t* zero_row;    // >= 1152 zero bytes
   uint32_t* err;              // device error word
 };
@@ -55,7 +55,7 @@ struct SparseArgs {
   int32_t grid;
   uint16_t* out;
   int64_t o_tok, o_head;
-  float* part_o;
+  uint16_t* part_o;
   float* part_lse;
   int32_t* row_meta;
   uint32_t* err;
@@ -86,16 +86,16 @@ struct PrefillArgs {
   uint32_t* err;
 };
 
-// Where the decode kernels put split rows' partial results (see mla_plan.h).
+// Where the decode kernels put split rows' parts (mla_plan.h).
 struct SplitPlan {
   int32_t T, H;
   int32_t nparts;     // 0 = balanced, >= 1 fixed
   int32_t grid;       // work-groups of the balanced mode
   uint16_t* out;      // bf16 [T, H, 512]
   int64_t o_tok, o_head;
-  float* part_o;      // [slots, H, 512]
+  uint16_t* part_o;   // bf16 [slots, H, 512]
   float* part_lse;    // [slots, H]
-  int32_t* row_meta;  // [2 + 2T]: total tiles, tiles per work-group, (first tile, count) per row
+  int32_t* row_meta;  // [2 + 2T]: the split rows' layout (mla_plan.h)
 };
 
 // Workspace needs of the split-KV paths.

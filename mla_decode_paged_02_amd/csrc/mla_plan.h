@@ -1,13 +1,23 @@
 // Work split of the decode kernels over the GPU, shared by the dense and sparse paths.
 //
-// Every query row's visible keys are cut into 64-key tiles.  Balanced mode: each
-// work-group computes the per-row tile counts itself (no host round trip), takes an equal
-// run of the concatenated tiles and walks the rows that run touches.  Rows it covers
-// completely are written straight to the output; the at most two rows it covers in part
-// leave a normalised partial output and its log2-sum-exp in slot 2*gid (the row holding
-// the run's first tile) or 2*gid + 1 (the row holding its last tile).  Fixed mode
-// (num_partitions = P): work-group gid = (row, part) takes the part-th of P equal tile
-// ranges of its row and uses slot gid.
+// Every query row's visible keys are cut into 64-key tiles.  Each work-group computes the
+// per-row tile counts itself (no host round trip).  Three modes:
+//   row parts (balanced, when every non-empty row can have a work-group of its own): with
+//     S the smallest tile count such that sum_t ceil(nt_t / S) <= grid, row t is cut into
+//     P_t = ceil(nt_t / S) near-equal parts, numbered in row order; work-group gid takes
+//     part gid, so it runs one segment with one prologue and one epilogue.  A row in
+//     several parts leaves each part's normalised output and log2-sum-exp in the slot of
+//     the part's number;
+//   stream (balanced, many rows): the concatenated tiles are cut into equal runs; a
+//     work-group walks the rows its run touches, writing rows it covers completely and
+//     leaving the at most two it covers in part in slot 2*gid (the row of the run's first
+//     tile) or 2*gid + 1 (the row of its last tile);
+//   fixed (num_partitions = P): work-group gid = (row, part) takes the part-th of P equal
+//     tile ranges of its row and uses slot gid.
+// Work-group 0 publishes every row's split in row_meta for the combine kernel, which
+// merges the parts of split rows by their log2-sum-exps: [0] = mode (0 stream, 1 row
+// parts), [1] = tiles per run (stream) or per part (row parts), then per row the pair
+// (a, b) of its RowSplit.  Fixed mode needs no table.
 //
 // Row geometry (sequence, visible key range) is gathered once per work-group into an LDS
 // table by a kernel-specific `fill` step, so the planning costs one round of independent
@@ -33,28 +43,54 @@ constexpr int kPlanMaxRows = 512;  // rows whose geometry the LDS table holds
 
 struct PlanLds {
   RowGeo geo[kPlanMaxRows];
-  int scan[1024];
+  int scan[1024];   // planning scratch; reused afterwards as the segments' page-id window
   int found[2];
   int zero[64];  // rows to clear found by this work-group, and their count in zero[63]
+  int red[68];   // block sums of the row-parts search, then its row count / total / max
 };
 
-// Block scan over one chunk: returns the inclusive prefix, sets the chunk total.
+// Sum / max over the wave, left in every lane, without LDS traffic: DPP moves combine lane
+// pairs (quad_perm 1,0,3,2 and 2,3,0,1), then mirrored halves of 8 and 16 lanes, and the
+// gfx950 lane swaps combine the four rows.  Block totals then take one LDS atomic per wave
+// (many lanes updating one LDS word serialise).
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_i32(int v) {
+  auto op = [](int x, int y) { return MAX ? max(x, y) : x + y; };
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = op((int)h[0], (int)h[1]);
+  const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  return op((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ int wave_sum_i32(int v) { return wave_reduce_i32<false>(v); }
+__device__ __forceinline__ int wave_max_i32(int v) { return wave_reduce_i32<true>(v); }
+
+// Block scan over one chunk of NT values: returns the inclusive prefix, sets the chunk
+// total.  Each wave scans its 64 values with lane shifts; wave totals meet in buf.
 template <int NT>
 __device__ __forceinline__ int plan_chunk_scan(int v, int* buf, int& chunk_total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
+  constexpr int NWV = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int off = 1; off < NT; off <<= 1) {
-    const int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(v, off);
+    if (lane >= off) v += up;
   }
-  const int incl = buf[tid];
-  chunk_total = buf[NT - 1];
+  if (lane == 63) buf[wave] = v;
   __syncthreads();
-  return incl;
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const int x = buf[w];
+    before += w < wave ? x : 0;
+    total += x;
+  }
+  chunk_total = total;
+  __syncthreads();  // buf is reused by the next call
+  return before + v;
 }
 
 // Zero the output row t (rows with no visible key).
@@ -65,6 +101,161 @@ __device__ void plan_zero_row(const SplitPlan& p, int t) {
     const int h = c / (kLatentDim / 8), c8 = c % (kLatentDim / 8);
     *(uint4*)(p.out + (int64_t)t * p.o_tok + (int64_t)h * p.o_head + c8 * 8) = make_uint4(0, 0, 0, 0);
   }
+}
+
+// Where the parts of a split row are (shared with the combine kernel).
+struct RowSplit {
+  int mode;  // 0 stream: a = the row's first tile in the concatenation, b = tiles per run
+             // 1 row parts: a = slot of part 0, b = parts;  2 fixed: a = t * P, b = P
+  int a, b;
+};
+
+__device__ __forceinline__ int split_count(const RowSplit& rs, int nt) {
+  return rs.mode == 0 ? (rs.a + nt - 1) / rs.b - rs.a / rs.b + 1 : rs.b;
+}
+
+// The split of row t as the combine kernel sees it; n = 0 when there is nothing to merge.
+__device__ __forceinline__ RowSplit row_split(const SplitPlan& p, int t, int& n) {
+  if (p.nparts >= 1) {
+    n = p.nparts > 1 ? p.nparts : 0;
+    return RowSplit{2, t * p.nparts, p.nparts};
+  }
+  const int mode = p.row_meta[0];
+  const RowSplit rs{mode, p.row_meta[2 + 2 * t], mode == 0 ? p.row_meta[1] : p.row_meta[3 + 2 * t]};
+  if (mode == 1) {
+    n = rs.b > 1 ? rs.b : 0;  // one part: written whole
+  } else {
+    const int nt = p.row_meta[3 + 2 * t];
+    n = nt > 0 && rs.b > 0 ? split_count(rs, nt) : 0;
+    if (n == 1) n = 0;  // one run covered the whole row and wrote it
+  }
+  return rs;
+}
+
+// slot of the row's c-th part
+__device__ __forceinline__ int split_slot(const RowSplit& rs, int c) {
+  if (rs.mode == 0) {
+    const int c0 = rs.a / rs.b;  // first run touching the row
+    // in run c0 the row holds the run's first tile only if it starts exactly there
+    return c == 0 ? (rs.a == c0 * rs.b ? 2 * c0 : 2 * c0 + 1) : 2 * (c0 + c);
+  }
+  return rs.a + c;
+}
+
+// Row-parts planning (see the mode list above), for a batch whose row geometry is in the
+// LDS table.  Returns false (before touching any output) when there are more non-empty
+// rows than work-groups or no visible key at all; otherwise sets this work-group's tile
+// range [s, e) of row r0 (r0 = -1: no part for it), pre = -1, writes row_meta (work-group
+// 0) and clears the rows without keys that fall to this work-group.
+template <int NT>
+__device__ __forceinline__ bool plan_row_parts(const SplitPlan& p, PlanLds& L, int& s, int& e, int& r0, int& pre) {
+  const int gid = blockIdx.x, tid = threadIdx.x;
+  constexpr int kRows = 64;  // red[64..66]: rows with keys, total tiles, largest row
+  for (int i = tid; i < 68; i += NT) L.red[i] = 0;
+  __syncthreads();
+  {
+    int rows = 0, total = 0, mx = 0;
+    for (int t = tid; t < p.T; t += NT) {
+      const int nt = geo_tiles(L.geo[t]);
+      rows += nt > 0;
+      total += nt;
+      mx = max(mx, nt);
+    }
+    rows = wave_sum_i32(rows);
+    total = wave_sum_i32(total);
+    mx = wave_max_i32(mx);
+    if ((tid & 63) == 0) {
+      atomicAdd(&L.red[kRows], rows);
+      atomicAdd(&L.red[kRows + 1], total);
+      atomicMax(&L.red[kRows + 2], mx);
+    }
+  }
+  __syncthreads();
+  const int rows = __builtin_amdgcn_readfirstlane(L.red[kRows]);
+  const int total = __builtin_amdgcn_readfirstlane(L.red[kRows + 1]);
+  const int maxnt = __builtin_amdgcn_readfirstlane(L.red[kRows + 2]);
+  if (rows == 0 || rows > p.grid) return false;
+
+  // smallest S with sum_t ceil(nt_t / S) <= grid: at least ceil(total / grid), at most the
+  // largest row (one part per row).  Each trial is one block sum in its own counter.
+  int trial = 0;
+  auto parts_fit = [&](int S) {
+    int c = 0;
+    for (int t = tid; t < p.T; t += NT) c += (geo_tiles(L.geo[t]) + S - 1) / S;
+    c = wave_sum_i32(c);
+    if ((tid & 63) == 0) atomicAdd(&L.red[trial], c);
+    __syncthreads();
+    const int sum = __builtin_amdgcn_readfirstlane(L.red[trial]);
+    ++trial;
+    return sum <= p.grid;
+  };
+  int S = max(1, (total + p.grid - 1) / p.grid);
+  if (S < maxnt && !parts_fit(S)) {
+    int lo = S, hi = maxnt;  // lo fails, hi fits
+    if (lo + 1 < hi && parts_fit(lo + 1)) hi = lo + 1;
+    else if (lo + 1 < hi) lo = lo + 1;
+    while (hi - lo > 1) {
+      const int mid = lo + (hi - lo) / 2;
+      if (parts_fit(mid)) hi = mid; else lo = mid;
+    }
+    S = hi;
+  } else if (S >= maxnt) {
+    S = maxnt;
+  }
+
+  // parts per row, their numbering, this work-group's part, rows to clear
+  if (tid == 0) {
+    L.found[0] = -1;
+    L.found[1] = 0;
+    L.zero[63] = 0;
+  }
+  __syncthreads();
+  int prefix = 0;
+  for (int base = 0; base < p.T; base += NT) {
+    const int t = base + tid;
+    const int nt = t < p.T ? geo_tiles(L.geo[t]) : 0;
+    const int P = (nt + S - 1) / S;
+    int ctot;
+    const int incl = plan_chunk_scan<NT>(P, L.scan, ctot);
+    const int first = prefix + incl - P;
+    if (t < p.T) {
+      if (gid == 0) {
+        p.row_meta[2 + 2 * t] = first;
+        p.row_meta[3 + 2 * t] = P;
+      }
+      if (P > 0 && first <= gid && gid < first + P) {
+        L.found[0] = t;
+        L.found[1] = gid - first;
+      }
+      if (nt == 0 && t % p.grid == gid) {
+        const int slot = atomicAdd(&L.zero[63], 1);
+        if (slot < 63) L.zero[slot] = t;
+      }
+    }
+    prefix += ctot;
+  }
+  if (gid == 0 && tid == 0) {
+    p.row_meta[0] = 1;  // row-parts mode
+    p.row_meta[1] = S;
+  }
+  __syncthreads();
+  const int nzero = __builtin_amdgcn_readfirstlane(L.zero[63]);
+  if (nzero <= 63) {
+    for (int i = 0; i < nzero; ++i) plan_zero_row<NT>(p, __builtin_amdgcn_readfirstlane(L.zero[i]));
+  } else {
+    for (int t = gid; t < p.T; t += p.grid)
+      if (geo_tiles(L.geo[t]) == 0) plan_zero_row<NT>(p, t);
+  }
+  r0 = __builtin_amdgcn_readfirstlane(L.found[0]);
+  pre = -1;
+  if (r0 >= 0) {
+    const int part = __builtin_amdgcn_readfirstlane(L.found[1]);
+    const int nt = geo_tiles(L.geo[r0]);
+    const int P = (nt + S - 1) / S;
+    s = (int)((long long)part * nt / P);
+    e = (int)((long long)(part + 1) * nt / P);
+  }
+  return true;
 }
 
 // Runs this work-group's share.
@@ -103,9 +294,11 @@ __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fi
     r0 = t;  // a run within a single row
     s = ta;
     e = tc;
+  } else if (table && plan_row_parts<NT>(p, L, s, e, r0, pre)) {
+    // row parts: one segment (or none) per work-group
+    if (r0 < 0) return;
   } else {
-    // per-row tile counts, prefix sums, the row holding tile s (and, for work-group 0,
-    // every row's tile range, which the combine kernel reads)
+    // per-row tile counts, prefix sums, the row holding tile s
     if (threadIdx.x == 0) {
       L.found[0] = -1;
       L.found[1] = 0;
@@ -131,7 +324,7 @@ __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fi
     s = gid * W;
     e = min(total, s + W);
     if (gid == 0 && threadIdx.x == 0) {
-      p.row_meta[0] = total;
+      p.row_meta[0] = 0;  // stream mode
       p.row_meta[1] = W;
     }
     int prefix = 0;
@@ -171,8 +364,9 @@ __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fi
     }
     if (s >= e || r0 < 0) return;
   }
-  // one call site for the segment work, whatever the mode
-  const bool fixed = p.nparts >= 1;
+  // one call site for the segment work, whatever the mode.  Fixed and row-parts modes
+  // (pre < 0) run the single tile range [s, e) of row r0 and use slot gid.
+  const bool fixed = p.nparts >= 1 || pre < 0;
   for (int r = r0; r < p.T && pre < e; ++r) {
     RowGeo g = row_geo(r);
     g.b = __builtin_amdgcn_readfirstlane(g.b);
@@ -183,7 +377,7 @@ __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fi
     const int run_end = fixed ? nt : pre + nt;
     const int ta = fixed ? s : max(s, pre) - pre;
     const int tc = fixed ? e : min(e, run_end) - pre;
-    const bool full = fixed ? p.nparts == 1 : (ta == 0 && tc == nt);
+    const bool full = p.nparts >= 1 ? p.nparts == 1 : (ta == 0 && tc == nt);
     const int slot = fixed ? gid : (pre <= s ? 2 * gid : 2 * gid + 1);
     segment(r, g, ta, tc, full, slot);
     if (fixed) break;

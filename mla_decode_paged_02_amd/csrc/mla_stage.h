@@ -62,10 +62,76 @@ __device__ __forceinline__ void wave_acc_init(WaveAcc<HB>& acc) {
 
 // valid: bit j set when key j of the stage is visible (block-uniform).  kscale (KSCALE
 // only): per-key factors of the stage in LDS, applied to the logit and to the value row.
-template <int HB, bool KSCALE>
+// Online softmax of one 16-head block of a stage: su0 / su1 are the score accumulators of
+// key tiles u = 0, 1 (lane 16g+n: head n, keys 8g + 4u + i).  Returns P^T as the MFMA
+// operand (lane 16g+n: head n, keys 8g..8g+7) and updates the running max m (log2 units,
+// the same in the four lanes of a head) and this lane's share l of the denominator.
+// The common case needs no cross-lane work: the max is only reduced over the four lanes of
+// a head when some lane's keys exceed m by more than kRescaleSlack; rescale(alpha) then
+// multiplies the block's O by alpha.
+template <bool KSCALE, class Rescale>
+__device__ __forceinline__ bf16x8 softmax_block(f32x4 su0, f32x4 su1, uint32_t valid, bool all_valid, int gq,
+                                                float scale_log2, const float (&ks8)[2][4], float& m, float& l,
+                                                Rescale rescale) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = su0[i] * scale_log2;
+    x[4 + i] = su1[i] * scale_log2;
+    if (KSCALE) {
+      x[i] *= ks8[0][i];
+      x[4 + i] *= ks8[1][i];
+    }
+  }
+  if (!all_valid) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = ((valid >> (8 * gq + j)) & 1u) ? x[j] : -INFINITY;
+  }
+  float lmax = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) lmax = fmaxf(lmax, x[j]);
+  if (__builtin_amdgcn_ballot_w64(lmax > m + kRescaleSlack) != 0) {
+    const float mx = wave_max_xor16_32(lmax);
+    const bool upd = mx > m + kRescaleSlack;  // the same in the four lanes of a head
+    const float m_new = upd ? mx : m;
+    const float alpha = upd ? fast_exp2(m - m_new) : 1.f;  // 0 while m is -inf
+    l *= alpha;
+    // O is still exactly zero while m is -inf: only a finite old max needs the multiply
+    if (__builtin_amdgcn_ballot_w64(upd && m != -INFINITY) != 0) rescale(alpha);
+    m = m_new;
+  }
+  const float mref = m == -INFINITY ? 0.f : m;  // a head with no visible key so far
+  bf16x8 pf;
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = fast_exp2(x[j] - mref);
+    pf[j] = (__bf16)(KSCALE ? p[j] * ks8[j >> 2][j & 3] : p[j]);
+  }
+  if (KSCALE) {
+    // the value row is code * scale: the scale is folded into the weight, not into l
+#pragma unroll
+    for (int j = 0; j < 8; ++j) l += p[j];
+  } else {
+    // sum the weights as rounded for the MFMA, so a constant V column is reproduced
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[j], pf[j + 1]}, one, l, false);
+  }
+  return pf;
+}
+
+// hook(ks) runs after the MFMAs of score k-step ks (0..17): the caller's slot for issuing the
+// next stage's loads so that they drain while the matrix cores work.
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <int HB, bool KSCALE, class Hook = NoHook>
 __device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const bf16x8 (&qf)[HB][18],
                                               WaveAcc<HB>& acc, uint32_t valid, float scale_log2,
-                                              const MLA_LDS float* kscale, const LaneGeo& g) {
+                                              const MLA_LDS float* kscale, const LaneGeo& g, Hook hook = Hook()) {
   // ---- S^T = K Q^T, fragments prefetched one k-step ahead
   f32x4 sacc[2][HB];
 #pragma unroll
@@ -96,10 +162,11 @@ __device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const 
         sacc[1][hb] = mfma16x16x32(k1, qf[hb][ks], sacc[1][hb]);
       }
       __builtin_amdgcn_sched_barrier(0);
+      hook(ks);
     }
   }
 
-  // ---- online softmax.  Lane 16g+n holds keys 8g + 4u + i for sacc[u][hb][i].
+  // ---- online softmax
   const bool all_valid = valid == 0xFFFFFFFFu;
   float ks8[2][4];
   if (KSCALE) {
@@ -113,48 +180,12 @@ __device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const 
   }
   bf16x8 pf[HB];
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    float x[2][4];
-    float mx = -INFINITY;
+  for (int hb = 0; hb < HB; ++hb)
+    pf[hb] = softmax_block<KSCALE>(sacc[0][hb], sacc[1][hb], valid, all_valid, g.gq, scale_log2, ks8, acc.m[hb],
+                                   acc.l[hb], [&](float alpha) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = sacc[u][hb][i] * scale_log2;
-        if (KSCALE) v *= ks8[u][i];
-        if (!all_valid) v = ((valid >> (8 * g.gq + 4 * u + i)) & 1u) ? v : -INFINITY;
-        x[u][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = wave_max_xor16_32(mx);
-    const bool need = mx > acc.m[hb] + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = need ? mx : acc.m[hb];
-      const float alpha = fast_exp2(acc.m[hb] - m_new);  // 0 while m is -inf
-      acc.l[hb] *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) acc.o[cb][hb] *= alpha;
-      acc.m[hb] = m_new;
-    }
-    float lsum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = x[u][i] == -INFINITY ? 0.f : fast_exp2(x[u][i] - acc.m[hb]);
-        if (KSCALE) {
-          // the value row is code * scale: fold the scale into the weight
-          pf[hb][4 * u + i] = (__bf16)(p * ks8[u][i]);
-          lsum += p;
-        } else {
-          // sum the weights as rounded for the MFMA, so a constant V column is reproduced
-          const __bf16 pb = (__bf16)p;
-          pf[hb][4 * u + i] = pb;
-          lsum += (float)pb;
-        }
-      }
-    acc.l[hb] += lsum;
-  }
+                                     for (int cb = 0; cb < 32; ++cb) acc.o[cb][hb] *= alpha;
+                                   });
 
   // ---- O^T += V^T P^T over the stage's 32 keys
   {
@@ -177,29 +208,25 @@ __device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const 
 template <int HB>
 __device__ __forceinline__ void stage_epilogue(const WaveAcc<HB>& acc, int lane, int h0, int t, bool full,
                                                int slot, int H, uint16_t* out, int64_t o_tok, int64_t o_head,
-                                               float* part_o, float* part_lse) {
+                                               uint16_t* part_o, float* part_lse) {
   const int gq = lane >> 4, ln = lane & 15;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const float l_tot = wave_sum_xor16_32(acc.l[hb]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int h = h0 + 16 * hb + ln;
-    if (full) {
-      uint16_t* orow = out + (int64_t)t * o_tok + (int64_t)h * o_head + 4 * gq;
+    // the final row, or a split row's normalised part (bf16 as well) and its log2-sum-exp
+    uint16_t* orow = full ? out + (int64_t)t * o_tok + (int64_t)h * o_head + 4 * gq
+                          : part_o + ((int64_t)slot * H + h) * kLatentDim + 4 * gq;
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) {
-        const uint32_t lo = (uint32_t)bf16_bits_rne(acc.o[cb][hb][0] * inv) |
-                            ((uint32_t)bf16_bits_rne(acc.o[cb][hb][1] * inv) << 16);
-        const uint32_t hi = (uint32_t)bf16_bits_rne(acc.o[cb][hb][2] * inv) |
-                            ((uint32_t)bf16_bits_rne(acc.o[cb][hb][3] * inv) << 16);
-        *(uint2*)(orow + 16 * cb) = make_uint2(lo, hi);
-      }
-    } else {
-      float* prow = part_o + ((int64_t)slot * H + h) * kLatentDim + 4 * gq;
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) *(f32x4*)(prow + 16 * cb) = acc.o[cb][hb] * inv;
-      if (gq == 0) part_lse[(int64_t)slot * H + h] = l_tot > 0.f ? acc.m[hb] + __log2f(l_tot) : -INFINITY;
+    for (int cb = 0; cb < 32; ++cb) {
+      const uint32_t lo = (uint32_t)bf16_bits_rne(acc.o[cb][hb][0] * inv) |
+                          ((uint32_t)bf16_bits_rne(acc.o[cb][hb][1] * inv) << 16);
+      const uint32_t hi = (uint32_t)bf16_bits_rne(acc.o[cb][hb][2] * inv) |
+                          ((uint32_t)bf16_bits_rne(acc.o[cb][hb][3] * inv) << 16);
+      *(uint2*)(orow + 16 * cb) = make_uint2(lo, hi);
     }
+    if (!full && gq == 0) part_lse[(int64_t)slot * H + h] = l_tot > 0.f ? acc.m[hb] + __log2f(l_tot) : -INFINITY;
   }
 }
 
@@ -265,11 +292,14 @@ __device__ __forceinline__ void wave_acc2_init(WaveAcc2& acc) {
   acc.l[0] = acc.l[1] = 0.f;
 }
 
-template <bool KSCALE>
+template <bool KSCALE, class Hook = NoHook>
 __device__ __forceinline__ void stage_compute2(const MLA_LDS uint8_t* buf, const bf16x8 (&qf)[2][18],
                                                WaveAcc2& acc, uint32_t valid, float scale_log2,
-                                               const MLA_LDS float* kscale, const LaneGeo& g) {
-  // ---- S^T = K Q^T: 2 key tiles x 2 head blocks, K fragments prefetched one k-step ahead
+                                               const MLA_LDS float* kscale, const LaneGeo& g, Hook hook = Hook()) {
+  // ---- S^T = K Q^T: 2 key tiles x 2 head blocks.  With one wave per SIMD nothing else
+  // hides LDS latency, so K fragments are read kPrefetch k-steps ahead of their MFMAs and
+  // scheduling barriers keep the compiler from regrouping the reads.
+  constexpr int kPrefetch = 2;
   f32x4 s00, s01, s10, s11;  // s<u><hb>
   {
     const MLA_LDS uint8_t* r0 = buf + g.rowA0 * kRowBytes;
@@ -277,33 +307,37 @@ __device__ __forceinline__ void stage_compute2(const MLA_LDS uint8_t* buf, const
     auto chunk = [&](int ks, int xa) {
       return ks < 16 ? ((4 * ks) ^ xa) : 64 + ((4 * (ks - 16)) ^ (xa & 7));
     };
-    bf16x8 k0 = *(const MLA_LDS bf16x8*)(r0 + chunk(0, g.xa0) * 16);
-    bf16x8 k1 = *(const MLA_LDS bf16x8*)(r1 + chunk(0, g.xa1) * 16);
+    bf16x8 kf[18][2];  // fully unrolled: only kPrefetch + 1 steps are live at a time
+#pragma unroll
+    for (int ks = 0; ks < kPrefetch; ++ks) {
+      kf[ks][0] = *(const MLA_LDS bf16x8*)(r0 + chunk(ks, g.xa0) * 16);
+      kf[ks][1] = *(const MLA_LDS bf16x8*)(r1 + chunk(ks, g.xa1) * 16);
+    }
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      bf16x8 n0 = k0, n1 = k1;
-      if (ks + 1 < 18) {
-        n0 = *(const MLA_LDS bf16x8*)(r0 + chunk(ks + 1, g.xa0) * 16);
-        n1 = *(const MLA_LDS bf16x8*)(r1 + chunk(ks + 1, g.xa1) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + kPrefetch < 18) {
+        kf[ks + kPrefetch][0] = *(const MLA_LDS bf16x8*)(r0 + chunk(ks + kPrefetch, g.xa0) * 16);
+        kf[ks + kPrefetch][1] = *(const MLA_LDS bf16x8*)(r1 + chunk(ks + kPrefetch, g.xa1) * 16);
       }
       if (ks == 0) {
-        mfma_v_first(s00, k0, qf[0][0]);
-        mfma_v_first(s10, k1, qf[0][0]);
-        mfma_v_first(s01, k0, qf[1][0]);
-        mfma_v_first(s11, k1, qf[1][0]);
+        mfma_v_first(s00, kf[0][0], qf[0][0]);
+        mfma_v_first(s10, kf[0][1], qf[0][0]);
+        mfma_v_first(s01, kf[0][0], qf[1][0]);
+        mfma_v_first(s11, kf[0][1], qf[1][0]);
       } else {
-        mfma_v(s00, k0, qf[0][ks]);
-        mfma_v(s10, k1, qf[0][ks]);
-        mfma_v(s01, k0, qf[1][ks]);
-        mfma_v(s11, k1, qf[1][ks]);
+        mfma_v(s00, kf[ks][0], qf[0][ks]);
+        mfma_v(s10, kf[ks][1], qf[0][ks]);
+        mfma_v(s01, kf[ks][0], qf[1][ks]);
+        mfma_v(s11, kf[ks][1], qf[1][ks]);
       }
-      k0 = n0;
-      k1 = n1;
+      hook(ks);
     }
+    __builtin_amdgcn_sched_barrier(0);
     mfma_fence_v4(s00, s01, s10, s11);
   }
 
-  // ---- online softmax.  Lane 16g+n holds keys 8g + 4u + i.
+  // ---- online softmax
   const bool all_valid = valid == 0xFFFFFFFFu;
   float ks8[2][4];
   if (KSCALE) {
@@ -317,77 +351,54 @@ __device__ __forceinline__ void stage_compute2(const MLA_LDS uint8_t* buf, const
   }
   bf16x8 pf[2];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const f32x4 su[2] = {hb == 0 ? s00 : s01, hb == 0 ? s10 : s11};
-    float x[2][4];
-    float mx = -INFINITY;
+  for (int hb = 0; hb < 2; ++hb)
+    pf[hb] = softmax_block<KSCALE>(hb == 0 ? s00 : s01, hb == 0 ? s10 : s11, valid, all_valid, g.gq, scale_log2,
+                                   ks8, acc.m[hb], acc.l[hb], [&](float alpha) {
+      // The previous stage's last writes of O were followed by this stage's score MFMAs,
+      // far more than the wait states a read needs.  One quad at a time through ordinary
+      // registers: each step is tied to the next quad so the compiler cannot lift all the
+      // reads ahead and run out of registers.
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = su[u][i] * scale_log2;
-        if (KSCALE) v *= ks8[u][i];
-        if (!all_valid) v = ((valid >> (8 * g.gq + 4 * u + i)) & 1u) ? v : -INFINITY;
-        x[u][i] = v;
-        mx = fmaxf(mx, v);
+      for (int cb = 0; cb < 32; ++cb) {
+        acc.o[2 * cb + hb] *= alpha;
+        if (cb + 1 < 32)
+          asm volatile("" : "+a"(acc.o[2 * cb + hb]), "+a"(acc.o[2 * cb + 2 + hb]));
+        else
+          asm volatile("" : "+a"(acc.o[2 * cb + hb]));
       }
-    mx = wave_max_xor16_32(mx);
-    const bool need = mx > acc.m[hb] + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      // the previous stage's last writes of O were followed by this stage's score MFMAs,
-      // far more than the wait states a read needs
-      const float m_new = need ? mx : acc.m[hb];
-      const float alpha = fast_exp2(acc.m[hb] - m_new);  // 0 while m is -inf
-      acc.l[hb] *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) acc.o[2 * cb + hb] *= alpha;
-      acc.m[hb] = m_new;
-    }
-    float lsum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = x[u][i] == -INFINITY ? 0.f : fast_exp2(x[u][i] - acc.m[hb]);
-        if (KSCALE) {
-          pf[hb][4 * u + i] = (__bf16)(p * ks8[u][i]);
-          lsum += p;
-        } else {
-          const __bf16 pb = (__bf16)p;
-          pf[hb][4 * u + i] = pb;
-          lsum += (float)pb;
-        }
-      }
-    acc.l[hb] += lsum;
-  }
+    });
   valu_fence_v2(pf[0], pf[1]);
 
-  // ---- O^T += V^T P^T, V fragments prefetched one column block ahead
+  // ---- O^T += V^T P^T, V^T fragments read kPrefetch column blocks ahead
   {
     const MLA_LDS uint8_t* v0b = buf + g.rowV0 * kRowBytes + g.vhalf;
     const MLA_LDS uint8_t* v1b = buf + g.rowV1 * kRowBytes + g.vhalf;
-    bf16x4 a0 = ds_read_tr16(v0b + ((0 ^ g.xv0) * 16));
-    bf16x4 a1 = ds_read_tr16(v1b + ((0 ^ g.xv1) * 16));
+    bf16x4 vt[32][2];  // fully unrolled: only kPrefetch + 1 blocks are live at a time
+#pragma unroll
+    for (int cb = 0; cb < kPrefetch; ++cb) {
+      vt[cb][0] = ds_read_tr16(v0b + (((2 * cb) ^ g.xv0) * 16));
+      vt[cb][1] = ds_read_tr16(v1b + (((2 * cb) ^ g.xv1) * 16));
+    }
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
-      bf16x4 n0 = a0, n1 = a1;
-      if (cb + 1 < 32) {
-        const int cc = 2 * (cb + 1);
-        n0 = ds_read_tr16(v0b + ((cc ^ g.xv0) * 16));
-        n1 = ds_read_tr16(v1b + ((cc ^ g.xv1) * 16));
+      __builtin_amdgcn_sched_barrier(0);
+      if (cb + kPrefetch < 32) {
+        const int cc = 2 * (cb + kPrefetch);
+        vt[cb + kPrefetch][0] = ds_read_tr16(v0b + ((cc ^ g.xv0) * 16));
+        vt[cb + kPrefetch][1] = ds_read_tr16(v1b + ((cc ^ g.xv1) * 16));
       }
-      const bf16x8 vf = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const bf16x8 vf = {vt[cb][0][0], vt[cb][0][1], vt[cb][0][2], vt[cb][0][3],
+                         vt[cb][1][0], vt[cb][1][1], vt[cb][1][2], vt[cb][1][3]};
       mfma_a(acc.o[2 * cb], vf, pf[0]);
       mfma_a(acc.o[2 * cb + 1], vf, pf[1]);
-      a0 = n0;
-      a1 = n1;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 __device__ __forceinline__ void stage_epilogue2(WaveAcc2& acc, int lane, int h0, int t, bool full, int slot,
                                                 int H, uint16_t* out, int64_t o_tok, int64_t o_head,
-                                                float* part_o, float* part_lse) {
+                                                uint16_t* part_o, float* part_lse) {
   mfma_fence_acc(acc.o);
   const int gq = lane >> 4, ln = lane & 15;
 #pragma unroll
@@ -395,21 +406,16 @@ __device__ __forceinline__ void stage_epilogue2(WaveAcc2& acc, int lane, int h0,
     const float l_tot = wave_sum_xor16_32(acc.l[hb]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int h = h0 + 16 * hb + ln;
-    if (full) {
-      uint16_t* orow = out + (int64_t)t * o_tok + (int64_t)h * o_head + 4 * gq;
+    uint16_t* orow = full ? out + (int64_t)t * o_tok + (int64_t)h * o_head + 4 * gq
+                          : part_o + ((int64_t)slot * H + h) * kLatentDim + 4 * gq;
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) {
-        const f32x4 v = acc.o[2 * cb + hb];
-        const uint32_t lo = (uint32_t)bf16_bits_rne(v[0] * inv) | ((uint32_t)bf16_bits_rne(v[1] * inv) << 16);
-        const uint32_t hi = (uint32_t)bf16_bits_rne(v[2] * inv) | ((uint32_t)bf16_bits_rne(v[3] * inv) << 16);
-        *(uint2*)(orow + 16 * cb) = make_uint2(lo, hi);
-      }
-    } else {
-      float* prow = part_o + ((int64_t)slot * H + h) * kLatentDim + 4 * gq;
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) *(f32x4*)(prow + 16 * cb) = acc.o[2 * cb + hb] * inv;
-      if (gq == 0) part_lse[(int64_t)slot * H + h] = l_tot > 0.f ? acc.m[hb] + __log2f(l_tot) : -INFINITY;
+    for (int cb = 0; cb < 32; ++cb) {
+      const f32x4 v = acc.o[2 * cb + hb];
+      const uint32_t lo = (uint32_t)bf16_bits_rne(v[0] * inv) | ((uint32_t)bf16_bits_rne(v[1] * inv) << 16);
+      const uint32_t hi = (uint32_t)bf16_bits_rne(v[2] * inv) | ((uint32_t)bf16_bits_rne(v[3] * inv) << 16);
+      *(uint2*)(orow + 16 * cb) = make_uint2(lo, hi);
     }
+    if (!full && gq == 0) part_lse[(int64_t)slot * H + h] = l_tot > 0.f ? acc.m[hb] + __log2f(l_tot) : -INFINITY;
   }
 }
 

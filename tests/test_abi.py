@@ -104,7 +104,7 @@ def test_workspace_size_grows_with_partitions():
     small = m.decode_workspace_bytes(64, 128, 1)
     big = m.decode_workspace_bytes(64, 128, 8)
     assert big > small > 0
-    assert m.decode_workspace_bytes(64, 128, 0) >= 2 * 256 * 128 * 512 * 4
+    assert m.decode_workspace_bytes(64, 128, 0) >= 2 * 256 * 128 * 512 * 2
 
 
 def test_binding_refuses_cpu_tensors():

@@ -138,3 +138,43 @@ def test_bad_page_id_is_flagged_not_faulted():
     got = decode_on_gpu(m, case, table=table)
     assert np.all(np.isfinite(to_f64(got)))
     assert m.check_device_errors() & 1
+
+
+@pytest.mark.parametrize("nrows", [300, 600])
+def test_many_rows_stream_split(nrows):
+    """More non-empty rows than work-groups: the stream split instead of row parts (and,
+    past the planning table's 512 rows, the per-row geometry search)."""
+    m = need_gpu()
+    rng = np.random.default_rng(nrows)
+    lens = [int(x) for x in rng.integers(1, 400, nrows)]
+    case = make_decode_case(200 + nrows, lens, 16, 64, name="many")
+    compare(to_f64(decode_on_gpu(m, case)), oracle_of(case), BF16_TOL, f"{nrows} rows")
+
+
+def test_row_parts_mixed_rows():
+    """Row parts with empty, one-tile and long rows side by side."""
+    m = need_gpu()
+    case = make_decode_case(17, [0, 1, 64, 65, 0, 5000, 130, 9000, 0, 3], 128, 64, name="mixed")
+    got = to_f64(decode_on_gpu(m, case))
+    compare(got, oracle_of(case), BF16_TOL, "mixed rows")
+    assert np.all(got[0] == 0) and np.all(got[4] == 0) and np.all(got[8] == 0)
+
+
+def test_alternating_shapes_reuse_workspace():
+    """Split rows are merged through per-row arrival counters that every launch leaves
+    cleared: calls of different shapes and split modes on one stream stay exact."""
+    m = need_gpu()
+    big = config_case(1)
+    small = make_decode_case(18, [5000, 3, 700], 64, 64, name="alt")
+    a = bits_of(decode_on_gpu(m, big))
+    raw = decode_on_gpu(m, small)
+    compare(to_f64(raw), oracle_of(small), BF16_TOL, "alt small")
+    b = bits_of(raw)
+    b5 = bits_of(decode_on_gpu(m, small, num_partitions=5))
+    for P in (0, 5, 0, 2, 5):
+        got = bits_of(decode_on_gpu(m, small, num_partitions=P))
+        if P == 0:
+            assert np.array_equal(got, b)
+        elif P == 5:
+            assert np.array_equal(got, b5)
+        assert np.array_equal(bits_of(decode_on_gpu(m, big)), a)
