@@ -83,7 +83,7 @@ bool supported_heads(int64_t h) { return h == 16 || h == 32 || h == 64 || h == 1
 // workspace: one grow-only buffer per (device, stream)
 // ---------------------------------------------------------------------------------------
 constexpr size_t kZeroRowBytes = 4096;  // the zero row (>= 1152 bytes) and the error word
-constexpr size_t kErrOffset = 2048;
+constexpr size_t kErrOffset = mla::kHdrErrOffset;
 constexpr size_t kHeaderBytes = kZeroRowBytes;
 constexpr int64_t kMaxRows = (int64_t)1 << 24;
 
@@ -132,9 +132,11 @@ mla_status grow_workspace(int device, void* stream, size_t need, bool capturing,
   void* p = nullptr;
   if (hipMalloc(&p, bytes) != hipSuccess) return fail(MLA_ERR_WORKSPACE, "hipMalloc(%zu) failed", bytes);
   // the zero row and the error word must start cleared; the rest needs no initial value
-  if (hipMemset(p, 0, kHeaderBytes) != hipSuccess) {
+  const float one = 1.f;
+  if (hipMemset(p, 0, kHeaderBytes) != hipSuccess ||
+      hipMemcpy((char*)p + mla::kSparseOneOffset, &one, sizeof(one), hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(p);
-    return fail(MLA_ERR_HIP, "hipMemset of the workspace header failed");
+    return fail(MLA_ERR_HIP, "initialising the workspace header failed");
   }
   w.base = p;
   w.bytes = bytes;
@@ -401,9 +403,95 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
                                    const mla_tensor* d_indices, const mla_tensor* topk_lengths,
                                    float scale, int32_t num_partitions, mla_tensor* out,
                                    void* stream) {
-  (void)q; (void)q_scale; (void)input_row_offsets; (void)latent_cache; (void)cache_scale;
-  (void)d_indices; (void)topk_lengths; (void)scale; (void)num_partitions; (void)out; (void)stream;
-  return fail(MLA_ERR_UNSUPPORTED, "sparse decode not built yet");
+  mla_status s;
+  if (!q) return fail(MLA_ERR_NULL_ARG, "q: descriptor is NULL");
+  const bool q_bf16 = q->dtype == MLA_DTYPE_BF16;
+  if ((s = check_tensor(q, "q", q_bf16 ? MLA_DTYPE_BF16 : MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
+  const int64_t T = q->shape[0], H = q->shape[1];
+  if (q->shape[2] != 576) return fail(MLA_ERR_SHAPE, "q: head width %lld, expected 576", (long long)q->shape[2]);
+  if (q_scale) {
+    if (q_bf16) return fail(MLA_ERR_VALUE, "q_scale must be NULL when q is bf16");
+    if ((s = check_1d(q_scale, "q_scale", MLA_DTYPE_F32, T)) != MLA_OK) return s;
+  }
+  if ((s = check_tensor(input_row_offsets, "input_row_offsets", MLA_DTYPE_U32, 1, false)) != MLA_OK) return s;
+  if (input_row_offsets->shape[0] < 2) return fail(MLA_ERR_SHAPE, "input_row_offsets: needs batch + 1 >= 2 entries");
+  if (!latent_cache) return fail(MLA_ERR_NULL_ARG, "latent_cache: descriptor is NULL");
+  if (latent_cache->dtype == MLA_DTYPE_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "sparse decode reads an fp8 e4m3 cache; a bf16 cache is not supported");
+  if ((s = check_tensor(latent_cache, "latent_cache", MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
+  if (latent_cache->shape[2] != 576) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576", (long long)latent_cache->shape[2]);
+  const int64_t NP = latent_cache->shape[0], PS = latent_cache->shape[1];
+  if (PS < 1) return fail(MLA_ERR_SHAPE, "latent_cache: page size must be >= 1");
+  if (PS > 1 && latent_cache->stride[1] != 576)
+    return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride 576)");
+  if (NP > 1 && latent_cache->stride[0] < PS * 576)
+    return fail(MLA_ERR_SHAPE, "latent_cache: pages overlap (page stride below page_size * 576)");
+  if (NP * PS > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 cache rows");
+  if (cache_scale) {
+    if ((s = check_tensor(cache_scale, "cache_scale", MLA_DTYPE_F32, 2, false)) != MLA_OK) return s;
+    if (cache_scale->shape[0] != NP || cache_scale->shape[1] != PS)
+      return fail(MLA_ERR_SHAPE, "cache_scale: shape must be [%lld, %lld]", (long long)NP, (long long)PS);
+  }
+  if ((s = check_tensor(d_indices, "d_indices", MLA_DTYPE_I32, 2, false)) != MLA_OK) return s;
+  if (d_indices->shape[0] != T) return fail(MLA_ERR_SHAPE, "d_indices: %lld rows, expected %lld", (long long)d_indices->shape[0], (long long)T);
+  if (d_indices->shape[1] > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "d_indices: too many columns");
+  if (T > 1 && d_indices->stride[0] < d_indices->shape[1])
+    return fail(MLA_ERR_SHAPE, "d_indices: row stride below the row length");
+  if ((s = check_1d(topk_lengths, "topk_lengths", MLA_DTYPE_I32, T)) != MLA_OK) return s;
+  if ((s = check_tensor(out, "out", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  if (out->shape[0] != T || out->shape[1] != H || out->shape[2] != 512)
+    return fail(MLA_ERR_SHAPE, "out: shape must be [%lld, %lld, 512]", (long long)T, (long long)H);
+  if (!supported_heads(H)) return fail(MLA_ERR_UNSUPPORTED, "num_heads %lld not in {16, 32, 64, 128}", (long long)H);
+  if (!std::isfinite(scale)) return fail(MLA_ERR_VALUE, "scale must be finite");
+  if (num_partitions > 4096) return fail(MLA_ERR_VALUE, "num_partitions %d above 4096", num_partitions);
+  if (T > kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 query rows");
+  if (T == 0) return ok();
+
+  bool cap = false;
+  if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
+  const int dev = current_device();
+  const int grid = cu_count(dev);
+  const int32_t nparts = num_partitions > 0 ? num_partitions : 0;
+  const DecodeLayout L = decode_layout(T, (int32_t)H, nparts, grid);
+  void* ws = nullptr;
+  if ((s = grow_workspace(dev, stream, L.total, cap, &ws)) != MLA_OK) return s;
+  char* w = (char*)ws + kHeaderBytes;
+
+  mla::SparseArgs a{};
+  a.q = (const uint8_t*)q->data;
+  a.q_tok = q->stride[0];
+  a.q_head = q->stride[1];
+  a.q_scale = q_scale ? (const float*)q_scale->data : nullptr;
+  a.cache = (const uint8_t*)latent_cache->data;
+  a.page_bytes = latent_cache->stride[0];
+  a.cache_scale = cache_scale ? (const float*)cache_scale->data : nullptr;
+  a.cs_page = cache_scale ? cache_scale->stride[0] : 0;
+  a.num_rows = NP * PS;
+  a.PS = (int32_t)PS;
+  a.idx = (const int32_t*)d_indices->data;
+  a.idx_row = d_indices->stride[0];
+  a.idx_cols = (int32_t)d_indices->shape[1];
+  a.topk = (const int32_t*)topk_lengths->data;
+  a.T = (int32_t)T;
+  a.H = (int32_t)H;
+  a.q_bf16 = q_bf16 ? 1 : 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.nparts = nparts;
+  a.grid = grid;
+  a.out = (uint16_t*)out->data;
+  a.o_tok = out->stride[0];
+  a.o_head = out->stride[1];
+  a.part_o = (uint16_t*)(w + L.part_o);
+  a.part_lse = (float*)(w + L.part_lse);
+  a.row_meta = (int32_t*)(w + L.meta);
+  a.zero_row = (const uint8_t*)ws;
+  a.err = (uint32_t*)((char*)ws + kErrOffset);
+  mla::KernelTimer tslot;
+  mla::KernelTimer* timer = profile_timer(&tslot);
+  const hipError_t e = mla::launch_sparse(a, (hipStream_t)stream, timer);
+  profile_keep(timer, e == hipSuccess);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "sparse decode launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla_tensor* v,

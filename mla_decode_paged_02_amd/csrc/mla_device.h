@@ -109,6 +109,15 @@ __device__ __forceinline__ void dma16(const void* src, MLA_LDS void* dst_wave_ba
                : "memory", "m0");
 }
 
+// 4 bytes per lane: lane l's dword lands at dst_wave_base + 4 l.
+__device__ __forceinline__ void dma4(const void* src, MLA_LDS void* dst_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
 // The same load with the source split into a wave-uniform 64-bit base (scalar registers)
 // and a per-lane 32-bit byte offset, which needs no per-lane 64-bit address arithmetic.
 __device__ __forceinline__ void dma16_base(const void* base, uint32_t off, MLA_LDS void* dst_wave_base) {
@@ -153,6 +162,15 @@ __device__ __forceinline__ float xor16_32_pair_max(float v, bool sum) {
 }
 __device__ __forceinline__ float wave_max_xor16_32(float v) { return xor16_32_pair_max(v, false); }
 __device__ __forceinline__ float wave_sum_xor16_32(float v) { return xor16_32_pair_max(v, true); }
+
+// Four OCP e4m3 codes (one dword) to four bf16 values, exactly (every e4m3 value is a
+// bf16 value): the gfx950 scaled pair conversion with scale 1.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
 
 __device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
   __bf16 b = (__bf16)f;

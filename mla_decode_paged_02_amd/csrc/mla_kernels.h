@@ -8,6 +8,11 @@
 
 namespace mla {
 
+// Workspace header: a zero row (>= 1152 zero bytes) at offset 0, the device error word at
+// kHdrErrOffset and the float 1.0 at kSparseOneOffset (the scale of rows without one).
+constexpr size_t kHdrErrOffset = 2048;
+constexpr size_t kSparseOneOffset = 2064;
+
 // Dense decode over a paged bf16 latent cache.
 struct DecodeArgs {
   const uint16_t* q;          // bf16 [T, H, 576]
@@ -35,29 +40,30 @@ struct DecodeArgs {
 
 // Sparse decode: each q row lists physical cache rows to attend to.
 struct SparseArgs {
-  const uint8_t* q;           // fp8 [T, H, 576] or bf16 (q_bf16)
+  const uint8_t* q;           // fp8 e4m3 [T, H, 576], or bf16 when q_bf16
   int64_t q_tok, q_head;      // element strides
-  const float* q_scale;       // [T] or null
-  const uint8_t* cache;       // fp8 or bf16 [num_pages, PS, 576]
-  int64_t page_elems;         // element stride between pages
-  const float* cache_scale;   // [num_pages, PS] (page stride cs_page) or null
-  int64_t cs_page;
-  int64_t num_pages;
+  const float* q_scale;       // [T] or null (= 1)
+  const uint8_t* cache;       // fp8 e4m3 [num_pages, PS, 576]; a page's rows are contiguous
+  int64_t page_bytes;         // byte stride between pages
+  const float* cache_scale;   // [num_pages, PS] or null (= 1)
+  int64_t cs_page;            // element stride between pages of cache_scale
+  int64_t num_rows;           // num_pages * PS: listed rows outside [0, num_rows) are skipped
   int32_t PS;
-  const int32_t* idx;         // [T, stride]
+  const int32_t* idx;         // [T, idx_row]
   int64_t idx_row;            // element stride between index rows
-  int32_t idx_cols;           // shape[1] of d_indices
+  int32_t idx_cols;           // shape[1] of d_indices (topk is clamped to it)
   const int32_t* topk;        // [T]
   int32_t T, H;
-  int32_t q_bf16, c_bf16;     // element types (1 = bf16, 0 = fp8 e4m3)
-  float scale_log2;
+  int32_t q_bf16;             // 1: q is bf16 (no q_scale)
+  float scale_log2;           // scale * log2(e)
   int32_t nparts;             // 0: balanced; >= 1 fixed
   int32_t grid;
-  uint16_t* out;
+  uint16_t* out;              // bf16 [T, H, 512]
   int64_t o_tok, o_head;
   uint16_t* part_o;
   float* part_lse;
   int32_t* row_meta;
+  const uint8_t* zero_row;    // >= 1152 zero bytes
   uint32_t* err;
 };
 

@@ -112,3 +112,48 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros((1, 16, 576), dtype=torch.bfloat16)
     with pytest.raises(m.MlaError):
         m.decode_paged(q, q, q, q, q, 0.1)
+
+
+def sparse_args(**over):
+    T, H, PS, NP = 4, 16, 64, 10
+    a = dict(q=_t(FAKE, 1, (T, H, 576)), qs=_t(FAKE, 2, (T,)), off=_t(FAKE, 4, (T + 1,)),
+             cache=_t(FAKE, 1, (NP, PS, 576)), cs=_t(FAKE, 2, (NP, PS)),
+             idx=_t(FAKE, 3, (T, 32)), topk=_t(FAKE, 3, (T,)), out=_t(FAKE, 0, (T, H, 512)),
+             scale=0.07, parts=0)
+    a.update(over)
+    return a
+
+
+def call_sparse(a):
+    lib = m.library()
+    ref = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    st = lib.mla_decode_paged_sparse(ref(a["q"]), ref(a["qs"]), ref(a["off"]), ref(a["cache"]),
+                                     ref(a["cs"]), ref(a["idx"]), ref(a["topk"]),
+                                     ctypes.c_float(a["scale"]), a["parts"], ref(a["out"]), None)
+    return st, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=_t(FAKE, 2, (4, 16, 576))), 3),                 # f32 q
+    (dict(q=_t(FAKE, 1, (4, 16, 512))), 2),                 # wrong head width
+    (dict(q=_t(FAKE, 0, (4, 16, 576))), 8),                 # bf16 q with a token scale
+    (dict(cache=_t(FAKE, 0, (10, 64, 576)), cs=None), 5),   # bf16 cache
+    (dict(cs=_t(FAKE, 2, (10, 32))), 2),                    # scale shape
+    (dict(idx=_t(FAKE, 3, (3, 32))), 2),                    # index rows != q rows
+    (dict(topk=_t(FAKE, 3, (5,))), 2),                      # topk length
+    (dict(out=_t(FAKE, 0, (4, 16, 128))), 2),               # out width
+    (dict(q=_t(FAKE, 1, (4, 48, 576)), out=_t(FAKE, 0, (4, 48, 512))), 5),  # head count
+    (dict(scale=float("inf")), 8),
+    (dict(cache=_t(FAKE, 1, (10, 64, 576), stride=(64 * 608, 608, 1))), 2),  # rows not contiguous
+])
+def test_sparse_validation(over, status):
+    st, msg = call_sparse(sparse_args(**over))
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_sparse_empty_batch_is_a_no_op():
+    st, _ = call_sparse(sparse_args(q=_t(FAKE, 1, (0, 16, 576)), qs=_t(FAKE, 2, (0,)),
+                                    idx=_t(FAKE, 3, (0, 32)), topk=_t(FAKE, 3, (0,)),
+                                    out=_t(FAKE, 0, (0, 16, 512))))
+    assert st == 0
