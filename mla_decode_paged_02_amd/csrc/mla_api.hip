@@ -499,9 +499,84 @@ mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla
                              const mla_tensor* input_row_offsets, const mla_tensor* page_table,
                              const mla_tensor* cache_lens, const mla_tensor* latent_cache,
                              float scale, int32_t mask, mla_tensor* out, void* stream) {
-  (void)q; (void)k; (void)v; (void)buffer_row_offsets; (void)cache_offsets; (void)input_row_offsets;
-  (void)page_table; (void)cache_lens; (void)latent_cache; (void)scale; (void)mask; (void)out; (void)stream;
-  return fail(MLA_ERR_UNSUPPORTED, "prefill not built yet");
+  mla_status s;
+  if ((s = check_tensor(q, "q", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  const int64_t Tq = q->shape[0], H = q->shape[1];
+  if (q->shape[2] != 192) return fail(MLA_ERR_SHAPE, "q: head width %lld, expected 192", (long long)q->shape[2]);
+  if ((s = check_tensor(k, "k", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  if ((s = check_tensor(v, "v", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  const int64_t Tk = k->shape[0];
+  if (k->shape[1] != H || k->shape[2] != 128) return fail(MLA_ERR_SHAPE, "k: shape must be [Tk, %lld, 128]", (long long)H);
+  if (v->shape[0] != Tk || v->shape[1] != H || v->shape[2] != 128)
+    return fail(MLA_ERR_SHAPE, "v: shape must be [%lld, %lld, 128]", (long long)Tk, (long long)H);
+  if ((s = check_tensor(input_row_offsets, "input_row_offsets", MLA_DTYPE_U32, 1, false)) != MLA_OK) return s;
+  const int64_t B = input_row_offsets->shape[0] - 1;
+  if (B < 1) return fail(MLA_ERR_SHAPE, "input_row_offsets: needs batch + 1 >= 2 entries");
+  if ((s = check_1d(buffer_row_offsets, "buffer_row_offsets", MLA_DTYPE_U32, B + 1)) != MLA_OK) return s;
+  if ((s = check_1d(cache_offsets, "cache_offsets", MLA_DTYPE_U32, B)) != MLA_OK) return s;
+  if ((s = check_tensor(page_table, "page_table", MLA_DTYPE_I32, 2, false)) != MLA_OK) return s;
+  if (page_table->shape[0] != B) return fail(MLA_ERR_SHAPE, "page_table: %lld rows, expected batch %lld", (long long)page_table->shape[0], (long long)B);
+  if ((s = check_1d(cache_lens, "cache_lens", MLA_DTYPE_I32, B)) != MLA_OK) return s;
+  if ((s = check_tensor(latent_cache, "latent_cache", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  if (latent_cache->shape[2] != 576) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576", (long long)latent_cache->shape[2]);
+  const int64_t PS = latent_cache->shape[1];
+  if (PS < 1) return fail(MLA_ERR_SHAPE, "latent_cache: page size must be >= 1");
+  if (PS > 1 && latent_cache->stride[1] != 576)
+    return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride 576)");
+  if ((s = check_tensor(out, "out", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  if (out->shape[0] != Tq || out->shape[1] != H || out->shape[2] != 128)
+    return fail(MLA_ERR_SHAPE, "out: shape must be [%lld, %lld, 128]", (long long)Tq, (long long)H);
+  if (H < 1 || H > 1024) return fail(MLA_ERR_UNSUPPORTED, "num_heads %lld not in [1, 1024]", (long long)H);
+  if (mask == MLA_MASK_SLIDING_WINDOW_CAUSAL) return fail(MLA_ERR_UNSUPPORTED, "prefill takes the causal or the null mask");
+  if (mask != MLA_MASK_NULL && mask != MLA_MASK_CAUSAL) return fail(MLA_ERR_VALUE, "mask %d unknown", mask);
+  if (!std::isfinite(scale)) return fail(MLA_ERR_VALUE, "scale must be finite");
+  if (Tq > kMaxRows || Tk > kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 query or key rows");
+  if (page_table->shape[1] * PS > (int64_t)1 << 40) return fail(MLA_ERR_UNSUPPORTED, "max_pages * page_size too large");
+  if (((Tq + 127) / 128 + B) * H > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many work-groups");
+  if (Tq == 0) return ok();
+
+  mla::PrefillArgs a{};
+  a.q = (const uint16_t*)q->data;
+  a.q_tok = q->stride[0];
+  a.q_head = q->stride[1];
+  a.k = (const uint16_t*)k->data;
+  a.k_tok = k->stride[0];
+  a.k_head = k->stride[1];
+  a.v = (const uint16_t*)v->data;
+  a.v_tok = v->stride[0];
+  a.v_head = v->stride[1];
+  a.buf_off = (const uint32_t*)buffer_row_offsets->data;
+  a.cache_off = (const uint32_t*)cache_offsets->data;
+  a.in_off = (const uint32_t*)input_row_offsets->data;
+  a.page_table = (const int32_t*)page_table->data;
+  a.pt_row = page_table->stride[0];
+  a.cache_lens = (const int32_t*)cache_lens->data;
+  a.cache = (const uint8_t*)latent_cache->data;
+  a.page_bytes = latent_cache->stride[0] * 2;
+  a.num_pages = latent_cache->shape[0];
+  a.B = (int32_t)B;
+  a.Tq = (int32_t)Tq;
+  a.Tk = (int32_t)Tk;
+  a.H = (int32_t)H;
+  a.PS = (int32_t)PS;
+  a.max_pages = (int32_t)page_table->shape[1];
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.mask = mask;
+  a.out = (uint16_t*)out->data;
+  a.o_tok = out->stride[0];
+  a.o_head = out->stride[1];
+  // the error word lives in the stream's workspace (allocated on first use)
+  bool cap = false;
+  if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
+  void* ws = nullptr;
+  if ((s = grow_workspace(current_device(), stream, 0, cap, &ws)) != MLA_OK) return s;
+  a.err = (uint32_t*)((char*)ws + kErrOffset);
+  mla::KernelTimer tslot;
+  mla::KernelTimer* timer = profile_timer(&tslot);
+  const hipError_t e = mla::launch_prefill(a, (hipStream_t)stream, timer);
+  profile_keep(timer, e == hipSuccess);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"

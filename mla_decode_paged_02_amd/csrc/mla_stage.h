@@ -62,15 +62,17 @@ __device__ __forceinline__ void wave_acc_init(WaveAcc<HB>& acc) {
 
 // valid: bit j set when key j of the stage is visible (block-uniform).  kscale (KSCALE
 // only): per-key factors of the stage in LDS, applied to the logit and to the value row.
-// Online softmax of one 16-head block of a stage: su0 / su1 are the score accumulators of
-// key tiles u = 0, 1 (lane 16g+n: head n, keys 8g + 4u + i).  Returns P^T as the MFMA
-// operand (lane 16g+n: head n, keys 8g..8g+7) and updates the running max m (log2 units,
-// the same in the four lanes of a head) and this lane's share l of the denominator.
+// Online softmax of one 16-row block of a stage (a row is a head in decode, a query in
+// prefill): su0 / su1 are the score accumulators of key tiles u = 0, 1 (lane 16g+n: row n,
+// keys 8g + 4u + i).  lane_bits: bit j set when key 8g + j counts for this lane's row
+// (all_valid: every key of the stage counts for every row).  Returns P^T as the MFMA
+// operand (lane 16g+n: row n, keys 8g..8g+7) and updates the running max m (log2 units,
+// the same in the four lanes of a row) and this lane's share l of the denominator.
 // The common case needs no cross-lane work: the max is only reduced over the four lanes of
 // a head when some lane's keys exceed m by more than kRescaleSlack; rescale(alpha) then
 // multiplies the block's O by alpha.
 template <bool KSCALE, class Rescale>
-__device__ __forceinline__ bf16x8 softmax_block(f32x4 su0, f32x4 su1, uint32_t valid, bool all_valid, int gq,
+__device__ __forceinline__ bf16x8 softmax_block(f32x4 su0, f32x4 su1, uint32_t lane_bits, bool all_valid,
                                                 float scale_log2, const float (&ks8)[2][4], float& m, float& l,
                                                 Rescale rescale) {
   float x[8];
@@ -85,7 +87,7 @@ __device__ __forceinline__ bf16x8 softmax_block(f32x4 su0, f32x4 su1, uint32_t v
   }
   if (!all_valid) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = ((valid >> (8 * gq + j)) & 1u) ? x[j] : -INFINITY;
+    for (int j = 0; j < 8; ++j) x[j] = ((lane_bits >> j) & 1u) ? x[j] : -INFINITY;
   }
   float lmax = x[0];
 #pragma unroll
@@ -181,7 +183,7 @@ __device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const 
   bf16x8 pf[HB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb)
-    pf[hb] = softmax_block<KSCALE>(sacc[0][hb], sacc[1][hb], valid, all_valid, g.gq, scale_log2, ks8, acc.m[hb],
+    pf[hb] = softmax_block<KSCALE>(sacc[0][hb], sacc[1][hb], valid >> (8 * g.gq), all_valid, scale_log2, ks8, acc.m[hb],
                                    acc.l[hb], [&](float alpha) {
 #pragma unroll
                                      for (int cb = 0; cb < 32; ++cb) acc.o[cb][hb] *= alpha;
@@ -352,7 +354,7 @@ __device__ __forceinline__ void stage_compute2(const MLA_LDS uint8_t* buf, const
   bf16x8 pf[2];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb)
-    pf[hb] = softmax_block<KSCALE>(hb == 0 ? s00 : s01, hb == 0 ? s10 : s11, valid, all_valid, g.gq, scale_log2,
+    pf[hb] = softmax_block<KSCALE>(hb == 0 ? s00 : s01, hb == 0 ? s10 : s11, valid >> (8 * g.gq), all_valid, scale_log2,
                                    ks8, acc.m[hb], acc.l[hb], [&](float alpha) {
       // The previous stage's last writes of O were followed by this stage's score MFMAs,
       // far more than the wait states a read needs.  One quad at a time through ordinary

@@ -157,3 +157,39 @@ def test_sparse_empty_batch_is_a_no_op():
                                     idx=_t(FAKE, 3, (0, 32)), topk=_t(FAKE, 3, (0,)),
                                     out=_t(FAKE, 0, (0, 16, 512))))
     assert st == 0
+
+
+def prefill_args(**over):
+    Tq, Tk, H, B, PS = 8, 12, 16, 2, 64
+    a = dict(q=_t(FAKE, 0, (Tq, H, 192)), k=_t(FAKE, 0, (Tk, H, 128)), v=_t(FAKE, 0, (Tk, H, 128)),
+             bro=_t(FAKE, 4, (B + 1,)), co=_t(FAKE, 4, (B,)), off=_t(FAKE, 4, (B + 1,)),
+             pt=_t(FAKE, 3, (B, 4)), lens=_t(FAKE, 3, (B,)), cache=_t(FAKE, 0, (8, PS, 576)),
+             out=_t(FAKE, 0, (Tq, H, 128)), scale=0.07, mask=1)
+    a.update(over)
+    return a
+
+
+def call_prefill(a):
+    lib = m.library()
+    r = ctypes.byref
+    st = lib.mla_prefill_paged(r(a["q"]), r(a["k"]), r(a["v"]), r(a["bro"]), r(a["co"]), r(a["off"]),
+                               r(a["pt"]), r(a["lens"]), r(a["cache"]), ctypes.c_float(a["scale"]),
+                               a["mask"], r(a["out"]), None)
+    return st, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=_t(FAKE, 0, (8, 16, 576))), 2),                # decode-width q
+    (dict(k=_t(FAKE, 0, (12, 8, 128))), 2),                # k heads
+    (dict(v=_t(FAKE, 0, (11, 16, 128))), 2),               # v rows != k rows
+    (dict(bro=_t(FAKE, 4, (4,))), 2),                      # offsets length
+    (dict(co=_t(FAKE, 3, (2,))), 3),                       # cache_offsets dtype
+    (dict(out=_t(FAKE, 0, (8, 16, 512))), 2),              # out width
+    (dict(mask=2), 5),                                     # sliding window: not for prefill
+    (dict(mask=7), 8),
+    (dict(scale=float("nan")), 8),
+])
+def test_prefill_validation(over, status):
+    st, msg = call_prefill(prefill_args(**over))
+    assert st == status, (st, msg)
+    assert msg
