@@ -1,19 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of MLA decode over a paged latent KV cache on one MI355X.
 
-Workload (the batch-decode configuration): batch 64, one query token per sequence,
-128 heads, head width 576 (512 latent + 64 rope), V = the 512 latent columns, cache
-lengths drawn uniformly from [1024, 4096] (seed 355001), page size 64 with a shuffled
-page table, bf16 q and cache ~ N(0, 1), scale 1/sqrt(192), causal mask, split-KV
-partitions chosen by the library.  A step is one call of the whole decode path
-(attention kernel + log-sum-exp combine) over the batch.
+Default workload (the batch-decode configuration C1): batch 64, one query token per
+sequence, 128 heads, head width 576 (512 latent + 64 rope), V = the 512 latent columns,
+cache lengths drawn uniformly from [1024, 4096] (seed 355001), page size 64 with a
+shuffled page table, bf16 q and cache ~ N(0, 1), scale 1/sqrt(192), causal mask, split-KV
+partitions chosen by the library.  A step is one call of the whole decode path (attention
+kernel + log-sum-exp combine) over the batch.
 
-The timed steps rotate over several independent copies of q and the cache (more bytes
-than the 256 MB last-level cache holds), so every step reads its cache rows from HBM.
-`value` is algorithmic bytes (every visible cache row once plus q) per step divided by
-the step time.  Prints one JSON line.
+The timed steps rotate over several independent copies of the inputs (more bytes than the
+256 MB last-level cache holds), so every step reads its cache rows from HBM.  `value` is
+algorithmic bytes (every visible cache row once plus q) per step divided by the step time.
+Prints one JSON line.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C1|C2|C0]
+Other workloads (--workload): C0 tiny decode, C2 long-context decode, C4 sparse fp8
+decode (GB/s, HBM roofline), C3 ragged prefill (TFLOP/s, bf16 MFMA roofline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C1]
 """
 import argparse
 import hashlib
@@ -27,22 +30,34 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode GB/s (% of HBM peak) + tokens/s, B=64 H=128 ctx≤4K, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c1_traffic.txt")
-KERNEL_SOURCES = ["mla_decode_paged_02_amd/csrc/mla_decode.hip",
-                  "mla_decode_paged_02_amd/csrc/mla_device.h"]
+CSRC = os.path.join(ROOT, "mla_decode_paged_02_amd", "csrc")
+
+DESCRIPTIONS = {
+    "C0": "C0: B=2 H=16 lens {37,100} PS=16, 1 query token per sequence, head 576 / V 512, causal, bf16",
+    "C1": "C1: B=64 H=128 lens U[1024,4096] PS=64, 1 query token per sequence, head 576 / V 512, causal, bf16",
+    "C2": "C2: B=8 H=128 lens {32768x4,65536x4} PS=64, 1 query token per sequence, head 576 / V 512, causal, bf16",
+    "C3": "C3: ragged causal prefill, new {512,1024,2048,3968} after {0,256,0,1024}, H=128, q 192 / v 128, bf16",
+    "C4": "C4: sparse decode, B=32 H=128, 16384 rows/seq PS=64, top-k U[1024,2048] of 2048 indices, fp8 e4m3 q and cache",
+}
+KERNELS = {"C0": "mla_decode_kernel", "C1": "mla_decode_kernel", "C2": "mla_decode_kernel",
+           "C3": "mla_prefill_kernel", "C4": "mla_sparse_kernel"}
 
 
 def kernel_digest():
+    """Digest of the kernel sources (the traffic summary is only used for the same code)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")) and name != "mla_api.hip":
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def read_traffic(workload):
     """HBM bytes per launch of the decode kernel from the committed counter summary, if it
-    was taken on the current kernel source and this workload; else None."""
+    was taken on the current kernel sources and this workload; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -59,16 +74,19 @@ def read_traffic(workload):
         return None
 
 
-def cpu_baseline(case, alg_bytes, budget_s=12.0):
-    """Time the float64 oracle (as it stands) on this host: whole passes over the
-    workload until about `budget_s` seconds are spent (at least one pass)."""
-    import oracle.mla_oracle as O
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
+        return max([int(p.get("num_threads", 1)) for p in threadpool_info()
+                    if p.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001 - report the affinity size if the BLAS is not visible
-        threads = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(case, alg_bytes, budget_s=12.0):
+    """Time the float64 oracle (as it stands) on this host: whole passes over the dense
+    decode workload until about `budget_s` seconds are spent (at least one pass)."""
+    import oracle.mla_oracle as O
     passes, spent = 0, 0.0
     while passes == 0 or (spent < budget_s and passes < 50):
         t0 = time.perf_counter()
@@ -77,9 +95,69 @@ def cpu_baseline(case, alg_bytes, budget_s=12.0):
         spent += time.perf_counter() - t0
         passes += 1
     return {"value": round(alg_bytes * passes / spent / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
+            "cores": blas_threads(), "kind": "oracle",
             "sample": f"{passes} full pass(es) of the {case.name} workload "
                       f"({case.total_q} query rows), {spent:.1f} s"}
+
+
+def setup(workload, copies, num_partitions, dev):
+    """Device inputs (rotated copies) and a step function for one workload."""
+    import numpy as np
+    import torch
+
+    import mla_decode_paged_02_amd as m
+    from synth import config_case
+
+    case = config_case(int(workload[1]))
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x).astype(np.int32)).to(dev)
+
+    def u8(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(dev)
+
+    def f32(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    n = max(1, copies)
+    if workload in ("C0", "C1", "C2"):
+        q0, c0 = bf16(case.q), bf16(case.latent_cache)
+        sets = [(q0, c0)] + [(q0.clone(), c0.clone()) for _ in range(n - 1)]
+        off, pt, lens = i32(case.input_row_offsets), i32(case.page_table), i32(case.cache_lens)
+        out = torch.empty((case.total_q, case.num_heads, 512), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            q, c = sets[i % len(sets)]
+            m.decode_paged(q, off, pt, lens, c, case.scale, mask=case.mask,
+                           local_window_size=case.window, num_partitions=num_partitions, out=out)
+        return case, step, case.total_q
+    if workload == "C4":
+        q0, c0 = u8(case.q8), u8(case.cache8)
+        sets = [(q0, c0)] + [(q0.clone(), c0.clone()) for _ in range(n - 1)]
+        qs, cs = f32(case.q_scale), f32(case.cache_scale)
+        off, idx, topk = i32(case.input_row_offsets), i32(case.d_indices), i32(case.topk_lengths)
+        out = torch.empty((case.total_q, case.q8.shape[1], 512), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            q, c = sets[i % len(sets)]
+            m.decode_paged_sparse(q, qs, off, c, cs, idx, topk, case.scale,
+                                  num_partitions=num_partitions, out=out)
+        return case, step, case.total_q
+    if workload == "C3":
+        q0, k0, v0 = bf16(case.q), bf16(case.k), bf16(case.v)
+        sets = [(q0, k0, v0)] + [(q0.clone(), k0.clone(), v0.clone()) for _ in range(min(n, 2) - 1)]
+        bro, co, off = i32(case.buffer_row_offsets), i32(case.cache_offsets), i32(case.input_row_offsets)
+        pt, lens, cache = i32(case.page_table), i32(case.cache_lens), bf16(case.latent_cache)
+        out = torch.empty((case.q.shape[0], case.q.shape[1], 128), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            q, k, v = sets[i % len(sets)]
+            m.prefill_paged(q, k, v, bro, co, off, pt, lens, cache, case.scale, mask=case.mask, out=out)
+        return case, step, int(case.q.shape[0])
+    raise SystemExit(f"unknown workload {workload}")
 
 
 def main():
@@ -88,7 +166,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4, help="rotated input copies")
-    ap.add_argument("--workload", default="C1", choices=["C0", "C1", "C2"])
+    ap.add_argument("--workload", default="C1", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--num-partitions", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -114,33 +192,18 @@ def main():
               "this decode path has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import mla_decode_paged_02_amd as m
-    from synth import algorithmic_bytes, algorithmic_flops, config_case
+    from synth import algorithmic_bytes, algorithmic_flops
 
-    k = int(args.workload[1])
-    case = config_case(k)
-    alg_bytes = algorithmic_bytes(case)
-    alg_flops = algorithmic_flops(case)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    q0, c0 = bf16(case.q), bf16(case.latent_cache)
-    copies = [(q0, c0)] + [(q0.clone(), c0.clone()) for _ in range(max(1, args.copies) - 1)]
-    off = torch.from_numpy(case.input_row_offsets.astype(np.int32)).to(dev)
-    pt = torch.from_numpy(case.page_table).to(dev)
-    lens = torch.from_numpy(case.cache_lens).to(dev)
-    out = torch.empty((case.total_q, case.num_heads, 512), dtype=torch.bfloat16, device=dev)
-
-    def step(i):
-        q, c = copies[i % len(copies)]
-        m.decode_paged(q, off, pt, lens, c, case.scale, mask=case.mask,
-                       local_window_size=case.window, num_partitions=args.num_partitions, out=out)
+    wl = args.workload
+    case, step, tokens = setup(wl, args.copies, args.num_partitions, dev)
+    alg_bytes = algorithmic_bytes(case)
+    alg_flops = algorithmic_flops(case)
+    prefill = wl == "C3"
 
     for i in range(args.warmup):
         step(i)
@@ -156,8 +219,7 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - w0) * 1e3
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step = ev0.elapsed_time(ev1) / args.steps
 
     # ---- warm-cache figure (same buffers every step), for context only
     torch.cuda.synchronize()
@@ -168,7 +230,7 @@ def main():
     torch.cuda.synchronize()
     warm_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- the attention kernel alone: HIP events around its launches on this stream
+    # ---- the main kernel alone: HIP events around its launches on this stream
     m.profile_enable(True)
     for i in range(args.steps):
         step(i)
@@ -178,11 +240,24 @@ def main():
     k_avg_ms = kms / max(1, launches)
 
     gbs = alg_bytes / (ms_step * 1e-3) / 1e9
-    achieved = alg_bytes / (k_avg_ms * 1e-3) / 1e9
+    tflops = alg_flops / (ms_step * 1e-3) / 1e12
+    if prefill:
+        achieved = alg_flops / (k_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+        metric, value, unit = "MLA prefill TFLOP/s (causal pairs x 2H(192+128)), 1 GPU", tflops, "TFLOP/s"
+    else:
+        achieved = alg_bytes / (k_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl)}
+        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else ''}decode GB/s, {wl}, 1 GPU"
+        value, unit = gbs, "GB/s"
+    roof.update({"kernel": KERNELS[wl], "kernel_avg_us": round(k_avg_ms * 1e3, 3),
+                 "kernel_launches_timed": launches})
     res = {
-        "metric": METRIC,
-        "value": round(gbs, 2),
-        "unit": "GB/s",
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -190,41 +265,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 in, bf16 MFMA" if wl == "C4" else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{case.name}: " + {0: "B=2 H=16 lens {37,100} PS=16",
-                                             1: "B=64 H=128 lens U[1024,4096] PS=64",
-                                             2: "B=8 H=128 lens {32768x4,65536x4} PS=64"}[k]
-                        + ", 1 query token per sequence, head 576 / V 512, causal, bf16",
-            "batch": case.batch,
-            "heads": case.num_heads,
-            "page_size": case.page_size,
+            "workload": DESCRIPTIONS[wl],
             "num_partitions": args.num_partitions if args.num_partitions > 0 else "library",
-            "rotated_input_copies": len(copies),
-            "seed": 355000 + k,
+            "rotated_input_copies": args.copies,
+            "seed": 355000 + int(wl[1]),
         },
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(case.total_q / (ms_step * 1e-3), 1),
+        "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "algorithmic_bytes_per_step": int(alg_bytes),
         "algorithmic_flops_per_step": int(alg_flops),
-        "tflops": round(alg_flops / (ms_step * 1e-3) / 1e12, 2),
-        "warm_cache_value": round(alg_bytes / (warm_ms * 1e-3) / 1e9, 2),
+        "tflops": round(tflops, 2),
+        "warm_cache_value": round((alg_flops / 1e12 if prefill else alg_bytes / 1e9) / (warm_ms * 1e-3), 2),
         "wall_ms_timed_region": round(wall_ms, 3),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic(case.name),
-            "kernel": "mla_decode_kernel",
-            "kernel_avg_us": round(k_avg_ms * 1e3, 3),
-            "kernel_launches_timed": launches,
-        },
+        "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if wl == "C1" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, alg_bytes)
     print(json.dumps(res), flush=True)
 
