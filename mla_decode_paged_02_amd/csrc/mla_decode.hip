@@ -249,8 +249,14 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
   int pa_n = 0;
   const int npro = nst < kNumBuf - 1 ? nst : kNumBuf - 1;
   auto direct_page = [&](int st) { return ld_const(pt + st * kStageKeys / a.PS); };
-  for (int k = 0; k < npro; ++k) issue(s_first + k, k, KPAGES != 0 ? direct_page(s_first + k) : 0);
-  if (KPAGES != 0 && kNumBuf - 1 < nst) pa_n = direct_page(s_first + kNumBuf - 1);
+  // all the prologue's page ids first (independent scalar loads: one latency, not four)
+  int pa_pro[kNumBuf];
+#pragma unroll
+  for (int k = 0; k < kNumBuf; ++k) pa_pro[k] = (KPAGES != 0 && k < nst) ? direct_page(s_first + k) : 0;
+#pragma unroll
+  for (int k = 0; k < kNumBuf - 1; ++k)
+    if (k < npro) issue(s_first + k, k, pa_pro[k]);
+  if (KPAGES != 0 && kNumBuf - 1 < nst) pa_n = pa_pro[kNumBuf - 1];
   if (KPAGES != 0) window_load();
 
   // ---- query fragments: B operand of S^T = K Q^T (lane holds q[h][32ks + 8gq .. +8]).
@@ -321,8 +327,12 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
   }
 
   if (bad_page) atomicOr(a.err, kErrPageId);
-  if constexpr (HB == 2)
-    stage_epilogue2(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
+  if constexpr (HB == 2) {
+    // every wave is done with the stage buffers before they take the output rows
+    stage_barrier();
+    stage_epilogue2(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse,
+                    tiles + wave * 32 * 1024);
+  }
   else
     stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
 }
@@ -330,6 +340,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
 template <int HB, int NW, int KPAGES>
 __global__ __launch_bounds__(NW * 64, 1) void mla_decode_kernel(const DecodeArgs a, const SplitPlan plan) {
   __shared__ __attribute__((aligned(1024))) uint8_t tiles_raw[kNumBuf * kStageBytes];
+  static_assert(kNumBuf * kStageBytes >= 4 * 32 * 1024, "epilogue staging");
   __shared__ PlanLds L;
   MLA_LDS uint8_t* tiles = (MLA_LDS uint8_t*)tiles_raw;
   plan_run<NW * 64>(

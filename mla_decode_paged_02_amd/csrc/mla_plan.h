@@ -4,16 +4,17 @@
 // per-row tile counts itself (no host round trip).  Three modes:
 //   row parts (balanced, when every non-empty row can have a work-group of its own): with
 //     S the smallest tile count such that sum_t ceil(nt_t / S) <= grid, row t is cut into
-//     P_t = ceil(nt_t / S) near-equal parts, numbered in row order; work-group gid takes
-//     part gid, so it runs one segment with one prologue and one epilogue.  A row in
+//     P_t = ceil(nt_t / S) near-equal parts, numbered in row order; a work-group takes one
+//     part, so it runs one segment with one prologue and one epilogue.  A row in
 //     several parts leaves each part's normalised output and log2-sum-exp in the slot of
 //     the part's number;
 //   stream (balanced, many rows): the concatenated tiles are cut into equal runs; a
 //     work-group walks the rows its run touches, writing rows it covers completely and
-//     leaving the at most two it covers in part in slot 2*gid (the row of the run's first
-//     tile) or 2*gid + 1 (the row of its last tile);
-//   fixed (num_partitions = P): work-group gid = (row, part) takes the part-th of P equal
-//     tile ranges of its row and uses slot gid.
+//     leaving the at most two it covers in part in slot 2*r (the row of run r's first
+//     tile) or 2*r + 1 (the row of its last tile);
+//   fixed (num_partitions = P): piece t * P + part takes the part-th of P equal tile
+//     ranges of row t and uses that slot.
+// Pieces are dealt to work-groups by plan_piece.
 // Work-group 0 publishes every row's split in row_meta for the combine kernel, which
 // merges the parts of split rows by their log2-sum-exps: [0] = mode (0 stream, 1 row
 // parts), [1] = tiles per run (stream) or per part (row parts), then per row the pair
@@ -93,6 +94,15 @@ __device__ __forceinline__ int plan_chunk_scan(int v, int* buf, int& chunk_total
   return before + v;
 }
 
+// The piece (part, run or fixed part) work-group gid takes.  Pieces are numbered so that
+// consecutive ones -- the parts of one row -- go to work-groups that the dispatcher places
+// on the same XCD (work-groups are dealt to the eight XCDs round-robin), where they share
+// that XCD's L2 for the row's query and page table.  Only the speed depends on this.
+__device__ __forceinline__ int plan_piece(int gid, int nwg) {
+  if (nwg % 8 != 0) return gid;
+  return (gid & 7) * (nwg >> 3) + (gid >> 3);
+}
+
 // Zero the output row t (rows with no visible key).
 template <int NT>
 __device__ void plan_zero_row(const SplitPlan& p, int t) {
@@ -148,7 +158,8 @@ __device__ __forceinline__ int split_slot(const RowSplit& rs, int c) {
 // range [s, e) of row r0 (r0 = -1: no part for it), pre = -1, writes row_meta (work-group
 // 0) and clears the rows without keys that fall to this work-group.
 template <int NT>
-__device__ __forceinline__ bool plan_row_parts(const SplitPlan& p, PlanLds& L, int& s, int& e, int& r0, int& pre) {
+__device__ __forceinline__ bool plan_row_parts(const SplitPlan& p, PlanLds& L, int piece, int& s, int& e, int& r0,
+                                               int& pre) {
   const int gid = blockIdx.x, tid = threadIdx.x;
   constexpr int kRows = 64;  // red[64..66]: rows with keys, total tiles, largest row
   for (int i = tid; i < 68; i += NT) L.red[i] = 0;
@@ -176,31 +187,48 @@ __device__ __forceinline__ bool plan_row_parts(const SplitPlan& p, PlanLds& L, i
   const int maxnt = __builtin_amdgcn_readfirstlane(L.red[kRows + 2]);
   if (rows == 0 || rows > p.grid) return false;
 
-  // smallest S with sum_t ceil(nt_t / S) <= grid: at least ceil(total / grid), at most the
-  // largest row (one part per row).  Each trial is one block sum in its own counter.
-  int trial = 0;
-  auto parts_fit = [&](int S) {
-    int c = 0;
-    for (int t = tid; t < p.T; t += NT) c += (geo_tiles(L.geo[t]) + S - 1) / S;
-    c = wave_sum_i32(c);
-    if ((tid & 63) == 0) atomicAdd(&L.red[trial], c);
-    __syncthreads();
-    const int sum = __builtin_amdgcn_readfirstlane(L.red[trial]);
-    ++trial;
-    return sum <= p.grid;
-  };
-  int S = max(1, (total + p.grid - 1) / p.grid);
-  if (S < maxnt && !parts_fit(S)) {
-    int lo = S, hi = maxnt;  // lo fails, hi fits
-    if (lo + 1 < hi && parts_fit(lo + 1)) hi = lo + 1;
-    else if (lo + 1 < hi) lo = lo + 1;
-    while (hi - lo > 1) {
-      const int mid = lo + (hi - lo) / 2;
-      if (parts_fit(mid)) hi = mid; else lo = mid;
+  // Smallest S with sum_t ceil(nt_t / S) <= grid.  It lies in [ceil(total / grid), hi]:
+  // every row rounds up by less than one part, so S >= total / (grid - rows) fits, and
+  // S = maxnt (one part per row) always fits.  One pass tests the first eight candidates
+  // together (one block sum each); a binary search covers a wider bracket.
+  const int S0 = max(1, (total + p.grid - 1) / p.grid);
+  const int hi = rows < p.grid ? min(maxnt, (total + (p.grid - rows) - 1) / (p.grid - rows)) : maxnt;
+  int S = hi;
+  {
+    int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int t = tid; t < p.T; t += NT) {
+      const int nt = geo_tiles(L.geo[t]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) c[k] += (nt + S0 + k - 1) / (S0 + k);
     }
-    S = hi;
-  } else if (S >= maxnt) {
-    S = maxnt;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      c[k] = wave_sum_i32(c[k]);
+      if ((tid & 63) == 0) atomicAdd(&L.red[k], c[k]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 7; k >= 0; --k)
+      if (S0 + k <= hi && __builtin_amdgcn_readfirstlane(L.red[k]) <= p.grid) S = S0 + k;
+  }
+  if (S == hi && S0 + 8 < hi) {
+    int trial = 8;  // counters red[8..63]
+    auto parts_fit = [&](int Sx) {
+      int c = 0;
+      for (int t = tid; t < p.T; t += NT) c += (geo_tiles(L.geo[t]) + Sx - 1) / Sx;
+      c = wave_sum_i32(c);
+      if ((tid & 63) == 0) atomicAdd(&L.red[trial], c);
+      __syncthreads();
+      const int sum = __builtin_amdgcn_readfirstlane(L.red[trial]);
+      ++trial;
+      return sum <= p.grid;
+    };
+    int lo = S0 + 7, up = hi;  // lo fails, up fits
+    while (up - lo > 1) {
+      const int mid = lo + (up - lo) / 2;
+      if (parts_fit(mid)) up = mid; else lo = mid;
+    }
+    S = up;
   }
 
   // parts per row, their numbering, this work-group's part, rows to clear
@@ -223,9 +251,9 @@ __device__ __forceinline__ bool plan_row_parts(const SplitPlan& p, PlanLds& L, i
         p.row_meta[2 + 2 * t] = first;
         p.row_meta[3 + 2 * t] = P;
       }
-      if (P > 0 && first <= gid && gid < first + P) {
+      if (P > 0 && first <= piece && piece < first + P) {
         L.found[0] = t;
-        L.found[1] = gid - first;
+        L.found[1] = piece - first;
       }
       if (nt == 0 && t % p.grid == gid) {
         const int slot = atomicAdd(&L.zero[63], 1);
@@ -267,6 +295,7 @@ template <int NT, class Fill, class GeoOf, class Segment>
 __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fill, GeoOf geo_of,
                                          Segment segment) {
   const int gid = blockIdx.x;
+  const int piece = plan_piece(gid, (int)gridDim.x);
   const bool table = p.T <= kPlanMaxRows;
   if (table) {
     fill(L);
@@ -279,7 +308,7 @@ __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fi
   int s = 0, e = 0, r0 = -1, pre = 0;
   if (p.nparts >= 1) {
     const int P = p.nparts;
-    const int t = gid / P, part = gid - t * P;
+    const int t = piece / P, part = piece - t * P;
     if (t >= p.T) return;
     const int nt = geo_tiles(row_geo(t));
     const int ta = (int)((long long)part * nt / P), tc = (int)((long long)(part + 1) * nt / P);
@@ -287,14 +316,14 @@ __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fi
       if (P == 1) {
         plan_zero_row<NT>(p, t);
       } else {
-        for (int h = threadIdx.x; h < p.H; h += NT) p.part_lse[(int64_t)gid * p.H + h] = -INFINITY;
+        for (int h = threadIdx.x; h < p.H; h += NT) p.part_lse[(int64_t)piece * p.H + h] = -INFINITY;
       }
       return;
     }
     r0 = t;  // a run within a single row
     s = ta;
     e = tc;
-  } else if (table && plan_row_parts<NT>(p, L, s, e, r0, pre)) {
+  } else if (table && plan_row_parts<NT>(p, L, piece, s, e, r0, pre)) {
     // row parts: one segment (or none) per work-group
     if (r0 < 0) return;
   } else {
@@ -321,7 +350,7 @@ __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fi
     }
     total = __builtin_amdgcn_readfirstlane(total);
     const int W = (total + p.grid - 1) / p.grid;
-    s = gid * W;
+    s = piece * W;
     e = min(total, s + W);
     if (gid == 0 && threadIdx.x == 0) {
       p.row_meta[0] = 0;  // stream mode
@@ -365,7 +394,7 @@ __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fi
     if (s >= e || r0 < 0) return;
   }
   // one call site for the segment work, whatever the mode.  Fixed and row-parts modes
-  // (pre < 0) run the single tile range [s, e) of row r0 and use slot gid.
+  // (pre < 0) run the single tile range [s, e) of row r0 and use slot `piece`.
   const bool fixed = p.nparts >= 1 || pre < 0;
   for (int r = r0; r < p.T && pre < e; ++r) {
     RowGeo g = row_geo(r);
@@ -378,7 +407,7 @@ __device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fi
     const int ta = fixed ? s : max(s, pre) - pre;
     const int tc = fixed ? e : min(e, run_end) - pre;
     const bool full = p.nparts >= 1 ? p.nparts == 1 : (ta == 0 && tc == nt);
-    const int slot = fixed ? gid : (pre <= s ? 2 * gid : 2 * gid + 1);
+    const int slot = fixed ? piece : (pre <= s ? 2 * piece : 2 * piece + 1);
     segment(r, g, ta, tc, full, slot);
     if (fixed) break;
     pre += nt;

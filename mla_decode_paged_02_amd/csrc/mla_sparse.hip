@@ -215,20 +215,26 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   }
 
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(a.err, kErrSparseIndex);
-  if constexpr (HB == 2)
-    stage_epilogue2(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
+  if constexpr (HB == 2) {
+    // every wave is done with the stage buffers before they take the output rows
+    stage_barrier();
+    stage_epilogue2(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse,
+                    tiles + wave * 32 * 1024);
+  }
   else
     stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
 }
 
 template <int HB, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs a, const SplitPlan plan) {
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles_raw[kSpTiles * kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t land_raw[kSpRaw * kRawStageBytes];
+  // the widened tiles, then the fp8 landing buffers, in one block: the epilogue stages up
+  // to 4 x 32 KB of output rows across both
+  __shared__ __attribute__((aligned(1024))) uint8_t buf_raw[kSpTiles * kStageBytes + kSpRaw * kRawStageBytes];
+  static_assert(kSpTiles * kStageBytes + kSpRaw * kRawStageBytes >= 4 * 32 * 1024, "epilogue staging");
   __shared__ __attribute__((aligned(256))) float ksc_raw[kSpScale * 64];
   __shared__ PlanLds L;
-  MLA_LDS uint8_t* tiles = (MLA_LDS uint8_t*)tiles_raw;
-  MLA_LDS uint8_t* land = (MLA_LDS uint8_t*)land_raw;
+  MLA_LDS uint8_t* tiles = (MLA_LDS uint8_t*)buf_raw;
+  MLA_LDS uint8_t* land = tiles + kSpTiles * kStageBytes;
   MLA_LDS float* ksc = (MLA_LDS float*)ksc_raw;
   plan_run<NW * 64>(
       plan, L, [&](PlanLds& l) { sparse_fill<NW * 64>(a, l); }, [&](int t) { return sparse_row_geo(a, t); },

@@ -398,26 +398,47 @@ __device__ __forceinline__ void stage_compute2(const MLA_LDS uint8_t* buf, const
   }
 }
 
+// Writes the wave's 32 heads h0 .. h0+31 of row t: the final bf16 output, or the split
+// row's normalised part (bf16) and its log2-sum-exp into `slot`.  The normalised values go
+// through this wave's 32 KB of LDS (`stage`, free once the last stage has been computed)
+// so that every store instruction writes one head's 1 KB row contiguously; head rows are
+// XOR-swizzled in 16-byte units so the transposing writes spread over the banks.
 __device__ __forceinline__ void stage_epilogue2(WaveAcc2& acc, int lane, int h0, int t, bool full, int slot,
                                                 int H, uint16_t* out, int64_t o_tok, int64_t o_head,
-                                                uint16_t* part_o, float* part_lse) {
+                                                uint16_t* part_o, float* part_lse, MLA_LDS uint8_t* stage) {
   mfma_fence_acc(acc.o);
   const int gq = lane >> 4, ln = lane & 15;
+  float inv[2];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const float l_tot = wave_sum_xor16_32(acc.l[hb]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int h = h0 + 16 * hb + ln;
-    uint16_t* orow = full ? out + (int64_t)t * o_tok + (int64_t)h * o_head + 4 * gq
-                          : part_o + ((int64_t)slot * H + h) * kLatentDim + 4 * gq;
+    inv[hb] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (!full && gq == 0)
+      part_lse[(int64_t)slot * H + h0 + 16 * hb + ln] = l_tot > 0.f ? acc.m[hb] + __log2f(l_tot) : -INFINITY;
+  }
+  // lane 16g+n holds columns 16cb + 4g .. +3 of head 16hb + n
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int hl = 16 * hb + ln;
+    MLA_LDS uint8_t* row = stage + hl * 1024;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
       const f32x4 v = acc.o[2 * cb + hb];
-      const uint32_t lo = (uint32_t)bf16_bits_rne(v[0] * inv) | ((uint32_t)bf16_bits_rne(v[1] * inv) << 16);
-      const uint32_t hi = (uint32_t)bf16_bits_rne(v[2] * inv) | ((uint32_t)bf16_bits_rne(v[3] * inv) << 16);
-      *(uint2*)(orow + 16 * cb) = make_uint2(lo, hi);
+      const uint32_t lo = (uint32_t)bf16_bits_rne(v[0] * inv[hb]) | ((uint32_t)bf16_bits_rne(v[1] * inv[hb]) << 16);
+      const uint32_t hi = (uint32_t)bf16_bits_rne(v[2] * inv[hb]) | ((uint32_t)bf16_bits_rne(v[3] * inv[hb]) << 16);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      *(MLA_LDS u32x2*)(row + ((32 * cb + 8 * gq) ^ ((hl & 15) << 4))) = u32x2{lo, hi};
     }
-    if (!full && gq == 0) part_lse[(int64_t)slot * H + h] = l_tot > 0.f ? acc.m[hb] + __log2f(l_tot) : -INFINITY;
+  }
+  lgkm_wait0();
+  uint16_t* base = full ? out + (int64_t)t * o_tok + (int64_t)h0 * o_head
+                        : part_o + ((int64_t)slot * H + h0) * kLatentDim;
+  const int64_t hstride = full ? o_head : kLatentDim;
+#pragma unroll 4
+  for (int hl = 0; hl < 32; ++hl) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = *(const MLA_LDS u32x4*)(stage + hl * 1024 + ((16 * lane) ^ ((hl & 15) << 4)));
+    *(u32x4*)(base + hl * hstride + 8 * lane) = w;
   }
 }
 
