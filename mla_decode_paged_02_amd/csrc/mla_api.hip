@@ -468,6 +468,7 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
   a.cs_page = cache_scale ? cache_scale->stride[0] : 0;
   a.num_rows = NP * PS;
   a.PS = (int32_t)PS;
+  a.flat = a.page_bytes == PS * 576 && (cache_scale == nullptr || a.cs_page == PS) ? 1 : 0;
   a.idx = (const int32_t*)d_indices->data;
   a.idx_row = d_indices->stride[0];
   a.idx_cols = (int32_t)d_indices->shape[1];

@@ -353,8 +353,13 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode_kernel(const DecodeArgs
 
 // ---------------------------------------------------------------------------------------
 // Combine: out = sum_c 2^(lse_c - M) O_c / sum_c 2^(lse_c - M) over the parts of a split
-// row, in a fixed order.  Block = (row, 4 heads); thread = (head, 8 columns).
+// row, in a fixed order.  Block = (row, 4 heads); thread = (head, 8 columns).  The parts
+// are read kCombineBatch at a time with every load of a batch in flight together (the
+// kernel is latency-bound: a serial chain of part loads would dominate it); a later batch
+// with a larger maximum rescales what is summed so far.
 // ---------------------------------------------------------------------------------------
+constexpr int kCombineBatch = 8;
+
 __global__ __launch_bounds__(256) void mla_combine_kernel(const SplitPlan p) {
   const int groups = p.H / 4;
   const int t = blockIdx.x / groups, hg = blockIdx.x - t * groups;
@@ -362,28 +367,49 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const SplitPlan p) {
   int n;
   const RowSplit rs = row_split(p, t, n);
   if (n == 0) return;  // the row was written whole (or cleared)
-  float M = -INFINITY;
-  for (int c = 0; c < n; ++c) M = fmaxf(M, p.part_lse[(int64_t)split_slot(rs, c) * p.H + h]);
+  float M = -INFINITY, den = 0.f;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int c0 = 0; c0 < n; c0 += kCombineBatch) {
+    float lv[kCombineBatch];
+    uint4 xv[kCombineBatch];
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      lv[j] = -INFINITY;
+      xv[j] = make_uint4(0, 0, 0, 0);
+      if (c0 + j < n) {
+        const int64_t sl = (int64_t)split_slot(rs, c0 + j) * p.H + h;
+        lv[j] = p.part_lse[sl];
+        xv[j] = *(const uint4*)(p.part_o + sl * kLatentDim + col);
+      }
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) mb = fmaxf(mb, lv[j]);
+    if (mb == -INFINITY) continue;
+    if (mb > M) {
+      const float r = fast_exp2(M - mb);  // 0 while M is -inf
+      den *= r;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= r;
+      M = mb;
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      if (lv[j] == -INFINITY) continue;  // a part that saw no key
+      const float w = fast_exp2(lv[j] - M);
+      den += w;
+      const uint32_t xw[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += w * __builtin_bit_cast(float, xw[i] << 16);
+        acc[2 * i + 1] += w * __builtin_bit_cast(float, xw[i] & 0xFFFF0000u);
+      }
+    }
+  }
   uint16_t* dst = p.out + (int64_t)t * p.o_tok + (int64_t)h * p.o_head + col;
   if (M == -INFINITY) {  // no part saw a key (an empty row split by a fixed count)
     *(uint4*)dst = make_uint4(0, 0, 0, 0);
     return;
-  }
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float den = 0.f;
-  for (int c = 0; c < n; ++c) {
-    const int sl = split_slot(rs, c);
-    const float l = p.part_lse[(int64_t)sl * p.H + h];
-    if (l == -INFINITY) continue;
-    const float w = fast_exp2(l - M);
-    den += w;
-    const uint4 x = *(const uint4*)(p.part_o + ((int64_t)sl * p.H + h) * kLatentDim + col);
-    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += w * __builtin_bit_cast(float, xw[j] << 16);
-      acc[2 * j + 1] += w * __builtin_bit_cast(float, xw[j] & 0xFFFF0000u);
-    }
   }
   const float inv = 1.f / den;
   uint32_t wd[4];

@@ -42,24 +42,18 @@ enum : uint32_t {
 enum : int { kMaskNull = 0, kMaskCausal = 1, kMaskSliding = 2 };
 
 // ---------------------------------------------------------------------------------------
-// LDS tile layout: stage rows of 72 16-byte chunks; chunk c of row r is stored at chunk
-// c ^ f(r) (c < 64) or c ^ (f(r) & 7) (the 8 rope chunks), which keeps the 16-byte reads
-// of the score step and the transposing reads of the value step free of bank conflicts
-// for both 32- and 64-bank LDS models.  The map is an involution.
+// LDS tile layout: stage rows of 72 16-byte chunks (1152 bytes, so consecutive rows start
+// half the 64 banks apart); chunk c of row r is stored at chunk c ^ s(r) with s(r) in 0..7,
+// a permutation inside each aligned group of 8 chunks.  s spreads the 16 rows of a score
+// read (16-byte reads, 16 lanes a cycle) and the 8 rows of a transposing value read
+// (8-byte reads, 32 lanes a cycle) over all banks, and because it leaves bits 3 and up of
+// the chunk index alone, every read of a stage is one per-lane base plus a compile-time
+// offset.  The map is an involution.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int swz_mask(int row) {
-  int f = 0;
-  f ^= (row & 1) ? 10 : 0;
-  f ^= (row & 2) ? 4 : 0;
-  f ^= (row & 4) ? 8 : 0;
-  f ^= (row & 8) ? 15 : 0;
-  f ^= (row & 16) ? 14 : 0;
-  return f;
+  return (((row >> 3) & 1) << 2) | (((row >> 1) & 1) << 1) | ((row >> 4) & 1);
 }
-__device__ __forceinline__ int swz_chunk(int row, int c) {
-  const int f = swz_mask(row);
-  return c ^ (c < 64 ? f : (f & 7));
-}
+__device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ swz_mask(row); }
 
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).  n is
 // clamped to the counter's 6-bit range; waiting for fewer outstanding loads than asked

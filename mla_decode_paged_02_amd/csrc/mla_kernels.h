@@ -49,6 +49,7 @@ struct SparseArgs {
   int64_t cs_page;            // element stride between pages of cache_scale
   int64_t num_rows;           // num_pages * PS: listed rows outside [0, num_rows) are skipped
   int32_t PS;
+  int32_t flat;               // 1: row r is at byte r * 576 and its scale at element r
   const int32_t* idx;         // [T, idx_row]
   int64_t idx_row;            // element stride between index rows
   int32_t idx_cols;           // shape[1] of d_indices (topk is clamped to it)

@@ -28,10 +28,13 @@ constexpr int kRawStageBytes = kStageKeys * kRawRowBytes;   // 18432
 constexpr int kRawPieces = kRawStageBytes / 16;             // 1152 sixteen-byte pieces
 constexpr int kRawPiecesPerRow = kRawRowBytes / 16;         // 36
 constexpr int kRawDma = kRawPieces / 64;                    // 18 wave-wide loads per stage
-constexpr int kSpTiles = 3;                                 // widened bf16 stage buffers
-constexpr int kSpRaw = 2;                                   // fp8 landing buffers
-constexpr int kSpScale = 4;                                 // per-key scale slots (64 floats)
+constexpr int kSpTiles = 2;    // widened bf16 tiles: the one computed, the one being widened
+constexpr int kSpRaw = 3;      // fp8 landing buffers: the one being widened, two in flight
+constexpr int kSpScale = 4;    // per-key scale slots (64 floats): stages k .. k+3
 constexpr int kIdxWindow = 1024;                            // list positions held in LDS
+constexpr int kSpStageLds = kSpTiles * kStageBytes + kSpRaw * kRawStageBytes;
+// the epilogue stages 4 x 32 KB of output rows over the same block
+constexpr int kSpLdsBytes = kSpStageLds > 4 * 32 * 1024 ? kSpStageLds : 4 * 32 * 1024;
 static_assert(sizeof(PlanLds::scan) == kIdxWindow * sizeof(int), "the window lives in the planning scratch");
 
 // Row t's list positions [0, min(topk[t], shape[1] of d_indices)).
@@ -46,6 +49,12 @@ __device__ __forceinline__ void sparse_fill(const SparseArgs& a, PlanLds& L) {
 }
 
 // One row segment: list positions of tiles [ta, tc) of row t.
+//
+// Pipeline (stage k = 32 list positions): at the top of step k the fp8 rows of stage k+1
+// have landed and stage k+2 may still be in flight; the step issues stage k+3 into the
+// landing buffer stage k was widened from, then computes stage k from its bf16 tile while
+// the hook of the score k-steps widens stage k+1 into the other tile.  One barrier per
+// stage orders all of it.
 template <int HB, int NW>
 __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint8_t* tiles, MLA_LDS uint8_t* raw,
                                                MLA_LDS float* kscale, MLA_LDS int* win, int t, const RowGeo& g,
@@ -53,6 +62,8 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   constexpr int NT = NW * 64;
   constexpr int kSlots = kRawDma + 1;                // the rows' pieces, then their scales
   constexpr int kPerWave = (kSlots + NW - 1) / NW;   // loads every wave issues per stage
+  constexpr int kWp = (kRawPieces + NT - 1) / NT;    // pieces each thread widens per stage
+  constexpr bool kTwoPhase = 2 * kWp <= 18;          // read and convert in separate k-steps
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gq = lane >> 4, ln = lane & 15;
@@ -87,10 +98,10 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   window_fill();
 
   bool bad = false;
-  // row of list position p (in the window), or -1 when the key does not count
-  auto row_of = [&](int p) -> int {
-    if (p < klo || p >= khi) return -1;
-    const int r = win[p - wbase];
+  // listed row of position p (read from the window), -1 when the key does not count
+  auto entry = [&](int p) -> int { return p >= klo && p < khi ? win[p - wbase] : -1; };
+  // the entry checked against the pool: rows past its end are skipped and flagged
+  auto checked = [&](int r) -> int {
     if (r < 0) return -1;  // the -1 fill (and any negative entry) is skipped
     if ((int64_t)r >= a.num_rows) {
       bad = true;
@@ -98,21 +109,25 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
     }
     return r;
   };
-  auto row_bytes_off = [&](int r) -> int64_t {
+  auto row_src = [&](int r) -> const uint8_t* {
+    if (a.flat) return a.cache + (int64_t)r * kRawRowBytes;
     const int pg = r / a.PS;
-    return (int64_t)pg * a.page_bytes + (int64_t)(r - pg * a.PS) * kRawRowBytes;
+    return a.cache + (int64_t)pg * a.page_bytes + (int64_t)(r - pg * a.PS) * kRawRowBytes;
   };
-  auto scale_ptr = [&](int r) -> const void* {
+  auto scale_src = [&](int r) -> const void* {
     if (r < 0) return a.zero_row;  // a key that does not count: weight 0
     if (a.cache_scale == nullptr) return a.zero_row + kSparseOneOffset;
+    if (a.flat) return a.cache_scale + r;
     const int pg = r / a.PS;
     return a.cache_scale + (int64_t)pg * a.cs_page + (r - pg * a.PS);
   };
 
-  // Loads of stage st into landing buffer rb and scale slot sb; returns the stage's mask of
-  // counting keys (block-uniform).  Every wave issues exactly kPerWave loads (the spare
-  // slots repeat the scale load), so one wait count serves all waves.
-  auto issue = [&](int st, int rb, int sb) -> uint32_t {
+  // Loads of stage st into landing buffer rb and scale slot sb, in three steps: the window
+  // reads of this lane's entries (issue_read), one load per slot jj (issue_slot) and the
+  // stage's mask of counting keys (issue_mask, block-uniform).  Every wave issues exactly
+  // kPerWave loads (the spare slots repeat the scale load), so one wait count serves all
+  // waves.  The window must cover the stage (issue_window).
+  auto issue_window = [&](int st) {  // block-uniform; drains the stage loads when it moves
     const int kbase = st * kStageKeys;
     if (min(kbase + kStageKeys, khi) - 1 >= wbase + kIdxWindow) {
       all_wait0();
@@ -120,42 +135,110 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
       wbase = max(kbase, klo);
       window_fill();
     }
+  };
+  auto window_covers = [&](int st) { return min(st * kStageKeys + kStageKeys, khi) - 1 < wbase + kIdxWindow; };
+  auto slot_of = [&](int jj) { return min(jj * NW + wave, kSlots - 1); };
+  auto issue_read = [&](int st, int (&rr)[kPerWave], int& rmask) {
+    const int kbase = st * kStageKeys;
     int lane_v = lane;
     asm volatile("" : "+v"(lane_v));
 #pragma unroll
     for (int jj = 0; jj < kPerWave; ++jj) {
-      int J = jj * NW + wave;
-      if (J >= kSlots) J = kSlots - 1;
-      if (J < kRawDma) {
-        const int c = J * 64 + lane_v;
+      const int J = slot_of(jj);
+      rr[jj] = entry(kbase + (J < kRawDma ? (J * 64 + lane_v) / kRawPiecesPerRow : (lane_v & 31)));
+    }
+    rmask = entry(kbase + (lane_v & 31));
+  };
+  // FLAT: rows at r * 576 and scales at element r (no page arithmetic)
+  auto issue_slot = [&](auto flat, int rb, int sb, int jj, int rj) {
+    constexpr bool FLAT = decltype(flat)::value;
+    const int J = slot_of(jj);
+    const int r = checked(rj);
+    if (J < kRawDma) {
+      int lane_v = lane;
+      asm volatile("" : "+v"(lane_v));
+      const int c = J * 64 + lane_v;
+      const int piece = c - (c / kRawPiecesPerRow) * kRawPiecesPerRow;
+      const uint8_t* row = FLAT ? a.cache + (int64_t)r * kRawRowBytes : row_src(r);
+      dma16((r >= 0 ? row : a.zero_row) + piece * 16, raw + rb * kRawStageBytes + J * 1024);
+    } else {
+      // lanes 32..63 repeat lanes 0..31 (the slot holds 64 floats)
+      const void* src = FLAT && r >= 0 && a.cache_scale != nullptr ? (const void*)(a.cache_scale + r) : scale_src(r);
+      dma4(src, kscale + sb * 64);
+    }
+  };
+  auto issue_mask = [&](int rmask) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && rmask >= 0 && (int64_t)rmask < a.num_rows);
+  };
+  auto issue = [&](int st, int rb, int sb) -> uint32_t {
+    issue_window(st);
+    int rr[kPerWave], rmask;
+    issue_read(st, rr, rmask);
+#pragma unroll
+    for (int jj = 0; jj < kPerWave; ++jj) issue_slot(std::false_type(), rb, sb, jj, rr[jj]);
+    return issue_mask(rmask);
+  };
+  // hook steps of the stage compute (value column blocks, when the score registers are
+  // free) that take stage k+3's loads: the window reads, then one slot every other step,
+  // then the mask
+  constexpr bool kHookIssue = kPerWave <= 5;
+  constexpr int kIssueRead = 18;
+
+  // landing buffer -> bf16 tile, swizzled like the dense tiles; piece i of this thread is
+  // read into wr[i] by take() and converted and stored by put().
+  // With 256 threads, thread (r, j) = (tid / 8, tid % 8) widens pieces j + 8i of row r: the
+  // source advances by 128 bytes per piece and, as the swizzle only flips the low three
+  // bits of a chunk index, each destination chunk by 256 bytes, so three per-thread offsets
+  // made once per stage serve every piece.  Other block sizes derive each piece's place
+  // from its index.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 wr[kWp];
+  constexpr bool kLinear = NT == 256;
+  struct WidenGeo {
+    int src, dst0, dst1;
+  };
+  auto widen_geo = [&]() -> WidenGeo {
+    int tid_v = tid;
+    asm volatile("" : "+v"(tid_v));
+    const int r = tid_v >> 3, j = tid_v & 7, f = swz_mask(r);
+    return WidenGeo{r * kRawRowBytes + 16 * j, r * kRowBytes + (((2 * j) ^ f) << 4),
+                    r * kRowBytes + (((2 * j + 1) ^ f) << 4)};
+  };
+  auto put_bf16 = [&](MLA_LDS uint8_t* d0, MLA_LDS uint8_t* d1, const u32x4& w) {
+    const uint2 b0 = e4m3x4_to_bf16x4(w[0]), b1 = e4m3x4_to_bf16x4(w[1]);
+    const uint2 b2 = e4m3x4_to_bf16x4(w[2]), b3 = e4m3x4_to_bf16x4(w[3]);
+    *(MLA_LDS u32x4*)d0 = u32x4{b0.x, b0.y, b1.x, b1.y};
+    *(MLA_LDS u32x4*)d1 = u32x4{b2.x, b2.y, b3.x, b3.y};
+  };
+  auto take = [&](const MLA_LDS uint8_t* src, int i, const WidenGeo& wg) {
+    if constexpr (kLinear) {
+      if (i < 4 || (tid & 7) < 4) wr[i] = *(const MLA_LDS u32x4*)(src + wg.src + 128 * i);
+    } else {
+      // the piece arithmetic is redone per call from an opaque copy of the thread id:
+      // hoisted out of the stage loop it would hold registers the stage compute needs
+      int tid_v = tid;
+      asm volatile("" : "+v"(tid_v));
+      const int c = tid_v + i * NT;
+      if (i * NT + NT <= kRawPieces || tid + i * NT < kRawPieces) wr[i] = *(const MLA_LDS u32x4*)(src + c * 16);
+    }
+  };
+  auto put = [&](MLA_LDS uint8_t* dst, int i, const WidenGeo& wg) {
+    if constexpr (kLinear) {
+      if (i < 4 || (tid & 7) < 4) put_bf16(dst + wg.dst0 + 256 * i, dst + wg.dst1 + 256 * i, wr[i]);
+    } else {
+      int tid_v = tid;
+      asm volatile("" : "+v"(tid_v));
+      const int c = tid_v + i * NT;
+      if (i * NT + NT <= kRawPieces || tid + i * NT < kRawPieces) {
         const int row = c / kRawPiecesPerRow, piece = c - row * kRawPiecesPerRow;
-        const int r = row_of(kbase + row);
-        const uint8_t* src = r >= 0 ? a.cache + row_bytes_off(r) + piece * 16 : a.zero_row + piece * 16;
-        dma16(src, raw + rb * kRawStageBytes + J * 1024);
-      } else {
-        // lanes 32..63 repeat lanes 0..31 (the slot holds 64 floats)
-        dma4(scale_ptr(row_of(kbase + (lane_v & 31))), kscale + sb * 64);
+        MLA_LDS uint8_t* rowp = dst + row * kRowBytes;
+        put_bf16(rowp + swz_chunk(row, 2 * piece) * 16, rowp + swz_chunk(row, 2 * piece + 1) * 16, wr[i]);
       }
     }
-    return (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && row_of(kbase + lane) >= 0);
   };
+  static_assert(!kLinear || kWp == 5, "256 threads: 4.5 pieces each");
 
-  // landing buffer rb (fp8 rows) -> bf16 tile dst, swizzled like the dense tiles
-  auto widen = [&](int rb, MLA_LDS uint8_t* dst) {
-    for (int c = tid; c < kRawPieces; c += NT) {
-      const int row = c / kRawPiecesPerRow, piece = c - row * kRawPiecesPerRow;
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 w = *(const MLA_LDS u32x4*)(raw + rb * kRawStageBytes + c * 16);
-      const uint2 b0 = e4m3x4_to_bf16x4(w[0]), b1 = e4m3x4_to_bf16x4(w[1]);
-      const uint2 b2 = e4m3x4_to_bf16x4(w[2]), b3 = e4m3x4_to_bf16x4(w[3]);
-      MLA_LDS uint8_t* rowp = dst + row * kRowBytes;
-      *(MLA_LDS u32x4*)(rowp + swz_chunk(row, 2 * piece) * 16) = u32x4{b0.x, b0.y, b1.x, b1.y};
-      *(MLA_LDS u32x4*)(rowp + swz_chunk(row, 2 * piece + 1) * 16) = u32x4{b2.x, b2.y, b3.x, b3.y};
-    }
-    lgkm_wait0();  // visible to the other waves after the next barrier
-  };
-
-  // ---- prologue: stages 0 and 1 in flight, q, then stage 0 widened and stage 2 issued
+  // ---- prologue: stages 0 and 1 in flight, q, then stage 2 issued and stage 0 widened
   uint32_t m0 = issue(s_first, 0, 0), m1 = 0, m2 = 0, m3 = 0;
   if (nst > 1) m1 = issue(s_first + 1, 1, 1);
 
@@ -187,28 +270,66 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   const float scale_log2 = a.scale_log2 * q_scale;
   all_wait0();
   stage_barrier();
-  widen(0, tiles);
-  stage_barrier();
-  if (nst > 2) m2 = issue(s_first + 2, 0, 2);
+  if (nst > 2) m2 = issue(s_first + 2, 2, 2);
+  {
+    const WidenGeo wg = widen_geo();
+#pragma unroll
+    for (int i = 0; i < kWp; ++i) {
+      take(raw, i, wg);
+      put(tiles, i, wg);
+    }
+  }
+  lgkm_wait0();
 
   using Acc = std::conditional_t<HB == 2, WaveAcc2, WaveAcc<HB>>;
   Acc acc;
   if constexpr (HB == 2) wave_acc2_init(acc); else wave_acc_init(acc);
-  const LaneGeo lg = make_lane_geo(lane);
 
 #pragma unroll 1
   for (int k = 0; k < nst; ++k) {
-    // stage k+1 has landed (k+2 may still be in flight); every wave is past stage k-1
+    // stage k+1 has landed (k+2 may be in flight); tile k is whole; every wave is past
+    // stage k-1, so its tile and the landing buffer of stage k are free
     if (k + 2 < nst) vm_wait_imm<kPerWave>(); else vm_wait_imm<0>();
     stage_barrier();
-    if (k + 1 < nst) widen((k + 1) % kSpRaw, tiles + ((k + 1) % kSpTiles) * kStageBytes);
-    stage_barrier();
-    if (k + 3 < nst) m3 = issue(s_first + k + 3, (k + 3) % kSpRaw, (k + 3) % kSpScale);
+    // stage k+3 goes into the landing buffer of stage k (widened during step k-1): from
+    // the compute's k-steps when the window covers it, else here
+    const bool ahead = k + 3 < nst;
+    const bool hook_issue = kHookIssue && a.flat && ahead && window_covers(s_first + k + 3);
+    if (ahead && !hook_issue) m3 = issue(s_first + k + 3, (k + 3) % kSpRaw, (k + 3) % kSpScale);
+    int rr[kPerWave], rmask = -1;
+    const bool next = k + 1 < nst;
+    const MLA_LDS uint8_t* wsrc = raw + ((k + 1) % kSpRaw) * kRawStageBytes;
+    MLA_LDS uint8_t* wdst = tiles + ((k + 1) % kSpTiles) * kStageBytes;
+    WidenGeo wg{0, 0, 0};
+    auto hook = [&](int ks) {
+      if (hook_issue) {
+        const int q = ks - kIssueRead;
+        if (q == 0) issue_read(s_first + k + 3, rr, rmask);
+        if (q >= 2 && q <= 2 * kPerWave && (q & 1) == 0)
+          issue_slot(std::true_type(), (k + 3) % kSpRaw, (k + 3) % kSpScale, q / 2 - 1, rr[q / 2 - 1]);
+        if (q == 2 * kPerWave + 1) m3 = issue_mask(rmask);
+      }
+      if (!next) return;
+      if (kLinear && ks == 0) wg = widen_geo();
+      if (kTwoPhase) {
+        if ((ks & 1) == 0 && ks / 2 < kWp) take(wsrc, ks / 2, wg);
+        if ((ks & 1) == 1 && ks / 2 < kWp) put(wdst, ks / 2, wg);
+      } else if (ks < kWp) {
+        take(wsrc, ks, wg);
+        put(wdst, ks, wg);
+      }
+    };
+    // the lane geometry is rebuilt per stage from an opaque lane id: kept across the stage
+    // loop it would take registers the compute needs
+    int lane_g = lane;
+    asm volatile("" : "+v"(lane_g));
+    const LaneGeo lg = make_lane_geo(lane_g);
     const MLA_LDS float* ks = kscale + (k % kSpScale) * 64;
     if constexpr (HB == 2)
-      stage_compute2<true>(tiles + (k % kSpTiles) * kStageBytes, qf, acc, m0, scale_log2, ks, lg);
+      stage_compute2<true>(tiles + (k % kSpTiles) * kStageBytes, qf, acc, m0, scale_log2, ks, lg, hook);
     else
-      stage_compute<HB, true>(tiles + (k % kSpTiles) * kStageBytes, qf, acc, m0, scale_log2, ks, lg);
+      stage_compute<HB, true>(tiles + (k % kSpTiles) * kStageBytes, qf, acc, m0, scale_log2, ks, lg, hook);
+    lgkm_wait0();  // the widened tile, before the barrier that hands it to the other waves
     m0 = m1;
     m1 = m2;
     m2 = m3;
@@ -227,10 +348,8 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
 
 template <int HB, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs a, const SplitPlan plan) {
-  // the widened tiles, then the fp8 landing buffers, in one block: the epilogue stages up
-  // to 4 x 32 KB of output rows across both
-  __shared__ __attribute__((aligned(1024))) uint8_t buf_raw[kSpTiles * kStageBytes + kSpRaw * kRawStageBytes];
-  static_assert(kSpTiles * kStageBytes + kSpRaw * kRawStageBytes >= 4 * 32 * 1024, "epilogue staging");
+  // the widened tiles, then the fp8 landing buffers
+  __shared__ __attribute__((aligned(1024))) uint8_t buf_raw[kSpLdsBytes];
   __shared__ __attribute__((aligned(256))) float ksc_raw[kSpScale * 64];
   __shared__ PlanLds L;
   MLA_LDS uint8_t* tiles = (MLA_LDS uint8_t*)buf_raw;

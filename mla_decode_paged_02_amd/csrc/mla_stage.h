@@ -25,25 +25,33 @@ struct WaveAcc {
   float l[HB];      // this lane's share of the softmax denominator
 };
 
-// Per-lane constants of the LDS access patterns.
+// Per-lane constants of the LDS access patterns: byte offsets within a stage.
+//   ka[u][p]  score read of key tile u at k-step ks with ks % 2 == p; k-step ks reads at
+//             ka[u][ks % 2] + 128 (ks / 2) (the rope k-steps 16, 17 included);
+//   va[u][j]  transposing value read of tile u for column block cb with cb % 4 == j, at
+//             va[u][j] + 128 (cb / 4).
 struct LaneGeo {
-  int gq, rowA0, rowA1, xa0, xa1, rowV0, rowV1, xv0, xv1, vhalf;
+  int gq;
+  int ka[2][2];
+  int va[2][4];
 };
 
 __device__ __forceinline__ LaneGeo make_lane_geo(int lane) {
   LaneGeo g;
   g.gq = lane >> 4;
   const int ln = lane & 15;
-  g.rowA0 = 8 * (ln >> 2) + (ln & 3);  // score tile u = 0 reads this key row; u = 1 adds 4
-  g.rowA1 = g.rowA0 + 4;
-  g.xa0 = g.gq ^ swz_mask(g.rowA0);
-  g.xa1 = g.gq ^ swz_mask(g.rowA1);
-  const int vr = ln >> 2, vq = lane & 3;  // transposing-read coordinates
-  g.rowV0 = 8 * g.gq + vr;
-  g.rowV1 = g.rowV0 + 4;
-  g.xv0 = (vq >> 1) ^ swz_mask(g.rowV0);
-  g.xv1 = (vq >> 1) ^ swz_mask(g.rowV1);
-  g.vhalf = (vq & 1) * 8;
+  const int vq = lane & 3;  // transposing-read coordinates: row 8gq + ln/4, chunk half vq
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ra = 8 * (ln >> 2) + (ln & 3) + 4 * u;  // key row of tile u, MFMA row ln
+    const int sa = swz_mask(ra);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) g.ka[u][p] = ra * kRowBytes + (((4 * p + g.gq) ^ sa) << 4);
+    const int rv = 8 * g.gq + (ln >> 2) + 4 * u;
+    const int sv = swz_mask(rv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g.va[u][j] = rv * kRowBytes + (((2 * j + (vq >> 1)) ^ sv) << 4) + 8 * (vq & 1);
+  }
   return g;
 }
 
@@ -124,8 +132,9 @@ __device__ __forceinline__ bf16x8 softmax_block(f32x4 su0, f32x4 su1, uint32_t l
   return pf;
 }
 
-// hook(ks) runs after the MFMAs of score k-step ks (0..17): the caller's slot for issuing the
-// next stage's loads so that they drain while the matrix cores work.
+// hook(ks) runs after the MFMAs of score k-step ks (0..17) and hook(18 + cb) after those of
+// value column block cb (0..31): the caller's slots for work on other stages (their loads,
+// their conversion) that runs while the matrix cores work.
 struct NoHook {
   __device__ __forceinline__ void operator()(int) const {}
 };
@@ -144,20 +153,10 @@ __device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const 
     // Two waves share each SIMD, so each wave issues its LDS reads just before use and
     // the other wave covers the latency.  Swizzled addresses are formed per read (one
     // xor and one add) rather than kept in registers.
-    const MLA_LDS uint8_t* r0 = buf + g.rowA0 * kRowBytes;
-    const MLA_LDS uint8_t* r1 = buf + g.rowA1 * kRowBytes;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      int c0, c1;
-      if (ks < 16) {
-        c0 = (4 * ks) ^ g.xa0;
-        c1 = (4 * ks) ^ g.xa1;
-      } else {
-        c0 = 64 + ((4 * (ks - 16)) ^ (g.xa0 & 7));
-        c1 = 64 + ((4 * (ks - 16)) ^ (g.xa1 & 7));
-      }
-      const bf16x8 k0 = *(const MLA_LDS bf16x8*)(r0 + c0 * 16);
-      const bf16x8 k1 = *(const MLA_LDS bf16x8*)(r1 + c1 * 16);
+      const bf16x8 k0 = *(const MLA_LDS bf16x8*)(buf + g.ka[0][ks & 1] + 128 * (ks >> 1));
+      const bf16x8 k1 = *(const MLA_LDS bf16x8*)(buf + g.ka[1][ks & 1] + 128 * (ks >> 1));
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         sacc[0][hb] = mfma16x16x32(k0, qf[hb][ks], sacc[0][hb]);
@@ -191,15 +190,14 @@ __device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const 
 
   // ---- O^T += V^T P^T over the stage's 32 keys
   {
-    const MLA_LDS uint8_t* v0b = buf + g.rowV0 * kRowBytes + g.vhalf;
-    const MLA_LDS uint8_t* v1b = buf + g.rowV1 * kRowBytes + g.vhalf;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
-      const bf16x4 a0 = ds_read_tr16(v0b + (((2 * cb) ^ g.xv0) * 16));
-      const bf16x4 a1 = ds_read_tr16(v1b + (((2 * cb) ^ g.xv1) * 16));
+      const bf16x4 a0 = ds_read_tr16(buf + g.va[0][cb & 3] + 128 * (cb >> 2));
+      const bf16x4 a1 = ds_read_tr16(buf + g.va[1][cb & 3] + 128 * (cb >> 2));
       const bf16x8 vf = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) acc.o[cb][hb] = mfma16x16x32(vf, pf[hb], acc.o[cb][hb]);
+      hook(18 + cb);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -304,23 +302,21 @@ __device__ __forceinline__ void stage_compute2(const MLA_LDS uint8_t* buf, const
   constexpr int kPrefetch = 2;
   f32x4 s00, s01, s10, s11;  // s<u><hb>
   {
-    const MLA_LDS uint8_t* r0 = buf + g.rowA0 * kRowBytes;
-    const MLA_LDS uint8_t* r1 = buf + g.rowA1 * kRowBytes;
-    auto chunk = [&](int ks, int xa) {
-      return ks < 16 ? ((4 * ks) ^ xa) : 64 + ((4 * (ks - 16)) ^ (xa & 7));
+    auto kread = [&](int u, int ks) {
+      return *(const MLA_LDS bf16x8*)(buf + g.ka[u][ks & 1] + 128 * (ks >> 1));
     };
     bf16x8 kf[18][2];  // fully unrolled: only kPrefetch + 1 steps are live at a time
 #pragma unroll
     for (int ks = 0; ks < kPrefetch; ++ks) {
-      kf[ks][0] = *(const MLA_LDS bf16x8*)(r0 + chunk(ks, g.xa0) * 16);
-      kf[ks][1] = *(const MLA_LDS bf16x8*)(r1 + chunk(ks, g.xa1) * 16);
+      kf[ks][0] = kread(0, ks);
+      kf[ks][1] = kread(1, ks);
     }
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
       if (ks + kPrefetch < 18) {
-        kf[ks + kPrefetch][0] = *(const MLA_LDS bf16x8*)(r0 + chunk(ks + kPrefetch, g.xa0) * 16);
-        kf[ks + kPrefetch][1] = *(const MLA_LDS bf16x8*)(r1 + chunk(ks + kPrefetch, g.xa1) * 16);
+        kf[ks + kPrefetch][0] = kread(0, ks + kPrefetch);
+        kf[ks + kPrefetch][1] = kread(1, ks + kPrefetch);
       }
       if (ks == 0) {
         mfma_v_first(s00, kf[0][0], qf[0][0]);
@@ -373,26 +369,25 @@ __device__ __forceinline__ void stage_compute2(const MLA_LDS uint8_t* buf, const
 
   // ---- O^T += V^T P^T, V^T fragments read kPrefetch column blocks ahead
   {
-    const MLA_LDS uint8_t* v0b = buf + g.rowV0 * kRowBytes + g.vhalf;
-    const MLA_LDS uint8_t* v1b = buf + g.rowV1 * kRowBytes + g.vhalf;
+    auto vread = [&](int u, int cb) { return ds_read_tr16(buf + g.va[u][cb & 3] + 128 * (cb >> 2)); };
     bf16x4 vt[32][2];  // fully unrolled: only kPrefetch + 1 blocks are live at a time
 #pragma unroll
     for (int cb = 0; cb < kPrefetch; ++cb) {
-      vt[cb][0] = ds_read_tr16(v0b + (((2 * cb) ^ g.xv0) * 16));
-      vt[cb][1] = ds_read_tr16(v1b + (((2 * cb) ^ g.xv1) * 16));
+      vt[cb][0] = vread(0, cb);
+      vt[cb][1] = vread(1, cb);
     }
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
       __builtin_amdgcn_sched_barrier(0);
       if (cb + kPrefetch < 32) {
-        const int cc = 2 * (cb + kPrefetch);
-        vt[cb + kPrefetch][0] = ds_read_tr16(v0b + ((cc ^ g.xv0) * 16));
-        vt[cb + kPrefetch][1] = ds_read_tr16(v1b + ((cc ^ g.xv1) * 16));
+        vt[cb + kPrefetch][0] = vread(0, cb + kPrefetch);
+        vt[cb + kPrefetch][1] = vread(1, cb + kPrefetch);
       }
       const bf16x8 vf = {vt[cb][0][0], vt[cb][0][1], vt[cb][0][2], vt[cb][0][3],
                          vt[cb][1][0], vt[cb][1][1], vt[cb][1][2], vt[cb][1][3]};
       mfma_a(acc.o[2 * cb], vf, pf[0]);
       mfma_a(acc.o[2 * cb + 1], vf, pf[1]);
+      hook(18 + cb);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
