@@ -244,8 +244,10 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
     }
   };
 
-  // ---- prologue: the first stages (KPAGES = 1: their page ids by scalar loads, which the
-  // full wait below covers), then the window for the loop
+  // ---- prologue: stage 0 (KPAGES = 1: the page ids of the first stages by scalar loads,
+  // which the full wait below covers), the window for the loop and the query.  Stages 1
+  // and 2 are issued at the top of the first step, after the wait: the wait then covers
+  // only what the first step needs, not a full pipeline of stages.
   int pa_n = 0;
   const int npro = nst < kNumBuf - 1 ? nst : kNumBuf - 1;
   auto direct_page = [&](int st) { return ld_const(pt + st * kStageKeys / a.PS); };
@@ -253,9 +255,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
   int pa_pro[kNumBuf];
 #pragma unroll
   for (int k = 0; k < kNumBuf; ++k) pa_pro[k] = (KPAGES != 0 && k < nst) ? direct_page(s_first + k) : 0;
-#pragma unroll
-  for (int k = 0; k < kNumBuf - 1; ++k)
-    if (k < npro) issue(s_first + k, k, pa_pro[k]);
+  issue(s_first, 0, pa_pro[0]);
   if (KPAGES != 0 && kNumBuf - 1 < nst) pa_n = pa_pro[kNumBuf - 1];
   if (KPAGES != 0) window_load();
 
@@ -300,6 +300,11 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
         if (younger >= 2) vm_wait_imm<2 * kDlo>(); else vm_wait_imm<kDlo>();
       }
       stage_barrier();
+    }
+    if (k == 0) {
+#pragma unroll
+      for (int j = 1; j < kNumBuf - 1; ++j)
+        if (j < npro) issue(s_first + j, j, pa_pro[j]);
     }
     // Refill the buffer stage k-1 used with stage k + kNumBuf - 1: a fast stage's loads are
     // spread over the score k-steps of this stage's compute, any other is issued here.
