@@ -195,16 +195,26 @@ __device__ __forceinline__ bool plan_row_parts(const SplitPlan& p, PlanLds& L, i
   const int hi = rows < p.grid ? min(maxnt, (total + (p.grid - rows) - 1) / (p.grid - rows)) : maxnt;
   int S = hi;
   {
-    int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int t = tid; t < p.T; t += NT) {
+    // each wave sums its own candidates over all rows (lane = row), so every lane divides
+    // by 8 / waves candidates only and no LDS atomics are needed
+    constexpr int kWaves = NT / 64;
+    constexpr int kPer = kWaves >= 8 ? 1 : 8 / kWaves;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int c[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) c[j] = 0;
+    for (int t = tid & 63; t < p.T; t += 64) {
       const int nt = geo_tiles(L.geo[t]);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) c[k] += (nt + S0 + k - 1) / (S0 + k);
+      for (int j = 0; j < kPer; ++j) {
+        const int Sx = S0 + wave * kPer + j;
+        c[j] += (nt + Sx - 1) / Sx;
+      }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      c[k] = wave_sum_i32(c[k]);
-      if ((tid & 63) == 0) atomicAdd(&L.red[k], c[k]);
+    for (int j = 0; j < kPer; ++j) {
+      c[j] = wave_sum_i32(c[j]);
+      if ((tid & 63) == 0 && wave * kPer + j < 8) L.red[wave * kPer + j] = c[j];
     }
     __syncthreads();
 #pragma unroll
