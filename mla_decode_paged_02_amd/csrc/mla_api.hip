@@ -566,11 +566,12 @@ mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla
   a.out = (uint16_t*)out->data;
   a.o_tok = out->stride[0];
   a.o_head = out->stride[1];
-  // the error word lives in the stream's workspace (allocated on first use)
+  // the error word and the zero row live in the stream's workspace (allocated on first use)
   bool cap = false;
   if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
   void* ws = nullptr;
   if ((s = grow_workspace(current_device(), stream, 0, cap, &ws)) != MLA_OK) return s;
+  a.zero_row = (const uint8_t*)ws;
   a.err = (uint32_t*)((char*)ws + kErrOffset);
   mla::KernelTimer tslot;
   mla::KernelTimer* timer = profile_timer(&tslot);

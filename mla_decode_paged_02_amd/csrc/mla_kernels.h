@@ -90,6 +90,7 @@ struct PrefillArgs {
   int32_t mask;
   uint16_t* out;              // bf16 [Tq, H, 128]
   int64_t o_tok, o_head;
+  const uint8_t* zero_row;    // >= 256 zero bytes (the stage loads of keys that do not count)
   uint32_t* err;
 };
 

@@ -9,11 +9,13 @@
 // causal mask it sees the keys at positions up to its own.
 //
 // Work-group = (sequence, head, block of 128 queries): four waves of 32 queries.  Keys
-// stream through LDS in stages of 32 (K tile 32 x 192, V tile 32 x 128, double buffered,
-// the next stage prefetched into registers while the current one is computed).  Per
-// wave and stage, as in the decode kernels, S^T = K Q^T with the key rows of each MFMA
-// tile permuted so the score accumulators are already the P^T operand, an online softmax
-// per query, then O^T += V^T P^T with transposing LDS reads.
+// stream through LDS in stages of 32 (no-rope K tile 32 x 128, rope tile 32 x 64, V tile
+// 32 x 128, triple buffered) by direct global->LDS loads: each lane's source offset within
+// a stage is fixed, so a stage whose keys all count and whose rope rows lie in one page
+// costs one scalar base per tensor and five load instructions per wave.  Per wave and
+// stage, as in the decode kernels, S^T = K Q^T with the key rows of each MFMA tile permuted
+// so the score accumulators are already the P^T operand, an online softmax per query, then
+// O^T += V^T P^T with transposing LDS reads.
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "mla_stage.h"
@@ -23,20 +25,26 @@ namespace mla {
 constexpr int kPfQ = 128;                    // queries per work-group
 constexpr int kPfWaves = 4;                  // 32 queries per wave
 constexpr int kPfNT = kPfWaves * 64;
-constexpr int kPfQkDim = 192, kPfVDim = 128;
-constexpr int kPfKRow = kPfQkDim * 2;        // 384 bytes: 16 no-rope chunks + 8 rope chunks
-constexpr int kPfVRow = kPfVDim * 2;         // 256 bytes
-constexpr int kPfKStage = kStageKeys * kPfKRow;
+constexpr int kPfKnRow = 256;                // bytes per key row: 128 no-rope columns
+constexpr int kPfKrRow = 128;                //                    64 rope columns
+constexpr int kPfVRow = 256;                 //                    128 value columns
+constexpr int kPfKnStage = kStageKeys * kPfKnRow;
+constexpr int kPfKrStage = kStageKeys * kPfKrRow;
 constexpr int kPfVStage = kStageKeys * kPfVRow;
-constexpr int kPfPieces = (kPfKStage + kPfVStage) / 16;   // 1280 sixteen-byte pieces per stage
-constexpr int kPfPerThread = kPfPieces / kPfNT;           // 5
-static_assert(kPfPieces % kPfNT == 0, "pieces are dealt evenly");
+constexpr int kPfStage = kPfKnStage + kPfKrStage + kPfVStage;  // 20 KB: [K no-rope | K rope | V]
+constexpr int kPfBufs = 3;
+constexpr int kPfDma = kPfStage / 1024;      // 20 wave-wide loads per stage
+constexpr int kPfDmaPerWave = kPfDma / kPfWaves;
+constexpr int kPfPidWindow = 256;            // page ids of the work-group's keys held in LDS
+static_assert(kPfDma % kPfWaves == 0 && kPfDmaPerWave == 5, "load slots dealt evenly");
 
-// LDS swizzles (chunk c of row r at position c ^ f(r), an involution within aligned
-// groups of 8 (K) or 16 (V) chunks) chosen so the 16 lanes of an MFMA operand read hit
-// distinct banks.
-__device__ __forceinline__ int pf_kswz(int r) { return ((r >> 1) & 1) | (((r >> 3) & 3) << 1); }
-__device__ __forceinline__ int pf_vswz(int r) { return (r & 3) << 1; }
+// LDS swizzles: chunk c of row r at position c ^ f(r).  Rows of 256 bytes start on the same
+// bank, so the 16 rows of a score read need 16 different 16-byte positions (f over four
+// bits); rope rows of 128 bytes alternate bank halves (three bits suffice); the value read
+// takes 32-byte chunk pairs of 8 rows, so f keeps pairs together (even values).
+__device__ __forceinline__ int pf_kn_swz(int r) { return (((r >> 3) & 3) << 2) | (r & 3); }
+__device__ __forceinline__ int pf_kr_swz(int r) { return (((r >> 3) & 3) << 1) | ((r >> 1) & 1); }
+__device__ __forceinline__ int pf_v_swz(int r) { return ((((r >> 3) & 1) << 2) | (r & 3)) << 1; }
 
 struct PfAcc {
   f32x4 o[8][2];  // lane 16g+n: O^T[16cb + 4g + i][query 16qb + n of the wave]
@@ -61,10 +69,9 @@ __device__ __forceinline__ bool pf_locate(const PrefillArgs& a, int j, int& b, i
 }
 
 __global__ __launch_bounds__(kPfNT, 2) void mla_prefill_kernel(const PrefillArgs a, int total_blocks) {
-  __shared__ __attribute__((aligned(1024))) uint8_t kt_raw[2 * kPfKStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t vt_raw[2 * kPfVStage];
-  MLA_LDS uint8_t* kt = (MLA_LDS uint8_t*)kt_raw;
-  MLA_LDS uint8_t* vt = (MLA_LDS uint8_t*)vt_raw;
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles_raw[kPfBufs * kPfStage];
+  __shared__ int pids[kPfPidWindow];
+  MLA_LDS uint8_t* tiles = (MLA_LDS uint8_t*)tiles_raw;
 
   // longest work first: the last query blocks (most keys under the causal mask) go out first
   const int w = blockIdx.x;
@@ -100,59 +107,101 @@ __global__ __launch_bounds__(kPfNT, 2) void mla_prefill_kernel(const PrefillArgs
   const int nst = (key_end + kStageKeys - 1) / kStageKeys;
   const int32_t* pt = a.page_table + (int64_t)b * a.pt_row;
 
-  // ---- stage loads: 5 sixteen-byte pieces per thread, staged in registers
-  bool bad = false;
-  uint4 stg[kPfPerThread];
-  auto fetch = [&](int st) {
+  // ---- page ids of the rope rows: logical pages [lp0, lp0 + kPfPidWindow) in LDS
+  const long long lp0 = co / a.PS;
+  const long long lp_end = key_end > 0 ? (co + key_end - 1) / a.PS + 1 : lp0;
+  for (int i = tid; i < kPfPidWindow; i += kPfNT) {
+    const long long lp = lp0 + i;
+    pids[i] = lp < lp_end && lp < a.max_pages ? pt[lp] : -1;
+  }
+
+  // ---- stage loads.  Wave w takes load slots w + 4i (i = 0..4) of the stage's 20: slots
+  // 0..7 the no-rope K rows (4 rows per 1 KB), 8..11 the rope rows (8 per 1 KB), 12..19
+  // the V rows; the slot's 1 KB lands at offset 1024 * slot of the stage buffer.
+  const int64_t kb = a.k_tok * 2, vb = a.v_tok * 2;   // bytes between key rows
+  const uint8_t* kbase = (const uint8_t*)a.k + ((int64_t)bo0 * a.k_tok + (int64_t)h * a.k_head) * 2;
+  const uint8_t* vbase = (const uint8_t*)a.v + ((int64_t)bo0 * a.v_tok + (int64_t)h * a.v_head) * 2;
+  // row and logical 16-byte chunk of this lane's piece in load i
+  auto slot_piece = [&](int i, int lane_v, int& row, int& c) {
+    const int G = wave + kPfWaves * i;
+    if (i < 2) {
+      row = 4 * G + (lane_v >> 4);
+      c = (lane_v & 15) ^ pf_kn_swz(row);
+    } else if (i == 2) {
+      row = 8 * (G - 8) + (lane_v >> 3);
+      c = (lane_v & 7) ^ pf_kr_swz(row);
+    } else {
+      row = 4 * (G - 12) + (lane_v >> 4);
+      c = (lane_v & 15) ^ pf_v_swz(row);
+    }
+  };
+  // fixed per-lane source offsets (fast stages): rows relative to the stage's first key
+  const bool fast_strides = kb * kStageKeys < (1ll << 31) && vb * kStageKeys < (1ll << 31);
+  uint32_t doff[kPfDmaPerWave];
 #pragma unroll
-    for (int i = 0; i < kPfPerThread; ++i) {
-      const int c = tid + i * kPfNT;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < 512) {  // no-rope key columns
-        const int row = c >> 4, part = c & 15, key = st * kStageKeys + row;
-        if (key < key_end)
-          v = *(const uint4*)(a.k + (int64_t)(bo0 + key) * a.k_tok + (int64_t)h * a.k_head + part * 8);
-      } else if (c < 768) {  // rope columns of the key's latent cache row
-        const int cc = c - 512, row = cc >> 3, part = cc & 7, key = st * kStageKeys + row;
-        if (key < key_end) {
+  for (int i = 0; i < kPfDmaPerWave; ++i) {
+    int row, c;
+    slot_piece(i, lane, row, c);
+    doff[i] = i < 2 ? (uint32_t)(row * kb + c * 16)
+                    : i == 2 ? (uint32_t)(row * kRowBytes + kLatentDim * 2 + c * 16) : (uint32_t)(row * vb + c * 16);
+  }
+  bool bad = false;
+  // page and slot of the first rope row of the next stage to issue (stages are issued in
+  // order), advanced by 32 positions per stage without a division
+  long long nx_lp = lp0;
+  int nx_slot = (int)(co - lp0 * a.PS);
+  auto issue = [&](int st, int buf) {
+    MLA_LDS uint8_t* dst = tiles + buf * kPfStage;
+    const int key0 = st * kStageKeys;
+    // the stage's rope rows in one valid page?
+    const long long lp = nx_lp;
+    const int slot0 = nx_slot;
+    nx_slot += kStageKeys;
+    while (nx_slot >= a.PS) {
+      nx_slot -= a.PS;
+      ++nx_lp;
+    }
+    int pid = -1;
+    if (lp - lp0 < kPfPidWindow) pid = __builtin_amdgcn_readfirstlane(pids[lp - lp0]);
+    const bool fast = fast_strides && key0 + kStageKeys <= key_end && slot0 + kStageKeys <= a.PS && pid >= 0 &&
+                      (int64_t)pid < a.num_pages;
+    if (fast) {
+      const uint8_t* kst = kbase + (int64_t)key0 * kb;
+      const uint8_t* vst = vbase + (int64_t)key0 * vb;
+      const uint8_t* rst = a.cache + (int64_t)pid * a.page_bytes + (int64_t)slot0 * kRowBytes;
+#pragma unroll
+      for (int i = 0; i < kPfDmaPerWave; ++i)
+        dma16_base(i < 2 ? kst : i == 2 ? rst : vst, doff[i], dst + (wave + kPfWaves * i) * 1024);
+      return;
+    }
+    // general stage: per-lane keys, pages and bounds (keys past the visible range and rows
+    // of invalid pages read the zero row)
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+#pragma unroll
+    for (int i = 0; i < kPfDmaPerWave; ++i) {
+      int row, c;
+      slot_piece(i, lane_v, row, c);
+      const int key = key0 + row;
+      const uint8_t* src = a.zero_row + c * 16;
+      if (key < key_end) {
+        if (i < 2) {
+          src = kbase + (int64_t)key * kb + c * 16;
+        } else if (i == 2) {
           const long long pos = co + key;
-          const long long lp = pos / a.PS;
-          const int pid = lp < a.max_pages ? pt[lp] : -1;
-          if (pid >= 0 && (int64_t)pid < a.num_pages)
-            v = *(const uint4*)(a.cache + (int64_t)pid * a.page_bytes + (pos - lp * a.PS) * kRowBytes +
-                                 kLatentDim * 2 + part * 16);
+          const long long lpk = pos / a.PS;
+          const int pk = lpk - lp0 < kPfPidWindow ? pids[lpk - lp0] : (lpk < a.max_pages ? pt[lpk] : -1);
+          if (pk >= 0 && (int64_t)pk < a.num_pages)
+            src = a.cache + (int64_t)pk * a.page_bytes + (pos - lpk * a.PS) * kRowBytes + kLatentDim * 2 + c * 16;
           else
             bad = true;
+        } else {
+          src = vbase + (int64_t)key * vb + c * 16;
         }
-      } else {  // value columns
-        const int cc = c - 768, row = cc >> 4, part = cc & 15, key = st * kStageKeys + row;
-        if (key < key_end)
-          v = *(const uint4*)(a.v + (int64_t)(bo0 + key) * a.v_tok + (int64_t)h * a.v_head + part * 8);
       }
-      stg[i] = v;
+      dma16(src, dst + (wave + kPfWaves * i) * 1024);
     }
   };
-  auto stash = [&](int buf) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int i = 0; i < kPfPerThread; ++i) {
-      const int c = tid + i * kPfNT;
-      MLA_LDS uint8_t* dst;
-      if (c < 512) {
-        const int row = c >> 4, part = c & 15;
-        dst = kt + buf * kPfKStage + row * kPfKRow + (part ^ pf_kswz(row)) * 16;
-      } else if (c < 768) {
-        const int cc = c - 512, row = cc >> 3, part = 16 + (cc & 7);
-        dst = kt + buf * kPfKStage + row * kPfKRow + (part ^ pf_kswz(row)) * 16;
-      } else {
-        const int cc = c - 768, row = cc >> 4, part = cc & 15;
-        dst = vt + buf * kPfVStage + row * kPfVRow + (part ^ pf_vswz(row)) * 16;
-      }
-      *(MLA_LDS u32x4*)dst = u32x4{stg[i].x, stg[i].y, stg[i].z, stg[i].w};
-    }
-  };
-
-  if (nst > 0) fetch(0);
 
   // ---- query fragments (B operand of S^T = K Q^T): lane holds q[query][32ks + 8gq .. +8]
   bf16x8 qf[2][6];
@@ -165,6 +214,12 @@ __global__ __launch_bounds__(kPfNT, 2) void mla_prefill_kernel(const PrefillArgs
                           : bf16x8{};
     }
   }
+  // the window is complete before the first stage reads it; all ordinary loads have
+  // landed before the stage loads start (their waits are the kernel's own)
+  all_wait0();
+  __syncthreads();
+  if (nst > 0) issue(0, 0);
+  if (nst > 1) issue(1, 1);
 
   PfAcc acc;
 #pragma unroll
@@ -177,32 +232,42 @@ __global__ __launch_bounds__(kPfNT, 2) void mla_prefill_kernel(const PrefillArgs
   const int vr = ln >> 2, vq = lane & 3;
   const int rowV0 = 8 * gq + vr, rowV1 = rowV0 + 4;
   const int vhalf = (vq & 1) * 8;
-  // positions of this lane's two queries (relative to the cache offset of key 0)
-  long long qrel[2];
+  // positions of this lane's two queries relative to the cache offset of key 0, clamped
+  // so that the per-stage mask arithmetic stays in 32 bits (keys are below 2^24)
+  auto rel = [&](long long t) { return (int)max(-(1ll << 30), min(1ll << 30, pos0 + t - co)); };
+  int qrel[2];
 #pragma unroll
-  for (int qb2 = 0; qb2 < 2; ++qb2) qrel[qb2] = pos0 + (tw + 16 * qb2 + ln) - co;
+  for (int qb2 = 0; qb2 < 2; ++qb2) qrel[qb2] = rel(tw + 16 * qb2 + ln);
+  const int wave_q0 = rel(tw);  // relative position of the wave's first query
 
-  if (nst > 0) {
-    stash(0);
-    __syncthreads();
-  }
 #pragma unroll 1
   for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) fetch(st + 1);
-    const MLA_LDS uint8_t* K = kt + buf * kPfKStage;
-    const MLA_LDS uint8_t* V = vt + buf * kPfVStage;
-    const int kbase = st * kStageKeys;
+    // stage st has landed (st+1 may be in flight); every wave is past stage st-1, whose
+    // buffer takes stage st+2
+    if (st + 1 < nst) vm_wait_imm<kPfDmaPerWave>(); else vm_wait_imm<0>();
+    stage_barrier();
+    if (st + 2 < nst) issue(st + 2, (st + 2) % kPfBufs);
+    const MLA_LDS uint8_t* Kn = tiles + (st % kPfBufs) * kPfStage;
+    const MLA_LDS uint8_t* Kr = Kn + kPfKnStage;
+    const MLA_LDS uint8_t* V = Kr + kPfKrStage;
+    const int kbase_st = st * kStageKeys;
 
-    // S^T = K Q^T: key tiles u = 0, 1 x query blocks
+    // S^T = K Q^T: key tiles u = 0, 1 x query blocks (k-steps 0..3 no-rope, 4..5 rope)
     f32x4 s[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) s[u][0] = s[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) {
-      const int c = 4 * ks + gq;
-      const bf16x8 k0 = *(const MLA_LDS bf16x8*)(K + rowA0 * kPfKRow + (c ^ pf_kswz(rowA0)) * 16);
-      const bf16x8 k1 = *(const MLA_LDS bf16x8*)(K + rowA1 * kPfKRow + (c ^ pf_kswz(rowA1)) * 16);
+      bf16x8 k0, k1;
+      if (ks < 4) {
+        const int c = 4 * ks + gq;
+        k0 = *(const MLA_LDS bf16x8*)(Kn + rowA0 * kPfKnRow + (c ^ pf_kn_swz(rowA0)) * 16);
+        k1 = *(const MLA_LDS bf16x8*)(Kn + rowA1 * kPfKnRow + (c ^ pf_kn_swz(rowA1)) * 16);
+      } else {
+        const int c = 4 * (ks - 4) + gq;
+        k0 = *(const MLA_LDS bf16x8*)(Kr + rowA0 * kPfKrRow + (c ^ pf_kr_swz(rowA0)) * 16);
+        k1 = *(const MLA_LDS bf16x8*)(Kr + rowA1 * kPfKrRow + (c ^ pf_kr_swz(rowA1)) * 16);
+      }
 #pragma unroll
       for (int qb2 = 0; qb2 < 2; ++qb2) {
         s[0][qb2] = mfma16x16x32(k0, qf[qb2][ks], s[0][qb2]);
@@ -210,20 +275,19 @@ __global__ __launch_bounds__(kPfNT, 2) void mla_prefill_kernel(const PrefillArgs
       }
     }
 
-    // masks: key kbase + 8gq + j (this lane's keys) against the end of the keys and, under
-    // the causal mask, against this lane's query position
-    const uint32_t stage_bits = range_bits(kbase, 0, key_end);
-    const bool all_valid = stage_bits == 0xFFFFFFFFu &&
-                           (a.mask != kMaskCausal || kbase + kStageKeys - 1 <= pos0 + tw - co);
+    // masks: key kbase_st + 8gq + j (this lane's keys) against the end of the keys and,
+    // under the causal mask, against this lane's query position
+    const uint32_t stage_bits = range_bits(kbase_st, 0, key_end);
+    const bool all_valid = stage_bits == 0xFFFFFFFFu && (a.mask != kMaskCausal || kbase_st + kStageKeys - 1 <= wave_q0);
     const float ks8[2][4] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
     bf16x8 pf[2];
 #pragma unroll
     for (int qb2 = 0; qb2 < 2; ++qb2) {
       uint32_t bits = (stage_bits >> (8 * gq)) & 0xFFu;
       if (a.mask == kMaskCausal) {
-        const long long lim = qrel[qb2] - (kbase + 8 * gq) + 1;  // keys j < lim are visible
-        const uint32_t cb = lim <= 0 ? 0u : (lim >= 8 ? 0xFFu : ((1u << lim) - 1u));
-        bits &= cb;
+        const int lim = qrel[qb2] - (kbase_st + 8 * gq) + 1;  // keys j < lim are visible
+        const uint32_t cbits = lim <= 0 ? 0u : (lim >= 8 ? 0xFFu : ((1u << lim) - 1u));
+        bits &= cbits;
       }
       pf[qb2] = softmax_block<false>(s[0][qb2], s[1][qb2], bits, all_valid, a.scale_log2, ks8, acc.m[qb2],
                                      acc.l[qb2], [&](float alpha) {
@@ -235,17 +299,12 @@ __global__ __launch_bounds__(kPfNT, 2) void mla_prefill_kernel(const PrefillArgs
     // O^T += V^T P^T
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
-      const bf16x4 a0 = ds_read_tr16(V + rowV0 * kPfVRow + ((2 * cb + (vq >> 1)) ^ pf_vswz(rowV0)) * 16 + vhalf);
-      const bf16x4 a1 = ds_read_tr16(V + rowV1 * kPfVRow + ((2 * cb + (vq >> 1)) ^ pf_vswz(rowV1)) * 16 + vhalf);
+      const int c = 2 * cb + (vq >> 1);
+      const bf16x4 a0 = ds_read_tr16(V + rowV0 * kPfVRow + (c ^ pf_v_swz(rowV0)) * 16 + vhalf);
+      const bf16x4 a1 = ds_read_tr16(V + rowV1 * kPfVRow + (c ^ pf_v_swz(rowV1)) * 16 + vhalf);
       const bf16x8 vf = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
       for (int qb2 = 0; qb2 < 2; ++qb2) acc.o[cb][qb2] = mfma16x16x32(vf, pf[qb2], acc.o[cb][qb2]);
-    }
-
-    if (st + 1 < nst) {
-      // the other buffer was last read in stage st - 1, before the previous barrier
-      stash(buf ^ 1);
-      __syncthreads();
     }
   }
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(a.err, kErrPageId);
