@@ -150,6 +150,9 @@ __global__ __launch_bounds__(kPfNT, 2) void mla_prefill_kernel(const PrefillArgs
   // order), advanced by 32 positions per stage without a division
   long long nx_lp = lp0;
   int nx_slot = (int)(co - lp0 * a.PS);
+  // the next stage's first K and V rows, advanced by 32 rows per stage
+  const uint8_t* nx_k = kbase;
+  const uint8_t* nx_v = vbase;
   auto issue = [&](int st, int buf) {
     MLA_LDS uint8_t* dst = tiles + buf * kPfStage;
     const int key0 = st * kStageKeys;
@@ -161,13 +164,15 @@ __global__ __launch_bounds__(kPfNT, 2) void mla_prefill_kernel(const PrefillArgs
       nx_slot -= a.PS;
       ++nx_lp;
     }
+    const uint8_t* kst = nx_k;
+    const uint8_t* vst = nx_v;
+    nx_k += kb * kStageKeys;
+    nx_v += vb * kStageKeys;
     int pid = -1;
     if (lp - lp0 < kPfPidWindow) pid = __builtin_amdgcn_readfirstlane(pids[lp - lp0]);
     const bool fast = fast_strides && key0 + kStageKeys <= key_end && slot0 + kStageKeys <= a.PS && pid >= 0 &&
                       (int64_t)pid < a.num_pages;
     if (fast) {
-      const uint8_t* kst = kbase + (int64_t)key0 * kb;
-      const uint8_t* vst = vbase + (int64_t)key0 * vb;
       const uint8_t* rst = a.cache + (int64_t)pid * a.page_bytes + (int64_t)slot0 * kRowBytes;
 #pragma unroll
       for (int i = 0; i < kPfDmaPerWave; ++i)
