@@ -45,13 +45,17 @@ KERNELS = {"C0": "mla_decode_kernel", "C1": "mla_decode_kernel", "C2": "mla_deco
            "C3": "mla_prefill_kernel", "C4": "mla_sparse_kernel"}
 
 
+# sources the dense decode and combine kernels are built from
+DECODE_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_kernels.h", "mla_plan.h", "mla_stage.h")
+
+
 def kernel_digest():
-    """Digest of the kernel sources (the traffic summary is only used for the same code)."""
+    """Digest of the dense decode kernel's sources (the traffic summary is only used for the
+    same code)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")) and name != "mla_api.hip":
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in DECODE_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -178,11 +178,16 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
   }
 
   bool bad_page = false;
-  // page of stage st from the window (KPAGES = 1)
+  // page of stage st from the window (KPAGES = 1); consecutive stages of one page reuse
+  // the id read last
+  int lp_last = -1, pid_last = -1;
   auto stage_page = [&](int st) {
     const int lp = st * kStageKeys / a.PS;
+    if (lp == lp_last) return pid_last;
     if (lp >= pbase + kPidWindow) window_move(lp);
-    return __builtin_amdgcn_readfirstlane(pids[lp - pbase]);
+    lp_last = lp;
+    pid_last = __builtin_amdgcn_readfirstlane(pids[lp - pbase]);
+    return pid_last;
   };
   // A stage whose keys are all visible and lie in one valid page is loaded from a scalar
   // base: fast_base() returns it, or null when the stage needs the general path.
