@@ -35,6 +35,16 @@ def test_ragged_small(H, ps):
         compare(to_f64(decode_on_gpu(m, case, num_partitions=P)), want, BF16_TOL, f"H={H} PS={ps} P={P}")
 
 
+@pytest.mark.parametrize("ps", [128, 256])
+def test_large_pages(ps):
+    """Pages holding several 32-key stages: consecutive stages reuse one page id."""
+    m = need_gpu()
+    case = make_decode_case(140 + ps, [1, 31, 33, 255, 257, 700, 1500], 128, ps, name="large-pages")
+    want = oracle_of(case)
+    for P in (0, 1, 3):
+        compare(to_f64(decode_on_gpu(m, case, num_partitions=P)), want, BF16_TOL, f"PS={ps} P={P}")
+
+
 @pytest.mark.parametrize("mask,window", [("null", -1), ("causal", -1), ("sliding_window_causal", 50)])
 def test_multi_token_masks(mask, window):
     m = need_gpu()

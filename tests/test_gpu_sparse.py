@@ -28,8 +28,11 @@ def sparse_on_gpu(m, case, num_partitions=0, d_indices=None, topk=None, cache8=N
         q_scale = f32_dev(case.q_scale) if case.q_scale is not None else None
     if cache_scale == "case":
         cache_scale = f32_dev(case.cache_scale) if case.cache_scale is not None else None
+    if cache8 is None:
+        cache8 = case.cache8
+    cd = cache8 if isinstance(cache8, torch.Tensor) else u8_dev(cache8)
     res = m.decode_paged_sparse(
-        qd, q_scale, i32_dev(case.input_row_offsets), u8_dev(case.cache8 if cache8 is None else cache8),
+        qd, q_scale, i32_dev(case.input_row_offsets), cd,
         cache_scale, i32_dev(case.d_indices if d_indices is None else d_indices),
         i32_dev(case.topk_lengths if topk is None else topk), case.scale,
         num_partitions=num_partitions)
@@ -137,3 +140,20 @@ def test_sparse_deterministic():
     a = bits_of(sparse_on_gpu(m, case))
     for _ in range(2):
         assert np.array_equal(a, bits_of(sparse_on_gpu(m, case)))
+
+
+def test_strided_pages_and_scales():
+    """Pages and scale rows with padding between them (views of larger buffers) take the
+    general loader, which derives each row's page and slot by division."""
+    import torch
+    m = need_gpu()
+    case = make_sparse_case(77, 4, 64, 700, 16, (100, 300), 300, name="sp-strided")
+    NP, PS = case.cache8.shape[0], case.page_size
+    big = torch.full((NP, PS + 3, 576), 0x7F, dtype=torch.uint8, device="cuda:0")  # NaN padding
+    big[:, :PS] = u8_dev(case.cache8)
+    sc = torch.full((NP, PS + 4), float("nan"), dtype=torch.float32, device="cuda:0")
+    sc[:, :PS] = f32_dev(case.cache_scale)
+    got = to_f64(sparse_on_gpu(m, case, cache8=big[:, :PS], cache_scale=sc[:, :PS]))
+    compare(got, oracle_of(case), FP8_TOL, "strided pages and scales")
+    flat = bits_of(sparse_on_gpu(m, case))
+    assert np.array_equal(bits_of(sparse_on_gpu(m, case, cache8=big[:, :PS], cache_scale=sc[:, :PS])), flat)
