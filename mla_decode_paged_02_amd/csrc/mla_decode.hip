@@ -91,6 +91,30 @@ __device__ __forceinline__ void decode_fill(const DecodeArgs& a, PlanLds& L) {
   }
 }
 
+// The same geometry written by one wave into its private 64-row table (at most 64 rows and
+// 64 sequences): lane b writes the rows of sequence b.  Off for the dense kernel: the
+// per-wave planning is faster by itself, but a second inlined copy of the segment code
+// raised the scalar-register spills of the stage loop more than it saved (measured).
+constexpr bool kDecodeSmallPlan = false;
+__device__ __forceinline__ void decode_fill_wave(const DecodeArgs& a, RowGeo* geo, int lane) {
+  if (lane < a.T) geo[lane] = RowGeo{-1, 0, 0};
+  if (lane < a.B) {
+    const int o0 = (int)a.offsets[lane], o1 = (int)a.offsets[lane + 1];
+    const long long L0 = a.cache_lens[lane];
+    if (o1 < o0 || o0 < 0 || o1 > a.T) {
+      atomicOr(a.err, kErrOffsets);
+    } else {
+      const long long Lb = clamp_len(a, L0, true);
+      const int n = o1 - o0;
+      for (int j = 0; j < n; ++j) {
+        RowGeo g{lane, 0, 0};
+        token_range(a, Lb, n, j, g.lo, g.hi);
+        geo[o0 + j] = g;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // One row segment: tiles [ta, tc) (relative to the row's first visible tile) of row t.
 //
@@ -355,7 +379,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode_kernel(const DecodeArgs
   MLA_LDS uint8_t* tiles = (MLA_LDS uint8_t*)tiles_raw;
   plan_run<NW * 64>(
       plan, L, [&](PlanLds& l) { decode_fill<NW * 64>(a, l); },
-      [&](int t) { return decode_row_geo(a, t); },
+      [&](int t) { return decode_row_geo(a, t); }, kDecodeSmallPlan && a.T <= 64 && a.B <= 64,
+      [&](RowGeo* geo, int lane) { decode_fill_wave(a, geo, lane); },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
         decode_segment<HB, NW, KPAGES>(a, tiles, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
       });

@@ -296,16 +296,95 @@ __device__ __forceinline__ bool plan_row_parts(const SplitPlan& p, PlanLds& L, i
   return true;
 }
 
+// Row-parts planning of a small batch (T <= 64) done by every wave on its own: lane t holds
+// row t, so the row sums, the split-size search and the prefix of the part counts are wave
+// reductions and a wave scan, with no block barrier.  fill_wave(geo, lane) writes rows
+// 0..T-1 of the wave's private table geo (64 entries).  The result is the plan
+// plan_row_parts makes (the smallest S that fits, parts numbered in row order).  Returns
+// false, before touching any output, when row parts do not apply.
+template <int NT, class FillWave>
+__device__ __forceinline__ bool plan_row_parts_small(const SplitPlan& p, PlanLds& L, int piece, FillWave fill_wave,
+                                                     RowGeo& g0, int& s, int& e, int& r0) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  RowGeo* wgeo = L.geo + 64 * wave;
+  fill_wave(wgeo, lane);
+  const RowGeo g = lane < p.T ? wgeo[lane] : RowGeo{-1, 0, 0};
+  const int nt = geo_tiles(g);
+  const int rows = wave_sum_i32(nt > 0 ? 1 : 0), total = wave_sum_i32(nt), maxnt = wave_max_i32(nt);
+  if (rows == 0 || rows > p.grid) return false;
+  // smallest S in [S0, hi] with sum_t ceil(nt_t / S) <= grid (S0 - 1 never fits, hi does)
+  const int S0 = max(1, (total + p.grid - 1) / p.grid);
+  const int hi = rows < p.grid ? min(maxnt, (total + (p.grid - rows) - 1) / (p.grid - rows)) : maxnt;
+  int lo = S0 - 1, up = hi;
+  while (up - lo > 1) {
+    const int mid = lo + (up - lo) / 2;
+    if (wave_sum_i32((nt + mid - 1) / mid) <= p.grid) up = mid; else lo = mid;
+  }
+  const int S = up;
+  const int P = (nt + S - 1) / S;
+  int incl = P;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  const int first = incl - P;
+  if (blockIdx.x == 0 && wave == 0 && lane < p.T) {
+    p.row_meta[2 + 2 * lane] = first;
+    p.row_meta[3 + 2 * lane] = P;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    p.row_meta[0] = 1;  // row-parts mode
+    p.row_meta[1] = S;
+  }
+  // rows without keys that fall to this work-group (every wave finds the same ones)
+  uint64_t zero = __builtin_amdgcn_ballot_w64(lane < p.T && nt == 0 && lane % p.grid == (int)blockIdx.x);
+  while (zero != 0) {
+    const int t = __builtin_ctzll(zero);
+    zero &= zero - 1;
+    plan_zero_row<NT>(p, t);
+  }
+  const uint64_t mine = __builtin_amdgcn_ballot_w64(P > 0 && first <= piece && piece < first + P);
+  r0 = -1;
+  if (mine == 0) return true;
+  r0 = __builtin_ctzll(mine);
+  const int part = piece - __builtin_amdgcn_readlane(first, r0);
+  const int Pr = __builtin_amdgcn_readlane(P, r0), ntr = __builtin_amdgcn_readlane(nt, r0);
+  s = (int)((long long)part * ntr / Pr);
+  e = (int)((long long)(part + 1) * ntr / Pr);
+  g0 = RowGeo{__builtin_amdgcn_readlane(g.b, r0), __builtin_amdgcn_readlane(g.lo, r0),
+              __builtin_amdgcn_readlane(g.hi, r0)};
+  return true;
+}
+
 // Runs this work-group's share.
 //   fill(L)          block-cooperatively writes L.geo[t] for every row t < p.T (only called
 //                    when p.T <= kPlanMaxRows), followed by a block barrier inside plan_run;
 //   geo_of(t)        the geometry of one row computed directly (used when p.T is larger);
+//   small, fill_wave when small holds (at most 64 rows, which fill_wave can write per
+//                    wave), row parts are planned per wave by plan_row_parts_small;
 //   segment(r, g, ta, tc, full, slot) processes tiles [ta, tc) of row r.
-template <int NT, class Fill, class GeoOf, class Segment>
-__device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fill, GeoOf geo_of,
-                                         Segment segment) {
+template <int NT, class Fill, class GeoOf, class FillWave, class Segment>
+__device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fill, GeoOf geo_of, bool small,
+                                         FillWave fill_wave, Segment segment) {
   const int gid = blockIdx.x;
   const int piece = plan_piece(gid, (int)gridDim.x);
+  if (small && p.nparts == 0 && p.T <= 64) {
+    // a call site of its own: nothing of the general planning stays live around it
+    RowGeo g0{0, 0, 0};
+    int s0 = 0, e0 = 0, r = -1;
+    if (plan_row_parts_small<NT>(p, L, piece, fill_wave, g0, s0, e0, r)) {
+      if (r >= 0) {
+        g0.b = __builtin_amdgcn_readfirstlane(g0.b);
+        g0.lo = __builtin_amdgcn_readfirstlane(g0.lo);
+        g0.hi = __builtin_amdgcn_readfirstlane(g0.hi);
+        segment(r, g0, s0, e0, geo_tiles(g0) == e0 - s0, piece);
+      }
+      return;
+    }
+    __syncthreads();  // every wave is done with its private table before the block one
+  }
   const bool table = p.T <= kPlanMaxRows;
   if (table) {
     fill(L);

@@ -360,6 +360,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs
   MLA_LDS float* ksc = (MLA_LDS float*)ksc_raw;
   plan_run<NW * 64>(
       plan, L, [&](PlanLds& l) { sparse_fill<NW * 64>(a, l); }, [&](int t) { return sparse_row_geo(a, t); },
+      a.T <= 64,
+      [&](RowGeo* geo, int lane) {
+        if (lane < a.T) geo[lane] = RowGeo{lane, 0, 2 * max(0, min(a.topk[lane], a.idx_cols))};
+      },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
         sparse_segment<HB, NW>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
       });
