@@ -92,10 +92,7 @@ __device__ __forceinline__ void decode_fill(const DecodeArgs& a, PlanLds& L) {
 }
 
 // The same geometry written by one wave into its private 64-row table (at most 64 rows and
-// 64 sequences): lane b writes the rows of sequence b.  Off for the dense kernel: the
-// per-wave planning is faster by itself, but a second inlined copy of the segment code
-// raised the scalar-register spills of the stage loop more than it saved (measured).
-constexpr bool kDecodeSmallPlan = false;
+// 64 sequences): lane b writes the rows of sequence b.
 __device__ __forceinline__ void decode_fill_wave(const DecodeArgs& a, RowGeo* geo, int lane) {
   if (lane < a.T) geo[lane] = RowGeo{-1, 0, 0};
   if (lane < a.B) {
@@ -371,15 +368,17 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
     stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
 }
 
-template <int HB, int NW, int KPAGES>
+// SMALL: balanced batch of at most 64 rows and 64 sequences, no more rows than work-groups
+// (planned per wave, see plan_run).
+template <int HB, int NW, int KPAGES, bool SMALL>
 __global__ __launch_bounds__(NW * 64, 1) void mla_decode_kernel(const DecodeArgs a, const SplitPlan plan) {
   __shared__ __attribute__((aligned(1024))) uint8_t tiles_raw[kNumBuf * kStageBytes];
   static_assert(kNumBuf * kStageBytes >= 4 * 32 * 1024, "epilogue staging");
   __shared__ PlanLds L;
   MLA_LDS uint8_t* tiles = (MLA_LDS uint8_t*)tiles_raw;
-  plan_run<NW * 64>(
+  plan_run<NW * 64, SMALL>(
       plan, L, [&](PlanLds& l) { decode_fill<NW * 64>(a, l); },
-      [&](int t) { return decode_row_geo(a, t); }, kDecodeSmallPlan && a.T <= 64 && a.B <= 64,
+      [&](int t) { return decode_row_geo(a, t); },
       [&](RowGeo* geo, int lane) { decode_fill_wave(a, geo, lane); },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
         decode_segment<HB, NW, KPAGES>(a, tiles, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
@@ -485,10 +484,14 @@ static SplitPlan plan_of(const DecodeArgs& a) {
 template <int HB, int NW>
 static hipError_t launch_decode_h(const DecodeArgs& a, const SplitPlan& p, hipStream_t stream) {
   const dim3 grid(a.nparts >= 1 ? a.T * a.nparts : a.grid), block(NW * 64);
-  if (a.PS % kStageKeys == 0)
-    hipLaunchKernelGGL((mla_decode_kernel<HB, NW, 1>), grid, block, 0, stream, a, p);
-  else
-    hipLaunchKernelGGL((mla_decode_kernel<HB, NW, 0>), grid, block, 0, stream, a, p);
+  const bool small = a.nparts == 0 && a.T <= 64 && a.B <= 64 && a.T <= a.grid;
+  if (a.PS % kStageKeys == 0) {
+    if (small) hipLaunchKernelGGL((mla_decode_kernel<HB, NW, 1, true>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_decode_kernel<HB, NW, 1, false>), grid, block, 0, stream, a, p);
+  } else {
+    if (small) hipLaunchKernelGGL((mla_decode_kernel<HB, NW, 0, true>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_decode_kernel<HB, NW, 0, false>), grid, block, 0, stream, a, p);
+  }
   return hipGetLastError();
 }
 

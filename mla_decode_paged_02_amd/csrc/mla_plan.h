@@ -296,14 +296,14 @@ __device__ __forceinline__ bool plan_row_parts(const SplitPlan& p, PlanLds& L, i
   return true;
 }
 
-// Row-parts planning of a small batch (T <= 64) done by every wave on its own: lane t holds
-// row t, so the row sums, the split-size search and the prefix of the part counts are wave
-// reductions and a wave scan, with no block barrier.  fill_wave(geo, lane) writes rows
-// 0..T-1 of the wave's private table geo (64 entries).  The result is the plan
-// plan_row_parts makes (the smallest S that fits, parts numbered in row order).  Returns
-// false, before touching any output, when row parts do not apply.
+// Row-parts planning of a small batch (T <= 64 rows, T <= grid) done by every wave on its
+// own: lane t holds row t, so the row sums, the split-size search and the prefix of the
+// part counts are wave reductions and a wave scan, with no block barrier.  fill_wave(geo,
+// lane) writes rows 0..T-1 of the wave's private table geo (64 entries).  The result is
+// the plan plan_row_parts makes (the smallest S that fits, parts numbered in row order);
+// a batch without any visible key gets no parts (every row is written as zeros).
 template <int NT, class FillWave>
-__device__ __forceinline__ bool plan_row_parts_small(const SplitPlan& p, PlanLds& L, int piece, FillWave fill_wave,
+__device__ __forceinline__ void plan_row_parts_small(const SplitPlan& p, PlanLds& L, int piece, FillWave fill_wave,
                                                      RowGeo& g0, int& s, int& e, int& r0) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -312,16 +312,18 @@ __device__ __forceinline__ bool plan_row_parts_small(const SplitPlan& p, PlanLds
   const RowGeo g = lane < p.T ? wgeo[lane] : RowGeo{-1, 0, 0};
   const int nt = geo_tiles(g);
   const int rows = wave_sum_i32(nt > 0 ? 1 : 0), total = wave_sum_i32(nt), maxnt = wave_max_i32(nt);
-  if (rows == 0 || rows > p.grid) return false;
   // smallest S in [S0, hi] with sum_t ceil(nt_t / S) <= grid (S0 - 1 never fits, hi does)
-  const int S0 = max(1, (total + p.grid - 1) / p.grid);
-  const int hi = rows < p.grid ? min(maxnt, (total + (p.grid - rows) - 1) / (p.grid - rows)) : maxnt;
-  int lo = S0 - 1, up = hi;
-  while (up - lo > 1) {
-    const int mid = lo + (up - lo) / 2;
-    if (wave_sum_i32((nt + mid - 1) / mid) <= p.grid) up = mid; else lo = mid;
+  int S = 1;
+  if (rows > 0) {
+    const int S0 = max(1, (total + p.grid - 1) / p.grid);
+    const int hi = rows < p.grid ? min(maxnt, (total + (p.grid - rows) - 1) / (p.grid - rows)) : maxnt;
+    int lo = S0 - 1, up = hi;
+    while (up - lo > 1) {
+      const int mid = lo + (up - lo) / 2;
+      if (wave_sum_i32((nt + mid - 1) / mid) <= p.grid) up = mid; else lo = mid;
+    }
+    S = up;
   }
-  const int S = up;
   const int P = (nt + S - 1) / S;
   int incl = P;
 #pragma unroll
@@ -347,7 +349,7 @@ __device__ __forceinline__ bool plan_row_parts_small(const SplitPlan& p, PlanLds
   }
   const uint64_t mine = __builtin_amdgcn_ballot_w64(P > 0 && first <= piece && piece < first + P);
   r0 = -1;
-  if (mine == 0) return true;
+  if (mine == 0) return;
   r0 = __builtin_ctzll(mine);
   const int part = piece - __builtin_amdgcn_readlane(first, r0);
   const int Pr = __builtin_amdgcn_readlane(P, r0), ntr = __builtin_amdgcn_readlane(nt, r0);
@@ -355,151 +357,150 @@ __device__ __forceinline__ bool plan_row_parts_small(const SplitPlan& p, PlanLds
   e = (int)((long long)(part + 1) * ntr / Pr);
   g0 = RowGeo{__builtin_amdgcn_readlane(g.b, r0), __builtin_amdgcn_readlane(g.lo, r0),
               __builtin_amdgcn_readlane(g.hi, r0)};
-  return true;
 }
 
 // Runs this work-group's share.
 //   fill(L)          block-cooperatively writes L.geo[t] for every row t < p.T (only called
 //                    when p.T <= kPlanMaxRows), followed by a block barrier inside plan_run;
 //   geo_of(t)        the geometry of one row computed directly (used when p.T is larger);
-//   small, fill_wave when small holds (at most 64 rows, which fill_wave can write per
-//                    wave), row parts are planned per wave by plan_row_parts_small;
+//   fill_wave        (SMALL) writes one wave's private row table, see plan_row_parts_small;
 //   segment(r, g, ta, tc, full, slot) processes tiles [ta, tc) of row r.
-template <int NT, class Fill, class GeoOf, class FillWave, class Segment>
-__device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fill, GeoOf geo_of, bool small,
-                                         FillWave fill_wave, Segment segment) {
+// SMALL (chosen by the host for balanced batches of at most 64 rows and 64 sequences, no
+// more rows than work-groups) plans per wave and has a single segment call site: the
+// general planner is not compiled in, which keeps the stage loop's registers free.
+template <int NT, bool SMALL, class Fill, class GeoOf, class FillWave, class Segment>
+__device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fill, GeoOf geo_of, FillWave fill_wave,
+                                         Segment segment) {
   const int gid = blockIdx.x;
   const int piece = plan_piece(gid, (int)gridDim.x);
-  if (small && p.nparts == 0 && p.T <= 64) {
-    // a call site of its own: nothing of the general planning stays live around it
+  if constexpr (SMALL) {
     RowGeo g0{0, 0, 0};
     int s0 = 0, e0 = 0, r = -1;
-    if (plan_row_parts_small<NT>(p, L, piece, fill_wave, g0, s0, e0, r)) {
-      if (r >= 0) {
-        g0.b = __builtin_amdgcn_readfirstlane(g0.b);
-        g0.lo = __builtin_amdgcn_readfirstlane(g0.lo);
-        g0.hi = __builtin_amdgcn_readfirstlane(g0.hi);
-        segment(r, g0, s0, e0, geo_tiles(g0) == e0 - s0, piece);
-      }
-      return;
+    plan_row_parts_small<NT>(p, L, piece, fill_wave, g0, s0, e0, r);
+    if (r >= 0) {
+      g0.b = __builtin_amdgcn_readfirstlane(g0.b);
+      g0.lo = __builtin_amdgcn_readfirstlane(g0.lo);
+      g0.hi = __builtin_amdgcn_readfirstlane(g0.hi);
+      segment(r, g0, s0, e0, geo_tiles(g0) == e0 - s0, piece);
     }
-    __syncthreads();  // every wave is done with its private table before the block one
-  }
-  const bool table = p.T <= kPlanMaxRows;
-  if (table) {
-    fill(L);
-    __syncthreads();
-  }
-  auto row_geo = [&](int t) { return table ? L.geo[t] : geo_of(t); };
-
-  // This work-group's share is the tile run [s, e) of the concatenated rows; r0 is the
-  // first row it touches and pre that row's first tile.
-  int s = 0, e = 0, r0 = -1, pre = 0;
-  if (p.nparts >= 1) {
-    const int P = p.nparts;
-    const int t = piece / P, part = piece - t * P;
-    if (t >= p.T) return;
-    const int nt = geo_tiles(row_geo(t));
-    const int ta = (int)((long long)part * nt / P), tc = (int)((long long)(part + 1) * nt / P);
-    if (ta == tc) {
-      if (P == 1) {
-        plan_zero_row<NT>(p, t);
-      } else {
-        for (int h = threadIdx.x; h < p.H; h += NT) p.part_lse[(int64_t)piece * p.H + h] = -INFINITY;
-      }
-      return;
-    }
-    r0 = t;  // a run within a single row
-    s = ta;
-    e = tc;
-  } else if (table && plan_row_parts<NT>(p, L, piece, s, e, r0, pre)) {
-    // row parts: one segment (or none) per work-group
-    if (r0 < 0) return;
+    return;
   } else {
-    // per-row tile counts, prefix sums, the row holding tile s
-    if (threadIdx.x == 0) {
-      L.found[0] = -1;
-      L.found[1] = 0;
-      L.zero[63] = 0;
+    const bool table = p.T <= kPlanMaxRows;
+    if (table) {
+      fill(L);
+      __syncthreads();
     }
-    __syncthreads();
-    int total = 0;
-    if (!table) {
+    auto row_geo = [&](int t) { return table ? L.geo[t] : geo_of(t); };
+
+    // This work-group's share is the tile run [s, e) of the concatenated rows; r0 is the
+    // first row it touches and pre that row's first tile.
+    int s = 0, e = 0, r0 = -1, pre = 0;
+    if (p.nparts >= 1) {
+      const int P = p.nparts;
+      const int t = piece / P, part = piece - t * P;
+      if (t >= p.T) return;
+      const int nt = geo_tiles(row_geo(t));
+      const int ta = (int)((long long)part * nt / P), tc = (int)((long long)(part + 1) * nt / P);
+      if (ta == tc) {
+        if (P == 1) {
+          plan_zero_row<NT>(p, t);
+        } else {
+          for (int h = threadIdx.x; h < p.H; h += NT) p.part_lse[(int64_t)piece * p.H + h] = -INFINITY;
+        }
+        return;
+      }
+      r0 = t;  // a run within a single row
+      s = ta;
+      e = tc;
+    } else if (table && plan_row_parts<NT>(p, L, piece, s, e, r0, pre)) {
+      // row parts: one segment (or none) per work-group
+      if (r0 < 0) return;
+    } else {
+      // per-row tile counts, prefix sums, the row holding tile s
+      if (threadIdx.x == 0) {
+        L.found[0] = -1;
+        L.found[1] = 0;
+        L.zero[63] = 0;
+      }
+      __syncthreads();
+      int total = 0;
+      if (!table) {
+        for (int base = 0; base < p.T; base += NT) {
+          const int t = base + threadIdx.x;
+          int ctot;
+          plan_chunk_scan<NT>(t < p.T ? geo_tiles(geo_of(t)) : 0, L.scan, ctot);
+          total += ctot;
+        }
+      } else {
+        for (int t = threadIdx.x; t < p.T; t += NT) total += geo_tiles(L.geo[t]);
+        int ctot;
+        plan_chunk_scan<NT>(total, L.scan, ctot);
+        total = ctot;
+      }
+      total = __builtin_amdgcn_readfirstlane(total);
+      const int W = (total + p.grid - 1) / p.grid;
+      s = piece * W;
+      e = min(total, s + W);
+      if (gid == 0 && threadIdx.x == 0) {
+        p.row_meta[0] = 0;  // stream mode
+        p.row_meta[1] = W;
+      }
+      int prefix = 0;
       for (int base = 0; base < p.T; base += NT) {
         const int t = base + threadIdx.x;
+        const int v = t < p.T ? geo_tiles(row_geo(t)) : 0;
         int ctot;
-        plan_chunk_scan<NT>(t < p.T ? geo_tiles(geo_of(t)) : 0, L.scan, ctot);
-        total += ctot;
+        const int incl = plan_chunk_scan<NT>(v, L.scan, ctot);
+        const int excl = prefix + incl - v;
+        if (t < p.T) {
+          if (gid == 0) {
+            p.row_meta[2 + 2 * t] = excl;
+            p.row_meta[3 + 2 * t] = v;
+          }
+          if (v > 0 && excl <= s && s < excl + v) {
+            L.found[0] = t;
+            L.found[1] = excl;
+          }
+          if (v == 0 && t % p.grid == gid) {
+            const int slot = atomicAdd(&L.zero[63], 1);
+            if (slot < 63) L.zero[slot] = t;
+          }
+        }
+        prefix += ctot;
       }
-    } else {
-      for (int t = threadIdx.x; t < p.T; t += NT) total += geo_tiles(L.geo[t]);
-      int ctot;
-      plan_chunk_scan<NT>(total, L.scan, ctot);
-      total = ctot;
-    }
-    total = __builtin_amdgcn_readfirstlane(total);
-    const int W = (total + p.grid - 1) / p.grid;
-    s = piece * W;
-    e = min(total, s + W);
-    if (gid == 0 && threadIdx.x == 0) {
-      p.row_meta[0] = 0;  // stream mode
-      p.row_meta[1] = W;
-    }
-    int prefix = 0;
-    for (int base = 0; base < p.T; base += NT) {
-      const int t = base + threadIdx.x;
-      const int v = t < p.T ? geo_tiles(row_geo(t)) : 0;
-      int ctot;
-      const int incl = plan_chunk_scan<NT>(v, L.scan, ctot);
-      const int excl = prefix + incl - v;
-      if (t < p.T) {
-        if (gid == 0) {
-          p.row_meta[2 + 2 * t] = excl;
-          p.row_meta[3 + 2 * t] = v;
-        }
-        if (v > 0 && excl <= s && s < excl + v) {
-          L.found[0] = t;
-          L.found[1] = excl;
-        }
-        if (v == 0 && t % p.grid == gid) {
-          const int slot = atomicAdd(&L.zero[63], 1);
-          if (slot < 63) L.zero[slot] = t;
-        }
+      __syncthreads();
+      // block-uniform values: keep the row walk in scalar registers
+      r0 = __builtin_amdgcn_readfirstlane(L.found[0]);
+      pre = __builtin_amdgcn_readfirstlane(L.found[1]);
+      // rows without visible keys are written as zeros, spread over the work-groups
+      const int nzero = __builtin_amdgcn_readfirstlane(L.zero[63]);
+      if (nzero <= 63) {
+        for (int i = 0; i < nzero; ++i) plan_zero_row<NT>(p, __builtin_amdgcn_readfirstlane(L.zero[i]));
+      } else {
+        for (int t = gid; t < p.T; t += p.grid)
+          if (geo_tiles(row_geo(t)) == 0) plan_zero_row<NT>(p, t);
       }
-      prefix += ctot;
+      if (s >= e || r0 < 0) return;
     }
-    __syncthreads();
-    // block-uniform values: keep the row walk in scalar registers
-    r0 = __builtin_amdgcn_readfirstlane(L.found[0]);
-    pre = __builtin_amdgcn_readfirstlane(L.found[1]);
-    // rows without visible keys are written as zeros, spread over the work-groups
-    const int nzero = __builtin_amdgcn_readfirstlane(L.zero[63]);
-    if (nzero <= 63) {
-      for (int i = 0; i < nzero; ++i) plan_zero_row<NT>(p, __builtin_amdgcn_readfirstlane(L.zero[i]));
-    } else {
-      for (int t = gid; t < p.T; t += p.grid)
-        if (geo_tiles(row_geo(t)) == 0) plan_zero_row<NT>(p, t);
+    // one call site for the segment work, whatever the mode.  Fixed and row-parts modes
+    // (pre < 0) run the single tile range [s, e) of row r0 and use slot `piece`.
+    const bool fixed = p.nparts >= 1 || pre < 0;
+    for (int r = r0; r < p.T && pre < e; ++r) {
+      RowGeo g = row_geo(r);
+      g.b = __builtin_amdgcn_readfirstlane(g.b);
+      g.lo = __builtin_amdgcn_readfirstlane(g.lo);
+      g.hi = __builtin_amdgcn_readfirstlane(g.hi);
+      const int nt = geo_tiles(g);
+      if (nt == 0) continue;
+      const int run_end = fixed ? nt : pre + nt;
+      const int ta = fixed ? s : max(s, pre) - pre;
+      const int tc = fixed ? e : min(e, run_end) - pre;
+      const bool full = p.nparts >= 1 ? p.nparts == 1 : (ta == 0 && tc == nt);
+      const int slot = fixed ? piece : (pre <= s ? 2 * piece : 2 * piece + 1);
+      segment(r, g, ta, tc, full, slot);
+      if (fixed) break;
+      pre += nt;
     }
-    if (s >= e || r0 < 0) return;
-  }
-  // one call site for the segment work, whatever the mode.  Fixed and row-parts modes
-  // (pre < 0) run the single tile range [s, e) of row r0 and use slot `piece`.
-  const bool fixed = p.nparts >= 1 || pre < 0;
-  for (int r = r0; r < p.T && pre < e; ++r) {
-    RowGeo g = row_geo(r);
-    g.b = __builtin_amdgcn_readfirstlane(g.b);
-    g.lo = __builtin_amdgcn_readfirstlane(g.lo);
-    g.hi = __builtin_amdgcn_readfirstlane(g.hi);
-    const int nt = geo_tiles(g);
-    if (nt == 0) continue;
-    const int run_end = fixed ? nt : pre + nt;
-    const int ta = fixed ? s : max(s, pre) - pre;
-    const int tc = fixed ? e : min(e, run_end) - pre;
-    const bool full = p.nparts >= 1 ? p.nparts == 1 : (ta == 0 && tc == nt);
-    const int slot = fixed ? piece : (pre <= s ? 2 * piece : 2 * piece + 1);
-    segment(r, g, ta, tc, full, slot);
-    if (fixed) break;
-    pre += nt;
   }
 }
 

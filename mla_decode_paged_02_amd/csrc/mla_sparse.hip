@@ -349,7 +349,9 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
     stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
 }
 
-template <int HB, int NW>
+// SMALL: balanced batch of at most 64 rows, no more rows than work-groups (planned per
+// wave, see plan_run).
+template <int HB, int NW, bool SMALL>
 __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs a, const SplitPlan plan) {
   // the widened tiles, then the fp8 landing buffers
   __shared__ __attribute__((aligned(1024))) uint8_t buf_raw[kSpLdsBytes];
@@ -358,9 +360,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs
   MLA_LDS uint8_t* tiles = (MLA_LDS uint8_t*)buf_raw;
   MLA_LDS uint8_t* land = tiles + kSpTiles * kStageBytes;
   MLA_LDS float* ksc = (MLA_LDS float*)ksc_raw;
-  plan_run<NW * 64>(
+  plan_run<NW * 64, SMALL>(
       plan, L, [&](PlanLds& l) { sparse_fill<NW * 64>(a, l); }, [&](int t) { return sparse_row_geo(a, t); },
-      a.T <= 64,
       [&](RowGeo* geo, int lane) {
         if (lane < a.T) geo[lane] = RowGeo{lane, 0, 2 * max(0, min(a.topk[lane], a.idx_cols))};
       },
@@ -390,7 +391,10 @@ static SplitPlan plan_of(const SparseArgs& a) {
 template <int HB, int NW>
 static hipError_t launch_sparse_h(const SparseArgs& a, const SplitPlan& p, hipStream_t stream) {
   const dim3 grid(a.nparts >= 1 ? a.T * a.nparts : a.grid), block(NW * 64);
-  hipLaunchKernelGGL((mla_sparse_kernel<HB, NW>), grid, block, 0, stream, a, p);
+  if (a.nparts == 0 && a.T <= 64 && a.T <= a.grid)
+    hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true>), grid, block, 0, stream, a, p);
+  else
+    hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false>), grid, block, 0, stream, a, p);
   return hipGetLastError();
 }
 
