@@ -54,6 +54,7 @@ mla_status check_tensor(const mla_tensor* t, const char* name, int32_t dtype, in
   bool empty = false;
   for (int i = 0; i < ndim; ++i) empty |= t->shape[i] == 0;
   if (!t->data && !empty) return fail(MLA_ERR_NULL_ARG, "%s: data pointer is NULL", name);
+  if (empty) return MLA_OK;  // no element is ever addressed: strides and alignment do not matter
   if (t->shape[ndim - 1] > 1 && t->stride[ndim - 1] != 1)
     return fail(MLA_ERR_SHAPE, "%s: innermost dimension must be contiguous", name);
   const size_t es = dtype_size(dtype);
@@ -329,7 +330,7 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
   if (latent_cache->shape[2] != 576) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576", (long long)latent_cache->shape[2]);
   const int64_t PS = latent_cache->shape[1];
   if (PS < 1) return fail(MLA_ERR_SHAPE, "latent_cache: page size must be >= 1");
-  if (latent_cache->shape[1] > 1 && latent_cache->stride[1] != 576)
+  if (latent_cache->shape[0] > 0 && latent_cache->shape[1] > 1 && latent_cache->stride[1] != 576)
     return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride 576)");
   if (latent_cache->shape[0] > 1 && latent_cache->stride[0] < PS * 576)
     return fail(MLA_ERR_SHAPE, "latent_cache: pages overlap (page stride below page_size * 576)");
@@ -422,7 +423,7 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
   if (latent_cache->shape[2] != 576) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576", (long long)latent_cache->shape[2]);
   const int64_t NP = latent_cache->shape[0], PS = latent_cache->shape[1];
   if (PS < 1) return fail(MLA_ERR_SHAPE, "latent_cache: page size must be >= 1");
-  if (PS > 1 && latent_cache->stride[1] != 576)
+  if (NP > 0 && PS > 1 && latent_cache->stride[1] != 576)
     return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride 576)");
   if (NP > 1 && latent_cache->stride[0] < PS * 576)
     return fail(MLA_ERR_SHAPE, "latent_cache: pages overlap (page stride below page_size * 576)");
@@ -522,7 +523,7 @@ mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla
   if (latent_cache->shape[2] != 576) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576", (long long)latent_cache->shape[2]);
   const int64_t PS = latent_cache->shape[1];
   if (PS < 1) return fail(MLA_ERR_SHAPE, "latent_cache: page size must be >= 1");
-  if (PS > 1 && latent_cache->stride[1] != 576)
+  if (latent_cache->shape[0] > 0 && PS > 1 && latent_cache->stride[1] != 576)
     return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride 576)");
   if ((s = check_tensor(out, "out", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
   if (out->shape[0] != Tq || out->shape[1] != H || out->shape[2] != 128)

@@ -139,6 +139,18 @@ def test_empty_rows_are_zero():
         assert np.all(got[0] == 0) and np.all(got[2] == 0)
 
 
+def test_no_visible_key_at_all():
+    """A batch whose every row is empty: every output row is written as zeros (over a NaN
+    filled buffer), balanced and fixed splits alike."""
+    import torch
+    m = need_gpu()
+    case = make_decode_case(16, [0, 0, 0], 32, 16, name="all-empty")
+    for P in (0, 1, 3):
+        out = torch.full((case.q.shape[0], 32, 512), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        got = to_f64(decode_on_gpu(m, case, num_partitions=P, out=out))
+        assert np.all(got == 0), f"P={P}"
+
+
 def test_bad_page_id_is_flagged_not_faulted():
     m = need_gpu()
     case = make_decode_case(16, [100, 200], 16, 64, name="badpid")

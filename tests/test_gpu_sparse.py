@@ -157,3 +157,27 @@ def test_strided_pages_and_scales():
     compare(got, oracle_of(case), FP8_TOL, "strided pages and scales")
     flat = bits_of(sparse_on_gpu(m, case))
     assert np.array_equal(bits_of(sparse_on_gpu(m, case, cache8=big[:, :PS], cache_scale=sc[:, :PS])), flat)
+
+
+def test_empty_lists():
+    """Rows whose lists are empty (top-k 0) or hold only skipped entries are zero; a batch
+    with no listed row at all writes every row as zeros (over a NaN filled buffer)."""
+    import torch
+    m = need_gpu()
+    case = make_sparse_case(78, 4, 16, 300, 16, (50, 120), 120, name="sp-empty")
+    topk = case.topk_lengths.copy()
+    topk[1] = 0
+    idx = case.d_indices.copy()
+    idx[2, :] = -1
+    got = to_f64(sparse_on_gpu(m, case, topk=topk, d_indices=idx))
+    compare(got, oracle_of(case, d_indices=idx, topk=topk), FP8_TOL, "empty lists")
+    assert np.all(got[1] == 0) and np.all(got[2] == 0)
+    zero = np.zeros_like(case.topk_lengths)
+    for P in (0, 1, 3):
+        out = torch.full((4, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        qd = u8_dev(case.q8)
+        res = m.decode_paged_sparse(qd, f32_dev(case.q_scale), i32_dev(case.input_row_offsets),
+                                    u8_dev(case.cache8), f32_dev(case.cache_scale), i32_dev(case.d_indices),
+                                    i32_dev(zero), case.scale, num_partitions=P, out=out)
+        torch.cuda.synchronize()
+        assert np.all(to_f64(res) == 0), f"P={P}"
