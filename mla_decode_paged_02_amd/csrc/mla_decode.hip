@@ -270,10 +270,26 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
     }
   };
 
+  // ---- query fragments: B operand of S^T = K Q^T (lane holds q[h][32ks + 8gq .. +8]),
+  // issued first so that their latency overlaps the page-id loads of the first stage.
+  // They are waited for completely below: the stage loads are invisible to the compiler's
+  // wait bookkeeping, so no ordinary vector-memory access may still be in flight, in its
+  // view, once the stage loop starts.
+  bf16x8 qf[HB][18];
+  {
+    const uint16_t* qrow = a.q + (int64_t)t * a.q_tok + 8 * gq;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const uint16_t* qh = qrow + (int64_t)(h0 + 16 * hb + ln) * a.q_head;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) qf[hb][ks] = *(const bf16x8*)(qh + 32 * ks);
+    }
+  }
+
   // ---- prologue: stage 0 (KPAGES = 1: the page ids of the first stages by scalar loads,
-  // which the full wait below covers), the window for the loop and the query.  Stages 1
-  // and 2 are issued at the top of the first step, after the wait: the wait then covers
-  // only what the first step needs, not a full pipeline of stages.
+  // which the full wait below covers) and the window for the loop.  Stages 1 and 2 are
+  // issued at the top of the first step, after the wait: the wait then covers only what
+  // the first step needs, not a full pipeline of stages.
   int pa_n = 0;
   const int npro = nst < kNumBuf - 1 ? nst : kNumBuf - 1;
   auto direct_page = [&](int st) { return ld_const(pt + st * kStageKeys / a.PS); };
@@ -285,20 +301,6 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
   if (KPAGES != 0 && kNumBuf - 1 < nst) pa_n = pa_pro[kNumBuf - 1];
   if (KPAGES != 0) window_load();
 
-  // ---- query fragments: B operand of S^T = K Q^T (lane holds q[h][32ks + 8gq .. +8]).
-  // They are loaded after the prologue's LDS loads and waited for completely: the stage
-  // loads are invisible to the compiler's wait bookkeeping, so no ordinary vector-memory
-  // access may still be in flight, in its view, once the stage loop starts.
-  bf16x8 qf[HB][18];
-  {
-    const uint16_t* qrow = a.q + (int64_t)t * a.q_tok + 8 * gq;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const uint16_t* qh = qrow + (int64_t)(h0 + 16 * hb + ln) * a.q_head;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) qf[hb][ks] = *(const bf16x8*)(qh + 32 * ks);
-    }
-  }
   all_wait0();
   if (KPAGES != 0) {
     window_store();
