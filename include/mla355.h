@@ -128,7 +128,7 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
  *   input_row_offsets  u32 [B + 1] (only its shape is checked: index lists are per row)
  *   latent_cache  fp8 e4m3 [num_pages, PS, 576] (or bf16, then cache_scale must be NULL)
  *   cache_scale   f32 [num_pages, PS] (one scale per cache row) or NULL = 1
- *   d_indices     i32 [T, indices_stride] (row stride = stride[0] >= shape[1]; shape[1] <= 2^29)
+ *   d_indices     i32 [T, indices_stride] (row stride = stride[0] >= shape[1])
  *   topk_lengths  i32 [T], values above shape[1] of d_indices are clamped to it
  *   scale, num_partitions, out   as for mla_decode_paged; out is bf16 [T, H, 512]
  */

@@ -435,7 +435,7 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
   }
   if ((s = check_tensor(d_indices, "d_indices", MLA_DTYPE_I32, 2, false)) != MLA_OK) return s;
   if (d_indices->shape[0] != T) return fail(MLA_ERR_SHAPE, "d_indices: %lld rows, expected %lld", (long long)d_indices->shape[0], (long long)T);
-  if (d_indices->shape[1] > (1 << 29)) return fail(MLA_ERR_UNSUPPORTED, "d_indices: more than 2^29 columns");
+  if (d_indices->shape[1] > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "d_indices: too many columns");
   if (T > 1 && d_indices->stride[0] < d_indices->shape[1])
     return fail(MLA_ERR_SHAPE, "d_indices: row stride below the row length");
   if ((s = check_1d(topk_lengths, "topk_lengths", MLA_DTYPE_I32, T)) != MLA_OK) return s;

@@ -26,7 +26,7 @@ constexpr int kLatentDim = 512;
 constexpr int kRowBytes = 1152;  // one bf16 cache row
 constexpr int kRowChunks = 72;   // 16-byte chunks per cache row
 constexpr int kStageKeys = 32;   // keys per pipeline stage
-constexpr int kTileKeys = 64;    // keys per scheduling tile (work-split granularity)
+constexpr int kTileKeys = 32;    // keys per scheduling tile (work-split granularity): one stage
 constexpr int kStageBytes = kStageKeys * kRowBytes;  // 36864
 constexpr int kDmaPerStage = kStageBytes / 1024;     // 36 wave-wide 16-byte loads
 constexpr int kNumBuf = 4;       // stage buffers in LDS

@@ -1,6 +1,6 @@
 // Work split of the decode kernels over the GPU, shared by the dense and sparse paths.
 //
-// Every query row's visible keys are cut into 64-key tiles.  Each work-group computes the
+// Every query row's visible keys are cut into 32-key tiles (one stage each).  Each work-group computes the
 // per-row tile counts itself (no host round trip).  Three modes:
 //   row parts (balanced, when every non-empty row can have a work-group of its own): with
 //     S the smallest tile count such that sum_t ceil(nt_t / S) <= grid, row t is cut into

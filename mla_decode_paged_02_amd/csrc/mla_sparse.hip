@@ -37,17 +37,15 @@ constexpr int kSpStageLds = kSpTiles * kStageBytes + kSpRaw * kRawStageBytes;
 constexpr int kSpLdsBytes = kSpStageLds > 4 * 32 * 1024 ? kSpStageLds : 4 * 32 * 1024;
 static_assert(sizeof(PlanLds::scan) == kIdxWindow * sizeof(int), "the window lives in the planning scratch");
 
-// Row t's list positions [0, min(topk[t], shape[1] of d_indices)), counted in half
-// positions: the planner's 64-unit tile is then one 32-entry stage, which splits the short
-// lists of sparse rows finer than whole pages would.
+// Row t's list positions [0, min(topk[t], shape[1] of d_indices)).
 __device__ __forceinline__ RowGeo sparse_row_geo(const SparseArgs& a, int t) {
   const int k = ld_const(a.topk + t);
-  return RowGeo{t, 0, 2 * max(0, min(k, a.idx_cols))};
+  return RowGeo{t, 0, max(0, min(k, a.idx_cols))};
 }
 
 template <int NT>
 __device__ __forceinline__ void sparse_fill(const SparseArgs& a, PlanLds& L) {
-  for (int t = threadIdx.x; t < a.T; t += NT) L.geo[t] = RowGeo{t, 0, 2 * max(0, min(a.topk[t], a.idx_cols))};
+  for (int t = threadIdx.x; t < a.T; t += NT) L.geo[t] = RowGeo{t, 0, max(0, min(a.topk[t], a.idx_cols))};
 }
 
 // One row segment: list positions of tiles [ta, tc) of row t.
@@ -71,10 +69,10 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   const int gq = lane >> 4, ln = lane & 15;
   const int h0 = wave * 16 * HB;
 
-  // list positions [klo, khi) of the tiles (the geometry counts half positions, all even)
+  // list positions [klo, khi) of the tiles
   const int first_tile = __builtin_amdgcn_readfirstlane(g.lo / kTileKeys);
-  const int klo = __builtin_amdgcn_readfirstlane(max(g.lo, (first_tile + ta) * kTileKeys)) / 2;
-  const int khi = __builtin_amdgcn_readfirstlane(min(g.hi, (first_tile + tc) * kTileKeys)) / 2;
+  const int klo = __builtin_amdgcn_readfirstlane(max(g.lo, (first_tile + ta) * kTileKeys));
+  const int khi = __builtin_amdgcn_readfirstlane(min(g.hi, (first_tile + tc) * kTileKeys));
   const int s_first = klo / kStageKeys;
   const int nst = (khi - 1) / kStageKeys - s_first + 1;
   const int32_t* ilist = a.idx + (int64_t)t * a.idx_row;
@@ -363,7 +361,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs
   plan_run<NW * 64, SMALL>(
       plan, L, [&](PlanLds& l) { sparse_fill<NW * 64>(a, l); }, [&](int t) { return sparse_row_geo(a, t); },
       [&](RowGeo* geo, int lane) {
-        if (lane < a.T) geo[lane] = RowGeo{lane, 0, 2 * max(0, min(a.topk[lane], a.idx_cols))};
+        if (lane < a.T) geo[lane] = RowGeo{lane, 0, max(0, min(a.topk[lane], a.idx_cols))};
       },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
         sparse_segment<HB, NW>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
