@@ -81,8 +81,11 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   all_wait0();
   stage_barrier();
 
-  // ---- index window: list positions [wbase, wbase + kIdxWindow), -1 outside [klo, khi)
+  // ---- index window: list positions [wbase, wbase + kIdxWindow), checked against the pool
+  // as they are stored: -1 outside [klo, khi), for negative entries (skipped) and for rows
+  // past the end of the pool (skipped and flagged)
   int wbase = klo;
+  bool bad = false;
   auto window_fill = [&]() {  // block-uniform, with no stage load in flight
     int v[kIdxWindow / NT];
 #pragma unroll
@@ -92,24 +95,21 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
     }
     all_wait0();
 #pragma unroll
-    for (int i = 0; i < kIdxWindow / NT; ++i) win[tid + i * NT] = v[i];
+    for (int i = 0; i < kIdxWindow / NT; ++i) {
+      int r = v[i];
+      if ((int64_t)r >= a.num_rows) {
+        bad = true;
+        r = -1;
+      }
+      win[tid + i * NT] = r < 0 ? -1 : r;
+    }
     lgkm_wait0();
     stage_barrier();
   };
   window_fill();
 
-  bool bad = false;
   // listed row of position p (read from the window), -1 when the key does not count
   auto entry = [&](int p) -> int { return p >= klo && p < khi ? win[p - wbase] : -1; };
-  // the entry checked against the pool: rows past its end are skipped and flagged
-  auto checked = [&](int r) -> int {
-    if (r < 0) return -1;  // the -1 fill (and any negative entry) is skipped
-    if ((int64_t)r >= a.num_rows) {
-      bad = true;
-      return -1;
-    }
-    return r;
-  };
   auto row_src = [&](int r) -> const uint8_t* {
     if (a.flat) return a.cache + (int64_t)r * kRawRowBytes;
     const int pg = r / a.PS;
@@ -154,7 +154,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   auto issue_slot = [&](auto flat, int rb, int sb, int jj, int rj) {
     constexpr bool FLAT = decltype(flat)::value;
     const int J = slot_of(jj);
-    const int r = checked(rj);
+    const int r = rj;
     if (J < kRawDma) {
       int lane_v = lane;
       asm volatile("" : "+v"(lane_v));
@@ -169,7 +169,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
     }
   };
   auto issue_mask = [&](int rmask) -> uint32_t {
-    return (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && rmask >= 0 && (int64_t)rmask < a.num_rows);
+    return (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && rmask >= 0);
   };
   auto issue = [&](int st, int rb, int sb) -> uint32_t {
     issue_window(st);
