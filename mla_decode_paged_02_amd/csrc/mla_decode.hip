@@ -212,27 +212,24 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
   };
   // A stage whose keys are all visible and lie in one valid page is loaded from a scalar
   // base: fast_base() returns it, or null when the stage needs the general path.
+  // (stage keys are never negative: the in-page offset is an unsigned remainder; the pool
+  // bound is compared in 32 bits, page ids being int32)
+  const int npages32 = (int)min(a.num_pages, (int64_t)INT32_MAX);
   auto fast_base = [&](int st, int pa) -> const uint8_t* {
     const int kbase = st * kStageKeys;
-    if (KPAGES != 0 && kbase >= klo && kbase + kStageKeys <= khi && pa >= 0 && (int64_t)pa < a.num_pages)
-      return a.cache + (int64_t)pa * a.page_bytes + (int64_t)(kbase - (kbase / a.PS) * a.PS) * kRowBytes;
+    if (KPAGES != 0 && kbase >= klo && kbase + kStageKeys <= khi && pa >= 0 && pa < npages32)
+      return a.cache + (int64_t)pa * a.page_bytes + (int64_t)((uint32_t)kbase % (uint32_t)a.PS) * kRowBytes;
     return nullptr;
   };
   // load jj of this wave for a fast stage (no-op past the wave's share)
   auto fast_load = [&](const uint8_t* base, MLA_LDS uint8_t* dst, int jj) {
     const int J = jj * NW + wave;
-    if (J < kDmaPerStage) dma16_base(base, dma_off[jj], dst + J * 1024);
+    if (kDmaPerStage % NW == 0 || J < kDmaPerStage) dma16_base(base, dma_off[jj], dst + J * 1024);
   };
-  auto issue = [&](int st, int bi, int pa) {
+  // general case: per-lane keys, pages and bounds (segment edges, invalid pages, page
+  // sizes that are not a multiple of the stage)
+  auto issue_general = [&](int st, int bi, int pa) {
     MLA_LDS uint8_t* dst = tiles + bi * kStageBytes;
-    const uint8_t* fb = fast_base(st, pa);
-    if (fb != nullptr) {
-#pragma unroll
-      for (int jj = 0; jj < kDmaMax; ++jj) fast_load(fb, dst, jj);
-      return;
-    }
-    // general case: per-lane keys, pages and bounds (segment edges, invalid pages, page
-    // sizes that are not a multiple of the stage)
     const int kbase = st * kStageKeys;
     const int lpa = kbase / a.PS;
     if (KPAGES == 0) {
@@ -246,7 +243,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
 #pragma unroll
     for (int jj = 0; jj < (kDmaPerStage + NW - 1) / NW; ++jj) {
       const int J = jj * NW + wave;
-      if (J >= kDmaPerStage) break;
+      if (kDmaPerStage % NW != 0 && J >= kDmaPerStage) break;
       const int sl = J * 64 + lane_v;
       const int row = sl / kRowChunks;
       const int cg = swz_chunk(row, sl - row * kRowChunks);
@@ -261,13 +258,23 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
           lp = lpa;
           pid = pa;
         }
-        if (pid >= 0 && (int64_t)pid < a.num_pages)
+        if (pid >= 0 && pid < npages32)
           src = a.cache + (int64_t)pid * a.page_bytes + (int64_t)(key - lp * a.PS) * kRowBytes + cg * 16;
         else
           bad_page = true;
       }
       dma16(src, dst + J * 1024);
     }
+  };
+  auto issue = [&](int st, int bi, int pa) {
+    const uint8_t* fb = fast_base(st, pa);
+    if (fb == nullptr) {
+      issue_general(st, bi, pa);
+      return;
+    }
+    MLA_LDS uint8_t* dst = tiles + bi * kStageBytes;
+#pragma unroll
+    for (int jj = 0; jj < kDmaMax; ++jj) fast_load(fb, dst, jj);
   };
 
   // ---- query fragments: B operand of S^T = K Q^T (lane holds q[h][32ks + 8gq .. +8]),
@@ -322,7 +329,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
       const int younger = KPAGES == 0 ? 0 : min(kNumBuf - 2, nst - 1 - k);
       constexpr int kDhi = (kDmaPerStage + NW - 1) / NW, kDlo = kDmaPerStage / NW;
       if (younger == 0) vm_wait_imm<0>();
-      else if (dpw == kDhi) {
+      else if (kDhi == kDlo || dpw == kDhi) {
         if (younger >= 2) vm_wait_imm<2 * kDhi>(); else vm_wait_imm<kDhi>();
       } else {
         if (younger >= 2) vm_wait_imm<2 * kDlo>(); else vm_wait_imm<kDlo>();
@@ -341,7 +348,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
     MLA_LDS uint8_t* fdst = tiles + (kn % kNumBuf) * kStageBytes;
     if (kn < nst) {
       fb = fast_base(s_first + kn, pa_n);
-      if (fb == nullptr) issue(s_first + kn, kn % kNumBuf, pa_n);
+      if (fb == nullptr) issue_general(s_first + kn, kn % kNumBuf, pa_n);
       if (KPAGES != 0 && kn + 1 < nst) pa_n = stage_page(s_first + kn + 1);
     }
     auto hook = [&](int ks) {
