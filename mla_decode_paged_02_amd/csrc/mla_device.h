@@ -42,16 +42,21 @@ enum : uint32_t {
 enum : int { kMaskNull = 0, kMaskCausal = 1, kMaskSliding = 2 };
 
 // ---------------------------------------------------------------------------------------
-// LDS tile layout: stage rows of 72 16-byte chunks (1152 bytes, so consecutive rows start
-// half the 64 banks apart); chunk c of row r is stored at chunk c ^ s(r) with s(r) in 0..7,
-// a permutation inside each aligned group of 8 chunks.  s spreads the 16 rows of a score
-// read (16-byte reads, 16 lanes a cycle) and the 8 rows of a transposing value read
-// (8-byte reads, 32 lanes a cycle) over all banks, and because it leaves bits 3 and up of
-// the chunk index alone, every read of a stage is one per-lane base plus a compile-time
-// offset.  The map is an involution.
+// LDS tile layout: stage rows of 72 16-byte chunks (1152 bytes); chunk c of row r is
+// stored at chunk c ^ s(r) with s(r) in 0..7, a permutation inside each aligned group of 8
+// chunks.  s is linear in the row bits r0..r4:
+//   s = (r1 ^ r3) << 2 | (r0 ^ r1 ^ r4) << 1 | r1,
+// chosen so that the score reads (16-byte reads of the 16 rows 8a + b + 4u, b < 4) and the
+// transposing value reads (8-byte reads of the rows 8g + b + 4u) meet each bank once per
+// cycle whether the LDS serves them as 64 banks with consecutive rows half a bank window
+// apart or as 128-byte windows in which every row starts at the same bank, and for each
+// lane grouping of the 16-byte reads that agrees with the measured conflict counts
+// (SQ_LDS_BANK_CONFLICT).  Because s leaves bits 3 and up of the chunk index alone, every
+// read of a stage is one per-lane base plus a compile-time offset.  The map is an
+// involution.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int swz_mask(int row) {
-  return (((row >> 3) & 1) << 2) | (((row >> 1) & 1) << 1) | ((row >> 4) & 1);
+  return ((((row >> 1) ^ (row >> 3)) & 1) << 2) | (((row ^ (row >> 1) ^ (row >> 4)) & 1) << 1) | ((row >> 1) & 1);
 }
 __device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ swz_mask(row); }
 
