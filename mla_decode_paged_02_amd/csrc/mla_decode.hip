@@ -6,12 +6,11 @@
 // local_window_size): for each query row t and head h, softmax over the visible cache
 // rows of scale * <q, row>, applied to the rows' 512 latent columns.
 //
-// Per work-group: all heads of one query row (8 waves x 16 heads at H = 128, two waves
-// per SIMD so one hides the other's LDS latency), so each cache row is read from HBM
-// exactly once.  Keys stream through LDS in 32-key stages
-// (4 buffers, 3 in flight) by direct global->LDS loads; the stage's page id is fetched
-// with a scalar load one stage ahead.  The work split is in mla_plan.h, the per-stage
-// MFMA / softmax work in mla_stage.h.
+// Per work-group: all heads of one query row (4 waves x 32 heads at H = 128, one wave per
+// SIMD, O in the accumulation registers), so each cache row is read from HBM exactly once.
+// Keys stream through LDS in 32-key stages (4 buffers, 3 in flight) by direct global->LDS
+// loads; page ids come from an LDS window of the row's page-table entries.  The work split
+// is in mla_plan.h, the per-stage MFMA / softmax work in mla_stage.h.
 #include <type_traits>
 
 #include "mla_device.h"
