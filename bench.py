@@ -14,7 +14,9 @@ algorithmic bytes (every visible cache row once plus q) per step divided by the 
 Prints one JSON line.
 
 Other workloads (--workload): C0 tiny decode, C2 long-context decode, C4 sparse fp8
-decode (GB/s, HBM roofline), C3 ragged prefill (TFLOP/s, bf16 MFMA roofline).
+decode (GB/s, HBM roofline), C3 ragged prefill (TFLOP/s, bf16 MFMA roofline), M2 / M4
+multi-token decode (the C1 batch with 2 / 4 causal query tokens per sequence; the
+algorithmic bytes count each cache row once per sequence, the read-once standard).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C1]
 """
@@ -40,9 +42,14 @@ DESCRIPTIONS = {
     "C2": "C2: B=8 H=128 lens {32768x4,65536x4} PS=64, 1 query token per sequence, head 576 / V 512, causal, bf16",
     "C3": "C3: ragged causal prefill, new {512,1024,2048,3968} after {0,256,0,1024}, H=128, q 192 / v 128, bf16",
     "C4": "C4: sparse decode, B=32 H=128, 16384 rows/seq PS=64, top-k U[1024,2048] of 2048 indices, fp8 e4m3 q and cache",
+    "M2": "M2: multi-token decode, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64) with 2 query tokens per sequence, causal within the new tokens, bf16",
+    "M4": "M4: multi-token decode, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64) with 4 query tokens per sequence, causal within the new tokens, bf16",
 }
+# multi-token workloads: (configuration they extend, query tokens per sequence)
+MULTI_TOKEN = {"M2": (1, 2), "M4": (1, 4)}
 KERNELS = {"C0": "mla_decode_kernel", "C1": "mla_decode_kernel", "C2": "mla_decode_kernel",
-           "C3": "mla_prefill_kernel", "C4": "mla_sparse_kernel"}
+           "C3": "mla_prefill_kernel", "C4": "mla_sparse_kernel", "M2": "mla_decode_kernel",
+           "M4": "mla_decode_kernel"}
 
 
 # sources the dense decode and combine kernels are built from
@@ -112,7 +119,11 @@ def setup(workload, copies, num_partitions, dev):
     import mla_decode_paged_02_amd as m
     from synth import config_case
 
-    case = config_case(int(workload[1]))
+    if workload in MULTI_TOKEN:
+        k, n_tok = MULTI_TOKEN[workload]
+        case = config_case(k, q_per_seq=n_tok)
+    else:
+        case = config_case(int(workload[1]))
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -127,7 +138,7 @@ def setup(workload, copies, num_partitions, dev):
         return None if x is None else torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
 
     n = max(1, copies)
-    if workload in ("C0", "C1", "C2"):
+    if workload in ("C0", "C1", "C2") or workload in MULTI_TOKEN:
         q0, c0 = bf16(case.q), bf16(case.latent_cache)
         sets = [(q0, c0)] + [(q0.clone(), c0.clone()) for _ in range(n - 1)]
         off, pt, lens = i32(case.input_row_offsets), i32(case.page_table), i32(case.cache_lens)
@@ -245,7 +256,19 @@ def main():
 
     gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     tflops = alg_flops / (ms_step * 1e-3) / 1e12
-    if prefill:
+    # the roofline that bounds the kernel: bf16 MFMA when its arithmetic intensity is past
+    # the ridge (peak FLOP/s over peak bytes/s), else HBM
+    mfma_bound = alg_flops / alg_bytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound and not prefill:
+        achieved = alg_flops / (k_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "hbm_achieved_gbs": round(alg_bytes / (k_avg_ms * 1e-3) / 1e9, 2)}
+        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else ''}decode GB/s, {wl}, 1 GPU"
+        if wl in MULTI_TOKEN:
+            metric = f"MLA multi-token decode GB/s (cache rows once per sequence), {wl}, 1 GPU"
+        value, unit = gbs, "GB/s"
+    elif prefill:
         achieved = alg_flops / (k_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
@@ -255,6 +278,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl)}
         metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else ''}decode GB/s, {wl}, 1 GPU"
+        if wl in MULTI_TOKEN:
+            metric = f"MLA multi-token decode GB/s (cache rows once per sequence), {wl}, 1 GPU"
         value, unit = gbs, "GB/s"
     roof.update({"kernel": KERNELS[wl], "kernel_avg_us": round(k_avg_ms * 1e3, 3),
                  "kernel_launches_timed": launches})
@@ -275,7 +300,7 @@ def main():
             "workload": DESCRIPTIONS[wl],
             "num_partitions": args.num_partitions if args.num_partitions > 0 else "library",
             "rotated_input_copies": args.copies,
-            "seed": 355000 + int(wl[1]),
+            "seed": 355000 + (MULTI_TOKEN[wl][0] if wl in MULTI_TOKEN else int(wl[1])),
         },
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

@@ -200,3 +200,14 @@ def test_alternating_shapes_reuse_workspace():
         elif P == 5:
             assert np.array_equal(got, b5)
         assert np.array_equal(bits_of(decode_on_gpu(m, big)), a)
+
+
+@pytest.mark.parametrize("n_tok", [2, 4])
+def test_c1_multi_token(n_tok):
+    """The C1 batch with 2 or 4 query tokens per sequence (causal within the new tokens):
+    every row matches the oracle, balanced and fixed splits alike."""
+    m = need_gpu()
+    case = config_case(1, q_per_seq=n_tok)
+    want = oracle_of(case)
+    for P in (0, 3):
+        compare(to_f64(decode_on_gpu(m, case, num_partitions=P)), want, BF16_TOL, f"C1 x{n_tok} P={P}")
