@@ -16,7 +16,8 @@ Prints one JSON line.
 Other workloads (--workload): C0 tiny decode, C2 long-context decode, C4 sparse fp8
 decode (GB/s, HBM roofline), C3 ragged prefill (TFLOP/s, bf16 MFMA roofline), M2 / M4
 multi-token decode (the C1 batch with 2 / 4 causal query tokens per sequence; the
-algorithmic bytes count each cache row once per sequence, the read-once standard).
+algorithmic bytes count each cache row once per sequence, the read-once standard), D8
+dense decode of the C1 batch over a paged fp8 cache.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C1]
 """
@@ -44,16 +45,17 @@ DESCRIPTIONS = {
     "C4": "C4: sparse decode, B=32 H=128, 16384 rows/seq PS=64, top-k U[1024,2048] of 2048 indices, fp8 e4m3 q and cache",
     "M2": "M2: multi-token decode, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64) with 2 query tokens per sequence, causal within the new tokens, bf16",
     "M4": "M4: multi-token decode, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64) with 4 query tokens per sequence, causal within the new tokens, bf16",
+    "D8": "D8: dense decode over a paged fp8 e4m3 cache, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64), one float32 scale per cache row and per q token",
 }
 # multi-token workloads: (configuration they extend, query tokens per sequence)
 MULTI_TOKEN = {"M2": (1, 2), "M4": (1, 4)}
 KERNELS = {"C0": "mla_decode_kernel", "C1": "mla_decode_kernel", "C2": "mla_decode_kernel",
            "C3": "mla_prefill_kernel", "C4": "mla_sparse_kernel", "M2": "mla_decode_kernel",
-           "M4": "mla_decode_kernel"}
+           "M4": "mla_decode_kernel", "D8": "mla_sparse_kernel"}
 
 
 # sources the dense decode and combine kernels are built from
-DECODE_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_kernels.h", "mla_plan.h", "mla_stage.h")
+DECODE_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_kernels.h", "mla_plan.h", "mla_rows.h", "mla_stage.h")
 
 
 def kernel_digest():
@@ -122,6 +124,8 @@ def setup(workload, copies, num_partitions, dev):
     if workload in MULTI_TOKEN:
         k, n_tok = MULTI_TOKEN[workload]
         case = config_case(k, q_per_seq=n_tok)
+    elif workload == "D8":
+        case = config_case(1, fp8=True)
     else:
         case = config_case(int(workload[1]))
 
@@ -148,6 +152,18 @@ def setup(workload, copies, num_partitions, dev):
             q, c = sets[i % len(sets)]
             m.decode_paged(q, off, pt, lens, c, case.scale, mask=case.mask,
                            local_window_size=case.window, num_partitions=num_partitions, out=out)
+        return case, step, case.total_q
+    if workload == "D8":
+        q0, c0 = u8(case.q8), u8(case.cache8)
+        sets = [(q0, c0)] + [(q0.clone(), c0.clone()) for _ in range(n - 1)]
+        qs, cs = f32(case.q_scale), f32(case.cache_scale)
+        off, pt, lens = i32(case.input_row_offsets), i32(case.page_table), i32(case.cache_lens)
+        out = torch.empty((case.total_q, case.num_heads, 512), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            q, c = sets[i % len(sets)]
+            m.decode_paged_fp8(q, qs, off, pt, lens, c, cs, case.scale, mask=case.mask,
+                               num_partitions=num_partitions, out=out)
         return case, step, case.total_q
     if workload == "C4":
         q0, c0 = u8(case.q8), u8(case.cache8)
@@ -264,7 +280,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "hbm_achieved_gbs": round(alg_bytes / (k_avg_ms * 1e-3) / 1e9, 2)}
-        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else ''}decode GB/s, {wl}, 1 GPU"
+        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else 'fp8 ' if wl == 'D8' else ''}decode GB/s, {wl}, 1 GPU"
         if wl in MULTI_TOKEN:
             metric = f"MLA multi-token decode GB/s (cache rows once per sequence), {wl}, 1 GPU"
         value, unit = gbs, "GB/s"
@@ -277,7 +293,7 @@ def main():
         achieved = alg_bytes / (k_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl)}
-        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else ''}decode GB/s, {wl}, 1 GPU"
+        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else 'fp8 ' if wl == 'D8' else ''}decode GB/s, {wl}, 1 GPU"
         if wl in MULTI_TOKEN:
             metric = f"MLA multi-token decode GB/s (cache rows once per sequence), {wl}, 1 GPU"
         value, unit = gbs, "GB/s"
@@ -294,13 +310,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 in, bf16 MFMA" if wl == "C4" else "bf16",
+        "dtype": "fp8-e4m3 in, bf16 MFMA" if wl in ("C4", "D8") else "bf16",
         "data": "synthetic",
         "config": {
             "workload": DESCRIPTIONS[wl],
             "num_partitions": args.num_partitions if args.num_partitions > 0 else "library",
             "rotated_input_copies": args.copies,
-            "seed": 355000 + (MULTI_TOKEN[wl][0] if wl in MULTI_TOKEN else int(wl[1])),
+            "seed": 355000 + (MULTI_TOKEN[wl][0] if wl in MULTI_TOKEN else 1 if wl == "D8" else int(wl[1])),
         },
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

@@ -140,6 +140,32 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
                                    void* stream);
 
 /*
+ * Dense MLA decode over a paged fp8 e4m3 latent cache
+ * (generic_flare_mla_decode_kv_cache_ragged: summary; Args q, q_scale_ptr, kv_collection,
+ * input_row_offsets, scale, output, num_partitions_in; Parameters mask_str,
+ * local_window_size, per_token_scale_rope_aware = False).  The same computation as
+ * mla_decode_paged, with every value stored as an e4m3 code times a float32 scale: the
+ * query's per token (shared by its heads), the cache's per row (all 576 columns).  The
+ * codes are widened exactly; the logits and P.V accumulate in fp32 from bf16 operands.
+ *
+ *   q                  fp8 e4m3 [T, H, 576]
+ *   q_scale            f32 [T] or NULL = 1
+ *   input_row_offsets, page_table, cache_lens, mask, local_window_size, scale,
+ *   num_partitions, out     as for mla_decode_paged
+ *   latent_cache       fp8 e4m3 [num_pages, PS, 576], rows of a page contiguous, any PS
+ *   cache_scale        f32 [num_pages, PS] or NULL = 1
+ *
+ * Errors as for mla_decode_paged; page ids outside the pool are skipped and set bit 1
+ * of the device error word (mla_check_device_errors).
+ */
+mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
+                                const mla_tensor* input_row_offsets, const mla_tensor* page_table,
+                                const mla_tensor* cache_lens, const mla_tensor* latent_cache,
+                                const mla_tensor* cache_scale, float scale, int32_t mask,
+                                int32_t local_window_size, int32_t num_partitions,
+                                mla_tensor* out, void* stream);
+
+/*
  * Ragged MLA prefill with per-head keys (generic_flare_mla_prefill_kv_cache_ragged:
  * summary; Args q, k, v, buffer_row_offsets, cache_offsets, input_row_offsets, scale,
  * output).  Key i of sequence b is row buffer_row_offsets[b] + i of k / v at cache

@@ -51,8 +51,9 @@ def library() -> ctypes.CDLL:
         i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
         lib.mla_decode_paged.argtypes = [P, P, P, P, P, f32, i32, i32, i32, P, vp]
         lib.mla_decode_paged_sparse.argtypes = [P, P, P, P, P, P, P, f32, i32, P, vp]
+        lib.mla_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, f32, i32, i32, i32, P, vp]
         lib.mla_prefill_paged.argtypes = [P, P, P, P, P, P, P, P, P, f32, i32, P, vp]
-        for fn in ("mla_decode_paged", "mla_decode_paged_sparse", "mla_prefill_paged",
+        for fn in ("mla_decode_paged", "mla_decode_paged_sparse", "mla_decode_paged_fp8", "mla_prefill_paged",
                    "mla_reserve_workspace", "mla_check_device_errors"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_decode_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32, i32]
@@ -155,6 +156,24 @@ def decode_paged_sparse(q, q_scale, input_row_offsets, latent_cache, cache_scale
     _check(library().mla_decode_paged_sparse(
         _desc(q), _desc(q_scale), _offsets(input_row_offsets), _desc(latent_cache),
         _desc(cache_scale), _desc(d_indices), _desc(topk_lengths), float(scale),
+        int(num_partitions), _desc(out), _stream(stream)))
+    return out
+
+
+def decode_paged_fp8(q, q_scale, input_row_offsets, page_table, cache_lens, latent_cache, cache_scale,
+                     scale, mask="causal", local_window_size=-1, num_partitions=0, out=None, stream=None):
+    """Dense MLA decode over a paged fp8 cache (mla_decode_paged_fp8).  q fp8 e4m3
+    [T, H, 576] with q_scale f32 [T] or None; latent_cache fp8 e4m3 [num_pages, PS, 576]
+    with cache_scale f32 [num_pages, PS] or None (torch float8_e4m3fn or uint8 codes);
+    returns out bf16 [T, H, 512]."""
+    import torch
+    _on_gpu(q, q_scale, input_row_offsets, page_table, cache_lens, latent_cache, cache_scale, out)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
+    _check(library().mla_decode_paged_fp8(
+        _desc(q), _desc(q_scale), _offsets(input_row_offsets), _desc(page_table), _desc(cache_lens),
+        _desc(latent_cache), _desc(cache_scale), float(scale),
+        MASKS[mask] if isinstance(mask, str) else int(mask), int(local_window_size),
         int(num_partitions), _desc(out), _stream(stream)))
     return out
 

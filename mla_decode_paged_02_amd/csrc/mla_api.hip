@@ -496,6 +496,103 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
   return ok();
 }
 
+mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
+                                const mla_tensor* input_row_offsets, const mla_tensor* page_table,
+                                const mla_tensor* cache_lens, const mla_tensor* latent_cache,
+                                const mla_tensor* cache_scale, float scale, int32_t mask,
+                                int32_t local_window_size, int32_t num_partitions, mla_tensor* out,
+                                void* stream) {
+  mla_status s;
+  if ((s = check_tensor(q, "q", MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
+  const int64_t T = q->shape[0], H = q->shape[1];
+  if (q->shape[2] != 576) return fail(MLA_ERR_SHAPE, "q: head width %lld, expected 576", (long long)q->shape[2]);
+  if (q_scale && (s = check_1d(q_scale, "q_scale", MLA_DTYPE_F32, T)) != MLA_OK) return s;
+  if ((s = check_tensor(input_row_offsets, "input_row_offsets", MLA_DTYPE_U32, 1, false)) != MLA_OK) return s;
+  const int64_t B = input_row_offsets->shape[0] - 1;
+  if (B < 1) return fail(MLA_ERR_SHAPE, "input_row_offsets: needs batch + 1 >= 2 entries");
+  if ((s = check_tensor(page_table, "page_table", MLA_DTYPE_I32, 2, false)) != MLA_OK) return s;
+  if (page_table->shape[0] != B) return fail(MLA_ERR_SHAPE, "page_table: %lld rows, expected batch %lld", (long long)page_table->shape[0], (long long)B);
+  if ((s = check_1d(cache_lens, "cache_lens", MLA_DTYPE_I32, B)) != MLA_OK) return s;
+  if ((s = check_tensor(latent_cache, "latent_cache", MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
+  if (latent_cache->shape[2] != 576) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576", (long long)latent_cache->shape[2]);
+  const int64_t NP = latent_cache->shape[0], PS = latent_cache->shape[1];
+  if (PS < 1) return fail(MLA_ERR_SHAPE, "latent_cache: page size must be >= 1");
+  if (NP > 0 && PS > 1 && latent_cache->stride[1] != 576)
+    return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride 576)");
+  if (NP > 1 && latent_cache->stride[0] < PS * 576)
+    return fail(MLA_ERR_SHAPE, "latent_cache: pages overlap (page stride below page_size * 576)");
+  if (NP * PS > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 cache rows");
+  if (cache_scale) {
+    if ((s = check_tensor(cache_scale, "cache_scale", MLA_DTYPE_F32, 2, false)) != MLA_OK) return s;
+    if (cache_scale->shape[0] != NP || cache_scale->shape[1] != PS)
+      return fail(MLA_ERR_SHAPE, "cache_scale: shape must be [%lld, %lld]", (long long)NP, (long long)PS);
+  }
+  if ((s = check_tensor(out, "out", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
+  if (out->shape[0] != T || out->shape[1] != H || out->shape[2] != 512)
+    return fail(MLA_ERR_SHAPE, "out: shape must be [%lld, %lld, 512]", (long long)T, (long long)H);
+  if (!supported_heads(H)) return fail(MLA_ERR_UNSUPPORTED, "num_heads %lld not in {16, 32, 64, 128}", (long long)H);
+  if (mask < MLA_MASK_NULL || mask > MLA_MASK_SLIDING_WINDOW_CAUSAL) return fail(MLA_ERR_VALUE, "mask %d unknown", mask);
+  if (mask == MLA_MASK_SLIDING_WINDOW_CAUSAL && local_window_size <= 0)
+    return fail(MLA_ERR_VALUE, "sliding-window mask needs local_window_size > 0");
+  if (!std::isfinite(scale)) return fail(MLA_ERR_VALUE, "scale must be finite");
+  if (num_partitions > 4096) return fail(MLA_ERR_VALUE, "num_partitions %d above 4096", num_partitions);
+  if (page_table->shape[1] * PS > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "max_pages * page_size above 2^30");
+  if (T > kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 query rows");
+  if (T == 0) return ok();
+
+  bool cap = false;
+  if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
+  const int dev = current_device();
+  const int grid = cu_count(dev);
+  const int32_t nparts = num_partitions > 0 ? num_partitions : 0;
+  const DecodeLayout L = decode_layout(T, (int32_t)H, nparts, grid);
+  void* ws = nullptr;
+  if ((s = grow_workspace(dev, stream, L.total, cap, &ws)) != MLA_OK) return s;
+  char* w = (char*)ws + kHeaderBytes;
+
+  mla::SparseArgs a{};
+  a.q = (const uint8_t*)q->data;
+  a.q_tok = q->stride[0];
+  a.q_head = q->stride[1];
+  a.q_scale = q_scale ? (const float*)q_scale->data : nullptr;
+  a.cache = (const uint8_t*)latent_cache->data;
+  a.page_bytes = latent_cache->stride[0];
+  a.cache_scale = cache_scale ? (const float*)cache_scale->data : nullptr;
+  a.cs_page = cache_scale ? cache_scale->stride[0] : 0;
+  a.num_rows = NP * PS;
+  a.PS = (int32_t)PS;
+  a.flat = a.page_bytes == PS * 576 && (cache_scale == nullptr || a.cs_page == PS) ? 1 : 0;
+  a.dense = 1;
+  a.offsets = (const uint32_t*)input_row_offsets->data;
+  a.page_table = (const int32_t*)page_table->data;
+  a.pt_row = page_table->stride[0];
+  a.cache_lens = (const int32_t*)cache_lens->data;
+  a.B = (int32_t)B;
+  a.max_pages = (int32_t)page_table->shape[1];
+  a.mask = mask;
+  a.window = local_window_size;
+  a.T = (int32_t)T;
+  a.H = (int32_t)H;
+  a.q_bf16 = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.nparts = nparts;
+  a.grid = grid;
+  a.out = (uint16_t*)out->data;
+  a.o_tok = out->stride[0];
+  a.o_head = out->stride[1];
+  a.part_o = (uint16_t*)(w + L.part_o);
+  a.part_lse = (float*)(w + L.part_lse);
+  a.row_meta = (int32_t*)(w + L.meta);
+  a.zero_row = (const uint8_t*)ws;
+  a.err = (uint32_t*)((char*)ws + kErrOffset);
+  mla::KernelTimer tslot;
+  mla::KernelTimer* timer = profile_timer(&tslot);
+  const hipError_t e = mla::launch_sparse(a, (hipStream_t)stream, timer);
+  profile_keep(timer, e == hipSuccess);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "fp8 decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla_tensor* v,
                              const mla_tensor* buffer_row_offsets, const mla_tensor* cache_offsets,
                              const mla_tensor* input_row_offsets, const mla_tensor* page_table,

@@ -38,7 +38,10 @@ struct DecodeArgs {
   uint32_t* err;              // device error word
 };
 
-// Sparse decode: each q row lists physical cache rows to attend to.
+// Decode over an fp8 e4m3 cache whose rows are gathered one by one: the sparse decode
+// (each q row lists physical cache rows to attend to) and, with dense = 1, the dense
+// decode over a paged fp8 cache (each q row attends to the visible rows of its sequence,
+// found through the page table).
 struct SparseArgs {
   const uint8_t* q;           // fp8 e4m3 [T, H, 576], or bf16 when q_bf16
   int64_t q_tok, q_head;      // element strides
@@ -54,6 +57,14 @@ struct SparseArgs {
   int64_t idx_row;            // element stride between index rows
   int32_t idx_cols;           // shape[1] of d_indices (topk is clamped to it)
   const int32_t* topk;        // [T]
+  // dense = 1: the rows of q row t are the visible positions of its sequence, physical
+  // row page_table[b][pos / PS] * PS + pos % PS (idx and topk are unused)
+  int32_t dense;
+  const uint32_t* offsets;    // [B + 1]
+  const int32_t* page_table;  // [B, max_pages]
+  int64_t pt_row;             // element stride between page-table rows
+  const int32_t* cache_lens;  // [B]
+  int32_t B, max_pages, mask, window;
   int32_t T, H;
   int32_t q_bf16;             // 1: q is bf16 (no q_scale)
   float scale_log2;           // scale * log2(e)

@@ -7,6 +7,11 @@
 // being page * PS + slot of the pool; the key of a listed row is its e4m3 codes times
 // the row's scale, the query the e4m3 codes times the token's scale.
 //
+// With dense = 1 the same kernel is the dense decode over a paged fp8 cache ([DEC]
+// Args kv_collection, q_scale_ptr; Parameters mask_str, local_window_size): the rows of
+// query row t are the positions its mask leaves visible, each mapped through the page
+// table of its sequence, so list position p is logical key p.
+//
 // The work split, the per-stage compute, the epilogue and the combine are those of the
 // dense decode (mla_plan.h, mla_stage.h, mla_decode.hip).  What differs is the loader:
 // the 32 listed rows of a stage (576 fp8 bytes each, gathered) land in an LDS staging
@@ -19,6 +24,7 @@
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "mla_plan.h"
+#include "mla_rows.h"
 #include "mla_stage.h"
 
 namespace mla {
@@ -76,6 +82,9 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   const int s_first = klo / kStageKeys;
   const int nst = (khi - 1) / kStageKeys - s_first + 1;
   const int32_t* ilist = a.idx + (int64_t)t * a.idx_row;
+  // dense: the page-table row of the sequence (g.b), list position p = logical key p
+  const int32_t* prow = a.dense ? a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.pt_row : nullptr;
+  const int npages32 = (int)min(a.num_rows / a.PS, (int64_t)INT32_MAX);
 
   // every wave must be done with the previous segment's buffers and window
   all_wait0();
@@ -85,19 +94,30 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   // as they are stored: -1 outside [klo, khi), for negative entries (skipped) and for rows
   // past the end of the pool (skipped and flagged)
   int wbase = klo;
-  bool bad = false;
+  bool bad = false, bad_page = false;
   auto window_fill = [&]() {  // block-uniform, with no stage load in flight
     int v[kIdxWindow / NT];
 #pragma unroll
     for (int i = 0; i < kIdxWindow / NT; ++i) {
       const int p = wbase + tid + i * NT;
-      v[i] = p < khi ? ilist[p] : -1;
+      v[i] = p < khi ? (a.dense ? prow[p / a.PS] : ilist[p]) : -1;
     }
     all_wait0();
 #pragma unroll
     for (int i = 0; i < kIdxWindow / NT; ++i) {
       int r = v[i];
-      if ((int64_t)r >= a.num_rows) {
+      if (a.dense) {
+        // page id -> physical row; a page outside the pool is skipped and flagged
+        const int p = wbase + tid + i * NT;
+        if (p < khi) {
+          if (r >= 0 && r < npages32) {
+            r = r * a.PS + (p - (p / a.PS) * a.PS);
+          } else {
+            bad_page = true;
+            r = -1;
+          }
+        }
+      } else if ((int64_t)r >= a.num_rows) {
         bad = true;
         r = -1;
       }
@@ -337,6 +357,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   }
 
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(a.err, kErrSparseIndex);
+  if (__builtin_amdgcn_ballot_w64(bad_page) != 0 && lane == 0) atomicOr(a.err, kErrPageId);
   if constexpr (HB == 2) {
     // every wave is done with the stage buffers before they take the output rows
     stage_barrier();
@@ -359,9 +380,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs
   MLA_LDS uint8_t* land = tiles + kSpTiles * kStageBytes;
   MLA_LDS float* ksc = (MLA_LDS float*)ksc_raw;
   plan_run<NW * 64, SMALL>(
-      plan, L, [&](PlanLds& l) { sparse_fill<NW * 64>(a, l); }, [&](int t) { return sparse_row_geo(a, t); },
+      plan, L,
+      [&](PlanLds& l) {
+        if (a.dense) decode_fill<NW * 64>(a, l); else sparse_fill<NW * 64>(a, l);
+      },
+      [&](int t) { return a.dense ? decode_row_geo(a, t) : sparse_row_geo(a, t); },
       [&](RowGeo* geo, int lane) {
-        if (lane < a.T) geo[lane] = RowGeo{lane, 0, max(0, min(a.topk[lane], a.idx_cols))};
+        if (a.dense) decode_fill_wave(a, geo, lane);
+        else if (lane < a.T) geo[lane] = RowGeo{lane, 0, max(0, min(a.topk[lane], a.idx_cols))};
       },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
         sparse_segment<HB, NW>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
@@ -389,7 +415,7 @@ static SplitPlan plan_of(const SparseArgs& a) {
 template <int HB, int NW>
 static hipError_t launch_sparse_h(const SparseArgs& a, const SplitPlan& p, hipStream_t stream) {
   const dim3 grid(a.nparts >= 1 ? a.T * a.nparts : a.grid), block(NW * 64);
-  if (a.nparts == 0 && a.T <= 64 && a.T <= a.grid)
+  if (a.nparts == 0 && a.T <= 64 && a.T <= a.grid && (!a.dense || a.B <= 64))
     hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true>), grid, block, 0, stream, a, p);
   else
     hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false>), grid, block, 0, stream, a, p);

@@ -278,6 +278,19 @@ def decode_sparse(q8, q_scale, input_row_offsets, cache8, cache_scale, d_indices
                              scale, rows)
 
 
+def decode_paged_fp8(q8, q_scale, input_row_offsets, page_table, cache_lens, cache8, cache_scale,
+                     page_size, scale, mask="causal", window=-1, rows=None):
+    """Dense MLA decode over a paged FP8 cache ([DEC] Args q_scale_ptr, kv_collection;
+    Parameters mask_str, local_window_size, per_token_scale_rope_aware = False): every stored
+    value is its E4M3 code value times the float32 scale of its q token (shared by the
+    heads) or cache row (all 576 columns); then the dense decode, in float64."""
+    q = e4m3_to_f64(q8)
+    if q_scale is not None:
+        q = q * np.asarray(q_scale, dtype=np.float64)[:, None, None]
+    return decode_paged_f64(q, input_row_offsets, page_table, cache_lens, _LazyE4M3(cache8, cache_scale),
+                            page_size, scale, mask, window, rows)
+
+
 class _LazyE4M3:
     """Dequantises only the gathered rows of a large E4M3 cache."""
 

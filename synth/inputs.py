@@ -184,15 +184,24 @@ def _poison_unused(cache, table, lens, page_size, spare, poison):
 @dataclasses.dataclass
 class DecodeCase:
     name: str
-    q: np.ndarray                  # uint16 [T, H, 576]
+    q: np.ndarray | None           # uint16 [T, H, 576] (None for an fp8 case)
     input_row_offsets: np.ndarray  # uint32 [B + 1]
     page_table: np.ndarray         # int32 [B, max_pages]
     cache_lens: np.ndarray         # int32 [B]
-    latent_cache: np.ndarray       # uint16 [num_pages, PS, 576]
+    latent_cache: np.ndarray | None  # uint16 [num_pages, PS, 576] (None for an fp8 case)
     page_size: int
     scale: float
     mask: str = "causal"
     window: int = -1
+    # fp8 cases: E4M3 codes with one float32 scale per q token / cache row
+    q8: np.ndarray | None = None           # uint8 [T, H, 576]
+    q_scale: np.ndarray | None = None      # float32 [T]
+    cache8: np.ndarray | None = None       # uint8 [num_pages, PS, 576]
+    cache_scale: np.ndarray | None = None  # float32 [num_pages, PS]
+
+    @property
+    def fp8(self) -> bool:
+        return self.q8 is not None
 
     @property
     def batch(self) -> int:
@@ -200,17 +209,20 @@ class DecodeCase:
 
     @property
     def total_q(self) -> int:
-        return int(self.q.shape[0])
+        return int((self.q8 if self.fp8 else self.q).shape[0])
 
     @property
     def num_heads(self) -> int:
-        return int(self.q.shape[1])
+        return int((self.q8 if self.fp8 else self.q).shape[1])
 
 
 def make_decode_case(seed, lens, num_heads, page_size, q_per_seq=1, mask="causal",
                      window=-1, tail="normal", spare_pages=0, shuffle=True,
-                     q_std=1.0, cache_std=1.0, max_pages=None, name="decode"):
-    """Dense decode inputs.  ``lens`` is a sequence or a callable rng -> lengths."""
+                     q_std=1.0, cache_std=1.0, max_pages=None, fp8=False, name="decode"):
+    """Dense decode inputs.  ``lens`` is a sequence or a callable rng -> lengths.
+
+    fp8: q and cache as E4M3 codes of the same N(0,1) draws, with one float32 scale per q
+    token (absmax over its heads) and per cache row (absmax over its 576 values)."""
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens(rng) if callable(lens) else lens, dtype=np.int32)
     B = len(lens)
@@ -219,6 +231,18 @@ def make_decode_case(seed, lens, num_heads, page_size, q_per_seq=1, mask="causal
     offsets[1:] = np.cumsum(n_q)
     T = int(offsets[-1])
     table, total, spare = _page_layout(rng, lens, page_size, spare_pages, shuffle, max_pages)
+    if fp8:
+        qf = _normal_bf16(seed, 1, (T, num_heads, HEAD_DIM), q_std, as_bits=False)
+        q8, q_scale = _quantise_rows(qf, axis=(1, 2))
+        del qf
+        c8, c_scale = _normal_e4m3_rows(seed, 2, (total, page_size, HEAD_DIM))
+        if tail == "nan":
+            _poison_unused(c8, table, lens, page_size, spare, np.uint8(E4M3_NAN_CODE))
+            _poison_unused(c_scale[..., None], table, lens, page_size, spare, np.float32(np.nan))
+        return DecodeCase(name=name, q=None, input_row_offsets=offsets, page_table=table,
+                          cache_lens=lens, latent_cache=None, page_size=page_size,
+                          scale=default_scale(), mask=mask, window=window, q8=q8,
+                          q_scale=q_scale, cache8=c8, cache_scale=c_scale)
     q = _normal_bf16(seed, 1, (T, num_heads, HEAD_DIM), q_std)
     cache = _normal_bf16(seed, 2, (total, page_size, HEAD_DIM), cache_std)
     if tail == "nan":
@@ -405,6 +429,10 @@ def algorithmic_bytes(case) -> int:
             if case.mask == "sliding_window_causal" and case.window > 0:
                 lo = max(0, (L - n) - case.window + 1)
             rows += max(0, L - lo)
+        if case.fp8:
+            row_bytes = HEAD_DIM + (4 if case.cache_scale is not None else 0)
+            qb = case.q8.size + (case.q_scale.size * 4 if case.q_scale is not None else 0)
+            return rows * row_bytes + qb
         return rows * HEAD_DIM * 2 + case.q.size * 2
     if isinstance(case, SparseCase):
         listed = int(sum(int(np.count_nonzero(case.d_indices[t, :case.topk_lengths[t]] >= 0))

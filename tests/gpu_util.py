@@ -75,3 +75,17 @@ def compare(got, want, tol, what=""):
     print(f"[parity] {what}: max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
     assert mx <= tol[0] and mean <= tol[1], f"{what}: max-abs {mx:.3e}, mean-abs {mean:.3e} vs {tol}"
     return mx, mean
+
+
+def decode_fp8_on_gpu(m, case, num_partitions=0, table=None, out=None):
+    """Dense fp8 decode of an fp8 DecodeCase through mla_decode_paged_fp8."""
+    import torch
+    q_scale = f32_dev(case.q_scale) if case.q_scale is not None else None
+    c_scale = f32_dev(case.cache_scale) if case.cache_scale is not None else None
+    res = m.decode_paged_fp8(u8_dev(case.q8), q_scale, i32_dev(case.input_row_offsets),
+                             i32_dev(case.page_table if table is None else table),
+                             i32_dev(case.cache_lens), u8_dev(case.cache8), c_scale, case.scale,
+                             mask=case.mask, local_window_size=case.window,
+                             num_partitions=num_partitions, out=out)
+    torch.cuda.synchronize()
+    return res

@@ -152,6 +152,44 @@ def pin_p1_sparse():
             close(lse[t, h], l, 1e-12)
 
 
+def pin_p1_dense_fp8():
+    """Dense fp8 decode against brute force on contiguous keys, dequantised independently
+    (torch's float8_e4m3fn widening times the row / token scales); the pool's unused
+    slots hold the NaN code with a NaN scale and must never be read."""
+    rng = np.random.default_rng(21)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    lens, n_tokens, H, ps = (13, 30), (2, 3), 2, 8
+    seq_codes = [rng.choice(finite, size=(L, D)).astype(np.uint8) for L in lens]
+    seq_scales = [rng.uniform(0.001, 0.01, size=L).astype(np.float32) for L in lens]
+    T = sum(n_tokens)
+    q8 = rng.choice(finite[(finite & 0x78) < 0x50], size=(T, H, D)).astype(np.uint8)
+    q_scale = rng.uniform(0.001, 0.01, size=T).astype(np.float32)
+    npages = [-(-L // ps) for L in lens]
+    total = sum(npages) + 2
+    perm = rng.permutation(total)
+    cache8 = np.full((total, ps, D), 0x7F, dtype=np.uint8)
+    c_scale = np.full((total, ps), np.nan, dtype=np.float32)
+    table = np.full((len(lens), max(npages)), -1, dtype=np.int32)
+    cur = 0
+    for b, L in enumerate(lens):
+        for j in range(npages[b]):
+            pid = int(perm[cur])
+            cur += 1
+            table[b, j] = pid
+            n = min(ps, L - j * ps)
+            cache8[pid, :n] = seq_codes[b][j * ps:j * ps + n]
+            c_scale[pid, :n] = seq_scales[b][j * ps:j * ps + n]
+    off = offsets_of(n_tokens)
+    qv = _torch_e4m3(q8) * q_scale.astype(np.float64)[:, None, None]
+    keys = [(_torch_e4m3(seq_codes[b]) * seq_scales[b].astype(np.float64)[:, None]).tolist() for b in range(2)]
+    for mask, window in (("causal", -1), ("sliding_window_causal", 4), ("null", -1)):
+        out, lse = O.decode_paged_fp8(q8, q_scale, off, table, np.array(lens, dtype=np.int32), cache8, c_scale,
+                                      ps, SCALE, mask, window)
+        bo, bl = decode_contiguous(qv.tolist(), keys, list(n_tokens), SCALE, mask, window)
+        close(out, bo, 1e-12)
+        close(lse, bl, 1e-12)
+
+
 def tiny_prefill(seed=5, new=(3, 4), prefix=(0, 2), H=2, page_size=4):
     rng = np.random.default_rng(seed)
     total = [a + b for a, b in zip(new, prefix)]
