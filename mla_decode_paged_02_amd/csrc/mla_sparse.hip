@@ -61,7 +61,8 @@ __device__ __forceinline__ void sparse_fill(const SparseArgs& a, PlanLds& L) {
 // landing buffer stage k was widened from, then computes stage k from its bf16 tile while
 // the hook of the score k-steps widens stage k+1 into the other tile.  One barrier per
 // stage orders all of it.
-template <int HB, int NW>
+// DENSE: rows from the page table (mla_decode_paged_fp8), else from d_indices.
+template <int HB, int NW, bool DENSE>
 __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint8_t* tiles, MLA_LDS uint8_t* raw,
                                                MLA_LDS float* kscale, MLA_LDS int* win, int t, const RowGeo& g,
                                                int ta, int tc, bool full, int slot) {
@@ -83,7 +84,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   const int nst = (khi - 1) / kStageKeys - s_first + 1;
   const int32_t* ilist = a.idx + (int64_t)t * a.idx_row;
   // dense: the page-table row of the sequence (g.b), list position p = logical key p
-  const int32_t* prow = a.dense ? a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.pt_row : nullptr;
+  const int32_t* prow = DENSE ? a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.pt_row : nullptr;
   const int npages32 = (int)min(a.num_rows / a.PS, (int64_t)INT32_MAX);
 
   // every wave must be done with the previous segment's buffers and window
@@ -100,13 +101,13 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
 #pragma unroll
     for (int i = 0; i < kIdxWindow / NT; ++i) {
       const int p = wbase + tid + i * NT;
-      v[i] = p < khi ? (a.dense ? prow[p / a.PS] : ilist[p]) : -1;
+      v[i] = p < khi ? (DENSE ? prow[p / a.PS] : ilist[p]) : -1;
     }
     all_wait0();
 #pragma unroll
     for (int i = 0; i < kIdxWindow / NT; ++i) {
       int r = v[i];
-      if (a.dense) {
+      if (DENSE) {
         // page id -> physical row; a page outside the pool is skipped and flagged
         const int p = wbase + tid + i * NT;
         if (p < khi) {
@@ -370,7 +371,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
 
 // SMALL: balanced batch of at most 64 rows, no more rows than work-groups (planned per
 // wave, see plan_run).
-template <int HB, int NW, bool SMALL>
+template <int HB, int NW, bool SMALL, bool DENSE>
 __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs a, const SplitPlan plan) {
   // the widened tiles, then the fp8 landing buffers
   __shared__ __attribute__((aligned(1024))) uint8_t buf_raw[kSpLdsBytes];
@@ -382,15 +383,17 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs
   plan_run<NW * 64, SMALL>(
       plan, L,
       [&](PlanLds& l) {
-        if (a.dense) decode_fill<NW * 64>(a, l); else sparse_fill<NW * 64>(a, l);
+        if constexpr (DENSE) decode_fill<NW * 64>(a, l); else sparse_fill<NW * 64>(a, l);
       },
-      [&](int t) { return a.dense ? decode_row_geo(a, t) : sparse_row_geo(a, t); },
+      [&](int t) {
+        if constexpr (DENSE) return decode_row_geo(a, t); else return sparse_row_geo(a, t);
+      },
       [&](RowGeo* geo, int lane) {
-        if (a.dense) decode_fill_wave(a, geo, lane);
+        if constexpr (DENSE) decode_fill_wave(a, geo, lane);
         else if (lane < a.T) geo[lane] = RowGeo{lane, 0, max(0, min(a.topk[lane], a.idx_cols))};
       },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
-        sparse_segment<HB, NW>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
+        sparse_segment<HB, NW, DENSE>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
       });
 }
 
@@ -415,10 +418,14 @@ static SplitPlan plan_of(const SparseArgs& a) {
 template <int HB, int NW>
 static hipError_t launch_sparse_h(const SparseArgs& a, const SplitPlan& p, hipStream_t stream) {
   const dim3 grid(a.nparts >= 1 ? a.T * a.nparts : a.grid), block(NW * 64);
-  if (a.nparts == 0 && a.T <= 64 && a.T <= a.grid && (!a.dense || a.B <= 64))
-    hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true>), grid, block, 0, stream, a, p);
-  else
-    hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false>), grid, block, 0, stream, a, p);
+  const bool small = a.nparts == 0 && a.T <= 64 && a.T <= a.grid && (!a.dense || a.B <= 64);
+  if (a.dense) {
+    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, true>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, true>), grid, block, 0, stream, a, p);
+  } else {
+    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, false>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, false>), grid, block, 0, stream, a, p);
+  }
   return hipGetLastError();
 }
 
