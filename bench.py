@@ -87,6 +87,28 @@ def read_traffic(workload):
         return None
 
 
+def hbm_read_ceiling(dev, gib=2, reps=20):
+    """Context, not a roofline peak: the read bandwidth of a plain device reduction
+    (row sums of a 2 GiB float32 tensor viewed as 16384 rows, every byte read once; the
+    fastest of the torch reductions tried on MI355X, ~6.2 TB/s), best of `reps` timed
+    passes, in GB/s."""
+    import torch
+    x = torch.ones((gib << 30) // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        x.view(16384, -1).sum(dim=1)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    nbytes = x.numel() * 4
+    del x
+    torch.cuda.empty_cache()
+    return round(nbytes / (best * 1e-3) / 1e9, 1)
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -328,6 +350,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if not prefill:
+        ceiling = hbm_read_ceiling(dev)
+        res["hbm_read_ceiling_gbs"] = ceiling
+        res["kernel_frac_of_read_ceiling"] = round(alg_bytes / (k_avg_ms * 1e-3) / 1e9 / ceiling, 4)
     if wl == "C1" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, alg_bytes)
     print(json.dumps(res), flush=True)
