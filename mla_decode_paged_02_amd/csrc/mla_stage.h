@@ -150,9 +150,10 @@ __device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const 
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) sacc[u][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
-    // Two waves share each SIMD, so each wave issues its LDS reads just before use and
-    // the other wave covers the latency.  Swizzled addresses are formed per read (one
-    // xor and one add) rather than kept in registers.
+    // Used for 16 and 32 heads (one or two waves, each on a SIMD of its own): the LDS
+    // reads are issued just before use and the compiler schedules their waits.
+    // Swizzled addresses are formed per read (one xor and one add) rather than kept in
+    // registers.
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
       const bf16x8 k0 = *(const MLA_LDS bf16x8*)(buf + g.ka[0][ks & 1] + 128 * (ks >> 1));
