@@ -17,7 +17,7 @@ Other workloads (--workload): C0 tiny decode, C2 long-context decode, C4 sparse 
 decode (GB/s, HBM roofline), C3 ragged prefill (TFLOP/s, bf16 MFMA roofline), M2 / M4
 multi-token decode (the C1 batch with 2 / 4 causal query tokens per sequence; the
 algorithmic bytes count each cache row once per sequence, the read-once standard), D8
-dense decode of the C1 batch over a paged fp8 cache.
+dense decode of the C1 batch over a paged fp8 cache, X4 the fp8 top-k indexer in front of C4.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C1]
 """
@@ -46,12 +46,14 @@ DESCRIPTIONS = {
     "M2": "M2: multi-token decode, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64) with 2 query tokens per sequence, causal within the new tokens, bf16",
     "M4": "M4: multi-token decode, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64) with 4 query tokens per sequence, causal within the new tokens, bf16",
     "D8": "D8: dense decode over a paged fp8 e4m3 cache, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64), one float32 scale per cache row and per q token",
+    "X4": "X4: fp8 top-k indexer in front of C4, 32 sequences x 16384 cache rows PS=64, 1 query token each, 64 heads of width 128, top 2048, causal",
 }
 # multi-token workloads: (configuration they extend, query tokens per sequence)
 MULTI_TOKEN = {"M2": (1, 2), "M4": (1, 4)}
 KERNELS = {"C0": "mla_decode_kernel", "C1": "mla_decode_kernel", "C2": "mla_decode_kernel",
            "C3": "mla_prefill_kernel", "C4": "mla_sparse_kernel", "M2": "mla_decode_kernel",
-           "M4": "mla_decode_kernel", "D8": "mla_sparse_kernel"}
+           "M4": "mla_decode_kernel", "D8": "mla_sparse_kernel",
+           "X4": "mla_indexer_kernel"}
 
 
 # sources the dense decode and combine kernels are built from
@@ -148,6 +150,9 @@ def setup(workload, copies, num_partitions, dev):
         case = config_case(k, q_per_seq=n_tok)
     elif workload == "D8":
         case = config_case(1, fp8=True)
+    elif workload == "X4":
+        from synth import indexer_config
+        case = indexer_config()
     else:
         case = config_case(int(workload[1]))
 
@@ -174,6 +179,17 @@ def setup(workload, copies, num_partitions, dev):
             q, c = sets[i % len(sets)]
             m.decode_paged(q, off, pt, lens, c, case.scale, mask=case.mask,
                            local_window_size=case.window, num_partitions=num_partitions, out=out)
+        return case, step, case.total_q
+    if workload == "X4":
+        q0, k0 = u8(case.q8), u8(case.k8)
+        sets = [(q0, k0)] + [(q0.clone(), k0.clone()) for _ in range(n - 1)]
+        qs, ks = f32(case.q_s), f32(case.k_scale)
+        off, pt, lens = i32(case.input_row_offsets), i32(case.page_table), i32(case.cache_lens)
+        out = torch.empty((case.total_q, case.top_k), dtype=torch.int32, device=dev)
+
+        def step(i):
+            q, k = sets[i % len(sets)]
+            m.indexer_paged_fp8(q, qs, off, pt, lens, k, ks, case.top_k, mask=case.mask, out=out)
         return case, step, case.total_q
     if workload == "D8":
         q0, c0 = u8(case.q8), u8(case.cache8)
@@ -303,6 +319,8 @@ def main():
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "hbm_achieved_gbs": round(alg_bytes / (k_avg_ms * 1e-3) / 1e9, 2)}
         metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else 'fp8 ' if wl == 'D8' else ''}decode GB/s, {wl}, 1 GPU"
+        if wl == "X4":
+            metric = "MLA fp8 top-k indexer GB/s (cache rows once per token), X4, 1 GPU"
         if wl in MULTI_TOKEN:
             metric = f"MLA multi-token decode GB/s (cache rows once per sequence), {wl}, 1 GPU"
         value, unit = gbs, "GB/s"
@@ -316,6 +334,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl)}
         metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else 'fp8 ' if wl == 'D8' else ''}decode GB/s, {wl}, 1 GPU"
+        if wl == "X4":
+            metric = "MLA fp8 top-k indexer GB/s (cache rows once per token), X4, 1 GPU"
         if wl in MULTI_TOKEN:
             metric = f"MLA multi-token decode GB/s (cache rows once per sequence), {wl}, 1 GPU"
         value, unit = gbs, "GB/s"
@@ -332,13 +352,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 in, bf16 MFMA" if wl in ("C4", "D8") else "bf16",
+        "dtype": "fp8-e4m3 in, bf16 MFMA" if wl in ("C4", "D8") else "fp8-e4m3 in, f32 scores" if wl == "X4" else "bf16",
         "data": "synthetic",
         "config": {
             "workload": DESCRIPTIONS[wl],
             "num_partitions": args.num_partitions if args.num_partitions > 0 else "library",
             "rotated_input_copies": args.copies,
-            "seed": 355000 + (MULTI_TOKEN[wl][0] if wl in MULTI_TOKEN else 1 if wl == "D8" else int(wl[1])),
+            "seed": 355000 + (MULTI_TOKEN[wl][0] if wl in MULTI_TOKEN else 1 if wl == "D8" else 5 if wl == "X4" else int(wl[1])),
         },
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

@@ -166,6 +166,34 @@ mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
                                 mla_tensor* out, void* stream);
 
 /*
+ * FP8 top-k indexer (mla_indexer_ragged_float8_paged: summary; Args output_indices, q,
+ * q_s, input_row_offsets, k_collection).  For query token t of sequence b the score of
+ * visible cache row r is sum_h q_s[t, h] * <e4m3(q[t, h, :]), e4m3(k[r, :])> * k_scale[r]
+ * (scores summed over the heads, one k scale per row); the mask leaves the rows a decode
+ * token at position cache_lens[b] - n_b + j sees.  Row t of out_indices receives the
+ * top_k highest-scoring visible rows as physical rows of the pool (page_id * PS + slot:
+ * the d_indices of mla_decode_paged_sparse), by descending score, equal scores by
+ * ascending position, then -1.  Scores are evaluated in float32.
+ *
+ *   q                  fp8 e4m3 [T, NH, D], D a multiple of 16 up to 256, D contiguous
+ *   q_s                f32 [T, NH]
+ *   input_row_offsets, page_table, cache_lens, mask, local_window_size
+ *                      as for mla_decode_paged; max_pages * PS <= 16384
+ *   k_cache            fp8 e4m3 [num_pages, PS, D], rows of a page contiguous, base and
+ *                      page stride multiples of 16 bytes
+ *   k_scale            f32 [num_pages, PS] or NULL = 1
+ *   out_indices        i32 [T, top_k], top_k in [1, 2048], written in full
+ *
+ * Page ids outside the pool rank last, are never returned and set bit 1 of the device
+ * error word.
+ */
+mla_status mla_indexer_paged_fp8(const mla_tensor* q, const mla_tensor* q_s,
+                                 const mla_tensor* input_row_offsets, const mla_tensor* page_table,
+                                 const mla_tensor* cache_lens, const mla_tensor* k_cache,
+                                 const mla_tensor* k_scale, int32_t mask, int32_t local_window_size,
+                                 mla_tensor* out_indices, void* stream);
+
+/*
  * Ragged MLA prefill with per-head keys (generic_flare_mla_prefill_kv_cache_ragged:
  * summary; Args q, k, v, buffer_row_offsets, cache_offsets, input_row_offsets, scale,
  * output).  Key i of sequence b is row buffer_row_offsets[b] + i of k / v at cache

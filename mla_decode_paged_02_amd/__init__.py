@@ -52,8 +52,9 @@ def library() -> ctypes.CDLL:
         lib.mla_decode_paged.argtypes = [P, P, P, P, P, f32, i32, i32, i32, P, vp]
         lib.mla_decode_paged_sparse.argtypes = [P, P, P, P, P, P, P, f32, i32, P, vp]
         lib.mla_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, f32, i32, i32, i32, P, vp]
+        lib.mla_indexer_paged_fp8.argtypes = [P, P, P, P, P, P, P, i32, i32, P, vp]
         lib.mla_prefill_paged.argtypes = [P, P, P, P, P, P, P, P, P, f32, i32, P, vp]
-        for fn in ("mla_decode_paged", "mla_decode_paged_sparse", "mla_decode_paged_fp8", "mla_prefill_paged",
+        for fn in ("mla_decode_paged", "mla_decode_paged_sparse", "mla_decode_paged_fp8", "mla_indexer_paged_fp8", "mla_prefill_paged",
                    "mla_reserve_workspace", "mla_check_device_errors"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_decode_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32, i32]
@@ -175,6 +176,22 @@ def decode_paged_fp8(q, q_scale, input_row_offsets, page_table, cache_lens, late
         _desc(latent_cache), _desc(cache_scale), float(scale),
         MASKS[mask] if isinstance(mask, str) else int(mask), int(local_window_size),
         int(num_partitions), _desc(out), _stream(stream)))
+    return out
+
+
+def indexer_paged_fp8(q, q_s, input_row_offsets, page_table, cache_lens, k_cache, k_scale, top_k,
+                      mask="causal", local_window_size=-1, out=None, stream=None):
+    """FP8 top-k indexer (mla_indexer_paged_fp8).  q fp8 e4m3 [T, NH, D] with q_s f32
+    [T, NH]; k_cache fp8 e4m3 [num_pages, PS, D] with k_scale f32 [num_pages, PS] or None;
+    returns int32 [T, top_k] physical rows, -1 filled."""
+    import torch
+    _on_gpu(q, q_s, input_row_offsets, page_table, cache_lens, k_cache, k_scale, out)
+    if out is None:
+        out = torch.empty((q.shape[0], int(top_k)), dtype=torch.int32, device=q.device)
+    _check(library().mla_indexer_paged_fp8(
+        _desc(q), _desc(q_s), _offsets(input_row_offsets), _desc(page_table), _desc(cache_lens),
+        _desc(k_cache), _desc(k_scale), MASKS[mask] if isinstance(mask, str) else int(mask),
+        int(local_window_size), _desc(out), _stream(stream)))
     return out
 
 

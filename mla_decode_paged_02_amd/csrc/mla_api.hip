@@ -593,6 +593,94 @@ mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
   return ok();
 }
 
+mla_status mla_indexer_paged_fp8(const mla_tensor* q, const mla_tensor* q_s,
+                                 const mla_tensor* input_row_offsets, const mla_tensor* page_table,
+                                 const mla_tensor* cache_lens, const mla_tensor* k_cache,
+                                 const mla_tensor* k_scale, int32_t mask, int32_t local_window_size,
+                                 mla_tensor* out_indices, void* stream) {
+  mla_status s;
+  if ((s = check_tensor(q, "q", MLA_DTYPE_FP8_E4M3, 3, false)) != MLA_OK) return s;
+  const int64_t T = q->shape[0], NH = q->shape[1], D = q->shape[2];
+  if (q->stride[2] != 1) return fail(MLA_ERR_SHAPE, "q: the head width must be contiguous");
+  if (D < 16 || D > mla::kIdxMaxDepth || D % 16 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "indexer head width %lld: a multiple of 16 up to %d", (long long)D, mla::kIdxMaxDepth);
+  if (NH < 1) return fail(MLA_ERR_SHAPE, "q: needs at least one head");
+  if ((s = check_tensor(q_s, "q_s", MLA_DTYPE_F32, 2, false)) != MLA_OK) return s;
+  if (q_s->shape[0] != T || q_s->shape[1] != NH || q_s->stride[1] != 1)
+    return fail(MLA_ERR_SHAPE, "q_s: shape must be [%lld, %lld], heads contiguous", (long long)T, (long long)NH);
+  if ((s = check_tensor(input_row_offsets, "input_row_offsets", MLA_DTYPE_U32, 1, false)) != MLA_OK) return s;
+  const int64_t B = input_row_offsets->shape[0] - 1;
+  if (B < 1) return fail(MLA_ERR_SHAPE, "input_row_offsets: needs batch + 1 >= 2 entries");
+  if ((s = check_tensor(page_table, "page_table", MLA_DTYPE_I32, 2, false)) != MLA_OK) return s;
+  if (page_table->shape[0] != B) return fail(MLA_ERR_SHAPE, "page_table: %lld rows, expected batch %lld", (long long)page_table->shape[0], (long long)B);
+  if ((s = check_1d(cache_lens, "cache_lens", MLA_DTYPE_I32, B)) != MLA_OK) return s;
+  if ((s = check_tensor(k_cache, "k_cache", MLA_DTYPE_FP8_E4M3, 3, false)) != MLA_OK) return s;
+  const int64_t NP = k_cache->shape[0], PS = k_cache->shape[1];
+  if (k_cache->shape[2] != D) return fail(MLA_ERR_SHAPE, "k_cache: row width %lld, expected %lld", (long long)k_cache->shape[2], (long long)D);
+  if (PS < 1) return fail(MLA_ERR_SHAPE, "k_cache: page size must be >= 1");
+  if (k_cache->stride[2] != 1 || (NP > 0 && PS > 1 && k_cache->stride[1] != D))
+    return fail(MLA_ERR_SHAPE, "k_cache: rows of a page must be contiguous");
+  if (NP > 1 && k_cache->stride[0] < PS * D) return fail(MLA_ERR_SHAPE, "k_cache: pages overlap");
+  if (k_cache->stride[0] % 16 != 0 || (uintptr_t)k_cache->data % 16 != 0)
+    return fail(MLA_ERR_ALIGNMENT, "k_cache: base and page stride must be multiples of 16 bytes");
+  if (NP * PS > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 cache rows");
+  if (k_scale) {
+    if ((s = check_tensor(k_scale, "k_scale", MLA_DTYPE_F32, 2, false)) != MLA_OK) return s;
+    if (k_scale->shape[0] != NP || k_scale->shape[1] != PS || (PS > 1 && k_scale->stride[1] != 1))
+      return fail(MLA_ERR_SHAPE, "k_scale: shape must be [%lld, %lld], rows contiguous", (long long)NP, (long long)PS);
+  }
+  if ((s = check_tensor(out_indices, "out_indices", MLA_DTYPE_I32, 2, false)) != MLA_OK) return s;
+  const int64_t K = out_indices->shape[1];
+  if (out_indices->shape[0] != T || out_indices->stride[1] != 1 || (T > 1 && out_indices->stride[0] < K))
+    return fail(MLA_ERR_SHAPE, "out_indices: shape must be [%lld, top_k], rows contiguous", (long long)T);
+  if (K < 1 || K > mla::kIdxMaxTopK) return fail(MLA_ERR_UNSUPPORTED, "top_k %lld not in [1, %d]", (long long)K, mla::kIdxMaxTopK);
+  if (page_table->shape[1] * PS > mla::kIdxMaxKeys)
+    return fail(MLA_ERR_UNSUPPORTED, "max_pages * page_size above %d rows per sequence", mla::kIdxMaxKeys);
+  if (mask < MLA_MASK_NULL || mask > MLA_MASK_SLIDING_WINDOW_CAUSAL) return fail(MLA_ERR_VALUE, "mask %d unknown", mask);
+  if (mask == MLA_MASK_SLIDING_WINDOW_CAUSAL && local_window_size <= 0)
+    return fail(MLA_ERR_VALUE, "sliding-window mask needs local_window_size > 0");
+  if (T > kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 query rows");
+  if (T == 0) return ok();
+
+  bool cap = false;
+  if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
+  void* ws = nullptr;
+  if ((s = grow_workspace(current_device(), stream, 0, cap, &ws)) != MLA_OK) return s;
+  mla::IndexerArgs a{};
+  a.q = (const uint8_t*)q->data;
+  a.q_tok = q->stride[0];
+  a.q_head = q->stride[1];
+  a.q_s = (const float*)q_s->data;
+  a.qs_tok = q_s->stride[0];
+  a.offsets = (const uint32_t*)input_row_offsets->data;
+  a.page_table = (const int32_t*)page_table->data;
+  a.pt_row = page_table->stride[0];
+  a.cache_lens = (const int32_t*)cache_lens->data;
+  a.k = (const uint8_t*)k_cache->data;
+  a.page_bytes = k_cache->stride[0];
+  a.num_pages = NP;
+  a.k_s = k_scale ? (const float*)k_scale->data : nullptr;
+  a.ks_page = k_scale ? k_scale->stride[0] : 0;
+  a.B = (int32_t)B;
+  a.T = (int32_t)T;
+  a.NH = (int32_t)NH;
+  a.depth = (int32_t)D;
+  a.PS = (int32_t)PS;
+  a.max_pages = (int32_t)page_table->shape[1];
+  a.mask = mask;
+  a.window = local_window_size;
+  a.top_k = (int32_t)K;
+  a.out = (int32_t*)out_indices->data;
+  a.out_row = out_indices->stride[0];
+  a.err = (uint32_t*)((char*)ws + kErrOffset);
+  mla::KernelTimer tslot;
+  mla::KernelTimer* timer = profile_timer(&tslot);
+  const hipError_t e = mla::launch_indexer(a, (hipStream_t)stream, timer);
+  profile_keep(timer, e == hipSuccess);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "indexer launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla_tensor* v,
                              const mla_tensor* buffer_row_offsets, const mla_tensor* cache_offsets,
                              const mla_tensor* input_row_offsets, const mla_tensor* page_table,

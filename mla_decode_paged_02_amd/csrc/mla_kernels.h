@@ -105,6 +105,30 @@ struct PrefillArgs {
   uint32_t* err;
 };
 
+// FP8 top-k indexer over a paged cache (mla_indexer.hip).
+constexpr int kIdxMaxKeys = 16384;  // visible rows per query token (scores sorted in LDS)
+constexpr int kIdxMaxDepth = 256;   // indexer head width
+constexpr int kIdxMaxTopK = 2048;
+struct IndexerArgs {
+  const uint8_t* q;           // fp8 e4m3 [T, NH, depth]
+  int64_t q_tok, q_head;      // element strides
+  const float* q_s;           // [T, NH] scales
+  int64_t qs_tok;
+  const uint32_t* offsets;    // [B + 1]
+  const int32_t* page_table;  // [B, max_pages]
+  int64_t pt_row;
+  const int32_t* cache_lens;  // [B]
+  const uint8_t* k;           // fp8 e4m3 [num_pages, PS, depth], rows of a page contiguous
+  int64_t page_bytes;
+  int64_t num_pages;
+  const float* k_s;           // [num_pages, PS] row scales or null (= 1)
+  int64_t ks_page;
+  int32_t B, T, NH, depth, PS, max_pages, mask, window, top_k;
+  int32_t* out;               // [T, top_k] physical rows, -1 filled
+  int64_t out_row;
+  uint32_t* err;
+};
+
 // Where the decode kernels put split rows' parts (mla_plan.h).
 struct SplitPlan {
   int32_t T, H;
@@ -131,5 +155,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const KernelTi
 hipError_t launch_combine(const SplitPlan& p, hipStream_t stream);
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream, const KernelTimer* timer);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, const KernelTimer* timer);
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const KernelTimer* timer);
 
 }  // namespace mla

@@ -291,6 +291,53 @@ def decode_paged_fp8(q8, q_scale, input_row_offsets, page_table, cache_lens, cac
                             page_size, scale, mask, window, rows)
 
 
+# --------------------------------------------------------------------------------------
+# FP8 top-k indexer
+# --------------------------------------------------------------------------------------
+
+def indexer_scores(q8_t, q_s_t, k8_rows, k_scale_rows):
+    """Scores of one query token against cache rows ([IDX] summary: the FP8 product of q
+    and the cached k with their scales, summed over all heads):
+    score[r] = sum_h q_s[h] * <e4m3(q[h]), e4m3(k[r])> * k_scale[r], in float64."""
+    q = e4m3_to_f64(q8_t)                               # [NH, D]
+    k = e4m3_to_f64(k8_rows)                            # [R, D]
+    per_head = k @ q.T                                  # [R, NH]
+    s = per_head @ np.asarray(q_s_t, dtype=np.float64)  # sum over heads
+    if k_scale_rows is not None:
+        s = s * np.asarray(k_scale_rows, dtype=np.float64)
+    return s
+
+
+def indexer_paged_fp8(q8, q_s, input_row_offsets, page_table, cache_lens, k8, k_scale, page_size,
+                      top_k, mask="causal", window=-1, return_scores=False):
+    """FP8 top-k indexer over a paged cache ([IDX] summary and Args output_indices, q, q_s,
+    input_row_offsets, k_collection).  Query token j of sequence b scores the rows its
+    mask leaves visible (the decode visibility); row t of the result holds the top_k
+    highest-scoring rows, as physical rows page_id * PS + slot, by descending score and
+    equal scores by ascending position, then -1.  With return_scores, also the visible
+    logical positions and their scores per row."""
+    T = q8.shape[0]
+    off = np.asarray(input_row_offsets, dtype=np.int64)
+    out = np.full((T, top_k), -1, dtype=np.int64)
+    seen = []
+    for b in range(len(cache_lens)):
+        n = int(off[b + 1] - off[b])
+        L = int(cache_lens[b])
+        for j in range(n):
+            t = int(off[b]) + j
+            lo, hi = visible_range(L, n, j, mask, window)
+            pos = np.arange(lo, hi, dtype=np.int64)
+            pages = np.asarray(page_table[b], dtype=np.int64)[pos // page_size]
+            slots = pos % page_size
+            ks = None if k_scale is None else k_scale[pages, slots]
+            sc = indexer_scores(q8[t], q_s[t], k8[pages, slots], ks) if len(pos) else np.zeros(0)
+            order = np.lexsort((pos, -sc))                  # score descending, then position
+            take = order[:top_k]
+            out[t, :len(take)] = pages[take] * page_size + slots[take]
+            seen.append((t, pos, sc))
+    return (out, seen) if return_scores else out
+
+
 class _LazyE4M3:
     """Dequantises only the gathered rows of a large E4M3 cache."""
 

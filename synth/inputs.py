@@ -44,6 +44,7 @@ __all__ = [
     "bf16_bits", "e4m3_codes", "DecodeCase", "SparseCase", "PrefillCase",
     "make_decode_case", "make_sparse_case", "make_prefill_case", "config_case",
     "CONFIG_DESCRIPTIONS", "algorithmic_bytes", "algorithmic_flops",
+    "IndexerCase", "make_indexer_case", "indexer_config",
 ]
 
 
@@ -326,6 +327,55 @@ def make_sparse_case(seed, batch, num_heads, rows_per_seq, page_size, topk_range
 
 
 # --------------------------------------------------------------------------------------
+# FP8 top-k indexer
+# --------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class IndexerCase:
+    name: str
+    q8: np.ndarray                 # uint8 E4M3 [T, NH, D]
+    q_s: np.ndarray                # float32 [T, NH] (one scale per token and head)
+    input_row_offsets: np.ndarray  # uint32 [B + 1]
+    page_table: np.ndarray         # int32 [B, max_pages]
+    cache_lens: np.ndarray         # int32 [B]
+    k8: np.ndarray                 # uint8 E4M3 [num_pages, PS, D]
+    k_scale: np.ndarray            # float32 [num_pages, PS] (one per cache row)
+    page_size: int
+    top_k: int
+    mask: str = "causal"
+    window: int = -1
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q8.shape[0])
+
+
+def make_indexer_case(seed, lens, num_heads, depth, page_size, top_k, q_per_seq=1, mask="causal",
+                      window=-1, name="indexer"):
+    """Indexer inputs: N(0,1) draws quantised to E4M3, q scaled per (token, head) and the
+    cache per row (absmax / 448), in a shuffled page pool."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens(rng) if callable(lens) else lens, dtype=np.int32)
+    B = len(lens)
+    n_q = np.broadcast_to(np.asarray(q_per_seq, dtype=np.int64), (B,))
+    offsets = np.zeros(B + 1, dtype=np.uint32)
+    offsets[1:] = np.cumsum(n_q)
+    T = int(offsets[-1])
+    table, total, _ = _page_layout(rng, lens, page_size, 0, True)
+    q8, q_s = _normal_e4m3_rows(seed, 5, (T, num_heads, depth))
+    k8, k_scale = _normal_e4m3_rows(seed, 6, (total, page_size, depth))
+    return IndexerCase(name=name, q8=q8, q_s=q_s, input_row_offsets=offsets, page_table=table,
+                       cache_lens=lens, k8=k8, k_scale=k_scale, page_size=page_size, top_k=top_k,
+                       mask=mask, window=window)
+
+
+def indexer_config():
+    """The indexer in front of the sparse workload C4: 32 sequences of 16384 cache rows,
+    one query token each, 64 indexer heads of width 128, top 2048 (seed 355005)."""
+    return make_indexer_case(355_005, [16384] * 32, 64, 128, 64, 2048, name="X4")
+
+
+# --------------------------------------------------------------------------------------
 # ragged prefill
 # --------------------------------------------------------------------------------------
 
@@ -442,6 +492,18 @@ def algorithmic_bytes(case) -> int:
         return listed * row_bytes + qb
     if isinstance(case, PrefillCase):
         return (case.q.size + case.k.size + case.v.size) * 2 + int(case.cache_lens.sum()) * ROPE_DIM * 2
+    if isinstance(case, IndexerCase):
+        rows = 0
+        off = case.input_row_offsets.astype(np.int64)
+        for b in range(len(case.cache_lens)):
+            L = int(case.cache_lens[b])
+            n = int(off[b + 1] - off[b])
+            if n == 0:
+                continue
+            lo = max(0, (L - n) - case.window + 1) if case.mask == "sliding_window_causal" else 0
+            rows += max(0, L - lo)
+        depth = case.q8.shape[2]
+        return rows * (depth + 4) + case.q8.size + case.q_s.size * 4
     raise TypeError(type(case))
 
 
@@ -477,4 +539,17 @@ def algorithmic_flops(case) -> int:
             # query j sits at L - n + j and sees keys 0..L-n+j under the causal mask
             pairs += n * (L - n) + n * (n + 1) // 2 if case.mask == "causal" else n * L
         return pairs * 2 * H * (PREFILL_QK_DIM + PREFILL_V_DIM)
+    if isinstance(case, IndexerCase):
+        NH, depth = case.q8.shape[1], case.q8.shape[2]
+        off = case.input_row_offsets.astype(np.int64)
+        pairs = 0
+        for b in range(len(case.cache_lens)):
+            L = int(case.cache_lens[b])
+            n = int(off[b + 1] - off[b])
+            for jj in range(n):
+                pos = L - n + jj
+                hi = L if case.mask == "null" else min(pos + 1, L)
+                lo = max(0, pos - case.window + 1) if case.mask == "sliding_window_causal" else 0
+                pairs += max(0, hi - lo)
+        return pairs * 2 * NH * depth
     raise TypeError(type(case))

@@ -190,6 +190,54 @@ def pin_p1_dense_fp8():
         close(lse, bl, 1e-12)
 
 
+def pin_p1_indexer():
+    """The indexer against scalar brute force: scores by plain loops over heads and
+    columns with math.fsum (torch's e4m3 widening), selection by a full sort of
+    (-score, position), physical rows through the page table, -1 fill."""
+    rng = np.random.default_rng(22)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    NH, Dk, ps, top_k = 3, 16, 4, 6
+    lens, n_tokens = (9, 3), (2, 1)
+    pages_needed = [-(-L // ps) for L in lens]
+    total = sum(pages_needed) + 1
+    k8 = rng.choice(finite, size=(total, ps, Dk)).astype(np.uint8)
+    k_scale = rng.uniform(0.5, 2.0, size=(total, ps)).astype(np.float32)
+    perm = rng.permutation(total)
+    table = np.full((2, max(pages_needed)), -1, dtype=np.int32)
+    cur = 0
+    for b in range(2):
+        for j in range(pages_needed[b]):
+            table[b, j] = perm[cur]
+            cur += 1
+    T = sum(n_tokens)
+    q8 = rng.choice(finite, size=(T, NH, Dk)).astype(np.uint8)
+    q_s = rng.uniform(0.5, 2.0, size=(T, NH)).astype(np.float32)
+    off = offsets_of(n_tokens)
+    for mask, window in (("causal", -1), ("null", -1), ("sliding_window_causal", 3)):
+        got = O.indexer_paged_fp8(q8, q_s, off, table, np.array(lens, dtype=np.int32), k8, k_scale, ps, top_k,
+                                  mask, window)
+        qv, kv = _torch_e4m3(q8), _torch_e4m3(k8)
+        t = 0
+        for b, L in enumerate(lens):
+            n = n_tokens[b]
+            for j in range(n):
+                pos_t = L - n + j
+                vis = []
+                for r in range(L):
+                    if mask != "null" and r > pos_t:
+                        continue
+                    if mask == "sliding_window_causal" and r <= pos_t - window:
+                        continue
+                    pg, sl = int(table[b, r // ps]), r % ps
+                    sc = math.fsum(float(q_s[t, h]) * math.fsum(qv[t, h, d] * kv[pg, sl, d] for d in range(Dk))
+                                   for h in range(NH)) * float(k_scale[pg, sl])
+                    vis.append((-sc, r, pg * ps + sl))
+                vis.sort()
+                want = [v[2] for v in vis[:top_k]] + [-1] * (top_k - min(top_k, len(vis)))
+                assert list(got[t]) == want, (mask, t, list(got[t]), want)
+                t += 1
+
+
 def tiny_prefill(seed=5, new=(3, 4), prefix=(0, 2), H=2, page_size=4):
     rng = np.random.default_rng(seed)
     total = [a + b for a, b in zip(new, prefix)]

@@ -1,0 +1,129 @@
+"""FP8 top-k indexer on the GPU (through the C ABI) against the float64 oracle, and the
+indexer chained into the sparse decode.
+
+Selection is an integer result decided by floating-point scores: the kernel decides on
+float32 scores, the oracle on float64 ones.  Rows whose scores lie within the float32
+error band of the k-th score are equally valid choices at the boundary, so the check is:
+the -1 fill and the number of valid entries exact; every entry a distinct visible row;
+every chosen row scoring at least the k-th score minus the band; the listed order
+non-increasing within the band; and all but a handful of boundary rows identical."""
+import numpy as np
+import pytest
+
+import oracle.mla_oracle as O
+from gpu_util import FP8_TOL, compare, f32_dev, i32_dev, need_gpu, to_f64, u8_dev
+from synth import indexer_config, make_indexer_case
+
+pytestmark = pytest.mark.gpu
+
+
+def run_indexer(m, c, table=None):
+    import torch
+    out = m.indexer_paged_fp8(u8_dev(c.q8), f32_dev(c.q_s), i32_dev(c.input_row_offsets),
+                              i32_dev(c.page_table if table is None else table), i32_dev(c.cache_lens),
+                              u8_dev(c.k8), f32_dev(c.k_scale), c.top_k, mask=c.mask,
+                              local_window_size=c.window)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.int64)
+
+
+def score_band(c, t, pos):
+    """float32 error band of row t's scores: (heads + width) * 2^-24 times the largest
+    sum of absolute products, with a factor 4 of margin."""
+    q = np.abs(O.e4m3_to_f64(c.q8[t])) * c.q_s[t][:, None].astype(np.float64)   # [NH, D]
+    qa = q.sum(axis=0)
+    b = np.searchsorted(c.input_row_offsets.astype(np.int64), t, side="right") - 1
+    ps = c.page_size
+    pages = c.page_table[b][pos // ps].astype(np.int64)
+    k = np.abs(O.e4m3_to_f64(c.k8[pages, pos % ps])) * c.k_scale[pages, pos % ps][:, None]
+    bound = float((k @ qa).max(initial=0.0))
+    NH, D = c.q8.shape[1], c.q8.shape[2]
+    return 4.0 * (NH + D) * 2.0 ** -24 * bound
+
+
+def check_indexer(got, c, what):
+    want, seen = O.indexer_paged_fp8(c.q8, c.q_s, c.input_row_offsets, c.page_table, c.cache_lens, c.k8,
+                                     c.k_scale, c.page_size, c.top_k, c.mask, c.window, return_scores=True)
+    ps = c.page_size
+    differ = 0
+    for t, pos, sc in seen:
+        b = np.searchsorted(c.input_row_offsets.astype(np.int64), t, side="right") - 1
+        k = min(c.top_k, len(pos))
+        row = got[t]
+        assert np.all(row[k:] == -1), f"{what} row {t}: entries past {k} not -1"
+        sel = row[:k]
+        assert np.all(sel >= 0), f"{what} row {t}: fewer than {k} entries"
+        assert len(np.unique(sel)) == k, f"{what} row {t}: repeated rows"
+        # physical row -> logical position through this sequence's page table
+        phys_of_pos = c.page_table[b][pos // ps].astype(np.int64) * ps + pos % ps
+        where = {int(p): i for i, p in enumerate(phys_of_pos)}
+        idx = np.array([where.get(int(r), -1) for r in sel])
+        assert np.all(idx >= 0), f"{what} row {t}: a row that is not visible"
+        if k == 0:
+            continue
+        band = score_band(c, t, pos)
+        kth = np.sort(sc)[::-1][k - 1]
+        chosen = sc[idx]
+        assert chosen.min() >= kth - band, f"{what} row {t}: a row below the k-th score by more than {band}"
+        assert np.all(np.diff(chosen) <= band), f"{what} row {t}: order not descending"
+        differ += int(np.count_nonzero(sel != want[t][:k]))
+    return differ
+
+
+@pytest.mark.parametrize("ps", [16, 64])
+@pytest.mark.parametrize("mask,window", [("causal", -1), ("null", -1), ("sliding_window_causal", 40)])
+def test_indexer_small(ps, mask, window):
+    m = need_gpu()
+    c = make_indexer_case(41, [1, 37, 100, 700, 64, 300], 8, 64, ps, 48, q_per_seq=[1, 2, 1, 3, 1, 2],
+                          mask=mask, window=window, name="idx-small")
+    differ = check_indexer(run_indexer(m, c), c, f"PS={ps} {mask}")
+    print(f"[parity] indexer PS={ps} {mask}: {differ} listed rows differ from the oracle's order", flush=True)
+
+
+def test_indexer_full_size():
+    """The indexer in front of C4: 32 sequences x 16384 rows, 64 heads of 128, top 2048."""
+    m = need_gpu()
+    c = indexer_config()
+    got = run_indexer(m, c)
+    differ = check_indexer(got, c, "X4")
+    total = c.total_q * c.top_k
+    print(f"[parity] indexer X4: {differ} of {total} listed rows differ from the oracle's order", flush=True)
+    assert differ <= total // 100
+
+
+def test_indexer_bad_page_is_flagged():
+    m = need_gpu()
+    c = make_indexer_case(42, [200, 300], 4, 32, 64, 16, name="idx-bad")
+    table = c.page_table.copy()
+    table[1, 2] = 10_000_000
+    m.check_device_errors()
+    got = run_indexer(m, c, table=table)
+    assert m.check_device_errors() & 1
+    pool = c.k8.shape[0] * c.page_size
+    assert np.all((got == -1) | ((got >= 0) & (got < pool)))
+
+
+def test_indexer_feeds_sparse_decode():
+    """Indexer -> sparse decode on the GPU against oracle indexer -> oracle sparse decode."""
+    import torch
+    from synth import make_decode_case
+    m = need_gpu()
+    lens, H, ps, top_k = [1500, 2048, 700, 1999], 32, 64, 256
+    idx_case = make_indexer_case(43, lens, 16, 64, ps, top_k, name="chain-idx")
+    dec = make_decode_case(43, lens, H, ps, fp8=True, name="chain-dec")
+    # the decode cache shares the indexer's page table (same pool geometry)
+    dec.page_table = idx_case.page_table
+    npages = idx_case.k8.shape[0]
+    assert dec.cache8.shape[0] == npages
+    got_idx = m.indexer_paged_fp8(u8_dev(idx_case.q8), f32_dev(idx_case.q_s), i32_dev(idx_case.input_row_offsets),
+                                  i32_dev(idx_case.page_table), i32_dev(idx_case.cache_lens), u8_dev(idx_case.k8),
+                                  f32_dev(idx_case.k_scale), top_k)
+    topk_len = i32_dev(np.full(len(lens), top_k, dtype=np.int32))
+    out = m.decode_paged_sparse(u8_dev(dec.q8), f32_dev(dec.q_scale), i32_dev(dec.input_row_offsets),
+                                u8_dev(dec.cache8), f32_dev(dec.cache_scale), got_idx, topk_len, dec.scale)
+    torch.cuda.synchronize()
+    want_idx = O.indexer_paged_fp8(idx_case.q8, idx_case.q_s, idx_case.input_row_offsets, idx_case.page_table,
+                                   idx_case.cache_lens, idx_case.k8, idx_case.k_scale, ps, top_k)
+    want, _ = O.decode_sparse(dec.q8, dec.q_scale, dec.input_row_offsets, dec.cache8, dec.cache_scale,
+                              want_idx.astype(np.int32), np.full(len(lens), top_k, dtype=np.int32), ps, dec.scale)
+    compare(to_f64(out), want, FP8_TOL, "indexer -> sparse decode")
