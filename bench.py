@@ -53,7 +53,7 @@ MULTI_TOKEN = {"M2": (1, 2), "M4": (1, 4)}
 KERNELS = {"C0": "mla_decode_kernel", "C1": "mla_decode_kernel", "C2": "mla_decode_kernel",
            "C3": "mla_prefill_kernel", "C4": "mla_sparse_kernel", "M2": "mla_decode_kernel",
            "M4": "mla_decode_kernel", "D8": "mla_sparse_kernel",
-           "X4": "mla_indexer_kernel"}
+           "X4": "mla_indexer_score_kernel + mla_indexer_select_kernel"}
 
 
 # sources the dense decode and combine kernels are built from

@@ -645,8 +645,12 @@ mla_status mla_indexer_paged_fp8(const mla_tensor* q, const mla_tensor* q_s,
   bool cap = false;
   if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
   void* ws = nullptr;
-  if ((s = grow_workspace(current_device(), stream, 0, cap, &ws)) != MLA_OK) return s;
+  const int64_t keys_row = page_table->shape[1] * PS;
+  if ((s = grow_workspace(current_device(), stream, (size_t)(T * keys_row) * sizeof(uint64_t), cap, &ws)) != MLA_OK)
+    return s;
   mla::IndexerArgs a{};
+  a.keys = (uint64_t*)((char*)ws + kHeaderBytes);
+  a.keys_row = keys_row;
   a.q = (const uint8_t*)q->data;
   a.q_tok = q->stride[0];
   a.q_head = q->stride[1];

@@ -14,12 +14,15 @@
 //
 // The sum over heads is linear, so a work-group first folds the token's heads into one
 // float32 query row qf[d] = sum_h q_s[t, h] * e4m3(q[t, h, d]) (heads in order), then
-// scores every visible row with one dot product of `depth` terms in float32.  One
-// work-group per query token: the scores of the token's visible rows (at most
-// kIdxMaxKeys) become 64-bit keys in LDS (order-preserving score bits, then the inverted
-// position, so every key is distinct); a radix select (eight 8-bit digits, most
-// significant first, histograms in LDS) finds the top_k-th largest key, the keys at or
-// above it are compacted, a bitonic sort orders those top_k, and they are written out.
+// scores every visible row with one dot product of `depth` terms in float32.  Two
+// kernels:
+//   score:  one work-group per (token, slice of kIdxSlice visible rows) writes each row's
+//           64-bit key (order-preserving score bits, then the inverted position, so every
+//           key is distinct) to a workspace row of the token;
+//   select: one work-group per token loads its keys (at most kIdxMaxKeys) into LDS, a
+//           radix select (eight 8-bit digits, most significant first, histograms in LDS)
+//           finds the top_k-th largest key, the keys at or above it are compacted, a
+//           bitonic sort orders those top_k, and they are written out.
 #include <stdint.h>
 
 #include "mla_device.h"
@@ -64,34 +67,30 @@ __device__ __forceinline__ void bitonic_desc(uint64_t* v, int n) {
   }
 }
 
-__global__ __launch_bounds__(kIdxThreads) void mla_indexer_kernel(const IndexerArgs a) {
-  __shared__ uint64_t keys[kIdxMaxKeys];
-  __shared__ uint64_t top[kIdxMaxTopK];
-  __shared__ float qf[kIdxMaxDepth];
-  __shared__ int hist[256];
-  __shared__ int sel_digit, sel_count;
-  const int t = blockIdx.x, tid = threadIdx.x;
+// The token's sequence (binary search of the offsets) and its visible rows [vlo, vhi).
+struct TokenRows {
+  int b, vlo, vhi;
+};
 
-  // ---- the token's sequence (binary search of the offsets) and its visible rows
+__device__ __forceinline__ TokenRows token_rows(const IndexerArgs& a, int t, bool report) {
   int lo_b = 0, hi_b = a.B;
   while (hi_b - lo_b > 1) {
     const int mid = (lo_b + hi_b) >> 1;
     if ((int)ld_const(a.offsets + mid) <= t) lo_b = mid; else hi_b = mid;
   }
-  const int b = lo_b;
-  const int o0 = (int)ld_const(a.offsets + b), o1 = (int)ld_const(a.offsets + b + 1);
-  int vlo = 0, vhi = 0;
+  TokenRows r{lo_b, 0, 0};
+  const int o0 = (int)ld_const(a.offsets + lo_b), o1 = (int)ld_const(a.offsets + lo_b + 1);
   if (t >= o0 && t < o1) {
-    long long L = ld_const(a.cache_lens + b);
+    long long L = ld_const(a.cache_lens + lo_b);
     const long long Lmax = (long long)a.max_pages * a.PS;
     if (L > Lmax) {
-      if (tid == 0) atomicOr(a.err, kErrCacheLen);
+      if (report) atomicOr(a.err, kErrCacheLen);
       L = Lmax;
     }
     if (L < 0) L = 0;
     const int n = o1 - o0, j = t - o0;
     if (a.mask == kMaskNull) {
-      vhi = (int)L;
+      r.vhi = (int)L;
     } else {
       const long long pos = L - n + j;
       long long h = pos + 1 < L ? pos + 1 : L;
@@ -102,13 +101,22 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_kernel(const IndexerA
         if (l < 0) l = 0;
         if (l > h) l = h;
       }
-      vlo = (int)l;
-      vhi = (int)h;
+      r.vlo = (int)l;
+      r.vhi = (int)h;
     }
-  } else if (tid == 0) {
+  } else if (report) {
     atomicOr(a.err, kErrOffsets);  // offsets that do not cover this row
   }
-  const int nvis = vhi - vlo;  // <= max_pages * PS <= kIdxMaxKeys (checked on the host)
+  return r;  // vhi - vlo <= max_pages * PS <= kIdxMaxKeys (checked on the host)
+}
+
+__global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const IndexerArgs a) {
+  __shared__ float qf[kIdxMaxDepth];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const TokenRows tr = token_rows(a, t, blockIdx.y == 0 && tid == 0);
+  const int vlo = tr.vlo, nvis = tr.vhi - tr.vlo, b = tr.b;
+  const int i0 = blockIdx.y * kIdxSlice, i1 = min(nvis, i0 + kIdxSlice);
+  if (i0 >= i1) return;  // block-uniform, before any barrier
 
   // ---- heads folded into one float32 query row
   for (int d = tid; d < a.depth; d += kIdxThreads) {
@@ -122,10 +130,11 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_kernel(const IndexerA
   }
   __syncthreads();
 
-  // ---- scores of the visible rows as distinct keys
+  // ---- scores of this slice's rows as distinct keys
   const int32_t* prow = a.page_table + (int64_t)b * a.pt_row;
+  uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
   bool bad = false;
-  for (int i = tid; i < nvis; i += kIdxThreads) {
+  for (int i = i0 + tid; i < i1; i += kIdxThreads) {
     uint64_t key;
     {
       const int pos = vlo + i;
@@ -155,9 +164,22 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_kernel(const IndexerA
       // the score's order bits, then the inverted position (equal scores: lower first)
       key = ((uint64_t)order_key(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)pos);
     }
-    keys[i] = key;
+    krow[i] = key;
   }
   if (bad) atomicOr(a.err, kErrPageId);
+}
+
+__global__ __launch_bounds__(kIdxThreads) void mla_indexer_select_kernel(const IndexerArgs a) {
+  __shared__ uint64_t keys[kIdxMaxKeys];
+  __shared__ uint64_t top[kIdxMaxTopK];
+  __shared__ int hist[256];
+  __shared__ int sel_digit, sel_count;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const TokenRows tr = token_rows(a, t, false);
+  const int nvis = tr.vhi - tr.vlo;
+  const int32_t* prow = a.page_table + (int64_t)tr.b * a.pt_row;
+  const uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
+  for (int i = tid; i < nvis; i += kIdxThreads) keys[i] = krow[i];
   if (tid == 0) sel_count = 0;
   __syncthreads();
 
@@ -225,7 +247,10 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_kernel(const IndexerA
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const KernelTimer* timer) {
   hipError_t e;
   if (timer && (e = hipEventRecord(timer->start, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_indexer_kernel, dim3(a.T), dim3(kIdxThreads), 0, stream, a);
+  const int slices = (int)((a.keys_row + kIdxSlice - 1) / kIdxSlice);
+  hipLaunchKernelGGL(mla_indexer_score_kernel, dim3(a.T, slices > 0 ? slices : 1), dim3(kIdxThreads), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_indexer_select_kernel, dim3(a.T), dim3(kIdxThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (timer && (e = hipEventRecord(timer->stop, stream)) != hipSuccess) return e;
   return hipSuccess;

@@ -109,6 +109,7 @@ struct PrefillArgs {
 constexpr int kIdxMaxKeys = 16384;  // visible rows per query token (scores sorted in LDS)
 constexpr int kIdxMaxDepth = 256;   // indexer head width
 constexpr int kIdxMaxTopK = 2048;
+constexpr int kIdxSlice = 1024;     // visible rows a scoring work-group takes
 struct IndexerArgs {
   const uint8_t* q;           // fp8 e4m3 [T, NH, depth]
   int64_t q_tok, q_head;      // element strides
@@ -126,6 +127,8 @@ struct IndexerArgs {
   int32_t B, T, NH, depth, PS, max_pages, mask, window, top_k;
   int32_t* out;               // [T, top_k] physical rows, -1 filled
   int64_t out_row;
+  uint64_t* keys;             // workspace [T, keys_row]: the scored rows' sort keys
+  int64_t keys_row;           // max_pages * PS
   uint32_t* err;
 };
 
