@@ -173,12 +173,15 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_select_kernel(const I
   __shared__ uint64_t keys[kIdxMaxKeys];
   __shared__ uint64_t top[kIdxMaxTopK];
   __shared__ int hist[256];
+  __shared__ int wave_tot[kIdxThreads / 64];
   __shared__ int sel_digit, sel_count;
+  static_assert(kIdxThreads == 256, "one thread per histogram bin");
   const int t = blockIdx.x, tid = threadIdx.x;
   const TokenRows tr = token_rows(a, t, false);
   const int nvis = tr.vhi - tr.vlo;
   const int32_t* prow = a.page_table + (int64_t)tr.b * a.pt_row;
   const uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
+#pragma unroll 4
   for (int i = tid; i < nvis; i += kIdxThreads) keys[i] = krow[i];
   if (tid == 0) sel_count = 0;
   __syncthreads();
@@ -195,27 +198,39 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_select_kernel(const I
       for (int d = tid; d < 256; d += kIdxThreads) hist[d] = 0;
       __syncthreads();
       const uint64_t hi_mask = shift == 56 ? 0 : ~0ull << (shift + 8);
+#pragma unroll 8
       for (int i = tid; i < nvis; i += kIdxThreads) {
         const uint64_t k = keys[i];
         if ((k & hi_mask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 0xFF)], 1);
       }
       __syncthreads();
-      if (tid == 0) {
-        // the digit where the count from the top reaches `need`
-        int acc = 0, d = 255;
-        for (; d > 0; --d) {
-          if (acc + hist[d] >= need) break;
-          acc += hist[d];
+      {
+        // the digit where the count from the top reaches `need`: thread tid takes digit
+        // 255 - tid, so a prefix sum over threads is the count of keys with a digit at or
+        // above it; the one thread where that count first reaches `need` writes the digit
+        const int d = 255 - tid, c = hist[d];
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int up = __shfl_up(incl, off);
+          if ((tid & 63) >= off) incl += up;
         }
-        sel_digit = d;
-        hist[0] = need - acc;  // still needed within digit d (read back below)
+        if ((tid & 63) == 63) wave_tot[tid >> 6] = incl;
+        __syncthreads();
+        for (int w = 0; w < (tid >> 6); ++w) incl += wave_tot[w];
+        if (c > 0 && incl >= need && incl - c < need) {
+          sel_digit = d;
+          sel_count = need - (incl - c);  // still needed within digit d
+        }
       }
       __syncthreads();
       prefix |= (uint64_t)sel_digit << shift;
-      need = hist[0];
+      need = sel_count;
       __syncthreads();
     }
     // keys are distinct: exactly nsel keys are >= the threshold `prefix`
+    if (tid == 0) sel_count = 0;
+    __syncthreads();
     for (int i = tid; i < nvis; i += kIdxThreads) {
       const uint64_t k = keys[i];
       if (k >= prefix) top[atomicAdd(&sel_count, 1)] = k;
