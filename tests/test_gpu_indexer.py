@@ -127,3 +127,37 @@ def test_indexer_feeds_sparse_decode():
     want, _ = O.decode_sparse(dec.q8, dec.q_scale, dec.input_row_offsets, dec.cache8, dec.cache_scale,
                               want_idx.astype(np.int32), np.full(len(lens), top_k, dtype=np.int32), ps, dec.scale)
     compare(to_f64(out), want, FP8_TOL, "indexer -> sparse decode")
+
+
+@pytest.mark.parametrize("num_heads,depth", [(3, 16), (5, 48), (64, 128), (7, 208), (2, 256)])
+def test_indexer_widths(num_heads, depth):
+    """Head widths from 16 to 256 (rows held in registers in 8 or 16 chunks) and head counts
+    that leave some fold groups empty; lengths over several 1024-row slices, top_k below,
+    at and above the visible count."""
+    m = need_gpu()
+    c = make_indexer_case(44 + depth, [1, 1023, 1024, 2500, 4097], num_heads, depth, 64, 1024,
+                          q_per_seq=[1, 2, 1, 3, 1], name=f"idx-w{depth}")
+    differ = check_indexer(run_indexer(m, c), c, f"NH={num_heads} D={depth}")
+    total = c.total_q * c.top_k
+    print(f"[parity] indexer NH={num_heads} D={depth}: {differ} of {total} listed rows differ", flush=True)
+    assert differ <= max(total // 100, 8)
+
+
+@pytest.mark.parametrize("top_k", [1, 700, 2048])
+def test_indexer_ties_exact(top_k):
+    """Cache rows drawn from three patterns with one shared scale: scores tie exactly in
+    float32 and in float64, so the order within a tie is decided by position alone (lower
+    first) and the result equals the oracle's entry for entry.  Groups of thousands of equal
+    scores keep the radix bin of the threshold large through the score digits."""
+    m = need_gpu()
+    c = make_indexer_case(45, [5000, 16384, 3001], 4, 64, 64, top_k, q_per_seq=[1, 1, 2], name="idx-ties")
+    rng = np.random.default_rng(4545)
+    pats = c.k8[0, :3].copy()
+    c.k8 = pats[rng.integers(0, 3, size=c.k8.shape[:2])]
+    c.k_scale = np.full_like(c.k_scale, 0.0078125)
+    got = run_indexer(m, c)
+    want = O.indexer_paged_fp8(c.q8, c.q_s, c.input_row_offsets, c.page_table, c.cache_lens, c.k8,
+                               c.k_scale, c.page_size, c.top_k, c.mask, c.window)
+    assert np.array_equal(got, want.astype(np.int64)), \
+        f"top_k={top_k}: {int(np.count_nonzero(got != want))} entries differ from the oracle"
+    print(f"[parity] indexer ties top_k={top_k}: exact", flush=True)
