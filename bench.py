@@ -229,6 +229,45 @@ def setup(workload, copies, num_partitions, dev):
     raise SystemExit(f"unknown workload {workload}")
 
 
+def graph_workspace_bytes(m, wl, case, num_partitions):
+    """Workspace a captured step needs: reserved on the capture stream before capturing."""
+    if wl == "X4":
+        return case.total_q * case.page_table.shape[1] * case.page_size * 8 + (1 << 20)
+    if wl == "C3":
+        return 1 << 20
+    heads = case.num_heads if hasattr(case, "num_heads") else int(case.q8.shape[1])
+    return m.decode_workspace_bytes(case.total_q, heads, num_partitions)
+
+
+def graph_step_ms(m, torch, step, copies, warmup, steps, ws_bytes):
+    """The same steps replayed from HIP graphs, one per rotated input copy, captured on a
+    side stream whose workspace is reserved first; milliseconds per replayed step."""
+    s = torch.cuda.Stream()
+    m.reserve_workspace(ws_bytes, stream=s)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(copies):
+            step(i)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % copies].replay()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(steps):
+        graphs[i % copies].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +277,7 @@ def main():
     ap.add_argument("--workload", default="C1", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--num-partitions", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay context figure")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to calibrate HBM byte counters)")
     args = ap.parse_args()
@@ -308,6 +348,12 @@ def main():
     m.profile_enable(False)
     k_avg_ms = kms / max(1, launches)
 
+    # ---- context: the same steps replayed from HIP graphs (no host work per step)
+    graph_ms = None
+    if not args.no_graph:
+        graph_ms = graph_step_ms(m, torch, step, max(1, args.copies), args.warmup, args.steps,
+                                 graph_workspace_bytes(m, wl, case, args.num_partitions))
+
     gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     tflops = alg_flops / (ms_step * 1e-3) / 1e12
     # the roofline that bounds the kernel: bf16 MFMA when its arithmetic intensity is past
@@ -366,6 +412,9 @@ def main():
         "algorithmic_flops_per_step": int(alg_flops),
         "tflops": round(tflops, 2),
         "warm_cache_value": round((alg_flops / 1e12 if prefill else alg_bytes / 1e9) / (warm_ms * 1e-3), 2),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "graph_value": None if graph_ms is None else
+        round((alg_flops / 1e12 if prefill else alg_bytes / 1e9) / (graph_ms * 1e-3), 2),
         "wall_ms_timed_region": round(wall_ms, 3),
         "roofline": roof,
         "cpu_baseline": None,
