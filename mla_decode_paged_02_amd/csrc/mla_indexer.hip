@@ -24,8 +24,9 @@
 //           first, histograms in LDS) finds the top_k-th largest key.  Once the bin that
 //           holds it has at most kIdxCand keys, one pass moves the keys above that bin to
 //           the output list and the bin's keys to a candidate list, and the remaining
-//           digits scan the candidates only.  A bitonic sort orders the top_k, and they are
-//           written out.
+//           digits scan the candidates only.  A bitonic sort (in registers and lane
+//           shuffles up to distance 64, LDS beyond) orders the top_k, and they are written
+//           out.
 #include <stdint.h>
 
 #include "mla_device.h"
@@ -53,22 +54,69 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Bitonic sort of n (a power of two) keys in LDS into descending order; each thread
-// takes compare-exchange pairs (i, i + jdist), i having bit jdist clear.
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int lane_mask) {
+  const uint32_t lo = __shfl_xor((unsigned)(v & 0xFFFFFFFFu), lane_mask);
+  const uint32_t hi = __shfl_xor((unsigned)(v >> 32), lane_mask);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort of n (a power of two, n <= 2 * kIdxSelThreads) keys in LDS into descending
+// order.  Thread tid holds elements 2 tid and 2 tid + 1 in registers: compare-exchange at
+// distance 1 stays in the thread, and distances 2 .. 64 pair lanes 1 .. 32 apart within
+// the wave (the partner of element e is e ^ jdist, in thread tid ^ jdist / 2), so neither
+// needs a barrier.  Distances of 128 and more go through LDS, one barrier per stage.
 __device__ __forceinline__ void bitonic_desc(uint64_t* v, int n) {
+  static_assert(kIdxMaxTopK <= 2 * kIdxSelThreads, "two keys per thread");
+  const int tid = threadIdx.x, e0 = 2 * tid;
+  uint64_t x[2] = {0, 0};
+  if (e0 < n) {
+    x[0] = v[e0];
+    x[1] = v[e0 + 1];
+  }
   for (int k = 2; k <= n; k <<= 1) {
-    for (int jdist = k >> 1; jdist > 0; jdist >>= 1) {
-      for (int j = threadIdx.x; j < (n >> 1); j += kIdxSelThreads) {
-        const int i = ((j & ~(jdist - 1)) << 1) | (j & (jdist - 1)), p = i + jdist;
-        const uint64_t x = v[i], y = v[p];
-        if ((i & k) == 0 ? x < y : x > y) {
-          v[i] = y;
-          v[p] = x;
-        }
+    if ((k >> 1) >= 128) {
+      if (e0 < n) {
+        v[e0] = x[0];
+        v[e0 + 1] = x[1];
       }
       __syncthreads();
+      for (int jdist = k >> 1; jdist >= 128; jdist >>= 1) {
+        for (int j = tid; j < (n >> 1); j += kIdxSelThreads) {
+          const int i = ((j & ~(jdist - 1)) << 1) | (j & (jdist - 1)), p = i + jdist;
+          const uint64_t lo = v[i], hi = v[p];
+          if ((i & k) == 0 ? lo < hi : lo > hi) {
+            v[i] = hi;
+            v[p] = lo;
+          }
+        }
+        __syncthreads();
+      }
+      if (e0 < n) {
+        x[0] = v[e0];
+        x[1] = v[e0 + 1];
+      }
+    }
+    for (int jdist = min(k >> 1, 64); jdist >= 2; jdist >>= 1) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = e0 + u;
+        const uint64_t y = shfl_xor64(x[u], jdist >> 1);
+        // the lower element of a descending pair keeps the larger key
+        const bool keep_max = ((e & jdist) == 0) == ((e & k) == 0);
+        x[u] = keep_max ? (x[u] > y ? x[u] : y) : (x[u] < y ? x[u] : y);
+      }
+    }
+    if ((e0 & k) == 0 ? x[0] < x[1] : x[0] > x[1]) {
+      const uint64_t tmp = x[0];
+      x[0] = x[1];
+      x[1] = tmp;
     }
   }
+  if (e0 < n) {
+    v[e0] = x[0];
+    v[e0 + 1] = x[1];
+  }
+  __syncthreads();
 }
 
 // The token's sequence (binary search of the offsets) and its visible rows [vlo, vhi).
@@ -231,8 +279,11 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   const int nvis = tr.vhi - tr.vlo;
   const int32_t* prow = a.page_table + (int64_t)tr.b * a.pt_row;
   const uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
-#pragma unroll 4
-  for (int i = tid; i < nvis; i += kIdxSelThreads) keys[i] = krow[i];
+#pragma unroll
+  for (int r = 0; r < kIdxMaxKeys / kIdxSelThreads; ++r) {
+    const int i = tid + r * kIdxSelThreads;
+    if (i < nvis) keys[i] = krow[i];
+  }
   if (tid == 0) {
     n_top = 0;
     n_cand = 0;
