@@ -54,10 +54,34 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int lane_mask) {
-  const uint32_t lo = __shfl_xor((unsigned)(v & 0xFFFFFFFFu), lane_mask);
-  const uint32_t hi = __shfl_xor((unsigned)(v >> 32), lane_mask);
-  return ((uint64_t)hi << 32) | lo;
+// The value of lane (lane ^ M): DPP quad permutes for M = 1, 2, a bitmask-mode swizzle
+// (lane ^ M within 32 lanes) for M = 4 .. 16, a bpermute for M = 32.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane distance");
+  if constexpr (M == 1)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  else if constexpr (M == 2)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  else if constexpr (M < 32)
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));  // and 0x1F, xor M
+  else
+    return (uint32_t)__shfl_xor((unsigned)v, M);
+}
+
+// One compare-exchange stage at element distance J (2 .. 64) on the thread's two keys
+// (elements e0 and e0 + 1), partners J / 2 lanes away.
+template <int J>
+__device__ __forceinline__ void lane_stage(uint64_t (&x)[2], int e0, int k) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = e0 + u;
+    const uint32_t lo = lane_xor<J / 2>((uint32_t)x[u]), hi = lane_xor<J / 2>((uint32_t)(x[u] >> 32));
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    // the lower element of a descending pair keeps the larger key
+    const bool keep_max = ((e & J) == 0) == ((e & k) == 0);
+    x[u] = keep_max ? (x[u] > y ? x[u] : y) : (x[u] < y ? x[u] : y);
+  }
 }
 
 // Bitonic sort of n (a power of two, n <= 2 * kIdxSelThreads) keys in LDS into descending
@@ -96,15 +120,14 @@ __device__ __forceinline__ void bitonic_desc(uint64_t* v, int n) {
         x[1] = v[e0 + 1];
       }
     }
-    for (int jdist = min(k >> 1, 64); jdist >= 2; jdist >>= 1) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = e0 + u;
-        const uint64_t y = shfl_xor64(x[u], jdist >> 1);
-        // the lower element of a descending pair keeps the larger key
-        const bool keep_max = ((e & jdist) == 0) == ((e & k) == 0);
-        x[u] = keep_max ? (x[u] > y ? x[u] : y) : (x[u] < y ? x[u] : y);
-      }
+    switch (min(k >> 1, 64)) {  // distances min(k / 2, 64) down to 2
+      case 64: lane_stage<64>(x, e0, k); [[fallthrough]];
+      case 32: lane_stage<32>(x, e0, k); [[fallthrough]];
+      case 16: lane_stage<16>(x, e0, k); [[fallthrough]];
+      case 8: lane_stage<8>(x, e0, k); [[fallthrough]];
+      case 4: lane_stage<4>(x, e0, k); [[fallthrough]];
+      case 2: lane_stage<2>(x, e0, k); [[fallthrough]];
+      default: break;
     }
     if ((e0 & k) == 0 ? x[0] < x[1] : x[0] > x[1]) {
       const uint64_t tmp = x[0];
