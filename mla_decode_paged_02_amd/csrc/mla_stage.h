@@ -434,7 +434,7 @@ __device__ __forceinline__ void stage_epilogue2(WaveAcc2& acc, int lane, int h0,
   for (int hl = 0; hl < 32; ++hl) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 w = *(const MLA_LDS u32x4*)(stage + hl * 1024 + ((16 * lane) ^ ((hl & 15) << 4)));
-    *(u32x4*)(base + hl * hstride + 8 * lane) = w;
+    __builtin_nontemporal_store(w, (u32x4*)(base + hl * hstride + 8 * lane));
   }
 }
 
