@@ -133,7 +133,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
   // load jj of this wave for a fast stage (no-op past the wave's share)
   auto fast_load = [&](const uint8_t* base, MLA_LDS uint8_t* dst, int jj) {
     const int J = jj * NW + wave;
-    if (kDmaPerStage % NW == 0 || J < kDmaPerStage) dma16_base(base, dma_off[jj], dst + J * 1024);
+    if (kDmaPerStage % NW == 0 || J < kDmaPerStage) dma16_base_nt(base, dma_off[jj], dst + J * 1024);
   };
   // general case: per-lane keys, pages and bounds (segment edges, invalid pages, page
   // sizes that are not a multiple of the stage)
@@ -172,7 +172,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
         else
           bad_page = true;
       }
-      dma16(src, dst + J * 1024);
+      dma16_nt(src, dst + J * 1024);
     }
   };
   auto issue = [&](int st, int bi, int pa) {

@@ -126,6 +126,21 @@ __device__ __forceinline__ void dma16_base(const void* base, uint32_t off, MLA_L
                : "s"(lds), "v"(off), "s"(base)
                : "memory", "m0");
 }
+// Streaming forms of dma16 / dma16_base for data read once (non-temporal cache policy).
+__device__ __forceinline__ void dma16_nt(const void* src, MLA_LDS void* dst_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_base_nt(const void* base, uint32_t off, MLA_LDS void* dst_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
