@@ -193,3 +193,98 @@ def test_prefill_validation(over, status):
     st, msg = call_prefill(prefill_args(**over))
     assert st == status, (st, msg)
     assert msg
+
+
+def fp8_decode_args(**over):
+    T, H, B, PS, NP = 4, 16, 2, 64, 10
+    a = dict(q=_t(FAKE, 1, (T, H, 576)), qs=_t(FAKE, 2, (T,)), off=_t(FAKE, 4, (B + 1,)),
+             pt=_t(FAKE, 3, (B, 8)), lens=_t(FAKE, 3, (B,)), cache=_t(FAKE, 1, (NP, PS, 576)),
+             cs=_t(FAKE, 2, (NP, PS)), out=_t(FAKE, 0, (T, H, 512)), scale=0.07, mask=1, window=-1,
+             parts=0)
+    a.update(over)
+    return a
+
+
+def call_fp8_decode(a):
+    lib = m.library()
+    ref = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    st = lib.mla_decode_paged_fp8(ref(a["q"]), ref(a["qs"]), ref(a["off"]), ref(a["pt"]), ref(a["lens"]),
+                                  ref(a["cache"]), ref(a["cs"]), a["scale"], a["mask"], a["window"],
+                                  a["parts"], ref(a["out"]), None)
+    return st, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1),
+    (dict(q=_t(FAKE, 0, (4, 16, 576))), 3),                 # bf16 q
+    (dict(q=_t(FAKE, 1, (4, 16, 512))), 2),                 # head width
+    (dict(qs=_t(FAKE, 2, (5,))), 2),                        # one scale per q row
+    (dict(off=_t(FAKE, 4, (1,))), 2),                       # no sequence
+    (dict(pt=_t(FAKE, 3, (3, 8))), 2),                      # page-table rows != batch
+    (dict(cache=_t(FAKE, 0, (10, 64, 576))), 3),            # bf16 cache
+    (dict(cache=_t(FAKE, 1, (10, 64, 576), stride=(64 * 608, 608, 1))), 2),  # rows not contiguous
+    (dict(cs=_t(FAKE, 2, (10, 32))), 2),                    # scale shape
+    (dict(out=_t(FAKE, 0, (4, 16, 576))), 2),               # out width
+    (dict(q=_t(FAKE, 1, (4, 48, 576)), out=_t(FAKE, 0, (4, 48, 512))), 5),  # head count
+    (dict(mask=9), 8),
+    (dict(mask=2, window=0), 8),
+    (dict(scale=float("nan")), 8),
+    (dict(parts=5000), 8),
+])
+def test_fp8_decode_validation(over, status):
+    st, msg = call_fp8_decode(fp8_decode_args(**over))
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_fp8_decode_empty_batch_is_ok_without_gpu():
+    st, msg = call_fp8_decode(fp8_decode_args(q=_t(FAKE, 1, (0, 16, 576)), qs=_t(FAKE, 2, (0,)),
+                                              out=_t(FAKE, 0, (0, 16, 512))))
+    assert st == 0, msg
+
+
+def indexer_args(**over):
+    T, NH, D, B, PS, NP, K = 4, 8, 128, 2, 64, 10, 32
+    a = dict(q=_t(FAKE, 1, (T, NH, D)), qs=_t(FAKE, 2, (T, NH)), off=_t(FAKE, 4, (B + 1,)),
+             pt=_t(FAKE, 3, (B, 8)), lens=_t(FAKE, 3, (B,)), k=_t(FAKE, 1, (NP, PS, D)),
+             ks=_t(FAKE, 2, (NP, PS)), mask=1, window=-1, out=_t(FAKE, 3, (T, K)))
+    a.update(over)
+    return a
+
+
+def call_indexer(a):
+    lib = m.library()
+    ref = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    st = lib.mla_indexer_paged_fp8(ref(a["q"]), ref(a["qs"]), ref(a["off"]), ref(a["pt"]), ref(a["lens"]),
+                                   ref(a["k"]), ref(a["ks"]), a["mask"], a["window"], ref(a["out"]), None)
+    return st, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1),
+    (dict(q=_t(FAKE, 0, (4, 8, 128))), 3),                  # bf16 q
+    (dict(q=_t(FAKE, 1, (4, 8, 100)), k=_t(FAKE, 1, (10, 64, 100))), 5),   # width not a multiple of 16
+    (dict(q=_t(FAKE, 1, (4, 8, 272)), k=_t(FAKE, 1, (10, 64, 272))), 5),   # width above 256
+    (dict(qs=_t(FAKE, 2, (4, 7))), 2),                      # one scale per (token, head)
+    (dict(off=_t(FAKE, 4, (1,))), 2),
+    (dict(pt=_t(FAKE, 3, (3, 8))), 2),
+    (dict(lens=_t(FAKE, 3, (3,))), 2),
+    (dict(k=_t(FAKE, 1, (10, 64, 64))), 2),                 # cache width != q width
+    (dict(k=_t(FAKE, 1, (10, 64, 128), stride=(64 * 128 + 8, 128, 1))), 4),  # page stride not 16-aligned
+    (dict(ks=_t(FAKE, 2, (10, 32))), 2),
+    (dict(out=_t(FAKE, 3, (4, 4096))), 5),                  # top_k above 2048
+    (dict(out=_t(FAKE, 3, (3, 32))), 2),                    # out rows != tokens
+    (dict(pt=_t(FAKE, 3, (2, 300))), 5),                    # more than 16384 rows per sequence
+    (dict(mask=5), 8),
+    (dict(mask=2, window=0), 8),
+])
+def test_indexer_validation(over, status):
+    st, msg = call_indexer(indexer_args(**over))
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_indexer_empty_batch_is_ok_without_gpu():
+    st, msg = call_indexer(indexer_args(q=_t(FAKE, 1, (0, 8, 128)), qs=_t(FAKE, 2, (0, 8)),
+                                        out=_t(FAKE, 3, (0, 32))))
+    assert st == 0, msg
