@@ -173,6 +173,22 @@ def test_many_rows_stream_split(nrows):
     compare(to_f64(decode_on_gpu(m, case)), oracle_of(case), BF16_TOL, f"{nrows} rows")
 
 
+@pytest.mark.parametrize("T,H,ps,max_len", [(8192, 16, 16, 48), (2048, 128, 64, 300)])
+def test_large_batch_sampled_rows(T, H, ps, max_len):
+    """Thousands of one-token sequences (lengths U[1, max_len]): far more rows than the
+    planning table and the work-groups, so each work-group streams many rows.  The whole
+    output is finite; the first, the last and 96 random rows are checked against the
+    oracle row by row."""
+    m = need_gpu()
+    rng = np.random.default_rng(T + H)
+    lens = [int(x) for x in rng.integers(1, max_len + 1, T)]
+    case = make_decode_case(300 + H, lens, H, ps, name="large-batch")
+    got = to_f64(decode_on_gpu(m, case))
+    assert np.all(np.isfinite(got))
+    rows = sorted(set([0, T - 1] + [int(r) for r in rng.choice(T, 96, replace=False)]))
+    compare(got[rows], oracle_of(case, rows=rows), BF16_TOL, f"{T} rows x {H} heads (sampled)")
+
+
 def test_row_parts_mixed_rows():
     """Row parts with empty, one-tile and long rows side by side."""
     m = need_gpu()
