@@ -161,3 +161,17 @@ def test_indexer_ties_exact(top_k):
     assert np.array_equal(got, want.astype(np.int64)), \
         f"top_k={top_k}: {int(np.count_nonzero(got != want))} entries differ from the oracle"
     print(f"[parity] indexer ties top_k={top_k}: exact", flush=True)
+
+
+@pytest.mark.parametrize("mask,window", [("causal", -1), ("sliding_window_causal", 1500)])
+def test_indexer_many_tokens_per_sequence(mask, window):
+    """128 query tokens per sequence (512 in all): each token sees its own causal or
+    sliding range, one selection work-group per token; the 128-row sequence has tokens that
+    see fewer rows than top_k."""
+    m = need_gpu()
+    c = make_indexer_case(46, [4000, 2500, 128, 3333], 8, 64, 64, 512, q_per_seq=128, mask=mask,
+                          window=window, name="idx-many")
+    differ = check_indexer(run_indexer(m, c), c, f"many tokens {mask}")
+    total = c.total_q * c.top_k
+    print(f"[parity] indexer 512 tokens {mask}: {differ} of {total} listed rows differ", flush=True)
+    assert differ <= max(total // 100, 8)
