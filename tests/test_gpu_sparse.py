@@ -58,6 +58,25 @@ def test_sparse_small(H, ps):
         compare(to_f64(sparse_on_gpu(m, case, num_partitions=P)), want, FP8_TOL, f"H={H} PS={ps} P={P}")
 
 
+@pytest.mark.parametrize("B,H,rows_per_seq,n_index", [(1024, 16, 256, 128), (600, 128, 128, 64)])
+def test_many_rows_sampled(B, H, rows_per_seq, n_index):
+    """Hundreds to a thousand one-token rows with lists of 0 .. n_index entries: more rows
+    than work-groups.  The whole output is finite and rows with an empty list are zero; the
+    first, the last and 96 random rows are checked against the oracle row by row, with the
+    library's split and with a fixed split of 2."""
+    m = need_gpu()
+    case = make_sparse_case(500 + H, B, H, rows_per_seq, 64, (0, n_index), n_index, name="sp-many")
+    rng = np.random.default_rng(B)
+    rows = sorted(set([0, B - 1] + [int(r) for r in rng.choice(B, 96, replace=False)]))
+    want = oracle_of(case, rows=rows)
+    empty = np.flatnonzero(case.topk_lengths == 0)
+    for P in (0, 2):
+        got = to_f64(sparse_on_gpu(m, case, num_partitions=P))
+        assert np.all(np.isfinite(got))
+        assert np.all(got[empty] == 0.0)
+        compare(got[rows], want, FP8_TOL, f"{B} rows x {H} heads P={P} (sampled)")
+
+
 def test_index_list_semantics():
     """Duplicates count twice, negative entries are skipped, entries past topk are never
     read (even when they name rows outside the pool), topk is clamped to the list width,
