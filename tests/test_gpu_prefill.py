@@ -62,6 +62,18 @@ def test_prefill_small(H, ps, mask):
     compare(to_f64(prefill_on_gpu(m, case)), oracle_of(case), BF16_TOL, f"H={H} PS={ps} {mask}")
 
 
+@pytest.mark.parametrize("mask", ["causal", "null"])
+def test_prefill_many_short_sequences(mask):
+    """300 sequences of 0 .. 40 new tokens after 0 .. 199 cached ones: hundreds of small
+    query blocks launched longest-first, many sequences without new tokens."""
+    m = need_gpu()
+    rng = np.random.default_rng(65)
+    new = [int(x) for x in rng.integers(0, 41, 300)]
+    prefix = [int(x) for x in rng.integers(0, 200, 300)]
+    case = make_prefill_case(65, new, prefix, 16, 16, mask=mask, name="pf-many")
+    compare(to_f64(prefill_on_gpu(m, case)), oracle_of(case), BF16_TOL, f"300 short sequences {mask}")
+
+
 def test_keys_of_new_tokens_only():
     """k / v hold only the new tokens, cache_offsets place them after the cached prefix."""
     m = need_gpu()
