@@ -308,6 +308,12 @@ def indexer_scores(q8_t, q_s_t, k8_rows, k_scale_rows):
     return s
 
 
+def rank_order(scores, positions):
+    """Indices that sort the scored rows for the top-k: descending score, equal scores by
+    ascending logical position (the reading of [IDX] Args output_indices used here)."""
+    return np.lexsort((np.asarray(positions), -np.asarray(scores, dtype=np.float64)))
+
+
 def indexer_paged_fp8(q8, q_s, input_row_offsets, page_table, cache_lens, k8, k_scale, page_size,
                       top_k, mask="causal", window=-1, return_scores=False):
     """FP8 top-k indexer over a paged cache ([IDX] summary and Args output_indices, q, q_s,
@@ -331,8 +337,7 @@ def indexer_paged_fp8(q8, q_s, input_row_offsets, page_table, cache_lens, k8, k_
             slots = pos % page_size
             ks = None if k_scale is None else k_scale[pages, slots]
             sc = indexer_scores(q8[t], q_s[t], k8[pages, slots], ks) if len(pos) else np.zeros(0)
-            order = np.lexsort((pos, -sc))                  # score descending, then position
-            take = order[:top_k]
+            take = rank_order(sc, pos)[:top_k]
             out[t, :len(take)] = pages[take] * page_size + slots[take]
             seen.append((t, pos, sc))
     return (out, seen) if return_scores else out

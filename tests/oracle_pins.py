@@ -238,6 +238,98 @@ def pin_p1_indexer():
                 t += 1
 
 
+def _paged_rows(k_rows, ps, rng, spare=1):
+    """Scatter the logical rows of each sequence over a shuffled pool of pages of ps rows."""
+    npages = [-(-len(k) // ps) for k in k_rows]
+    total = sum(npages) + spare
+    perm = rng.permutation(total)
+    pool = np.zeros((total, ps, k_rows[0].shape[1]), dtype=np.uint8)
+    table = np.full((len(k_rows), max(npages)), -1, dtype=np.int32)
+    cur = 0
+    for b, rows in enumerate(k_rows):
+        for j in range(npages[b]):
+            table[b, j] = perm[cur]
+            chunk = rows[j * ps:(j + 1) * ps]
+            pool[perm[cur], :len(chunk)] = chunk
+            cur += 1
+    return pool, table
+
+
+def pin_p1_indexer_head_weights():
+    """The per-head weights q_s decide the order ([IDX] Args q_s): codes of moderate size
+    (|value| in [0.5, 2)) and q_s log-uniform over 1e-2..1e2, so that the unweighted head
+    sum ranks the rows differently (checked here); the oracle must match scalar brute
+    force, loops over heads and columns with math.fsum on torch's e4m3 widening."""
+    rng = np.random.default_rng(23)
+    moderate = np.array([c for c in range(256) if ((c >> 3) & 0xF) in (6, 7)], dtype=np.uint8)
+    NH, Dk, ps, top_k = 4, 16, 4, 5
+    lens, n_tokens = (23, 14), (1, 2)
+    k_rows = [rng.choice(moderate, size=(L, Dk)).astype(np.uint8) for L in lens]
+    k8, table = _paged_rows(k_rows, ps, rng)
+    k_scale = rng.uniform(0.5, 2.0, size=k8.shape[:2]).astype(np.float32)
+    T = sum(n_tokens)
+    q8 = rng.choice(moderate, size=(T, NH, Dk)).astype(np.uint8)
+    q_s = (10.0 ** rng.uniform(-2.0, 2.0, size=(T, NH))).astype(np.float32)
+    off = offsets_of(n_tokens)
+    qv, kv = _torch_e4m3(q8), _torch_e4m3(k8)
+    got = O.indexer_paged_fp8(q8, q_s, off, table, np.array(lens, dtype=np.int32), k8, k_scale, ps, top_k,
+                              "causal", -1)
+    weights_matter = False
+    t = 0
+    for b, L in enumerate(lens):
+        n = n_tokens[b]
+        for j in range(n):
+            pos_t = L - n + j
+            weighted, unweighted = [], []
+            for r in range(pos_t + 1):
+                pg, sl = int(table[b, r // ps]), r % ps
+                dots = [math.fsum(qv[t, h, d] * kv[pg, sl, d] for d in range(Dk)) for h in range(NH)]
+                ks = float(k_scale[pg, sl])
+                weighted.append((-math.fsum(float(q_s[t, h]) * dots[h] for h in range(NH)) * ks, r, pg * ps + sl))
+                unweighted.append((-math.fsum(dots) * ks, r, pg * ps + sl))
+            weighted.sort()
+            unweighted.sort()
+            want = [v[2] for v in weighted[:top_k]]
+            weights_matter |= want != [v[2] for v in unweighted[:top_k]]
+            assert list(got[t]) == want, (t, list(got[t]), want)
+            t += 1
+    assert weights_matter, "the inputs must make the head weights change the top-k"
+
+
+def pin_indexer_exact_ties():
+    """Equal scores rank by ascending logical position (the reading of [IDX] Args
+    output_indices).  Sequence 0: every row identical, so the top-k are the first k
+    visible positions.  Sequence 1: three rows of a high-scoring pattern at positions
+    {2, 5, 9}, the rest of one low-scoring pattern; top 5 = those three, then positions 0
+    and 1.  Expectations are written out by construction, through the page table."""
+    rng = np.random.default_rng(24)
+    Dk, ps, top_k = 16, 4, 5
+    one = 0x38  # e4m3 code of 1.0
+    hi_row = np.full(Dk, one, dtype=np.uint8)
+    lo_row = np.zeros(Dk, dtype=np.uint8)
+    lo_row[0] = one
+    seq0 = np.tile(hi_row, (13, 1))
+    seq1 = np.tile(lo_row, (11, 1))
+    seq1[[2, 5, 9]] = hi_row
+    k8, table = _paged_rows([seq0, seq1], ps, rng)
+    k_scale = np.ones(k8.shape[:2], dtype=np.float32)
+    q8 = np.full((3, 2, Dk), one, dtype=np.uint8)
+    q_s = np.array([[1.0, 0.5]] * 3, dtype=np.float32)
+    off = offsets_of((2, 1))
+    lens = np.array([13, 11], dtype=np.int32)
+
+    def phys(b, positions):
+        return [int(table[b, p // ps]) * ps + p % ps for p in positions]
+
+    got = O.indexer_paged_fp8(q8, q_s, off, table, lens, k8, k_scale, ps, top_k, "causal", -1)
+    assert list(got[0]) == phys(0, [0, 1, 2, 3, 4])      # token at position 11
+    assert list(got[1]) == phys(0, [0, 1, 2, 3, 4])      # token at position 12
+    assert list(got[2]) == phys(1, [2, 5, 9, 0, 1])
+    got = O.indexer_paged_fp8(q8, q_s, off, table, lens, k8, k_scale, ps, top_k, "sliding_window_causal", 4)
+    assert list(got[0]) == phys(0, [8, 9, 10, 11]) + [-1]
+    assert list(got[2]) == phys(1, [9, 7, 8, 10]) + [-1]
+
+
 def tiny_prefill(seed=5, new=(3, 4), prefix=(0, 2), H=2, page_size=4):
     rng = np.random.default_rng(seed)
     total = [a + b for a, b in zip(new, prefix)]

@@ -13,6 +13,7 @@ _attend = O.attend
 _visible = O.visible_range
 _rows = O.logical_rows
 _sparse_rows = O.sparse_rows
+_rank_order = O.rank_order
 
 
 def m_scale_dropped(mp):
@@ -133,10 +134,24 @@ def m_bf16_low_half(mp):
     mp.setattr(O, "bf16_to_f64", dec)
 
 
+def m_indexer_unweighted_heads(mp):
+    """The head scores summed without their q_s weights."""
+    def scores(q8_t, q_s_t, k8_rows, k_scale_rows):
+        s = (O.e4m3_to_f64(k8_rows) @ O.e4m3_to_f64(q8_t).T).sum(axis=1)
+        return s if k_scale_rows is None else s * np.asarray(k_scale_rows, dtype=np.float64)
+    mp.setattr(O, "indexer_scores", scores)
+
+
+def m_indexer_ties_reversed(mp):
+    """Equal scores ranked by descending position."""
+    mp.setattr(O, "rank_order", lambda sc, pos: np.lexsort((-np.asarray(pos), -np.asarray(sc, dtype=np.float64))))
+
+
 MUTANTS = [m_scale_dropped, m_values_shifted, m_causal_off_by_one, m_token_order_reversed,
            m_page_slot_swapped, m_combine_unweighted, m_no_max_subtraction, m_softmax_over_heads,
            m_lse_without_max, m_e4m3_bias8, m_sparse_ignores_topk, m_sparse_keeps_pads,
-           m_prefill_rope_at_query, m_bf16_low_half]
+           m_prefill_rope_at_query, m_bf16_low_half,
+           m_indexer_unweighted_heads, m_indexer_ties_reversed]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
