@@ -50,10 +50,19 @@ Readings of points the pages leave open (each also listed in the design notes):
     of sequence b is k/v row buffer_row_offsets[b] + i at cache position
     cache_offsets[b] + i; query j is at cache_lens[b] - n_b + j.
 
+  * Attention sink and second KV stream ([DEC] Args attn_sink_ptr, extra_k,
+    extra_d_indices, extra_indices_stride, extra_topk_lengths, extra_scales_ptr; the
+    page names them without a formula): the sink is one logit per head, shared by the
+    whole batch and not multiplied by scale, that joins the softmax denominator and
+    carries no value; the extra stream is a second index list per query row over a
+    second fp8 cache with its own row scales, and the row attends to the rows of both
+    lists under one softmax.
+
 Pins: every function here is checked in tests/test_oracle_pins.py against brute
 force, closed forms and invariants.  Parity unpinned: the sliding-window width
 convention, the empty-set convention, duplicate sparse indices (only their listed
-multiplicity is defined by the reading above).
+multiplicity is defined by the reading above), and the attention-sink and
+extra-stream semantics (the pins check the reading above, which no page fixes).
 """
 from __future__ import annotations
 
@@ -105,32 +114,39 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 
 def attend(q_rows: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float,
-           visible: np.ndarray | None = None, return_probs: bool = False):
+           visible: np.ndarray | None = None, return_probs: bool = False,
+           sink: np.ndarray | None = None):
     """softmax(scale * q k^T) v for every query row (a head, or a query of one head).
 
     q_rows [R, Dk], keys [N, Dk], values [N, Dv] (float64); ``visible`` [R, N] marks
     the keys each row may see (all when None).  Returns out [R, Dv] and lse [R] (the
     natural log of sum_r exp(s_r) over visible keys), plus the probabilities [R, N] on
     request.  A row that sees no key gets out = 0 and lse = -inf.
+
+    ``sink`` [R] (optional): one more logit per row, already in logit units (not scaled),
+    that joins the softmax denominator and carries no value ([DEC] Args attn_sink_ptr;
+    the reading used here): out = sum_r e^{s_r} v_r / (e^{sink} + sum_r e^{s_r}), and
+    lse includes e^{sink}.  A row with no visible key then gets out = 0, lse = sink.
     """
     R = q_rows.shape[0]
     N = keys.shape[0]
     out = np.zeros((R, values.shape[1]))
     lse = np.full(R, -np.inf)
     probs = np.zeros((R, N))
-    if N > 0:
-        s = float(scale) * (q_rows @ keys.T)
-        if visible is not None:
-            s = np.where(visible, s, -np.inf)
-        live = np.any(np.isfinite(s), axis=1) if visible is not None else np.ones(R, dtype=bool)
-        if live.any():
-            sl = s[live]
-            m = sl.max(axis=1)
-            p = np.exp(sl - m[:, None])
-            l = p.sum(axis=1)
-            out[live] = (p @ values) / l[:, None]
-            lse[live] = m + np.log(l)
-            probs[live] = p / l[:, None]
+    snk = np.full(R, -np.inf) if sink is None else np.asarray(sink, dtype=np.float64).reshape(R)
+    s = float(scale) * (q_rows @ keys.T) if N > 0 else np.zeros((R, 0))
+    if visible is not None and N > 0:
+        s = np.where(visible, s, -np.inf)
+    row_max = s.max(axis=1, initial=-np.inf)
+    m = np.maximum(row_max, snk)
+    live = ~np.isneginf(m)  # NaN logits propagate; only a row with nothing to weigh is empty
+    if live.any():
+        ml = m[live]
+        p = np.exp(s[live] - ml[:, None])
+        l = p.sum(axis=1) + np.exp(snk[live] - ml)
+        out[live] = (p @ values) / l[:, None]
+        lse[live] = ml + np.log(l)
+        probs[live] = p / l[:, None]
     if return_probs:
         return out, lse, probs
     return out, lse
@@ -251,9 +267,16 @@ def sparse_rows(d_indices_row, topk_length, pool_rows):
 
 
 def decode_sparse_f64(q, input_row_offsets, cache, d_indices, topk_lengths, page_size, scale,
-                      rows=None):
+                      rows=None, extra=None, attn_sink=None):
     """Sparse decode on float64 arrays (already dequantised): q [T, H, 576],
-    cache [num_pages, PS, 576]; each q row attends to its listed rows, no positional mask."""
+    cache [num_pages, PS, 576]; each q row attends to its listed rows, no positional mask.
+
+    extra = (cache2, d_indices2, topk_lengths2, page_size2) (optional): a second KV stream
+    ([DEC] Args extra_k, extra_d_indices, extra_indices_stride, extra_topk_lengths; the
+    reading used here): row t's second list names rows of cache2 by the same rules, and
+    row t attends to the rows of both lists under one softmax.
+    attn_sink [H] (optional): one sink logit per head shared by the batch ([DEC] Args
+    attn_sink_ptr, read as one weight set for the whole batch), see attend()."""
     T, H, _ = q.shape
     rows = list(range(T)) if rows is None else [int(r) for r in rows]
     pool_rows = cache.shape[0] * page_size
@@ -262,20 +285,33 @@ def decode_sparse_f64(q, input_row_offsets, cache, d_indices, topk_lengths, page
     for i, t in enumerate(rows):
         phys = sparse_rows(d_indices[t], topk_lengths[t], pool_rows)
         k = cache[phys // page_size, phys % page_size]
-        out[i], lse[i] = attend(q[t], k, value_columns(k), scale)
+        if extra is not None:
+            cache2, idx2, topk2, ps2 = extra
+            phys2 = sparse_rows(idx2[t], topk2[t], cache2.shape[0] * ps2)
+            k = np.concatenate([k, cache2[phys2 // ps2, phys2 % ps2]], axis=0)
+        out[i], lse[i] = attend(q[t], k, value_columns(k), scale, sink=attn_sink)
     return out, lse
 
 
 def decode_sparse(q8, q_scale, input_row_offsets, cache8, cache_scale, d_indices, topk_lengths,
-                  page_size, scale, rows=None):
+                  page_size, scale, rows=None, extra=None, attn_sink=None):
     """Sparse FP8 decode: values are E4M3 code value times the float32 scale of the q
-    token / cache row ([DEC] Args q_scale_ptr; [IDX] Args k_collection scales)."""
+    token / cache row ([DEC] Args q_scale_ptr; [IDX] Args k_collection scales).
+
+    extra = (cache8_2, cache_scale_2, d_indices_2, topk_lengths_2, page_size_2) names the
+    second KV stream with its own row scales ([DEC] Args extra_k, extra_scales_ptr,
+    extra_d_indices, extra_topk_lengths); attn_sink [H] the sink logits (see
+    decode_sparse_f64)."""
     q = e4m3_to_f64(q8)
     if q_scale is not None:
         q = q * np.asarray(q_scale, dtype=np.float64)[:, None, None]
     cache = _LazyE4M3(cache8, cache_scale)
+    ex = None
+    if extra is not None:
+        c8b, csb, idxb, topkb, psb = extra
+        ex = (_LazyE4M3(c8b, csb), idxb, topkb, psb)
     return decode_sparse_f64(q, input_row_offsets, cache, d_indices, topk_lengths, page_size,
-                             scale, rows)
+                             scale, rows, extra=ex, attn_sink=attn_sink)
 
 
 def decode_paged_fp8(q8, q_scale, input_row_offsets, page_table, cache_lens, cache8, cache_scale,

@@ -7,15 +7,19 @@ its own masking loop, math.fsum for every sum, and exp with the row maximum subt
 import math
 
 
-def attention_row(q_vec, keys, vals, scale):
-    """One head: q_vec [D], keys [N][D], vals [N][Dv] -> (out [Dv], lse)."""
-    if not keys:
-        return [0.0] * (len(vals[0]) if vals else 0), -math.inf
+def attention_row(q_vec, keys, vals, scale, sink=None, dv=None):
+    """One head: q_vec [D], keys [N][D], vals [N][Dv] -> (out [Dv], lse).
+
+    sink: an optional extra logit that adds e^sink to the denominator (and to the
+    log-sum-exp) and nothing to the numerator.  dv: the value width when keys is empty."""
+    dv = len(vals[0]) if vals else (dv or 0)
     logits = [scale * math.fsum(a * b for a, b in zip(q_vec, k)) for k in keys]
-    top = max(logits)
+    terms = logits + ([sink] if sink is not None else [])
+    if not terms or max(terms) == -math.inf:
+        return [0.0] * dv, -math.inf
+    top = max(terms)
     w = [math.exp(x - top) for x in logits]
-    tot = math.fsum(w)
-    dv = len(vals[0])
+    tot = math.fsum(w + ([math.exp(sink - top)] if sink is not None else []))
     out = [math.fsum(w[r] * vals[r][c] for r in range(len(keys))) / tot for c in range(dv)]
     return out, top + math.log(tot)
 

@@ -330,6 +330,138 @@ def pin_indexer_exact_ties():
     assert list(got[2]) == phys(1, [9, 7, 8, 10]) + [-1]
 
 
+def tiny_sparse_extra(seed=30, H=2, T=3):
+    """A sparse case with a second KV stream (its own fp8 pool, page size and row scales)
+    and per-head sink logits."""
+    rng = np.random.default_rng(seed)
+    base = tiny_sparse(seed=seed, H=H, T=T)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    pages2, ps2, stride2 = 3, 4, 6
+    cache8_2 = rng.choice(finite, size=(pages2, ps2, D)).astype(np.uint8)
+    c_scale_2 = rng.uniform(0.001, 0.01, size=(pages2, ps2)).astype(np.float32)
+    idx2 = rng.integers(0, pages2 * ps2, size=(T, stride2)).astype(np.int32)
+    idx2[1, 0] = -1                       # a pad inside the counted prefix is skipped
+    topk2 = np.array([4, 0, 6], dtype=np.int32)[:T]
+    sink = rng.normal(0.0, 2.0, size=H)
+    base.update(cache8_2=cache8_2, c_scale_2=c_scale_2, idx2=idx2, topk2=topk2, ps2=ps2, sink=sink)
+    return base
+
+
+def _run_sparse_extra(c, extra=True, sink=True):
+    ex = (c["cache8_2"], c["c_scale_2"], c["idx2"], c["topk2"], c["ps2"]) if extra else None
+    return O.decode_sparse(c["q8"], c["q_scale"], c["off"], c["cache8"], c["c_scale"], c["idx"], c["topk"],
+                           c["page_size"], SCALE, extra=ex, attn_sink=c["sink"] if sink else None)
+
+
+def pin_p1_sparse_extra_stream_and_sink():
+    """Sparse decode with a second KV stream and sink logits against scalar brute force:
+    the keys of a row are its listed main rows then its listed extra rows (each widened by
+    torch's e4m3 conversion times its own pool's row scale), one softmax over all of them
+    plus e^sink[h] in the denominator."""
+    c = tiny_sparse_extra()
+    out, lse = _run_sparse_extra(c)
+    qv = _torch_e4m3(c["q8"]) * c["q_scale"][:, None, None].astype(np.float64)
+    kv1 = _torch_e4m3(c["cache8"]) * c["c_scale"][..., None].astype(np.float64)
+    kv2 = _torch_e4m3(c["cache8_2"]) * c["c_scale_2"][..., None].astype(np.float64)
+    ps, ps2 = c["page_size"], c["ps2"]
+    for t in range(qv.shape[0]):
+        keys = []
+        for i in range(int(c["topk"][t])):
+            r = int(c["idx"][t, i])
+            if 0 <= r < kv1.shape[0] * ps:
+                keys.append(kv1[r // ps, r % ps].tolist())
+        for i in range(int(c["topk2"][t])):
+            r = int(c["idx2"][t, i])
+            if 0 <= r < kv2.shape[0] * ps2:
+                keys.append(kv2[r // ps2, r % ps2].tolist())
+        for h in range(qv.shape[1]):
+            bo, bl = attention_row(qv[t, h].tolist(), keys, [k[:DV] for k in keys], SCALE,
+                                   sink=float(c["sink"][h]), dv=DV)
+            close(out[t, h], bo, 1e-12)
+            close(lse[t, h], bl, 1e-12)
+
+
+def pin_sink_at_minus_infinity_is_no_sink():
+    """A sink logit of -inf adds e^-inf = 0: exactly the result without a sink."""
+    c = tiny_sparse_extra(seed=31)
+    c["sink"] = np.full_like(c["sink"], -np.inf)
+    a = _run_sparse_extra(c)
+    b = _run_sparse_extra(c, sink=False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def pin_sink_one_key_closed_form():
+    """One key of logit s and a sink s*: out = v / (1 + e^(s* - s)), lse = log(e^s + e^s*)
+    (the sink never enters the numerator and is not multiplied by scale)."""
+    rng = np.random.default_rng(32)
+    q = rng.standard_normal((1, 3, D))
+    key = rng.standard_normal((1, 1, D))
+    sink = np.array([-1.5, 0.3, 4.0])
+    out, lse = O.decode_sparse_f64(q, np.array([0, 1], np.uint32), key, np.array([[0]], np.int32),
+                                   np.array([1], np.int32), 1, SCALE, attn_sink=sink)
+    s = SCALE * (q[0] @ key[0, 0])
+    want = key[0, 0, :DV][None, :] / (1.0 + np.exp(sink - s))[:, None]
+    close(out[0], want, 1e-14)
+    close(lse[0], np.logaddexp(s, sink), 1e-13)
+    # no key at all: the sink takes all the weight
+    out0, lse0 = O.decode_sparse_f64(q, np.array([0, 1], np.uint32), key, np.array([[-1]], np.int32),
+                                     np.array([1], np.int32), 1, SCALE, attn_sink=sink)
+    assert np.all(out0 == 0.0)
+    close(lse0[0], sink, 0.0)
+
+
+def pin_sink_is_a_zero_valued_part():
+    """Adding a sink equals merging the sink-free result with a part of output 0 and
+    log-sum-exp sink (the split-KV merge of generic_flare_mla_decode_kv_cache_ragged)."""
+    c = tiny_sparse_extra(seed=33)
+    with_sink = _run_sparse_extra(c)
+    without = _run_sparse_extra(c, sink=False)
+    for t in range(with_sink[0].shape[0]):
+        o, l = O.combine([(without[0][t], without[1][t]),
+                          (np.zeros_like(without[0][t]), np.asarray(c["sink"], dtype=np.float64))])
+        close(with_sink[0][t], o, 1e-13)
+        close(with_sink[1][t], l, 1e-12)
+
+
+def pin_extra_stream_is_one_merged_pool():
+    """A second stream equals one stream over a pool that holds both caches' rows (page
+    size 1, the extra rows placed after the main ones, their indices shifted by the main
+    pool's row count), without reference to the merge algebra."""
+    c = tiny_sparse_extra(seed=34)
+    got = _run_sparse_extra(c)
+    ps, ps2 = c["page_size"], c["ps2"]
+    n1 = c["cache8"].shape[0] * ps
+    pool = np.concatenate([c["cache8"].reshape(-1, 1, D), c["cache8_2"].reshape(-1, 1, D)])
+    scales = np.concatenate([c["c_scale"].reshape(-1, 1), c["c_scale_2"].reshape(-1, 1)])
+    T = c["idx"].shape[0]
+    width = c["idx"].shape[1] + c["idx2"].shape[1]
+    idx = np.full((T, width), -1, dtype=np.int32)
+    topk = np.zeros(T, dtype=np.int32)
+    for t in range(T):
+        a = [int(x) for x in c["idx"][t, :c["topk"][t]]]
+        b = [int(x) + n1 if x >= 0 else -1 for x in c["idx2"][t, :c["topk2"][t]]]
+        idx[t, :len(a) + len(b)] = a + b
+        topk[t] = len(a) + len(b)
+    want = O.decode_sparse(c["q8"], c["q_scale"], c["off"], pool, scales, idx, topk, 1, SCALE,
+                           attn_sink=c["sink"])
+    close(got[0], want[0], 1e-13)
+    close(got[1], want[1], 1e-12)
+
+
+def pin_extra_stream_is_combine_of_streams():
+    """Attention over both lists equals the log-sum-exp merge of attention over each list
+    alone (P8 algebra on a key partition)."""
+    c = tiny_sparse_extra(seed=35)
+    both = _run_sparse_extra(c, sink=False)
+    main = _run_sparse_extra(c, extra=False, sink=False)
+    c2 = dict(c, cache8=c["cache8_2"], c_scale=c["c_scale_2"], idx=c["idx2"], topk=c["topk2"], page_size=c["ps2"])
+    other = _run_sparse_extra(c2, extra=False, sink=False)
+    for t in range(both[0].shape[0]):
+        o, l = O.combine([(main[0][t], main[1][t]), (other[0][t], other[1][t])])
+        close(both[0][t], o, 1e-13)
+        close(both[1][t], l, 1e-12)
+
+
 def tiny_prefill(seed=5, new=(3, 4), prefix=(0, 2), H=2, page_size=4):
     rng = np.random.default_rng(seed)
     total = [a + b for a, b in zip(new, prefix)]

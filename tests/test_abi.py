@@ -288,3 +288,51 @@ def test_indexer_empty_batch_is_ok_without_gpu():
     st, msg = call_indexer(indexer_args(q=_t(FAKE, 1, (0, 8, 128)), qs=_t(FAKE, 2, (0, 8)),
                                         out=_t(FAKE, 3, (0, 32))))
     assert st == 0, msg
+
+
+def _parts_brute(batch, keys, grid):
+    """Most pieces one row gets from the balanced split, by direct search: row parts take
+    the smallest S with batch * ceil(nt / S) <= grid; stream runs of ceil(batch * nt /
+    grid) tiles over the concatenated rows."""
+    nt = -(-keys // 32)
+    if batch <= grid:
+        S = next(S for S in range(1, nt + 1) if batch * -(-nt // S) <= grid)
+        return -(-nt // S)
+    W = -(-batch * nt // grid)
+    return max(len({i // W for i in range(b * nt, (b + 1) * nt)}) for b in range(batch))
+
+
+def _grid():
+    import torch
+    if torch.cuda.is_available():
+        return torch.cuda.get_device_properties(0).multi_processor_count
+    return 256  # the library's count when no device answers
+
+
+@pytest.mark.parametrize("batch,max_pages,ps", [(64, 64, 64), (8, 1024, 64), (2, 7, 16), (1, 1, 1),
+                                               (256, 4, 64), (300, 3, 64), (1000, 1, 16), (64, 2, 32)])
+def test_decode_num_partitions(batch, max_pages, ps):
+    """mla_decode_num_partitions (generic_flare_mla_decode_kv_cache_ragged, Args
+    num_partitions_in) against a direct search of the balanced split."""
+    got = m.decode_num_partitions(batch, 128, max_pages, ps)
+    assert got == _parts_brute(batch, max_pages * ps, _grid())
+
+
+def test_decode_num_partitions_rejects_bad_arguments():
+    for args in [(0, 128, 8, 64), (4, 100, 8, 64), (4, 128, 0, 64), (4, 128, 8, 0), (4, 128, 1 << 30, 64),
+                 ((1 << 24) + 1, 128, 1, 64)]:
+        assert m.decode_num_partitions(*args) == 0, args
+
+
+def test_profile_read_each_without_launches():
+    """Timing on, no call made: nothing bracketed (the ring is created on the host only
+    when a device answers; without one the enable call reports a HIP error)."""
+    try:
+        m.profile_enable(True)
+    except m.MlaError as e:
+        assert e.status == 7
+        return
+    try:
+        assert m.profile_read_each() == []
+    finally:
+        m.profile_enable(False)

@@ -71,6 +71,23 @@ def test_c2_long_context_split():
         compare(to_f64(decode_on_gpu(m, case, num_partitions=P)), want, BF16_TOL, f"C2 P={P}")
 
 
+@pytest.mark.parametrize("ps,lens,mask", [(16, [20011, 300], "causal"), (64, [70001, 5000], "causal"),
+                                           (16, [21000], "sliding_window_causal")])
+def test_page_window_refill(ps, lens, mask):
+    """One segment longer than the kernel's 1024-entry page-id window, so the window is
+    refilled inside the stage loop: PS=16 (per-key page lookups) and PS=64 (one page per
+    stage), whole rows at num_partitions=1 and the library's own split
+    (generic_flare_mla_decode_kv_cache_ragged, Args num_partitions_in)."""
+    m = need_gpu()
+    window = 19000 if mask == "sliding_window_causal" else -1
+    case = make_decode_case(300 + ps, lens, 16, ps, mask=mask, window=window, name="window-refill")
+    assert max(lens) // ps > 1024
+    want = oracle_of(case)
+    for P in (1, 0, 2):
+        compare(to_f64(decode_on_gpu(m, case, num_partitions=P)), want, BF16_TOL,
+                f"PS={ps} lens={lens} {mask} P={P}")
+
+
 def test_page_permutation_bitwise():
     """Physical page placement never changes the bits of the result."""
     m = need_gpu()

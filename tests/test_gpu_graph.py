@@ -115,3 +115,52 @@ def test_graph_indexer():
 
     ws = T * keys_row * 8 + (1 << 20)
     check_replays(m, variants, call, make_out, -7, ws, "indexer")
+
+
+def test_graph_survives_workspace_growth():
+    """A graph captured on a stream keeps replaying correctly after an eager call on the
+    same stream has grown that stream's workspace: the outgrown buffer is retired, not
+    freed (generic_flare_mla_decode_kv_cache_ragged, Args num_partitions_in: the
+    capturable-graph path)."""
+    import torch
+    m = need_gpu()
+    lens, H = [1500, 3000, 64, 4096, 1, 2222], 128
+    c = make_decode_case(64, lens, H, 64, name="graph-grow")
+    b = {"q": bf16_dev(c.q), "off": i32_dev(c.input_row_offsets), "pt": i32_dev(c.page_table),
+         "lens": i32_dev(c.cache_lens), "cache": bf16_dev(c.latent_cache)}
+    T = c.total_q
+
+    def call(out, parts):
+        m.decode_paged(b["q"], b["off"], b["pt"], b["lens"], b["cache"], c.scale, num_partitions=parts, out=out)
+
+    want = torch.empty(T, H, 512, dtype=torch.bfloat16, device="cuda")
+    call(want, 0)  # eager, default stream
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    out = torch.empty_like(want)
+    m.reserve_workspace(m.decode_workspace_bytes(T, H, 0), stream=s)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(out, 0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(out, 0)
+    torch.cuda.synchronize()
+    # an eager call on the capture stream that needs more than twice the reserved slots
+    big_parts = 200
+    assert m.decode_workspace_bytes(T, H, big_parts) > 2 * m.decode_workspace_bytes(T, H, 0)
+    other = torch.empty_like(want)
+    with torch.cuda.stream(s):
+        call(other, big_parts)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {rep} after growth differs"
+        with torch.cuda.stream(s):
+            call(other, big_parts)
+        torch.cuda.synchronize()
+    assert m.check_device_errors(stream=s) == 0
+    print("[graph] 3 replays after the capture stream's workspace grew equal the eager call", flush=True)

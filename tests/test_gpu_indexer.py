@@ -5,8 +5,9 @@ Selection is an integer result decided by floating-point scores: the kernel deci
 float32 scores, the oracle on float64 ones.  Rows whose scores lie within the float32
 error band of the k-th score are equally valid choices at the boundary, so the check is:
 the -1 fill and the number of valid entries exact; every entry a distinct visible row;
-every chosen row scoring at least the k-th score minus the band; the listed order
-non-increasing within the band; and all but a handful of boundary rows identical."""
+every chosen row scoring at least the k-th score minus the band; every visible row
+scoring above the k-th score plus the band chosen; the listed order non-increasing within
+the band; and at most 1% of the listed rows different from the oracle's list."""
 import numpy as np
 import pytest
 
@@ -66,6 +67,10 @@ def check_indexer(got, c, what):
         chosen = sc[idx]
         assert chosen.min() >= kth - band, f"{what} row {t}: a row below the k-th score by more than {band}"
         assert np.all(np.diff(chosen) <= band), f"{what} row {t}: order not descending"
+        # every visible row scoring clearly above the k-th must have been chosen
+        clear = np.flatnonzero(sc > kth + band)
+        missing = np.setdiff1d(clear, idx)
+        assert missing.size == 0, f"{what} row {t}: {missing.size} rows above the k-th score plus the band left out"
         differ += int(np.count_nonzero(sel != want[t][:k]))
     return differ
 
@@ -77,7 +82,24 @@ def test_indexer_small(ps, mask, window):
     c = make_indexer_case(41, [1, 37, 100, 700, 64, 300], 8, 64, ps, 48, q_per_seq=[1, 2, 1, 3, 1, 2],
                           mask=mask, window=window, name="idx-small")
     differ = check_indexer(run_indexer(m, c), c, f"PS={ps} {mask}")
-    print(f"[parity] indexer PS={ps} {mask}: {differ} listed rows differ from the oracle's order", flush=True)
+    listed = sum(min(c.top_k, hi - lo) for hi, lo in _visible_counts(c))
+    print(f"[parity] indexer PS={ps} {mask}: {differ} of {listed} listed rows differ from the oracle's order",
+          flush=True)
+    # rows that differ are boundary choices within the float32 band (checked above); at
+    # most 1% of the listed rows may be such choices
+    assert differ <= max(1, listed // 100)
+
+
+def _visible_counts(c):
+    """(hi, lo) of every query row's visible range, from the oracle's reading."""
+    off = c.input_row_offsets.astype(np.int64)
+    res = []
+    for b, L in enumerate(c.cache_lens):
+        n = int(off[b + 1] - off[b])
+        for j in range(n):
+            lo, hi = O.visible_range(int(L), n, j, c.mask, c.window)
+            res.append((hi, lo))
+    return res
 
 
 def test_indexer_full_size():

@@ -14,6 +14,7 @@ _visible = O.visible_range
 _rows = O.logical_rows
 _sparse_rows = O.sparse_rows
 _rank_order = O.rank_order
+_decode_sparse_f64 = O.decode_sparse_f64
 
 
 def m_scale_dropped(mp):
@@ -147,11 +148,55 @@ def m_indexer_ties_reversed(mp):
     mp.setattr(O, "rank_order", lambda sc, pos: np.lexsort((-np.asarray(pos), -np.asarray(sc, dtype=np.float64))))
 
 
+def m_sink_dropped(mp):
+    mp.setattr(O, "attend", lambda q, k, v, scale, visible=None, return_probs=False, sink=None:
+               _attend(q, k, v, scale, visible, return_probs))
+
+
+def m_sink_scaled(mp):
+    """The sink logit multiplied by the attention scale like a dot product."""
+    def att(q, k, v, scale, visible=None, return_probs=False, sink=None):
+        return _attend(q, k, v, scale, visible, return_probs, None if sink is None else np.asarray(sink) * scale)
+    mp.setattr(O, "attend", att)
+
+
+def m_sink_in_numerator(mp):
+    """The sink treated as a key whose value row is all ones."""
+    def att(q, k, v, scale, visible=None, return_probs=False, sink=None):
+        if sink is None:
+            return _attend(q, k, v, scale, visible, return_probs)
+        R = q.shape[0]
+        s = scale * (q @ k.T) if k.shape[0] else np.zeros((R, 0))
+        snk = np.asarray(sink, dtype=np.float64)
+        m = np.maximum(s.max(axis=1, initial=-np.inf), snk)
+        p = np.exp(s - m[:, None])
+        ps = np.exp(snk - m)
+        l = p.sum(axis=1) + ps
+        out = (p @ v + ps[:, None]) / l[:, None]
+        lse = m + np.log(l)
+        return (out, lse, p / l[:, None]) if return_probs else (out, lse)
+    mp.setattr(O, "attend", att)
+
+
+def m_extra_stream_ignored(mp):
+    mp.setattr(O, "decode_sparse_f64", lambda *a, extra=None, **kw: _decode_sparse_f64(*a, extra=None, **kw))
+
+
+def m_extra_reads_main_cache(mp):
+    """The second list's rows looked up in the main cache."""
+    def dsp(q, off, cache, idx, topk, ps, scale, rows=None, extra=None, attn_sink=None):
+        if extra is not None:
+            extra = (cache, extra[1], extra[2], ps)
+        return _decode_sparse_f64(q, off, cache, idx, topk, ps, scale, rows, extra=extra, attn_sink=attn_sink)
+    mp.setattr(O, "decode_sparse_f64", dsp)
+
+
 MUTANTS = [m_scale_dropped, m_values_shifted, m_causal_off_by_one, m_token_order_reversed,
            m_page_slot_swapped, m_combine_unweighted, m_no_max_subtraction, m_softmax_over_heads,
            m_lse_without_max, m_e4m3_bias8, m_sparse_ignores_topk, m_sparse_keeps_pads,
            m_prefill_rope_at_query, m_bf16_low_half,
-           m_indexer_unweighted_heads, m_indexer_ties_reversed]
+           m_indexer_unweighted_heads, m_indexer_ties_reversed, m_sink_dropped, m_sink_scaled,
+           m_sink_in_numerator, m_extra_stream_ignored, m_extra_reads_main_cache]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
