@@ -111,6 +111,17 @@ def hbm_read_ceiling(dev, gib=2, reps=20):
     return round(nbytes / (best * 1e-3) / 1e9, 1)
 
 
+def pct(values, q):
+    """q-th percentile (linear interpolation) of a list of numbers."""
+    v = sorted(values)
+    if not v:
+        return float("nan")
+    x = (len(v) - 1) * q / 100.0
+    lo = int(x)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (x - lo)
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -318,19 +329,22 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps, synchronised on both sides
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- timed region: exactly `steps` steps, synchronised on both sides; an event
+    # between consecutive steps gives each step's own duration as well
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record()
+    evs[0].record()
     for i in range(args.steps):
         step(i)
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - w0) * 1e3
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_each = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
 
     # ---- warm-cache figure (same buffers every step), for context only
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
     for _ in range(args.steps):
@@ -339,14 +353,21 @@ def main():
     torch.cuda.synchronize()
     warm_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- the main kernel alone: HIP events around its launches on this stream
+    # ---- the main kernel alone: the library brackets each launch with a pair of HIP
+    # events (created once, before these steps) on the launch stream; at least 50 calls
+    kernel_calls = max(args.steps, 50)
     m.profile_enable(True)
-    for i in range(args.steps):
+    for i in range(kernel_calls):
         step(i)
     torch.cuda.synchronize()
-    kms, launches = m.profile_read()
+    k_each = m.profile_read_each()
     m.profile_enable(False)
-    k_avg_ms = kms / max(1, launches)
+    launches = len(k_each)
+    k_avg_ms = pct(k_each, 50)
+    step_ms_median = pct(step_each, 50)
+    if k_avg_ms > step_ms_median:
+        print(f"warning: median kernel time {k_avg_ms * 1e3:.2f} us exceeds the median step time "
+              f"{step_ms_median * 1e3:.2f} us", file=sys.stderr)
 
     # ---- context: the same steps replayed from HIP graphs (no host work per step)
     graph_ms = None
@@ -385,8 +406,11 @@ def main():
         if wl in MULTI_TOKEN:
             metric = f"MLA multi-token decode GB/s (cache rows once per sequence), {wl}, 1 GPU"
         value, unit = gbs, "GB/s"
-    roof.update({"kernel": KERNELS[wl], "kernel_avg_us": round(k_avg_ms * 1e3, 3),
-                 "kernel_launches_timed": launches})
+    roof.update({"kernel": KERNELS[wl],
+                 "kernel_us": {"median": round(k_avg_ms * 1e3, 3), "p10": round(pct(k_each, 10) * 1e3, 3),
+                               "p90": round(pct(k_each, 90) * 1e3, 3), "mean": round(sum(k_each) / max(1, launches) * 1e3, 3)},
+                 "kernel_launches_timed": launches,
+                 "kernel_median_le_step_median": bool(k_avg_ms <= step_ms_median)})
     res = {
         "metric": metric,
         "value": round(value, 2),
@@ -395,6 +419,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_us": {"median": round(step_ms_median * 1e3, 3), "p10": round(pct(step_each, 10) * 1e3, 3),
+                    "p90": round(pct(step_each, 90) * 1e3, 3)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -37,7 +37,13 @@
  *     library, one grow-only buffer per (device, stream).  It is allocated on first
  *     use; a call issued while `stream` is capturing a graph must find it already large
  *     enough (see mla_reserve_workspace), else it returns MLA_ERR_WORKSPACE.  Calls on
- *     one stream are ordered, so they may share that stream's workspace.
+ *     one stream are ordered, so they may share that stream's workspace.  When a later
+ *     call (or mla_reserve_workspace) outside capture needs a larger one, the stream is
+ *     synchronised, a new buffer takes over and the old one is retired, not freed:
+ *     graphs captured earlier on that stream keep replaying into the old buffer, which
+ *     stays allocated until mla_shutdown.  The device error word moves to the new buffer
+ *     at that point; errors raised later by replays of such older graphs land in the
+ *     retired buffer and are not reported by mla_check_device_errors.
  *   - At most 2^24 query rows per call.
  */
 #ifndef MLA355_H_
@@ -126,7 +132,7 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
  *   q             fp8 e4m3 [T, H, 576] (or bf16, then q_scale must be NULL)
  *   q_scale       f32 [T] (one scale per query token, shared by its heads) or NULL = 1
  *   input_row_offsets  u32 [B + 1] (only its shape is checked: index lists are per row)
- *   latent_cache  fp8 e4m3 [num_pages, PS, 576] (or bf16, then cache_scale must be NULL)
+ *   latent_cache  fp8 e4m3 [num_pages, PS, 576] (a bf16 cache is refused: MLA_ERR_UNSUPPORTED)
  *   cache_scale   f32 [num_pages, PS] (one scale per cache row) or NULL = 1
  *   d_indices     i32 [T, indices_stride] (row stride = stride[0] >= shape[1])
  *   topk_lengths  i32 [T], values above shape[1] of d_indices are clamped to it
@@ -138,6 +144,43 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
                                    const mla_tensor* d_indices, const mla_tensor* topk_lengths,
                                    float scale, int32_t num_partitions, mla_tensor* out,
                                    void* stream);
+
+/*
+ * Sparse MLA decode with an attention sink and a second KV stream
+ * (generic_flare_mla_decode_kv_cache_ragged: Args attn_sink_ptr, extra_k,
+ * extra_d_indices, extra_indices_stride, extra_topk_lengths, extra_scales_ptr; the page
+ * names these arguments without a formula, so what follows is this library's reading).
+ * Everything mla_decode_paged_sparse takes, plus:
+ *
+ *   attn_sink          f32 [H] or NULL: one logit per head, shared by every query row of
+ *                      the call and not multiplied by `scale`.  It adds e^attn_sink[h] to
+ *                      the softmax denominator and nothing to the numerator:
+ *                      out[t,h] = sum_r e^{s_r} v_r / (e^{attn_sink[h]} + sum_r e^{s_r}),
+ *                      so a row whose lists hold no key gets out = 0.
+ *   extra_cache        fp8 e4m3 [extra_pages, extra_PS, 576] or NULL: the second stream's
+ *                      pool (rows of a page contiguous)
+ *   extra_cache_scale  f32 [extra_pages, extra_PS] or NULL = 1: its row scales
+ *   extra_d_indices    i32 [T, extra_stride], row stride = extra_indices_stride: row t's
+ *                      second list, physical rows page * extra_PS + slot of extra_cache,
+ *                      read by the rules of d_indices (first extra_topk_lengths[t]
+ *                      entries, negatives skipped, duplicates counted)
+ *   extra_topk_lengths i32 [T]
+ *
+ * Row t attends to the rows of both lists under one softmax (one set of weights over the
+ * union).  extra_cache, extra_d_indices and extra_topk_lengths come together or not at
+ * all; with them, each pool must hold fewer than 2^30 rows.  Second-list rows outside
+ * extra_cache are skipped and set bit 1 of the device error word.  With neither a sink nor
+ * a second stream this is mla_decode_paged_sparse.
+ */
+mla_status mla_decode_paged_sparse_ext(const mla_tensor* q, const mla_tensor* q_scale,
+                                       const mla_tensor* input_row_offsets,
+                                       const mla_tensor* latent_cache, const mla_tensor* cache_scale,
+                                       const mla_tensor* d_indices, const mla_tensor* topk_lengths,
+                                       const mla_tensor* attn_sink, const mla_tensor* extra_cache,
+                                       const mla_tensor* extra_cache_scale,
+                                       const mla_tensor* extra_d_indices,
+                                       const mla_tensor* extra_topk_lengths, float scale,
+                                       int32_t num_partitions, mla_tensor* out, void* stream);
 
 /*
  * Dense MLA decode over a paged fp8 e4m3 latent cache
@@ -155,7 +198,7 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
  *   latent_cache       fp8 e4m3 [num_pages, PS, 576], rows of a page contiguous, any PS
  *   cache_scale        f32 [num_pages, PS] or NULL = 1
  *
- * Errors as for mla_decode_paged; page ids outside the pool are skipped and set bit 1
+ * Errors as for mla_decode_paged; page ids outside the pool are skipped and set bit 0
  * of the device error word (mla_check_device_errors).
  */
 mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
@@ -184,7 +227,7 @@ mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
  *   k_scale            f32 [num_pages, PS] or NULL = 1
  *   out_indices        i32 [T, top_k], top_k in [1, 2048], written in full
  *
- * Page ids outside the pool rank last, are never returned and set bit 1 of the device
+ * Page ids outside the pool rank last, are never returned and set bit 0 of the device
  * error word.
  */
 mla_status mla_indexer_paged_fp8(const mla_tensor* q, const mla_tensor* q_s,
@@ -215,6 +258,19 @@ mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla
                              const mla_tensor* cache_lens, const mla_tensor* latent_cache,
                              float scale, int32_t mask, mla_tensor* out, void* stream);
 
+/* The split-KV partition count the library's balanced split gives each query row of a
+ * dense decode (generic_flare_mla_decode_kv_cache_ragged: Args num_partitions_in, the
+ * capturable-graph partition override).  Host only, no device access: the count is
+ * planned for `batch` sequences of one query token each whose rows all hold
+ * max_pages * page_size visible keys, on the current device's compute units.  Calls with
+ * num_partitions <= 0 plan from the actual cache lengths on the device; passing this
+ * value as num_partitions instead fixes the split of every row (rows shorter than the
+ * longest then get the same number of smaller parts).  Returns 0 when an argument is out
+ * of range (batch < 1 or above 2^24, num_heads not in {16, 32, 64, 128}, max_pages or
+ * page_size < 1, or max_pages * page_size above 2^30). */
+int32_t mla_decode_num_partitions(int64_t batch, int64_t num_heads, int64_t max_pages,
+                                  int32_t page_size);
+
 /* Workspace bytes a decode call with these sizes needs (host only, no device access).
  * num_partitions as in mla_decode_paged; device selects the CU count (-1 = current). */
 size_t mla_decode_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t num_partitions,
@@ -230,15 +286,23 @@ mla_status mla_reserve_workspace(int32_t device, void* stream, size_t bytes);
  * max_pages * PS.  *flags receives the word (0 = clean). */
 mla_status mla_check_device_errors(int32_t device, void* stream, uint32_t* flags);
 
-/* Kernel timing for measurement tools.  While enabled, every call brackets its main
- * kernel (the attention kernel, not the combine) with two HIP events recorded on the
- * call's stream; mla_profile_read synchronises those events, returns the summed
- * milliseconds and the number of bracketed launches, and forgets them.  Leave it
- * disabled (the default) in graph-captured code.  Host-side bookkeeping only. */
+/* Kernel timing for measurement tools.  Enabling creates a ring of 4096 HIP event pairs
+ * once (no event is created on a call's path) and restarts the count.  While enabled,
+ * every call brackets its main kernel (the attention kernel, not the combine) with the
+ * next pair, recorded on the call's stream; calls past the ring's capacity are not timed.
+ * mla_profile_read_each synchronises the pairs used since the last read, writes each
+ * bracketed launch's milliseconds (up to `capacity` of them, in call order), sets
+ * *launches to the number bracketed and starts over; it returns MLA_ERR_WORKSPACE when
+ * launches went untimed because the ring was full.  mla_profile_read gives their sum
+ * instead.  Leave timing disabled (the default) in graph-captured code.  Host-side
+ * bookkeeping only; mla_shutdown destroys the ring. */
 mla_status mla_profile_enable(int32_t enable);
+mla_status mla_profile_read_each(double* ms_each, int64_t capacity, int64_t* launches);
 mla_status mla_profile_read(double* total_ms, int64_t* launches);
 
-/* Free every workspace the library holds (all devices, all streams). */
+/* Free every workspace the library holds (all devices, all streams, retired ones
+ * included) and the timing events.  Graphs captured from library calls must not be
+ * replayed afterwards. */
 void mla_shutdown(void);
 
 const char* mla_status_string(mla_status s);

@@ -13,8 +13,9 @@ import os
 
 __all__ = [
     "LIBRARY_PATH", "MlaError", "library", "decode_paged", "decode_paged_sparse",
-    "prefill_paged", "decode_workspace_bytes", "reserve_workspace", "check_device_errors",
-    "shutdown", "version", "profile_enable", "profile_read", "MASKS", "STATUS",
+    "decode_paged_sparse_ext", "decode_paged_fp8", "indexer_paged_fp8", "prefill_paged", "decode_num_partitions",
+    "decode_workspace_bytes", "reserve_workspace", "check_device_errors", "shutdown",
+    "version", "profile_enable", "profile_read", "profile_read_each", "MASKS", "STATUS",
 ]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla355.so")
@@ -51,10 +52,11 @@ def library() -> ctypes.CDLL:
         i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
         lib.mla_decode_paged.argtypes = [P, P, P, P, P, f32, i32, i32, i32, P, vp]
         lib.mla_decode_paged_sparse.argtypes = [P, P, P, P, P, P, P, f32, i32, P, vp]
+        lib.mla_decode_paged_sparse_ext.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, f32, i32, P, vp]
         lib.mla_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, f32, i32, i32, i32, P, vp]
         lib.mla_indexer_paged_fp8.argtypes = [P, P, P, P, P, P, P, i32, i32, P, vp]
         lib.mla_prefill_paged.argtypes = [P, P, P, P, P, P, P, P, P, f32, i32, P, vp]
-        for fn in ("mla_decode_paged", "mla_decode_paged_sparse", "mla_decode_paged_fp8", "mla_indexer_paged_fp8", "mla_prefill_paged",
+        for fn in ("mla_decode_paged", "mla_decode_paged_sparse", "mla_decode_paged_sparse_ext", "mla_decode_paged_fp8", "mla_indexer_paged_fp8", "mla_prefill_paged",
                    "mla_reserve_workspace", "mla_check_device_errors"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_decode_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32, i32]
@@ -65,6 +67,11 @@ def library() -> ctypes.CDLL:
         lib.mla_profile_enable.restype = ctypes.c_int
         lib.mla_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         lib.mla_profile_read.restype = ctypes.c_int
+        lib.mla_profile_read_each.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int64,
+                                              ctypes.POINTER(ctypes.c_int64)]
+        lib.mla_profile_read_each.restype = ctypes.c_int
+        lib.mla_decode_num_partitions.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, i32]
+        lib.mla_decode_num_partitions.restype = ctypes.c_int32
         lib.mla_shutdown.argtypes = []
         lib.mla_shutdown.restype = None
         lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -161,6 +168,25 @@ def decode_paged_sparse(q, q_scale, input_row_offsets, latent_cache, cache_scale
     return out
 
 
+def decode_paged_sparse_ext(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices,
+                            topk_lengths, scale, attn_sink=None, extra_cache=None, extra_cache_scale=None,
+                            extra_d_indices=None, extra_topk_lengths=None, num_partitions=0, out=None,
+                            stream=None):
+    """Sparse MLA decode with an attention sink (f32 [H] logits) and a second KV stream
+    (mla_decode_paged_sparse_ext); returns out bf16 [T, H, 512]."""
+    import torch
+    _on_gpu(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices, topk_lengths, attn_sink,
+            extra_cache, extra_cache_scale, extra_d_indices, extra_topk_lengths, out)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
+    _check(library().mla_decode_paged_sparse_ext(
+        _desc(q), _desc(q_scale), _offsets(input_row_offsets), _desc(latent_cache),
+        _desc(cache_scale), _desc(d_indices), _desc(topk_lengths), _desc(attn_sink), _desc(extra_cache),
+        _desc(extra_cache_scale), _desc(extra_d_indices), _desc(extra_topk_lengths), float(scale),
+        int(num_partitions), _desc(out), _stream(stream)))
+    return out
+
+
 def decode_paged_fp8(q, q_scale, input_row_offsets, page_table, cache_lens, latent_cache, cache_scale,
                      scale, mask="causal", local_window_size=-1, num_partitions=0, out=None, stream=None):
     """Dense MLA decode over a paged fp8 cache (mla_decode_paged_fp8).  q fp8 e4m3
@@ -211,6 +237,14 @@ def prefill_paged(q, k, v, buffer_row_offsets, cache_offsets, input_row_offsets,
     return out
 
 
+def decode_num_partitions(batch, num_heads, max_pages, page_size) -> int:
+    """The split-KV partition count the balanced split gives each row of a batch of
+    `batch` single-token sequences of max_pages * page_size keys (mla_decode_num_partitions;
+    0 for out-of-range arguments)."""
+    return int(library().mla_decode_num_partitions(int(batch), int(num_heads), int(max_pages),
+                                                   int(page_size)))
+
+
 def decode_workspace_bytes(total_q, num_heads, num_partitions=0, device=-1) -> int:
     return int(library().mla_decode_workspace_bytes(int(total_q), int(num_heads),
                                                     int(num_partitions), int(device)))
@@ -236,6 +270,14 @@ def profile_read() -> tuple[float, int]:
     ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
     _check(library().mla_profile_read(ctypes.byref(ms), ctypes.byref(n)))
     return float(ms.value), int(n.value)
+
+
+def profile_read_each(capacity: int = 4096) -> list[float]:
+    """Milliseconds of each bracketed kernel since the last read, in call order."""
+    buf = (ctypes.c_double * max(1, int(capacity)))()
+    n = ctypes.c_int64(0)
+    _check(library().mla_profile_read_each(buf, int(capacity), ctypes.byref(n)))
+    return [float(buf[i]) for i in range(min(int(n.value), int(capacity)))]
 
 
 def shutdown() -> None:

@@ -95,6 +95,9 @@ struct Workspace {
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
+// Outgrown workspaces, kept until mla_shutdown: a graph captured earlier may still hold
+// their addresses, so they are never freed while the library is in use.
+std::vector<std::pair<int, void*>> g_ws_retired;
 std::map<int, int> g_cu_count;
 
 int current_device() {
@@ -123,12 +126,6 @@ mla_status grow_workspace(int device, void* stream, size_t need, bool capturing,
   }
   if (capturing)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed while the stream is capturing; reserve it first", need);
-  if (w.base) {
-    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess || hipFree(w.base) != hipSuccess)
-      return fail(MLA_ERR_HIP, "could not release the old workspace");
-    w.base = nullptr;
-    w.bytes = 0;
-  }
   size_t bytes = need + need / 4;  // headroom so slowly growing calls do not reallocate
   void* p = nullptr;
   if (hipMalloc(&p, bytes) != hipSuccess) return fail(MLA_ERR_WORKSPACE, "hipMalloc(%zu) failed", bytes);
@@ -138,6 +135,18 @@ mla_status grow_workspace(int device, void* stream, size_t need, bool capturing,
       hipMemcpy((char*)p + mla::kSparseOneOffset, &one, sizeof(one), hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(p);
     return fail(MLA_ERR_HIP, "initialising the workspace header failed");
+  }
+  if (w.base) {
+    // The old buffer is retired, not freed (graphs captured on this stream may still
+    // replay into it).  Its error word carries over once the stream's work has finished.
+    uint32_t flags = 0;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
+        hipMemcpy(&flags, (char*)w.base + kErrOffset, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy((char*)p + kErrOffset, &flags, 4, hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(p);
+      return fail(MLA_ERR_HIP, "could not move the device error word to the grown workspace");
+    }
+    g_ws_retired.emplace_back(device, w.base);
   }
   w.base = p;
   w.bytes = bytes;
@@ -155,34 +164,70 @@ mla_status stream_capturing(void* stream, bool* capturing) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The most pieces the balanced split of the decode kernels (mla_plan.h) cuts one query row
+// into, for `batch` rows of `keys` visible keys each over `grid` work-groups.  Row parts
+// (batch <= grid): the smallest S with batch * ceil(nt / S) <= grid tiles per part, nt the
+// row's 32-key tiles, so ceil(nt / S) parts; stream (batch > grid): runs of
+// ceil(batch * nt / grid) tiles over the concatenated rows, the most runs one row meets.
+int32_t balanced_parts_per_row(int64_t batch, int64_t keys, int grid) {
+  const int64_t nt = (keys + 31) / 32;
+  if (batch <= grid) {
+    const int64_t per_row = grid / batch;  // parts every row may have
+    const int64_t S = (nt + per_row - 1) / per_row;
+    return (int32_t)((nt + S - 1) / S);
+  }
+  const int64_t W = (batch * nt + grid - 1) / grid;
+  int64_t most = 1;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t first = b * nt / W, last = ((b + 1) * nt - 1) / W;
+    if (last - first + 1 > most) most = last - first + 1;
+  }
+  return (int32_t)most;
+}
+
 // ---------------------------------------------------------------------------------------
-// optional kernel timing
+// optional kernel timing: a ring of event pairs created when timing is enabled, so that
+// no call creates an event (event creation on the call path would delay the host enough
+// for the GPU to drain its queue, and the gaps would be timed as kernel time)
 // ---------------------------------------------------------------------------------------
+constexpr int kProfileSlots = 4096;
 std::mutex g_prof_mu;
 bool g_prof_on = false;
-std::vector<mla::KernelTimer> g_prof_events;
+std::vector<mla::KernelTimer> g_prof_ring;  // created by mla_profile_enable
+std::vector<char> g_prof_live;              // slot i was recorded by a launch
+int64_t g_prof_used = 0;                    // slots handed out since the last read
+int64_t g_prof_dropped = 0;                 // launches past the ring's capacity (not timed)
 
-// Returns a timer to pass to a launcher, or null when timing is off.
-mla::KernelTimer* profile_timer(mla::KernelTimer* slot) {
+// Reserves the next timer of the ring (copied into *slot, its index in *index), or
+// returns null when timing is off or the ring is full.
+mla::KernelTimer* profile_timer(mla::KernelTimer* slot, int64_t* index) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on) return nullptr;
-  if (hipEventCreate(&slot->start) != hipSuccess) return nullptr;
-  if (hipEventCreate(&slot->stop) != hipSuccess) {
-    (void)hipEventDestroy(slot->start);
+  if (!g_prof_on || g_prof_ring.empty()) return nullptr;
+  if (g_prof_used >= (int64_t)g_prof_ring.size()) {
+    ++g_prof_dropped;
     return nullptr;
   }
+  *index = g_prof_used++;
+  *slot = g_prof_ring[(size_t)*index];
+  g_prof_live[(size_t)*index] = 0;
   return slot;
 }
 
-void profile_keep(mla::KernelTimer* t, bool launched) {
-  if (!t) return;
+void profile_keep(mla::KernelTimer* t, int64_t index, bool launched) {
+  if (!t || !launched) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (launched) {
-    g_prof_events.push_back(*t);
-  } else {
-    (void)hipEventDestroy(t->start);
-    (void)hipEventDestroy(t->stop);
+  if (index >= 0 && index < (int64_t)g_prof_live.size()) g_prof_live[(size_t)index] = 1;
+}
+
+void profile_destroy_ring() {
+  for (auto& t : g_prof_ring) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
   }
+  g_prof_ring.clear();
+  g_prof_live.clear();
+  g_prof_used = 0;
+  g_prof_dropped = 0;
 }
 
 // Past the header: the split rows' parts (bf16), their log2-sum-exps and the split table.
@@ -251,71 +296,129 @@ mla_status mla_check_device_errors(int32_t device, void* stream, uint32_t* flags
   if (!flags) return fail(MLA_ERR_NULL_ARG, "flags is NULL");
   *flags = 0;
   const int dev = device < 0 ? current_device() : device;
-  void* base = nullptr;
+  std::vector<void*> words;
   {
     std::lock_guard<std::mutex> lk(g_ws_mu);
     auto it = g_ws.find({dev, stream});
-    if (it == g_ws.end()) return ok();
-    base = it->second.base;
+    if (it != g_ws.end()) words.push_back((char*)it->second.base + kErrOffset);
   }
-  uint32_t v = 0;
-  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
-      hipMemcpy(&v, (char*)base + kErrOffset, 4, hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemset((char*)base + kErrOffset, 0, 4) != hipSuccess)
+  if (words.empty()) return ok();
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
     return fail(MLA_ERR_HIP, "reading the device error word failed");
-  *flags = v;
+  const uint32_t zero = 0;
+  for (void* w : words) {
+    uint32_t v = 0;
+    if (hipMemcpy(&v, w, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(w, &zero, 4, hipMemcpyHostToDevice) != hipSuccess)
+      return fail(MLA_ERR_HIP, "reading the device error word failed");
+    *flags |= v;
+  }
   return ok();
 }
+
 
 mla_status mla_profile_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = enable != 0;
+  if (g_prof_on && g_prof_ring.empty()) {
+    std::vector<mla::KernelTimer> ring;
+    ring.reserve(kProfileSlots);
+    for (int i = 0; i < kProfileSlots; ++i) {
+      mla::KernelTimer t;
+      if (hipEventCreate(&t.start) != hipSuccess) break;
+      if (hipEventCreate(&t.stop) != hipSuccess) {
+        (void)hipEventDestroy(t.start);
+        break;
+      }
+      ring.push_back(t);
+    }
+    if ((int)ring.size() != kProfileSlots) {
+      for (auto& t : ring) {
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.stop);
+      }
+      g_prof_on = false;
+      return fail(MLA_ERR_HIP, "creating the timing events failed");
+    }
+    g_prof_ring.swap(ring);
+    g_prof_live.assign(kProfileSlots, 0);
+  }
+  g_prof_used = 0;
+  g_prof_dropped = 0;
+  return ok();
+}
+
+mla_status mla_profile_read_each(double* ms_each, int64_t capacity, int64_t* launches) {
+  if (!launches || (capacity > 0 && !ms_each)) return fail(MLA_ERR_NULL_ARG, "output pointers are NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  bool bad = false;
+  int64_t n = 0;
+  for (int64_t i = 0; i < g_prof_used; ++i) {
+    if (!g_prof_live[(size_t)i]) continue;  // a slot whose launch failed
+    const auto& t = g_prof_ring[(size_t)i];
+    float ms = 0.f;
+    if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess)
+      bad = true;
+    if (n < capacity) ms_each[n] = ms;
+    ++n;
+  }
+  *launches = n;
+  const int64_t dropped = g_prof_dropped;
+  g_prof_used = 0;
+  g_prof_dropped = 0;
+  if (bad) return fail(MLA_ERR_HIP, "reading kernel timing events failed");
+  if (dropped > 0) return fail(MLA_ERR_WORKSPACE, "%lld launches past the %d timing slots were not timed",
+                               (long long)dropped, kProfileSlots);
   return ok();
 }
 
 mla_status mla_profile_read(double* total_ms, int64_t* launches) {
   if (!total_ms || !launches) return fail(MLA_ERR_NULL_ARG, "output pointers are NULL");
-  std::vector<mla::KernelTimer> ev;
-  {
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    ev.swap(g_prof_events);
-  }
+  std::vector<double> each(kProfileSlots);
+  const mla_status s = mla_profile_read_each(each.data(), (int64_t)each.size(), launches);
   double sum = 0.0;
-  bool bad = false;
-  for (auto& t : ev) {
-    float ms = 0.f;
-    if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess)
-      bad = true;
-    sum += ms;
-    (void)hipEventDestroy(t.start);
-    (void)hipEventDestroy(t.stop);
-  }
+  for (int64_t i = 0; i < *launches && i < (int64_t)each.size(); ++i) sum += each[(size_t)i];
   *total_ms = sum;
-  *launches = (int64_t)ev.size();
-  if (bad) return fail(MLA_ERR_HIP, "reading kernel timing events failed");
-  return ok();
+  return s;
 }
 
 void mla_shutdown(void) {
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    profile_destroy_ring();
+    g_prof_on = false;
+  }
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  for (auto& kv : g_ws) {
-    if (kv.second.base) {
-      int cur = 0;
-      (void)hipGetDevice(&cur);
-      (void)hipSetDevice(kv.first.first);
-      (void)hipDeviceSynchronize();
-      (void)hipFree(kv.second.base);
-      (void)hipSetDevice(cur);
-    }
+  std::vector<std::pair<int, void*>> all = g_ws_retired;
+  for (auto& kv : g_ws)
+    if (kv.second.base) all.emplace_back(kv.first.first, kv.second.base);
+  for (auto& dp : all) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(dp.first);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(dp.second);
+    (void)hipSetDevice(cur);
   }
   g_ws.clear();
+  g_ws_retired.clear();
 }
 
-mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_offsets,
-                            const mla_tensor* page_table, const mla_tensor* cache_lens,
-                            const mla_tensor* latent_cache, float scale, int32_t mask,
-                            int32_t local_window_size, int32_t num_partitions, mla_tensor* out,
-                            void* stream) {
+int32_t mla_decode_num_partitions(int64_t batch, int64_t num_heads, int64_t max_pages, int32_t page_size) {
+  if (batch < 1 || batch > kMaxRows || !supported_heads(num_heads) || max_pages < 1 || page_size < 1 ||
+      max_pages * page_size > (int64_t)1 << 30)
+    return 0;
+  return balanced_parts_per_row(batch, max_pages * page_size, cu_count(current_device()));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The dense decode.
+mla_status decode_impl(const mla_tensor* q, const mla_tensor* input_row_offsets, const mla_tensor* page_table,
+                       const mla_tensor* cache_lens, const mla_tensor* latent_cache, float scale, int32_t mask,
+                       int32_t local_window_size, int32_t num_partitions, mla_tensor* out, void* stream) {
   mla_status s;
   if ((s = check_tensor(q, "q", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
   const int64_t T = q->shape[0], H = q->shape[1];
@@ -347,12 +450,12 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
   if (T > kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 query rows");
   if (T == 0) return ok();
 
-  bool cap = false;
-  if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
   const int dev = current_device();
   const int grid = cu_count(dev);
   const int32_t nparts = num_partitions > 0 ? num_partitions : 0;
   const DecodeLayout L = decode_layout(T, (int32_t)H, nparts, grid);
+  bool cap = false;
+  if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
   void* ws = nullptr;
   if ((s = grow_workspace(dev, stream, L.total, cap, &ws)) != MLA_OK) return s;
   char* w = (char*)ws + kHeaderBytes;
@@ -387,23 +490,39 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
   a.zero_row = (const uint8_t*)ws;
   a.err = (uint32_t*)((char*)ws + kErrOffset);
   mla::KernelTimer tslot;
-  mla::KernelTimer* timer = profile_timer(&tslot);
+  int64_t tindex = -1;
+  mla::KernelTimer* timer = profile_timer(&tslot, &tindex);
   const hipError_t e = mla::launch_decode(a, (hipStream_t)stream, timer);
-  profile_keep(timer, e == hipSuccess);
+  profile_keep(timer, tindex, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
-}  // extern "C"
+}  // namespace
 
 extern "C" {
 
-mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scale,
-                                   const mla_tensor* input_row_offsets,
-                                   const mla_tensor* latent_cache, const mla_tensor* cache_scale,
-                                   const mla_tensor* d_indices, const mla_tensor* topk_lengths,
-                                   float scale, int32_t num_partitions, mla_tensor* out,
-                                   void* stream) {
+mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_offsets,
+                            const mla_tensor* page_table, const mla_tensor* cache_lens,
+                            const mla_tensor* latent_cache, float scale, int32_t mask,
+                            int32_t local_window_size, int32_t num_partitions, mla_tensor* out,
+                            void* stream) {
+  return decode_impl(q, input_row_offsets, page_table, cache_lens, latent_cache, scale, mask, local_window_size,
+                     num_partitions, out, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The sparse decode with its optional parts: sink logits and a second stream (null = none).
+mla_status sparse_impl(const mla_tensor* q, const mla_tensor* q_scale, const mla_tensor* input_row_offsets,
+                       const mla_tensor* latent_cache, const mla_tensor* cache_scale,
+                       const mla_tensor* d_indices, const mla_tensor* topk_lengths,
+                       const mla_tensor* attn_sink, const mla_tensor* extra_cache,
+                       const mla_tensor* extra_cache_scale, const mla_tensor* extra_d_indices,
+                       const mla_tensor* extra_topk_lengths, float scale, int32_t num_partitions,
+                       mla_tensor* out, void* stream) {
   mla_status s;
   if (!q) return fail(MLA_ERR_NULL_ARG, "q: descriptor is NULL");
   const bool q_bf16 = q->dtype == MLA_DTYPE_BF16;
@@ -443,6 +562,41 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
   if (out->shape[0] != T || out->shape[1] != H || out->shape[2] != 512)
     return fail(MLA_ERR_SHAPE, "out: shape must be [%lld, %lld, 512]", (long long)T, (long long)H);
   if (!supported_heads(H)) return fail(MLA_ERR_UNSUPPORTED, "num_heads %lld not in {16, 32, 64, 128}", (long long)H);
+  if (attn_sink && (s = check_1d(attn_sink, "attn_sink", MLA_DTYPE_F32, H)) != MLA_OK) return s;
+  // the second stream: all four descriptors or none of its index parts
+  const bool xtra = extra_d_indices != nullptr || extra_topk_lengths != nullptr || extra_cache != nullptr;
+  int64_t XNP = 0, XPS = 0;
+  if (xtra) {
+    if (!extra_d_indices || !extra_topk_lengths || !extra_cache)
+      return fail(MLA_ERR_NULL_ARG, "the extra stream needs extra_cache, extra_d_indices and extra_topk_lengths");
+    if ((s = check_tensor(extra_cache, "extra_cache", MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
+    if (extra_cache->shape[2] != 576)
+      return fail(MLA_ERR_SHAPE, "extra_cache: row width %lld, expected 576", (long long)extra_cache->shape[2]);
+    XNP = extra_cache->shape[0];
+    XPS = extra_cache->shape[1];
+    if (XPS < 1) return fail(MLA_ERR_SHAPE, "extra_cache: page size must be >= 1");
+    if (XNP > 0 && XPS > 1 && extra_cache->stride[1] != 576)
+      return fail(MLA_ERR_SHAPE, "extra_cache: rows of a page must be contiguous (stride 576)");
+    if (XNP > 1 && extra_cache->stride[0] < XPS * 576)
+      return fail(MLA_ERR_SHAPE, "extra_cache: pages overlap (page stride below page_size * 576)");
+    if (extra_cache_scale) {
+      if ((s = check_tensor(extra_cache_scale, "extra_cache_scale", MLA_DTYPE_F32, 2, false)) != MLA_OK) return s;
+      if (extra_cache_scale->shape[0] != XNP || extra_cache_scale->shape[1] != XPS)
+        return fail(MLA_ERR_SHAPE, "extra_cache_scale: shape must be [%lld, %lld]", (long long)XNP, (long long)XPS);
+    }
+    if ((s = check_tensor(extra_d_indices, "extra_d_indices", MLA_DTYPE_I32, 2, false)) != MLA_OK) return s;
+    if (extra_d_indices->shape[0] != T)
+      return fail(MLA_ERR_SHAPE, "extra_d_indices: %lld rows, expected %lld", (long long)extra_d_indices->shape[0], (long long)T);
+    if (extra_d_indices->shape[1] > INT32_MAX / 2 || d_indices->shape[1] > INT32_MAX / 2)
+      return fail(MLA_ERR_UNSUPPORTED, "index lists too wide for two streams");
+    if (T > 1 && extra_d_indices->stride[0] < extra_d_indices->shape[1])
+      return fail(MLA_ERR_SHAPE, "extra_d_indices: row stride below the row length");
+    if ((s = check_1d(extra_topk_lengths, "extra_topk_lengths", MLA_DTYPE_I32, T)) != MLA_OK) return s;
+    if (NP * PS >= (int64_t)mla::kExtraRowBit || XNP * XPS >= (int64_t)mla::kExtraRowBit)
+      return fail(MLA_ERR_UNSUPPORTED, "with an extra stream each pool holds fewer than 2^30 rows");
+  } else if (extra_cache_scale) {
+    return fail(MLA_ERR_VALUE, "extra_cache_scale given without an extra stream");
+  }
   if (!std::isfinite(scale)) return fail(MLA_ERR_VALUE, "scale must be finite");
   if (num_partitions > 4096) return fail(MLA_ERR_VALUE, "num_partitions %d above 4096", num_partitions);
   if (T > kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 query rows");
@@ -488,12 +642,55 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
   a.row_meta = (int32_t*)(w + L.meta);
   a.zero_row = (const uint8_t*)ws;
   a.err = (uint32_t*)((char*)ws + kErrOffset);
+  a.sink = attn_sink ? (const float*)attn_sink->data : nullptr;
+  if (xtra) {
+    a.flat = 0;  // rows of both pools go through the per-row address path
+    a.xidx = (const int32_t*)extra_d_indices->data;
+    a.xidx_row = extra_d_indices->stride[0];
+    a.xidx_cols = (int32_t)extra_d_indices->shape[1];
+    a.xtopk = (const int32_t*)extra_topk_lengths->data;
+    a.xcache = (const uint8_t*)extra_cache->data;
+    a.xpage_bytes = extra_cache->stride[0];
+    a.xcache_scale = extra_cache_scale ? (const float*)extra_cache_scale->data : nullptr;
+    a.xcs_page = extra_cache_scale ? extra_cache_scale->stride[0] : 0;
+    a.xnum_rows = XNP * XPS;
+    a.xPS = (int32_t)XPS;
+  }
   mla::KernelTimer tslot;
-  mla::KernelTimer* timer = profile_timer(&tslot);
+  int64_t tindex = -1;
+  mla::KernelTimer* timer = profile_timer(&tslot, &tindex);
   const hipError_t e = mla::launch_sparse(a, (hipStream_t)stream, timer);
-  profile_keep(timer, e == hipSuccess);
+  profile_keep(timer, tindex, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "sparse decode launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scale,
+                                   const mla_tensor* input_row_offsets,
+                                   const mla_tensor* latent_cache, const mla_tensor* cache_scale,
+                                   const mla_tensor* d_indices, const mla_tensor* topk_lengths,
+                                   float scale, int32_t num_partitions, mla_tensor* out,
+                                   void* stream) {
+  return sparse_impl(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices, topk_lengths, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, scale, num_partitions, out, stream);
+}
+
+mla_status mla_decode_paged_sparse_ext(const mla_tensor* q, const mla_tensor* q_scale,
+                                       const mla_tensor* input_row_offsets,
+                                       const mla_tensor* latent_cache, const mla_tensor* cache_scale,
+                                       const mla_tensor* d_indices, const mla_tensor* topk_lengths,
+                                       const mla_tensor* attn_sink, const mla_tensor* extra_cache,
+                                       const mla_tensor* extra_cache_scale,
+                                       const mla_tensor* extra_d_indices,
+                                       const mla_tensor* extra_topk_lengths, float scale,
+                                       int32_t num_partitions, mla_tensor* out, void* stream) {
+  return sparse_impl(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices, topk_lengths, attn_sink,
+                     extra_cache, extra_cache_scale, extra_d_indices, extra_topk_lengths, scale, num_partitions,
+                     out, stream);
 }
 
 mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
@@ -586,9 +783,10 @@ mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
   a.zero_row = (const uint8_t*)ws;
   a.err = (uint32_t*)((char*)ws + kErrOffset);
   mla::KernelTimer tslot;
-  mla::KernelTimer* timer = profile_timer(&tslot);
+  int64_t tindex = -1;
+  mla::KernelTimer* timer = profile_timer(&tslot, &tindex);
   const hipError_t e = mla::launch_sparse(a, (hipStream_t)stream, timer);
-  profile_keep(timer, e == hipSuccess);
+  profile_keep(timer, tindex, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "fp8 decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -678,9 +876,10 @@ mla_status mla_indexer_paged_fp8(const mla_tensor* q, const mla_tensor* q_s,
   a.out_row = out_indices->stride[0];
   a.err = (uint32_t*)((char*)ws + kErrOffset);
   mla::KernelTimer tslot;
-  mla::KernelTimer* timer = profile_timer(&tslot);
+  int64_t tindex = -1;
+  mla::KernelTimer* timer = profile_timer(&tslot, &tindex);
   const hipError_t e = mla::launch_indexer(a, (hipStream_t)stream, timer);
-  profile_keep(timer, e == hipSuccess);
+  profile_keep(timer, tindex, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "indexer launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -764,9 +963,10 @@ mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla
   a.zero_row = (const uint8_t*)ws;
   a.err = (uint32_t*)((char*)ws + kErrOffset);
   mla::KernelTimer tslot;
-  mla::KernelTimer* timer = profile_timer(&tslot);
+  int64_t tindex = -1;
+  mla::KernelTimer* timer = profile_timer(&tslot, &tindex);
   const hipError_t e = mla::launch_prefill(a, (hipStream_t)stream, timer);
-  profile_keep(timer, e == hipSuccess);
+  profile_keep(timer, tindex, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -280,10 +280,10 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, MLA_LDS uint
     // every wave is done with the stage buffers before they take the output rows
     stage_barrier();
     stage_epilogue2(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse,
-                    tiles + wave * 32 * 1024);
+                    tiles + wave * 32 * 1024, nullptr);
   }
   else
-    stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
+    stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse, nullptr);
 }
 
 // SMALL: balanced batch of at most 64 rows and 64 sequences, no more rows than work-groups
@@ -363,6 +363,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const SplitPlan p) {
     *(uint4*)dst = make_uint4(0, 0, 0, 0);
     return;
   }
+  // a sink logit weighs into the denominator only (it carries no value)
+  if (p.sink != nullptr) den += fast_exp2(p.sink[h] * 1.4426950408889634f - M);
   const float inv = 1.f / den;
   uint32_t wd[4];
 #pragma unroll
@@ -396,6 +398,7 @@ static SplitPlan plan_of(const DecodeArgs& a) {
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
   p.row_meta = a.row_meta;
+  p.sink = nullptr;
   return p;
 }
 

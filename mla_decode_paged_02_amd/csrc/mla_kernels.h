@@ -77,7 +77,23 @@ struct SparseArgs {
   int32_t* row_meta;
   const uint8_t* zero_row;    // >= 1152 zero bytes
   uint32_t* err;
+  // Extended sparse decode only (the kernels' EXT variant): sink logits, and a second
+  // stream (xidx null = none) -- row t also attends to the rows its second list names in a
+  // second fp8 pool, under the same softmax.  Both pools then hold fewer than 2^30 rows (a
+  // second-pool row is marked by kExtraRowBit in the index window).
+  const float* sink;          // [H] sink logits (natural-log units), or null
+  const int32_t* xidx;        // [T, xidx_row]
+  int64_t xidx_row;
+  int32_t xidx_cols;
+  const int32_t* xtopk;       // [T]
+  const uint8_t* xcache;      // fp8 e4m3 [x pages, xPS, 576]
+  int64_t xpage_bytes;
+  const float* xcache_scale;  // [x pages, xPS] or null (= 1)
+  int64_t xcs_page;
+  int64_t xnum_rows;
+  int32_t xPS;
 };
+constexpr int32_t kExtraRowBit = 1 << 30;
 
 // Ragged prefill with per-head keys and values.
 struct PrefillArgs {
@@ -142,6 +158,7 @@ struct SplitPlan {
   uint16_t* part_o;   // bf16 [slots, H, 512]
   float* part_lse;    // [slots, H]
   int32_t* row_meta;  // [2 + 2T]: the split rows' layout (mla_plan.h)
+  const float* sink;  // [H] sink logits merged into split rows' denominators, or null
 };
 
 // Workspace needs of the split-KV paths.

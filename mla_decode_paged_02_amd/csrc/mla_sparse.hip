@@ -43,15 +43,26 @@ constexpr int kSpStageLds = kSpTiles * kStageBytes + kSpRaw * kRawStageBytes;
 constexpr int kSpLdsBytes = kSpStageLds > 4 * 32 * 1024 ? kSpStageLds : 4 * 32 * 1024;
 static_assert(sizeof(PlanLds::scan) == kIdxWindow * sizeof(int), "the window lives in the planning scratch");
 
-// Row t's list positions [0, min(topk[t], shape[1] of d_indices)).
+// Row t's list positions [0, n): its first min(topk[t], shape[1] of d_indices) entries,
+// then (EXT with a second stream) the first min(xtopk[t], its width) entries of its second
+// list.
+__device__ __forceinline__ int sparse_main_len(const SparseArgs& a, int t) {
+  return max(0, min(ld_const(a.topk + t), a.idx_cols));
+}
+template <bool XTRA>
+__device__ __forceinline__ int sparse_len(const SparseArgs& a, int t) {
+  int n = sparse_main_len(a, t);
+  if (XTRA && a.xidx != nullptr) n += max(0, min(ld_const(a.xtopk + t), a.xidx_cols));
+  return n;
+}
+template <bool XTRA>
 __device__ __forceinline__ RowGeo sparse_row_geo(const SparseArgs& a, int t) {
-  const int k = ld_const(a.topk + t);
-  return RowGeo{t, 0, max(0, min(k, a.idx_cols))};
+  return RowGeo{t, 0, sparse_len<XTRA>(a, t)};
 }
 
-template <int NT>
+template <int NT, bool XTRA>
 __device__ __forceinline__ void sparse_fill(const SparseArgs& a, PlanLds& L) {
-  for (int t = threadIdx.x; t < a.T; t += NT) L.geo[t] = RowGeo{t, 0, max(0, min(a.topk[t], a.idx_cols))};
+  for (int t = threadIdx.x; t < a.T; t += NT) L.geo[t] = RowGeo{t, 0, sparse_len<XTRA>(a, t)};
 }
 
 // One row segment: list positions of tiles [ta, tc) of row t.
@@ -61,8 +72,10 @@ __device__ __forceinline__ void sparse_fill(const SparseArgs& a, PlanLds& L) {
 // landing buffer stage k was widened from, then computes stage k from its bf16 tile while
 // the hook of the score k-steps widens stage k+1 into the other tile.  One barrier per
 // stage orders all of it.
-// DENSE: rows from the page table (mla_decode_paged_fp8), else from d_indices.
-template <int HB, int NW, bool DENSE>
+// DENSE: rows from the page table (mla_decode_paged_fp8), else from d_indices.  XTRA (the
+// extended sparse decode): the sink logits, and the second list when there is one, whose
+// rows are held in the window with kExtraRowBit set.
+template <int HB, int NW, bool DENSE, bool XTRA>
 __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint8_t* tiles, MLA_LDS uint8_t* raw,
                                                MLA_LDS float* kscale, MLA_LDS int* win, int t, const RowGeo& g,
                                                int ta, int tc, bool full, int slot) {
@@ -83,6 +96,9 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   const int s_first = klo / kStageKeys;
   const int nst = (khi - 1) / kStageKeys - s_first + 1;
   const int32_t* ilist = a.idx + (int64_t)t * a.idx_row;
+  // XTRA: positions from nmain on are the second list's (block-uniform)
+  const int nmain = XTRA && a.xidx != nullptr ? __builtin_amdgcn_readfirstlane(sparse_main_len(a, t)) : INT32_MAX;
+  const int32_t* xlist = XTRA ? a.xidx + (int64_t)t * a.xidx_row : nullptr;
   // dense: the page-table row of the sequence (g.b), list position p = logical key p
   const int32_t* prow = DENSE ? a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.pt_row : nullptr;
   const int npages32 = (int)min(a.num_rows / a.PS, (int64_t)INT32_MAX);
@@ -101,13 +117,26 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
 #pragma unroll
     for (int i = 0; i < kIdxWindow / NT; ++i) {
       const int p = wbase + tid + i * NT;
-      v[i] = p < khi ? (DENSE ? prow[p / a.PS] : ilist[p]) : -1;
+      if (XTRA)
+        v[i] = p < khi ? (p < nmain ? ilist[p] : xlist[p - nmain]) : -1;
+      else
+        v[i] = p < khi ? (DENSE ? prow[p / a.PS] : ilist[p]) : -1;
     }
     all_wait0();
 #pragma unroll
     for (int i = 0; i < kIdxWindow / NT; ++i) {
       int r = v[i];
-      if (DENSE) {
+      if (XTRA && wbase + tid + i * NT >= nmain) {
+        // a second-stream row: checked against its own pool, then marked
+        if (r >= 0) {
+          if ((int64_t)r >= a.xnum_rows) {
+            bad = true;
+            r = -1;
+          } else {
+            r |= kExtraRowBit;
+          }
+        }
+      } else if (DENSE) {
         // page id -> physical row; a page outside the pool is skipped and flagged
         const int p = wbase + tid + i * NT;
         if (p < khi) {
@@ -132,12 +161,21 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   // listed row of position p (read from the window), -1 when the key does not count
   auto entry = [&](int p) -> int { return p >= klo && p < khi ? win[p - wbase] : -1; };
   auto row_src = [&](int r) -> const uint8_t* {
+    if (XTRA && (r & kExtraRowBit)) {
+      const int rx = r & ~kExtraRowBit, pg = rx / a.xPS;
+      return a.xcache + (int64_t)pg * a.xpage_bytes + (int64_t)(rx - pg * a.xPS) * kRawRowBytes;
+    }
     if (a.flat) return a.cache + (int64_t)r * kRawRowBytes;
     const int pg = r / a.PS;
     return a.cache + (int64_t)pg * a.page_bytes + (int64_t)(r - pg * a.PS) * kRawRowBytes;
   };
   auto scale_src = [&](int r) -> const void* {
     if (r < 0) return a.zero_row;  // a key that does not count: weight 0
+    if (XTRA && (r & kExtraRowBit)) {
+      if (a.xcache_scale == nullptr) return a.zero_row + kSparseOneOffset;
+      const int rx = r & ~kExtraRowBit, pg = rx / a.xPS;
+      return a.xcache_scale + (int64_t)pg * a.xcs_page + (rx - pg * a.xPS);
+    }
     if (a.cache_scale == nullptr) return a.zero_row + kSparseOneOffset;
     if (a.flat) return a.cache_scale + r;
     const int pg = r / a.PS;
@@ -363,15 +401,16 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
     // every wave is done with the stage buffers before they take the output rows
     stage_barrier();
     stage_epilogue2(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse,
-                    tiles + wave * 32 * 1024);
+                    tiles + wave * 32 * 1024, XTRA ? a.sink : nullptr);
   }
   else
-    stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse);
+    stage_epilogue<HB>(acc, lane, h0, t, full, slot, a.H, a.out, a.o_tok, a.o_head, a.part_o, a.part_lse,
+                       XTRA ? a.sink : nullptr);
 }
 
 // SMALL: balanced batch of at most 64 rows, no more rows than work-groups (planned per
 // wave, see plan_run).
-template <int HB, int NW, bool SMALL, bool DENSE>
+template <int HB, int NW, bool SMALL, bool DENSE, bool XTRA>
 __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs a, const SplitPlan plan) {
   // the widened tiles, then the fp8 landing buffers
   __shared__ __attribute__((aligned(1024))) uint8_t buf_raw[kSpLdsBytes];
@@ -383,17 +422,17 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs
   plan_run<NW * 64, SMALL>(
       plan, L,
       [&](PlanLds& l) {
-        if constexpr (DENSE) decode_fill<NW * 64>(a, l); else sparse_fill<NW * 64>(a, l);
+        if constexpr (DENSE) decode_fill<NW * 64>(a, l); else sparse_fill<NW * 64, XTRA>(a, l);
       },
       [&](int t) {
-        if constexpr (DENSE) return decode_row_geo(a, t); else return sparse_row_geo(a, t);
+        if constexpr (DENSE) return decode_row_geo(a, t); else return sparse_row_geo<XTRA>(a, t);
       },
       [&](RowGeo* geo, int lane) {
         if constexpr (DENSE) decode_fill_wave(a, geo, lane);
-        else if (lane < a.T) geo[lane] = RowGeo{lane, 0, max(0, min(a.topk[lane], a.idx_cols))};
+        else if (lane < a.T) geo[lane] = RowGeo{lane, 0, sparse_len<XTRA>(a, lane)};
       },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
-        sparse_segment<HB, NW, DENSE>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
+        sparse_segment<HB, NW, DENSE, XTRA>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
       });
 }
 
@@ -412,6 +451,7 @@ static SplitPlan plan_of(const SparseArgs& a) {
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
   p.row_meta = a.row_meta;
+  p.sink = a.sink;
   return p;
 }
 
@@ -420,11 +460,14 @@ static hipError_t launch_sparse_h(const SparseArgs& a, const SplitPlan& p, hipSt
   const dim3 grid(a.nparts >= 1 ? a.T * a.nparts : a.grid), block(NW * 64);
   const bool small = a.nparts == 0 && a.T <= 64 && a.T <= a.grid && (!a.dense || a.B <= 64);
   if (a.dense) {
-    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, true>), grid, block, 0, stream, a, p);
-    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, true>), grid, block, 0, stream, a, p);
+    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, true, false>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, true, false>), grid, block, 0, stream, a, p);
+  } else if (a.xidx != nullptr || a.sink != nullptr) {
+    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, false, true>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, false, true>), grid, block, 0, stream, a, p);
   } else {
-    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, false>), grid, block, 0, stream, a, p);
-    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, false>), grid, block, 0, stream, a, p);
+    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, false, false>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, false, false>), grid, block, 0, stream, a, p);
   }
   return hipGetLastError();
 }

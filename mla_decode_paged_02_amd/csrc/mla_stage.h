@@ -204,18 +204,27 @@ __device__ __forceinline__ void stage_compute(const MLA_LDS uint8_t* buf, const 
   }
 }
 
+// The reciprocal of a finished row's softmax denominator: this wave's summed weights l_tot
+// (relative to the running max m, log2 units), plus e^sink of the head's sink logit when
+// there is one (that weight carries no value).  0 when nothing was weighed.
+__device__ __forceinline__ float row_inverse(float l_tot, float m, const float* sink, int h) {
+  float den = l_tot;
+  if (sink != nullptr) den += fast_exp2(sink[h] * 1.4426950408889634f - m);  // +inf while m is -inf
+  return den > 0.f ? 1.f / den : 0.f;
+}
+
 // Writes the wave's heads h0 + 16hb + n of row t: final bf16 output, or the normalised
-// partial and its log2-sum-exp into `slot`.
+// partial and its log2-sum-exp into `slot` (a split row's sink joins in the combine).
 template <int HB>
 __device__ __forceinline__ void stage_epilogue(const WaveAcc<HB>& acc, int lane, int h0, int t, bool full,
                                                int slot, int H, uint16_t* out, int64_t o_tok, int64_t o_head,
-                                               uint16_t* part_o, float* part_lse) {
+                                               uint16_t* part_o, float* part_lse, const float* sink) {
   const int gq = lane >> 4, ln = lane & 15;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const float l_tot = wave_sum_xor16_32(acc.l[hb]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int h = h0 + 16 * hb + ln;
+    const float inv = full ? row_inverse(l_tot, acc.m[hb], sink, h) : (l_tot > 0.f ? 1.f / l_tot : 0.f);
     // the final row, or a split row's normalised part (bf16 as well) and its log2-sum-exp
     uint16_t* orow = full ? out + (int64_t)t * o_tok + (int64_t)h * o_head + 4 * gq
                           : part_o + ((int64_t)slot * H + h) * kLatentDim + 4 * gq;
@@ -401,14 +410,15 @@ __device__ __forceinline__ void stage_compute2(const MLA_LDS uint8_t* buf, const
 // XOR-swizzled in 16-byte units so the transposing writes spread over the banks.
 __device__ __forceinline__ void stage_epilogue2(WaveAcc2& acc, int lane, int h0, int t, bool full, int slot,
                                                 int H, uint16_t* out, int64_t o_tok, int64_t o_head,
-                                                uint16_t* part_o, float* part_lse, MLA_LDS uint8_t* stage) {
+                                                uint16_t* part_o, float* part_lse, MLA_LDS uint8_t* stage,
+                                                const float* sink) {
   mfma_fence_acc(acc.o);
   const int gq = lane >> 4, ln = lane & 15;
   float inv[2];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const float l_tot = wave_sum_xor16_32(acc.l[hb]);
-    inv[hb] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    inv[hb] = full ? row_inverse(l_tot, acc.m[hb], sink, h0 + 16 * hb + ln) : (l_tot > 0.f ? 1.f / l_tot : 0.f);
     if (!full && gq == 0)
       part_lse[(int64_t)slot * H + h0 + 16 * hb + ln] = l_tot > 0.f ? acc.m[hb] + __log2f(l_tot) : -INFINITY;
   }

@@ -336,3 +336,48 @@ def test_profile_read_each_without_launches():
         assert m.profile_read_each() == []
     finally:
         m.profile_enable(False)
+
+
+def call_sparse_ext(a, sink=None, xcache=None, xcs=None, xidx=None, xtopk=None):
+    lib = m.library()
+    ref = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    st = lib.mla_decode_paged_sparse_ext(ref(a["q"]), ref(a["qs"]), ref(a["off"]), ref(a["cache"]),
+                                         ref(a["cs"]), ref(a["idx"]), ref(a["topk"]), ref(sink), ref(xcache),
+                                         ref(xcs), ref(xidx), ref(xtopk), ctypes.c_float(a["scale"]),
+                                         a["parts"], ref(a["out"]), None)
+    return st, lib.mla_last_error_message().decode()
+
+
+def _xstream(**over):
+    T = 4
+    x = dict(xcache=_t(FAKE, 1, (6, 16, 576)), xcs=_t(FAKE, 2, (6, 16)), xidx=_t(FAKE, 3, (T, 20)),
+             xtopk=_t(FAKE, 3, (T,)))
+    x.update(over)
+    return x
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sink=_t(FAKE, 2, (15,))), 2),                                   # sink per head
+    (dict(sink=_t(FAKE, 3, (16,))), 3),                                   # sink dtype
+    (dict(xcache=_t(FAKE, 1, (6, 16, 576))), 1),                          # pool without lists
+    (dict(xidx=_t(FAKE, 3, (4, 20)), xtopk=_t(FAKE, 3, (4,))), 1),         # lists without a pool
+    (dict(xcs=_t(FAKE, 2, (6, 16))), 8),                                  # scales without a stream
+    (_xstream(xcache=_t(FAKE, 0, (6, 16, 576))), 3),                      # bf16 second pool
+    (_xstream(xcs=_t(FAKE, 2, (6, 8))), 2),                               # second-pool scale shape
+    (_xstream(xidx=_t(FAKE, 3, (3, 20))), 2),                             # second-list rows != q rows
+    (_xstream(xtopk=_t(FAKE, 3, (5,))), 2),                               # second topk length
+    (_xstream(xcache=_t(FAKE, 1, (1 << 26, 16, 576)), xcs=None), 5),      # second pool of 2^30 rows
+])
+def test_sparse_ext_validation(kw, status):
+    st, msg = call_sparse_ext(sparse_args(), **kw)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_sparse_ext_empty_batch_is_a_no_op():
+    a = sparse_args(q=_t(FAKE, 1, (0, 16, 576)), qs=_t(FAKE, 2, (0,)), idx=_t(FAKE, 3, (0, 32)),
+                    topk=_t(FAKE, 3, (0,)), out=_t(FAKE, 0, (0, 16, 512)))
+    st, _ = call_sparse_ext(a, sink=_t(FAKE, 2, (16,)), **_xstream(xidx=_t(FAKE, 3, (0, 20)),
+                                                                    xtopk=_t(FAKE, 3, (0,))))
+    assert st == 0
+
