@@ -271,6 +271,30 @@ mla_status mla_prefill_paged(const mla_tensor* q, const mla_tensor* k, const mla
 int32_t mla_decode_num_partitions(int64_t batch, int64_t num_heads, int64_t max_pages,
                                   int32_t page_size);
 
+/*
+ * mla_decode_paged without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops that forbid hipMalloc.  Same
+ * arguments, results and errors as mla_decode_paged; the split-KV workspace is a fixed
+ * array of mla_decode_noalloc_scratch_bytes() bytes of device memory that the library
+ * holds on each GPU it runs on until the process ends (65.5 MiB: the balanced split of up
+ * to 128 heads over up to 256 compute units, or a fixed split of up to 512 part slots of
+ * 128 heads, and a split table of up to 2^16 query rows).  A call needing more returns
+ * MLA_ERR_WORKSPACE before launching anything.  The call never allocates (no hipMalloc,
+ * no hipFree); its first call on a device looks the array up and clears its header with a
+ * kernel on `stream` (outside capture it then synchronises `stream` once).  Every call on
+ * one GPU shares that array: calls that overlap in time on one GPU (different streams, or
+ * graph replays running concurrently) race and must not be issued.  Its device error word
+ * is read and cleared by mla_check_device_errors (any stream of the device).
+ */
+mla_status mla_decode_paged_noalloc(const mla_tensor* q, const mla_tensor* input_row_offsets,
+                                    const mla_tensor* page_table, const mla_tensor* cache_lens,
+                                    const mla_tensor* latent_cache, float scale, int32_t mask,
+                                    int32_t local_window_size, int32_t num_partitions,
+                                    mla_tensor* out, void* stream);
+
+/* Size in bytes of the per-GPU array mla_decode_paged_noalloc works in (host only). */
+size_t mla_decode_noalloc_scratch_bytes(void);
+
 /* Workspace bytes a decode call with these sizes needs (host only, no device access).
  * num_partitions as in mla_decode_paged; device selects the CU count (-1 = current). */
 size_t mla_decode_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t num_partitions,
@@ -280,7 +304,8 @@ size_t mla_decode_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t nu
  * not allowed while `stream` is capturing).  device -1 = the current device. */
 mla_status mla_reserve_workspace(int32_t device, void* stream, size_t bytes);
 
-/* Synchronise `stream`, read and clear the device error word of (device, stream):
+/* Synchronise `stream`, read and clear the device error word of (device, stream), and of
+ * the device's no-allocation scratch array once mla_decode_paged_noalloc has run there:
  * bit 0 a page id outside [0, num_pages) was met, bit 1 a sparse index outside the
  * pool, bit 2 offsets that decrease or exceed the q rows, bit 3 a cache length above
  * max_pages * PS.  *flags receives the word (0 = clean). */

@@ -12,7 +12,8 @@ import ctypes
 import os
 
 __all__ = [
-    "LIBRARY_PATH", "MlaError", "library", "decode_paged", "decode_paged_sparse",
+    "LIBRARY_PATH", "MlaError", "library", "decode_paged", "decode_paged_noalloc",
+    "decode_noalloc_scratch_bytes", "decode_paged_sparse",
     "decode_paged_sparse_ext", "decode_paged_fp8", "indexer_paged_fp8", "prefill_paged", "decode_num_partitions",
     "decode_workspace_bytes", "reserve_workspace", "check_device_errors", "shutdown",
     "version", "profile_enable", "profile_read", "profile_read_each", "MASKS", "STATUS",
@@ -51,12 +52,15 @@ def library() -> ctypes.CDLL:
         P = ctypes.POINTER(MlaTensor)
         i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
         lib.mla_decode_paged.argtypes = [P, P, P, P, P, f32, i32, i32, i32, P, vp]
+        lib.mla_decode_paged_noalloc.argtypes = [P, P, P, P, P, f32, i32, i32, i32, P, vp]
+        lib.mla_decode_noalloc_scratch_bytes.argtypes = []
+        lib.mla_decode_noalloc_scratch_bytes.restype = ctypes.c_size_t
         lib.mla_decode_paged_sparse.argtypes = [P, P, P, P, P, P, P, f32, i32, P, vp]
         lib.mla_decode_paged_sparse_ext.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, f32, i32, P, vp]
         lib.mla_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, f32, i32, i32, i32, P, vp]
         lib.mla_indexer_paged_fp8.argtypes = [P, P, P, P, P, P, P, i32, i32, P, vp]
         lib.mla_prefill_paged.argtypes = [P, P, P, P, P, P, P, P, P, f32, i32, P, vp]
-        for fn in ("mla_decode_paged", "mla_decode_paged_sparse", "mla_decode_paged_sparse_ext", "mla_decode_paged_fp8", "mla_indexer_paged_fp8", "mla_prefill_paged",
+        for fn in ("mla_decode_paged", "mla_decode_paged_noalloc", "mla_decode_paged_sparse", "mla_decode_paged_sparse_ext", "mla_decode_paged_fp8", "mla_indexer_paged_fp8", "mla_prefill_paged",
                    "mla_reserve_workspace", "mla_check_device_errors"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_decode_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32, i32]
@@ -151,6 +155,26 @@ def decode_paged(q, input_row_offsets, page_table, cache_lens, latent_cache, sca
         _desc(latent_cache), float(scale), MASKS[mask] if isinstance(mask, str) else int(mask),
         int(local_window_size), int(num_partitions), _desc(out), _stream(stream)))
     return out
+
+
+def decode_paged_noalloc(q, input_row_offsets, page_table, cache_lens, latent_cache, scale,
+                         mask="causal", local_window_size=-1, num_partitions=0, out=None, stream=None):
+    """decode_paged through mla_decode_paged_noalloc (the library allocates nothing; its
+    workspace is a fixed per-GPU array).  `out` should be given by callers that cannot
+    allocate; without it one is allocated here, by torch."""
+    import torch
+    _on_gpu(q, input_row_offsets, page_table, cache_lens, latent_cache, out)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
+    _check(library().mla_decode_paged_noalloc(
+        _desc(q), _offsets(input_row_offsets), _desc(page_table), _desc(cache_lens),
+        _desc(latent_cache), float(scale), MASKS[mask] if isinstance(mask, str) else int(mask),
+        int(local_window_size), int(num_partitions), _desc(out), _stream(stream)))
+    return out
+
+
+def decode_noalloc_scratch_bytes() -> int:
+    return int(library().mla_decode_noalloc_scratch_bytes())
 
 
 def decode_paged_sparse(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices,

@@ -245,6 +245,53 @@ DecodeLayout decode_layout(int64_t T, int32_t H, int32_t nparts, int32_t grid) {
   return L;
 }
 
+// ---------------------------------------------------------------------------------------
+// No-allocation variant: the dense decode's workspace in a fixed array of device memory
+// (per GPU, for the life of the process), for callers that cannot allocate (graph
+// capture, serving loops that forbid hipMalloc).  Its layout is the stream workspace's:
+// the header (zero row, error word) and then the split parts.  The limit covers the
+// balanced split of up to 128 heads over up to 256 compute units (512 part slots of
+// 128 x 512 bf16) and the split table of up to 2^16 query rows.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = ((size_t)65 << 20) + ((size_t)1 << 19);  // 65.5 MiB
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void scratch_header_init(uint8_t* base) {
+  // the zero row and the error word start cleared
+  for (int i = threadIdx.x; i < (int)(kHeaderBytes / 16); i += blockDim.x)
+    reinterpret_cast<uint4*>(base)[i] = make_uint4(0, 0, 0, 0);
+}
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;  // device address of `scratch` on each device
+std::map<int, bool> g_scratch_ready; // header cleared (by a call outside capture)
+
+// The device address of this device's scratch array, its header cleared before any work
+// the caller queues next on `stream`.
+mla_status scratch_base(int device, void* stream, bool capturing, void** base) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(device);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+    it = g_scratch_ptr.emplace(device, ptr).first;
+  }
+  if (!g_scratch_ready[device]) {
+    // a kernel, not a memset: the clear may be captured into a graph
+    hipLaunchKernelGGL(scratch_header_init, dim3(1), dim3(256), 0, (hipStream_t)stream, (uint8_t*)it->second);
+    if (hipGetLastError() != hipSuccess) return fail(MLA_ERR_HIP, "clearing the scratch header failed");
+    if (!capturing) {
+      if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return fail(MLA_ERR_HIP, "clearing the scratch header failed");
+      g_scratch_ready[device] = true;
+    }
+  }
+  *base = it->second;
+  return MLA_OK;
+}
+
 }  // namespace
 
 namespace mla {
@@ -296,11 +343,18 @@ mla_status mla_check_device_errors(int32_t device, void* stream, uint32_t* flags
   if (!flags) return fail(MLA_ERR_NULL_ARG, "flags is NULL");
   *flags = 0;
   const int dev = device < 0 ? current_device() : device;
+  // the stream's workspace and, when the no-allocation decode has run on this device, the
+  // scratch array's header
   std::vector<void*> words;
   {
     std::lock_guard<std::mutex> lk(g_ws_mu);
     auto it = g_ws.find({dev, stream});
     if (it != g_ws.end()) words.push_back((char*)it->second.base + kErrOffset);
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end() && g_scratch_ready[dev]) words.push_back((char*)it->second + kErrOffset);
   }
   if (words.empty()) return ok();
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
@@ -316,6 +370,7 @@ mla_status mla_check_device_errors(int32_t device, void* stream, uint32_t* flags
   return ok();
 }
 
+size_t mla_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 mla_status mla_profile_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -415,10 +470,11 @@ int32_t mla_decode_num_partitions(int64_t batch, int64_t num_heads, int64_t max_
 
 namespace {
 
-// The dense decode.
+// The dense decode; fixed_ws selects the scratch array instead of the stream workspace.
 mla_status decode_impl(const mla_tensor* q, const mla_tensor* input_row_offsets, const mla_tensor* page_table,
                        const mla_tensor* cache_lens, const mla_tensor* latent_cache, float scale, int32_t mask,
-                       int32_t local_window_size, int32_t num_partitions, mla_tensor* out, void* stream) {
+                       int32_t local_window_size, int32_t num_partitions, mla_tensor* out, void* stream,
+                       bool fixed_ws) {
   mla_status s;
   if ((s = check_tensor(q, "q", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
   const int64_t T = q->shape[0], H = q->shape[1];
@@ -454,10 +510,17 @@ mla_status decode_impl(const mla_tensor* q, const mla_tensor* input_row_offsets,
   const int grid = cu_count(dev);
   const int32_t nparts = num_partitions > 0 ? num_partitions : 0;
   const DecodeLayout L = decode_layout(T, (int32_t)H, nparts, grid);
+  if (fixed_ws && L.total + kHeaderBytes > kScratchBytes)
+    return fail(MLA_ERR_WORKSPACE, "the call needs %zu bytes of workspace, above the %zu-byte scratch array",
+                L.total + kHeaderBytes, kScratchBytes);
   bool cap = false;
   if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
   void* ws = nullptr;
-  if ((s = grow_workspace(dev, stream, L.total, cap, &ws)) != MLA_OK) return s;
+  if (fixed_ws) {
+    if ((s = scratch_base(dev, stream, cap, &ws)) != MLA_OK) return s;
+  } else if ((s = grow_workspace(dev, stream, L.total, cap, &ws)) != MLA_OK) {
+    return s;
+  }
   char* w = (char*)ws + kHeaderBytes;
 
   mla::DecodeArgs a{};
@@ -508,7 +571,16 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
                             int32_t local_window_size, int32_t num_partitions, mla_tensor* out,
                             void* stream) {
   return decode_impl(q, input_row_offsets, page_table, cache_lens, latent_cache, scale, mask, local_window_size,
-                     num_partitions, out, stream);
+                     num_partitions, out, stream, false);
+}
+
+mla_status mla_decode_paged_noalloc(const mla_tensor* q, const mla_tensor* input_row_offsets,
+                                    const mla_tensor* page_table, const mla_tensor* cache_lens,
+                                    const mla_tensor* latent_cache, float scale, int32_t mask,
+                                    int32_t local_window_size, int32_t num_partitions, mla_tensor* out,
+                                    void* stream) {
+  return decode_impl(q, input_row_offsets, page_table, cache_lens, latent_cache, scale, mask, local_window_size,
+                     num_partitions, out, stream, true);
 }
 
 }  // extern "C"

@@ -381,3 +381,17 @@ def test_sparse_ext_empty_batch_is_a_no_op():
                                                                     xtopk=_t(FAKE, 3, (0,))))
     assert st == 0
 
+
+def test_noalloc_refuses_oversized_calls_without_a_gpu():
+    """mla_decode_paged_noalloc checks the workspace a call needs against its fixed array
+    before touching the device."""
+    lib = m.library()
+    assert lib.mla_decode_noalloc_scratch_bytes() == int(65.5 * 2 ** 20)
+    T, H = 64, 128
+    a = decode_args(q=_t(FAKE, 0, (T, H, 576)), off=_t(FAKE, 4, (T + 1,)), pt=_t(FAKE, 3, (T, 8)),
+                    lens=_t(FAKE, 3, (T,)), out=_t(FAKE, 0, (T, H, 512)), parts=100)
+    ref = ctypes.byref
+    st = lib.mla_decode_paged_noalloc(ref(a["q"]), ref(a["off"]), ref(a["pt"]), ref(a["lens"]), ref(a["cache"]),
+                                      ctypes.c_float(a["scale"]), a["mask"], a["window"], a["parts"], ref(a["out"]),
+                                      None)
+    assert st == 6, lib.mla_last_error_message()
