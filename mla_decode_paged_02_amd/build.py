@@ -23,8 +23,9 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags (none at present).
-EXTRA = {}
+# Per-source extra flags.  The batch decode keeps its running scores in ordinary registers
+# (the accumulation registers hold the output tile): its score MFMAs use the VGPR form.
+EXTRA = {"mla_decode2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

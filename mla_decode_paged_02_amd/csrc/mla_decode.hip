@@ -420,8 +420,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const KernelTi
   const SplitPlan p = plan_of(a);
   hipError_t e;
   if (timer && (e = hipEventRecord(timer->start, stream)) != hipSuccess) return e;
+  const bool small = a.nparts == 0 && a.T <= 64 && a.B <= 64 && a.T <= a.grid;
   switch (a.H) {
-    case 128: e = launch_decode_h<2, 4>(a, p, stream); break;
+    case 128: e = small ? launch_decode2(a, p, stream) : launch_decode_h<2, 4>(a, p, stream); break;
     case 64: e = launch_decode_h<2, 2>(a, p, stream); break;
     case 32: e = launch_decode_h<1, 2>(a, p, stream); break;
     case 16: e = launch_decode_h<1, 1>(a, p, stream); break;

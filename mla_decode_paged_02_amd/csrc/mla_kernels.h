@@ -173,6 +173,10 @@ struct KernelTimer {
 // Launchers (return the HIP status of the launches).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const KernelTimer* timer);
 hipError_t launch_combine(const SplitPlan& p, hipStream_t stream);
+// The dense decode kernel that splits the value columns over the waves (mla_decode2.hip):
+// 128 heads, the balanced split of at most 64 rows and sequences, no more rows than
+// work-groups.
+hipError_t launch_decode2(const DecodeArgs& a, const SplitPlan& p, hipStream_t stream);
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream, const KernelTimer* timer);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, const KernelTimer* timer);
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const KernelTimer* timer);

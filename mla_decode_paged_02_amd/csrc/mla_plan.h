@@ -302,8 +302,8 @@ __device__ __forceinline__ bool plan_row_parts(const SplitPlan& p, PlanLds& L, i
 // lane) writes rows 0..T-1 of the wave's private table geo (64 entries).  The result is
 // the plan plan_row_parts makes (the smallest S that fits, parts numbered in row order);
 // a batch without any visible key gets no parts (every row is written as zeros).
-template <int NT, class FillWave>
-__device__ __forceinline__ void plan_row_parts_small(const SplitPlan& p, PlanLds& L, int piece, FillWave fill_wave,
+template <int NT, class PL, class FillWave>
+__device__ __forceinline__ void plan_row_parts_small(const SplitPlan& p, PL& L, int piece, FillWave fill_wave,
                                                      RowGeo& g0, int& s, int& e, int& r0) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -368,8 +368,10 @@ __device__ __forceinline__ void plan_row_parts_small(const SplitPlan& p, PlanLds
 // SMALL (chosen by the host for balanced batches of at most 64 rows and 64 sequences, no
 // more rows than work-groups) plans per wave and has a single segment call site: the
 // general planner is not compiled in, which keeps the stage loop's registers free.
-template <int NT, bool SMALL, class Fill, class GeoOf, class FillWave, class Segment>
-__device__ __forceinline__ void plan_run(const SplitPlan& p, PlanLds& L, Fill fill, GeoOf geo_of, FillWave fill_wave,
+// PL: the kernel's LDS planning block (PlanLds, or with SMALL any block whose geo array
+// holds 64 rows per wave).
+template <int NT, bool SMALL, class PL, class Fill, class GeoOf, class FillWave, class Segment>
+__device__ __forceinline__ void plan_run(const SplitPlan& p, PL& L, Fill fill, GeoOf geo_of, FillWave fill_wave,
                                          Segment segment) {
   const int gid = blockIdx.x;
   const int piece = plan_piece(gid, (int)gridDim.x);
