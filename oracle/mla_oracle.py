@@ -50,6 +50,13 @@ Readings of points the pages leave open (each also listed in the design notes):
     of sequence b is k/v row buffer_row_offsets[b] + i at cache position
     cache_offsets[b] + i; query j is at cache_lens[b] - n_b + j.
 
+  * Rope-aware layout ([DEC] Parameters per_token_scale_rope_aware, which names an
+    interleaved FP8+BF16 layout of q and the cache without fixing it): each 576-wide
+    head row is stored as 640 bytes, its 512 latent values as E4M3 codes followed by
+    its 64 rope values as little-endian bfloat16; the token's (q) or row's (cache)
+    float32 scale multiplies the latent codes only, the rope values are taken as
+    stored.  V is the dequantised latent part, as above.
+
   * Attention sink and second KV stream ([DEC] Args attn_sink_ptr, extra_k,
     extra_d_indices, extra_indices_stride, extra_topk_lengths, extra_scales_ptr; the
     page names them without a formula): the sink is one logit per head, shared by the
@@ -325,6 +332,58 @@ def decode_paged_fp8(q8, q_scale, input_row_offsets, page_table, cache_lens, cac
         q = q * np.asarray(q_scale, dtype=np.float64)[:, None, None]
     return decode_paged_f64(q, input_row_offsets, page_table, cache_lens, _LazyE4M3(cache8, cache_scale),
                             page_size, scale, mask, window, rows)
+
+
+ROPE_ROW_BYTES = LATENT_DIM + 2 * ROPE_DIM  # 640
+
+
+def rope_aware_to_f64(raw, scales):
+    """Rows in the rope-aware layout ([DEC] Parameters per_token_scale_rope_aware) to
+    float64 [..., 576]: bytes 0..511 are E4M3 latent codes, times the row's scale
+    (None = 1); bytes 512..639 are the 64 rope values, little-endian bfloat16, unscaled."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    assert raw.shape[-1] == ROPE_ROW_BYTES, raw.shape
+    lat = e4m3_to_f64(raw[..., :LATENT_DIM])
+    if scales is not None:
+        lat = lat * np.asarray(scales, dtype=np.float64)[..., None]
+    rope_bits = np.ascontiguousarray(raw[..., LATENT_DIM:]).view("<u2")
+    return np.concatenate([lat, bf16_to_f64(rope_bits)], axis=-1)
+
+
+class _LazyRopeAware:
+    """Dequantises only the gathered rows of a large rope-aware cache."""
+
+    def __init__(self, raw, scales):
+        self.raw = raw
+        self.scales = scales
+        self.shape = raw.shape[:-1] + (HEAD_DIM,)
+
+    def __getitem__(self, idx):
+        return rope_aware_to_f64(self.raw[idx], None if self.scales is None else self.scales[idx])
+
+
+def _rope_aware_q(q_raw, q_scale):
+    T, H = q_raw.shape[:2]
+    qs = None if q_scale is None else np.broadcast_to(np.asarray(q_scale, dtype=np.float64)[:, None], (T, H))
+    return rope_aware_to_f64(q_raw, qs)
+
+
+def decode_paged_fp8_rope_aware(q_raw, q_scale, input_row_offsets, page_table, cache_lens, cache_raw,
+                                cache_scale, page_size, scale, mask="causal", window=-1, rows=None):
+    """Dense MLA decode with q [T, H, 640] and the paged cache [pages, PS, 640] in the
+    rope-aware layout (see rope_aware_to_f64; q_scale [T] per token, cache_scale
+    [pages, PS] per row), then the dense decode in float64."""
+    q = _rope_aware_q(q_raw, q_scale)
+    return decode_paged_f64(q, input_row_offsets, page_table, cache_lens, _LazyRopeAware(cache_raw, cache_scale),
+                            page_size, scale, mask, window, rows)
+
+
+def decode_sparse_rope_aware(q_raw, q_scale, input_row_offsets, cache_raw, cache_scale, d_indices,
+                             topk_lengths, page_size, scale, rows=None):
+    """Sparse decode ([DEC] Parameters sparse_mla) over a rope-aware cache."""
+    q = _rope_aware_q(q_raw, q_scale)
+    return decode_sparse_f64(q, input_row_offsets, _LazyRopeAware(cache_raw, cache_scale), d_indices,
+                             topk_lengths, page_size, scale, rows)
 
 
 # --------------------------------------------------------------------------------------

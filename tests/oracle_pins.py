@@ -190,6 +190,104 @@ def pin_p1_dense_fp8():
         close(lse, bl, 1e-12)
 
 
+def _torch_bf16(bits):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float32).numpy().astype(np.float64)
+
+
+def _rope_rows(rng, n, finite):
+    """n rope-aware rows (640 bytes: 512 E4M3 codes, then 64 bf16 rope values) with their
+    independent float64 reading: torch's e4m3 widening times the scale, torch's bf16."""
+    codes = rng.choice(finite, size=(n, 512)).astype(np.uint8)
+    rope = (rng.standard_normal((n, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    raw = np.concatenate([codes, rope.astype("<u2").view(np.uint8).reshape(n, 128)], axis=1)
+    return raw, codes, rope
+
+
+def pin_rope_aware_row_layout():
+    """One hand-built row: the latent codes sit at bytes 0..511 and take the scale, the
+    rope values are little-endian bf16 at bytes 512..639 and do not."""
+    raw = np.zeros((1, 640), dtype=np.uint8)
+    raw[0, 0] = 0x38          # E4M3 1.0
+    raw[0, 511] = 0xC0        # E4M3 -2.0
+    raw[0, 512:514] = (0x80, 0x3F)  # bf16 0x3F80 = 1.0, low byte first
+    raw[0, 638:640] = (0x40, 0xC0)  # bf16 0xC040 = -3.0
+    got = O.rope_aware_to_f64(raw, np.array([0.25], dtype=np.float32))
+    want = np.zeros((1, 576))
+    want[0, 0], want[0, 511], want[0, 512], want[0, 575] = 0.25, -0.5, 1.0, -3.0
+    close(got, want, 0.0)
+
+
+def pin_rope_aware_dense_fp8():
+    """Dense decode over a rope-aware cache against brute force on contiguous keys read
+    independently; one cache row has scale 0, which silences its latent part only.  The
+    pool's unused slots hold NaN codes and NaN scales and must never be read."""
+    rng = np.random.default_rng(41)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    small = finite[(finite & 0x78) < 0x50]
+    lens, n_tokens, H, ps = (11, 26), (2, 3), 2, 8
+    T = sum(n_tokens)
+    seq = [_rope_rows(rng, L, finite) for L in lens]
+    scales = [rng.uniform(0.001, 0.01, size=L).astype(np.float32) for L in lens]
+    scales[1][4] = 0.0
+    qraw, qcodes, qrope = _rope_rows(rng, T * H, small)
+    qraw, qcodes, qrope = qraw.reshape(T, H, 640), qcodes.reshape(T, H, 512), qrope.reshape(T, H, 64)
+    q_scale = rng.uniform(0.01, 0.1, size=T).astype(np.float32)
+    npages = [-(-L // ps) for L in lens]
+    total = sum(npages) + 2
+    perm = rng.permutation(total)
+    cache = np.full((total, ps, 640), 0xFF, dtype=np.uint8)
+    c_scale = np.full((total, ps), np.nan, dtype=np.float32)
+    table = np.full((len(lens), max(npages)), -1, dtype=np.int32)
+    cur = 0
+    for b, L in enumerate(lens):
+        for j in range(npages[b]):
+            pid = int(perm[cur])
+            cur += 1
+            table[b, j] = pid
+            n = min(ps, L - j * ps)
+            cache[pid, :n] = seq[b][0][j * ps:j * ps + n]
+            c_scale[pid, :n] = scales[b][j * ps:j * ps + n]
+    off = offsets_of(n_tokens)
+    qv = np.concatenate([_torch_e4m3(qcodes) * q_scale.astype(np.float64)[:, None, None], _torch_bf16(qrope)], axis=2)
+    keys = [np.concatenate([_torch_e4m3(seq[b][1]) * scales[b].astype(np.float64)[:, None], _torch_bf16(seq[b][2])],
+                           axis=1).tolist() for b in range(2)]
+    for mask, window in (("causal", -1), ("sliding_window_causal", 5), ("null", -1)):
+        out, lse = O.decode_paged_fp8_rope_aware(qraw, q_scale, off, table, np.array(lens, dtype=np.int32), cache,
+                                                 c_scale, ps, SCALE, mask, window)
+        bo, bl = decode_contiguous(qv.tolist(), keys, list(n_tokens), SCALE, mask, window)
+        close(out, bo, 1e-12)
+        close(lse, bl, 1e-12)
+
+
+def pin_rope_aware_sparse():
+    """Sparse decode over a rope-aware cache against attention_row on the listed rows."""
+    rng = np.random.default_rng(42)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    small = finite[(finite & 0x78) < 0x50]
+    H, ps, pages, T, stride = 2, 8, 4, 3, 7
+    raw, codes, rope = _rope_rows(rng, pages * ps, finite)
+    c_scale = rng.uniform(0.001, 0.01, size=pages * ps).astype(np.float32)
+    qraw, qcodes, qrope = _rope_rows(rng, T * H, small)
+    q_scale = rng.uniform(0.01, 0.1, size=T).astype(np.float32)
+    idx = rng.integers(0, pages * ps, size=(T, stride)).astype(np.int32)
+    idx[1, 0] = -1
+    topk = np.array([5, 3, 7], dtype=np.int32)
+    out, lse = O.decode_sparse_rope_aware(qraw.reshape(T, H, 640), q_scale, np.arange(T + 1, dtype=np.uint32),
+                                          raw.reshape(pages, ps, 640), c_scale.reshape(pages, ps), idx, topk, ps,
+                                          SCALE)
+    kv = np.concatenate([_torch_e4m3(codes) * c_scale.astype(np.float64)[:, None], _torch_bf16(rope)], axis=1)
+    qv = np.concatenate([_torch_e4m3(qcodes).reshape(T, H, 512) * q_scale.astype(np.float64)[:, None, None],
+                         _torch_bf16(qrope).reshape(T, H, 64)], axis=2)
+    for t in range(T):
+        keys = [kv[int(r)].tolist() for r in idx[t, :topk[t]] if r >= 0]
+        for h in range(H):
+            o, l = attention_row(qv[t, h].tolist(), keys, [k[:DV] for k in keys], SCALE)
+            close(out[t, h], o, 1e-12)
+            close(lse[t, h], l, 1e-12)
+
+
 def pin_p1_indexer():
     """The indexer against scalar brute force: scores by plain loops over heads and
     columns with math.fsum (torch's e4m3 widening), selection by a full sort of

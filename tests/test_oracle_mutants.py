@@ -191,12 +191,39 @@ def m_extra_reads_main_cache(mp):
     mp.setattr(O, "decode_sparse_f64", dsp)
 
 
+_rope_aware = O.rope_aware_to_f64
+
+
+def m_rope_scaled(mp):
+    """The row scale applied to the rope values as well."""
+    def f(raw, scales):
+        v = _rope_aware(raw, None)
+        return v if scales is None else v * np.asarray(scales, dtype=np.float64)[..., None]
+    mp.setattr(O, "rope_aware_to_f64", f)
+
+
+def m_rope_big_endian(mp):
+    """The rope values read with their bytes swapped."""
+    def f(raw, scales):
+        raw = np.array(raw, dtype=np.uint8, copy=True)
+        r = raw[..., 512:].reshape(raw.shape[:-1] + (64, 2))
+        raw[..., 512:] = r[..., ::-1].reshape(raw.shape[:-1] + (128,))
+        return _rope_aware(raw, scales)
+    mp.setattr(O, "rope_aware_to_f64", f)
+
+
+def m_rope_unscaled_latent(mp):
+    """The latent codes left without their scale."""
+    mp.setattr(O, "rope_aware_to_f64", lambda raw, scales: _rope_aware(raw, None))
+
+
 MUTANTS = [m_scale_dropped, m_values_shifted, m_causal_off_by_one, m_token_order_reversed,
            m_page_slot_swapped, m_combine_unweighted, m_no_max_subtraction, m_softmax_over_heads,
            m_lse_without_max, m_e4m3_bias8, m_sparse_ignores_topk, m_sparse_keeps_pads,
            m_prefill_rope_at_query, m_bf16_low_half,
            m_indexer_unweighted_heads, m_indexer_ties_reversed, m_sink_dropped, m_sink_scaled,
-           m_sink_in_numerator, m_extra_stream_ignored, m_extra_reads_main_cache]
+           m_sink_in_numerator, m_extra_stream_ignored, m_extra_reads_main_cache,
+           m_rope_scaled, m_rope_big_endian, m_rope_unscaled_latent]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
