@@ -129,10 +129,13 @@ mla_status mla_decode_paged(const mla_tensor* q, const mla_tensor* input_row_off
  * entries (the -1 fill) are skipped, duplicates count as often as they are listed.
  * A listed value is a physical row of the pool: page * PS + slot.
  *
- *   q             fp8 e4m3 [T, H, 576] (or bf16, then q_scale must be NULL)
+ *   q             fp8 e4m3 [T, H, 576] (or bf16, then q_scale must be NULL), or u8
+ *                 [T, H, 640] in the rope-aware layout of mla_decode_paged_fp8
  *   q_scale       f32 [T] (one scale per query token, shared by its heads) or NULL = 1
  *   input_row_offsets  u32 [B + 1] (only its shape is checked: index lists are per row)
- *   latent_cache  fp8 e4m3 [num_pages, PS, 576] (a bf16 cache is refused: MLA_ERR_UNSUPPORTED)
+ *   latent_cache  fp8 e4m3 [num_pages, PS, 576] (a bf16 cache is refused: MLA_ERR_UNSUPPORTED),
+ *                 or u8 [num_pages, PS, 640] in the rope-aware layout (Parameters
+ *                 per_token_scale_rope_aware; see mla_decode_paged_fp8), q alike
  *   cache_scale   f32 [num_pages, PS] (one scale per cache row) or NULL = 1
  *   d_indices     i32 [T, indices_stride] (row stride = stride[0] >= shape[1])
  *   topk_lengths  i32 [T], values above shape[1] of d_indices are clamped to it
@@ -170,7 +173,8 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
  * union).  extra_cache, extra_d_indices and extra_topk_lengths come together or not at
  * all; with them, each pool must hold fewer than 2^30 rows.  Second-list rows outside
  * extra_cache are skipped and set bit 1 of the device error word.  With neither a sink nor
- * a second stream this is mla_decode_paged_sparse.
+ * a second stream this is mla_decode_paged_sparse.  A rope-aware (640-byte) q and cache
+ * with a sink or a second stream is refused with MLA_ERR_UNSUPPORTED.
  */
 mla_status mla_decode_paged_sparse_ext(const mla_tensor* q, const mla_tensor* q_scale,
                                        const mla_tensor* input_row_offsets,
@@ -186,16 +190,25 @@ mla_status mla_decode_paged_sparse_ext(const mla_tensor* q, const mla_tensor* q_
  * Dense MLA decode over a paged fp8 e4m3 latent cache
  * (generic_flare_mla_decode_kv_cache_ragged: summary; Args q, q_scale_ptr, kv_collection,
  * input_row_offsets, scale, output, num_partitions_in; Parameters mask_str,
- * local_window_size, per_token_scale_rope_aware = False).  The same computation as
+ * local_window_size, per_token_scale_rope_aware).  The same computation as
  * mla_decode_paged, with every value stored as an e4m3 code times a float32 scale: the
  * query's per token (shared by its heads), the cache's per row (all 576 columns).  The
  * codes are widened exactly; the logits and P.V accumulate in fp32 from bf16 operands.
  *
- *   q                  fp8 e4m3 [T, H, 576]
+ * Rope-aware layout (per_token_scale_rope_aware; chosen when the cache rows are 640
+ * bytes wide, and q must then be too): each 576-wide head row of q and the cache is
+ * stored as its 512 latent values in e4m3 followed by its 64 rope values as
+ * little-endian bf16, and the token / row scale multiplies the latent codes only.  The
+ * rope values enter the logits divided by their scale and multiplied back in fp32, so
+ * they carry one extra bf16 rounding; scales of magnitude below 2^-40 are taken as 2^-40
+ * for that (their latent part then contributes about nothing, their rope in full).
+ *
+ *   q                  fp8 e4m3 [T, H, 576], or u8 [T, H, 640] in the rope-aware layout
  *   q_scale            f32 [T] or NULL = 1
  *   input_row_offsets, page_table, cache_lens, mask, local_window_size, scale,
  *   num_partitions, out     as for mla_decode_paged
- *   latent_cache       fp8 e4m3 [num_pages, PS, 576], rows of a page contiguous, any PS
+ *   latent_cache       fp8 e4m3 [num_pages, PS, 576], or u8 [num_pages, PS, 640] in the
+ *                      rope-aware layout; rows of a page contiguous, any PS
  *   cache_scale        f32 [num_pages, PS] or NULL = 1
  *
  * Errors as for mla_decode_paged; page ids outside the pool are skipped and set bit 0

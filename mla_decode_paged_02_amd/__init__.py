@@ -180,7 +180,8 @@ def decode_noalloc_scratch_bytes() -> int:
 def decode_paged_sparse(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices,
                         topk_lengths, scale, num_partitions=0, out=None, stream=None):
     """Sparse MLA decode (mla_decode_paged_sparse).  q / latent_cache fp8 e4m3 (torch
-    float8_e4m3fn or uint8 codes) or bf16; returns out bf16 [T, H, 512]."""
+    float8_e4m3fn or uint8 codes) or bf16, or uint8 rows of 640 bytes in the rope-aware
+    layout; returns out bf16 [T, H, 512]."""
     import torch
     _on_gpu(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices, topk_lengths, out)
     if out is None:
@@ -216,7 +217,9 @@ def decode_paged_fp8(q, q_scale, input_row_offsets, page_table, cache_lens, late
     """Dense MLA decode over a paged fp8 cache (mla_decode_paged_fp8).  q fp8 e4m3
     [T, H, 576] with q_scale f32 [T] or None; latent_cache fp8 e4m3 [num_pages, PS, 576]
     with cache_scale f32 [num_pages, PS] or None (torch float8_e4m3fn or uint8 codes);
-    returns out bf16 [T, H, 512]."""
+    q [T, H, 640] and latent_cache [num_pages, PS, 640] (uint8) select the rope-aware
+    layout (512 e4m3 latent codes, then 64 little-endian bf16 rope values, the scale on the
+    codes only); returns out bf16 [T, H, 512]."""
     import torch
     _on_gpu(q, q_scale, input_row_offsets, page_table, cache_lens, latent_cache, cache_scale, out)
     if out is None:

@@ -600,24 +600,28 @@ mla_status sparse_impl(const mla_tensor* q, const mla_tensor* q_scale, const mla
   const bool q_bf16 = q->dtype == MLA_DTYPE_BF16;
   if ((s = check_tensor(q, "q", q_bf16 ? MLA_DTYPE_BF16 : MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
   const int64_t T = q->shape[0], H = q->shape[1];
-  if (q->shape[2] != 576) return fail(MLA_ERR_SHAPE, "q: head width %lld, expected 576", (long long)q->shape[2]);
+  if (!latent_cache) return fail(MLA_ERR_NULL_ARG, "latent_cache: descriptor is NULL");
+  // the row width picks the layout: 576 all e4m3, 640 rope-aware (q and cache alike)
+  const int64_t RW = latent_cache->ndim == 3 && latent_cache->shape[2] == 640 ? 640 : 576;
+  if (q->shape[2] != RW)
+    return fail(MLA_ERR_SHAPE, "q: head width %lld, expected %lld (the cache's row width)", (long long)q->shape[2], (long long)RW);
+  if (RW == 640 && q_bf16) return fail(MLA_ERR_VALUE, "the rope-aware layout needs an fp8 q");
   if (q_scale) {
     if (q_bf16) return fail(MLA_ERR_VALUE, "q_scale must be NULL when q is bf16");
     if ((s = check_1d(q_scale, "q_scale", MLA_DTYPE_F32, T)) != MLA_OK) return s;
   }
   if ((s = check_tensor(input_row_offsets, "input_row_offsets", MLA_DTYPE_U32, 1, false)) != MLA_OK) return s;
   if (input_row_offsets->shape[0] < 2) return fail(MLA_ERR_SHAPE, "input_row_offsets: needs batch + 1 >= 2 entries");
-  if (!latent_cache) return fail(MLA_ERR_NULL_ARG, "latent_cache: descriptor is NULL");
   if (latent_cache->dtype == MLA_DTYPE_BF16)
     return fail(MLA_ERR_UNSUPPORTED, "sparse decode reads an fp8 e4m3 cache; a bf16 cache is not supported");
   if ((s = check_tensor(latent_cache, "latent_cache", MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
-  if (latent_cache->shape[2] != 576) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576", (long long)latent_cache->shape[2]);
+  if (latent_cache->shape[2] != RW) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576 or 640", (long long)latent_cache->shape[2]);
   const int64_t NP = latent_cache->shape[0], PS = latent_cache->shape[1];
   if (PS < 1) return fail(MLA_ERR_SHAPE, "latent_cache: page size must be >= 1");
-  if (NP > 0 && PS > 1 && latent_cache->stride[1] != 576)
-    return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride 576)");
-  if (NP > 1 && latent_cache->stride[0] < PS * 576)
-    return fail(MLA_ERR_SHAPE, "latent_cache: pages overlap (page stride below page_size * 576)");
+  if (NP > 0 && PS > 1 && latent_cache->stride[1] != RW)
+    return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride %lld)", (long long)RW);
+  if (NP > 1 && latent_cache->stride[0] < PS * RW)
+    return fail(MLA_ERR_SHAPE, "latent_cache: pages overlap (page stride below page_size * %lld)", (long long)RW);
   if (NP * PS > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 cache rows");
   if (cache_scale) {
     if ((s = check_tensor(cache_scale, "cache_scale", MLA_DTYPE_F32, 2, false)) != MLA_OK) return s;
@@ -637,6 +641,8 @@ mla_status sparse_impl(const mla_tensor* q, const mla_tensor* q_scale, const mla
   if (attn_sink && (s = check_1d(attn_sink, "attn_sink", MLA_DTYPE_F32, H)) != MLA_OK) return s;
   // the second stream: all four descriptors or none of its index parts
   const bool xtra = extra_d_indices != nullptr || extra_topk_lengths != nullptr || extra_cache != nullptr;
+  if (RW == 640 && (xtra || attn_sink || extra_cache_scale))
+    return fail(MLA_ERR_UNSUPPORTED, "the rope-aware layout is not supported with a sink or a second stream");
   int64_t XNP = 0, XPS = 0;
   if (xtra) {
     if (!extra_d_indices || !extra_topk_lengths || !extra_cache)
@@ -695,7 +701,8 @@ mla_status sparse_impl(const mla_tensor* q, const mla_tensor* q_scale, const mla
   a.cs_page = cache_scale ? cache_scale->stride[0] : 0;
   a.num_rows = NP * PS;
   a.PS = (int32_t)PS;
-  a.flat = a.page_bytes == PS * 576 && (cache_scale == nullptr || a.cs_page == PS) ? 1 : 0;
+  a.flat = a.page_bytes == PS * RW && (cache_scale == nullptr || a.cs_page == PS) ? 1 : 0;
+  a.rope = RW == 640 ? 1 : 0;
   a.idx = (const int32_t*)d_indices->data;
   a.idx_row = d_indices->stride[0];
   a.idx_cols = (int32_t)d_indices->shape[1];
@@ -774,7 +781,11 @@ mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
   mla_status s;
   if ((s = check_tensor(q, "q", MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
   const int64_t T = q->shape[0], H = q->shape[1];
-  if (q->shape[2] != 576) return fail(MLA_ERR_SHAPE, "q: head width %lld, expected 576", (long long)q->shape[2]);
+  if (!latent_cache) return fail(MLA_ERR_NULL_ARG, "latent_cache: descriptor is NULL");
+  // the row width picks the layout: 576 all e4m3, 640 rope-aware (q and cache alike)
+  const int64_t RW = latent_cache->ndim == 3 && latent_cache->shape[2] == 640 ? 640 : 576;
+  if (q->shape[2] != RW)
+    return fail(MLA_ERR_SHAPE, "q: head width %lld, expected %lld (the cache's row width)", (long long)q->shape[2], (long long)RW);
   if (q_scale && (s = check_1d(q_scale, "q_scale", MLA_DTYPE_F32, T)) != MLA_OK) return s;
   if ((s = check_tensor(input_row_offsets, "input_row_offsets", MLA_DTYPE_U32, 1, false)) != MLA_OK) return s;
   const int64_t B = input_row_offsets->shape[0] - 1;
@@ -783,13 +794,13 @@ mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
   if (page_table->shape[0] != B) return fail(MLA_ERR_SHAPE, "page_table: %lld rows, expected batch %lld", (long long)page_table->shape[0], (long long)B);
   if ((s = check_1d(cache_lens, "cache_lens", MLA_DTYPE_I32, B)) != MLA_OK) return s;
   if ((s = check_tensor(latent_cache, "latent_cache", MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
-  if (latent_cache->shape[2] != 576) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576", (long long)latent_cache->shape[2]);
+  if (latent_cache->shape[2] != RW) return fail(MLA_ERR_SHAPE, "latent_cache: row width %lld, expected 576 or 640", (long long)latent_cache->shape[2]);
   const int64_t NP = latent_cache->shape[0], PS = latent_cache->shape[1];
   if (PS < 1) return fail(MLA_ERR_SHAPE, "latent_cache: page size must be >= 1");
-  if (NP > 0 && PS > 1 && latent_cache->stride[1] != 576)
-    return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride 576)");
-  if (NP > 1 && latent_cache->stride[0] < PS * 576)
-    return fail(MLA_ERR_SHAPE, "latent_cache: pages overlap (page stride below page_size * 576)");
+  if (NP > 0 && PS > 1 && latent_cache->stride[1] != RW)
+    return fail(MLA_ERR_SHAPE, "latent_cache: rows of a page must be contiguous (stride %lld)", (long long)RW);
+  if (NP > 1 && latent_cache->stride[0] < PS * RW)
+    return fail(MLA_ERR_SHAPE, "latent_cache: pages overlap (page stride below page_size * %lld)", (long long)RW);
   if (NP * PS > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 cache rows");
   if (cache_scale) {
     if ((s = check_tensor(cache_scale, "cache_scale", MLA_DTYPE_F32, 2, false)) != MLA_OK) return s;
@@ -830,7 +841,8 @@ mla_status mla_decode_paged_fp8(const mla_tensor* q, const mla_tensor* q_scale,
   a.cs_page = cache_scale ? cache_scale->stride[0] : 0;
   a.num_rows = NP * PS;
   a.PS = (int32_t)PS;
-  a.flat = a.page_bytes == PS * 576 && (cache_scale == nullptr || a.cs_page == PS) ? 1 : 0;
+  a.flat = a.page_bytes == PS * RW && (cache_scale == nullptr || a.cs_page == PS) ? 1 : 0;
+  a.rope = RW == 640 ? 1 : 0;
   a.dense = 1;
   a.offsets = (const uint32_t*)input_row_offsets->data;
   a.page_table = (const int32_t*)page_table->data;

@@ -43,16 +43,16 @@ struct DecodeArgs {
 // decode over a paged fp8 cache (each q row attends to the visible rows of its sequence,
 // found through the page table).
 struct SparseArgs {
-  const uint8_t* q;           // fp8 e4m3 [T, H, 576], or bf16 when q_bf16
+  const uint8_t* q;           // fp8 e4m3 [T, H, 576] (640 bytes with rope), or bf16 when q_bf16
   int64_t q_tok, q_head;      // element strides
   const float* q_scale;       // [T] or null (= 1)
-  const uint8_t* cache;       // fp8 e4m3 [num_pages, PS, 576]; a page's rows are contiguous
+  const uint8_t* cache;       // fp8 e4m3 [num_pages, PS, 576 or 640 with rope]; a page's rows are contiguous
   int64_t page_bytes;         // byte stride between pages
   const float* cache_scale;   // [num_pages, PS] or null (= 1)
   int64_t cs_page;            // element stride between pages of cache_scale
   int64_t num_rows;           // num_pages * PS: listed rows outside [0, num_rows) are skipped
   int32_t PS;
-  int32_t flat;               // 1: row r is at byte r * 576 and its scale at element r
+  int32_t flat;               // 1: row r is at byte r * (576 or 640) and its scale at element r
   const int32_t* idx;         // [T, idx_row]
   int64_t idx_row;            // element stride between index rows
   int32_t idx_cols;           // shape[1] of d_indices (topk is clamped to it)
@@ -67,6 +67,7 @@ struct SparseArgs {
   int32_t B, max_pages, mask, window;
   int32_t T, H;
   int32_t q_bf16;             // 1: q is bf16 (no q_scale)
+  int32_t rope;               // 1: q and cache rows are 640-byte rope-aware rows (e4m3 latent, bf16 rope)
   float scale_log2;           // scale * log2(e)
   int32_t nparts;             // 0: balanced; >= 1 fixed
   int32_t grid;

@@ -19,6 +19,17 @@
 // them to bf16 (exact: every e4m3 value is a bf16 value) into the swizzled tile layout
 // the compute reads.  The row scale enters the logit and the value weight (KSCALE), the
 // token scale the logit scale.
+//
+// With ROPE the rows of q and the cache are in the rope-aware layout ([DEC] Parameters
+// per_token_scale_rope_aware): 640 bytes, the 512 latent values as e4m3 codes, then the 64
+// rope values as bf16, the token / row scale applying to the codes only.  The widening
+// stores a key's rope values divided by its scale (and the query fragments the query's
+// rope values divided by the token scale), so the scaled logit of the common path is
+// sigma_q sigma_k <q8, k8> + <q_rope, k_rope>, up to the bf16 rounding of those quotients.
+// A scale of magnitude below 2^-40 is taken as 2^-40 on both sides of that quotient: the
+// latent part of such a row or token then contributes (about 2^-31 of a code) nothing
+// while its rope still counts in full, and a product of two such quotients (2^80 times the
+// rope values) stays far inside the fp32 range of the accumulators.
 #include <type_traits>
 
 #include "mla_device.h"
@@ -29,16 +40,24 @@
 
 namespace mla {
 
-constexpr int kRawRowBytes = 576;                           // one fp8 cache row
-constexpr int kRawStageBytes = kStageKeys * kRawRowBytes;   // 18432
-constexpr int kRawPieces = kRawStageBytes / 16;             // 1152 sixteen-byte pieces
-constexpr int kRawPiecesPerRow = kRawRowBytes / 16;         // 36
-constexpr int kRawDma = kRawPieces / 64;                    // 18 wave-wide loads per stage
+// Geometry of the raw rows: 576 bytes (all e4m3), or 640 in the rope-aware layout.
+template <bool ROPE>
+struct RawRows {
+  static constexpr int kRowBytes = ROPE ? 640 : 576;            // one cache row
+  static constexpr int kStageBytes = kStageKeys * kRowBytes;     // 18432 / 20480
+  static constexpr int kPieces = kStageBytes / 16;               // sixteen-byte pieces
+  static constexpr int kPiecesPerRow = kRowBytes / 16;           // 36 / 40
+  static constexpr int kDma = kPieces / 64;                      // 18 / 20 wave-wide loads
+};
+constexpr int kRawStageBytesMax = RawRows<true>::kStageBytes;
+constexpr float kRopeMinScale = 0x1p-40f;
+// the row or token scale as the rope-aware path uses it (see the header)
+__device__ __forceinline__ float rope_scale(float s) { return fabsf(s) < kRopeMinScale ? kRopeMinScale : s; }
 constexpr int kSpTiles = 2;    // widened bf16 tiles: the one computed, the one being widened
 constexpr int kSpRaw = 3;      // fp8 landing buffers: the one being widened, two in flight
 constexpr int kSpScale = 4;    // per-key scale slots (64 floats): stages k .. k+3
 constexpr int kIdxWindow = 1024;                            // list positions held in LDS
-constexpr int kSpStageLds = kSpTiles * kStageBytes + kSpRaw * kRawStageBytes;
+constexpr int kSpStageLds = kSpTiles * kStageBytes + kSpRaw * kRawStageBytesMax;
 // the epilogue stages 4 x 32 KB of output rows over the same block
 constexpr int kSpLdsBytes = kSpStageLds > 4 * 32 * 1024 ? kSpStageLds : 4 * 32 * 1024;
 static_assert(sizeof(PlanLds::scan) == kIdxWindow * sizeof(int), "the window lives in the planning scratch");
@@ -75,11 +94,17 @@ __device__ __forceinline__ void sparse_fill(const SparseArgs& a, PlanLds& L) {
 // DENSE: rows from the page table (mla_decode_paged_fp8), else from d_indices.  XTRA (the
 // extended sparse decode): the sink logits, and the second list when there is one, whose
 // rows are held in the window with kExtraRowBit set.
-template <int HB, int NW, bool DENSE, bool XTRA>
+template <int HB, int NW, bool DENSE, bool XTRA, bool ROPE>
 __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint8_t* tiles, MLA_LDS uint8_t* raw,
                                                MLA_LDS float* kscale, MLA_LDS int* win, int t, const RowGeo& g,
                                                int ta, int tc, bool full, int slot) {
   constexpr int NT = NW * 64;
+  static_assert(!(ROPE && XTRA), "the second stream is read in the all-e4m3 layout only");
+  constexpr int kRawRowBytes = RawRows<ROPE>::kRowBytes;
+  constexpr int kRawStageBytes = RawRows<ROPE>::kStageBytes;
+  constexpr int kRawPieces = RawRows<ROPE>::kPieces;
+  constexpr int kRawPiecesPerRow = RawRows<ROPE>::kPiecesPerRow;
+  constexpr int kRawDma = RawRows<ROPE>::kDma;
   constexpr int kSlots = kRawDma + 1;                // the rows' pieces, then their scales
   constexpr int kPerWave = (kSlots + NW - 1) / NW;   // loads every wave issues per stage
   constexpr int kWp = (kRawPieces + NT - 1) / NT;    // pieces each thread widens per stage
@@ -255,14 +280,31 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   u32x4 wr[kWp];
   constexpr bool kLinear = NT == 256;
   struct WidenGeo {
-    int src, dst0, dst1;
+    int src, dst0, dst1, dstr;  // dstr (ROPE): the chunk of rope values 8j..8j+7
   };
   auto widen_geo = [&]() -> WidenGeo {
     int tid_v = tid;
     asm volatile("" : "+v"(tid_v));
     const int r = tid_v >> 3, j = tid_v & 7, f = swz_mask(r);
     return WidenGeo{r * kRawRowBytes + 16 * j, r * kRowBytes + (((2 * j) ^ f) << 4),
-                    r * kRowBytes + (((2 * j + 1) ^ f) << 4)};
+                    r * kRowBytes + (((2 * j + 1) ^ f) << 4), r * kRowBytes + ((64 | (j ^ f)) << 4)};
+  };
+  // ROPE: eight bf16 rope values of row r of the stage, divided by the row's scale; the
+  // thread of the row's first rope piece leaves the scale as used in the stage's slot
+  auto put_rope = [&](MLA_LDS uint8_t* d, const u32x4& w, MLA_LDS float* ksl, int r, bool first) {
+    const float sg = rope_scale(ksl[r]), inv = 1.f / sg;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __builtin_bit_cast(float, w[i] << 16) * inv;
+      const float hi = __builtin_bit_cast(float, w[i] & 0xFFFF0000u) * inv;
+      o[i] = (uint32_t)bf16_bits_rne(lo) | ((uint32_t)bf16_bits_rne(hi) << 16);
+    }
+    *(MLA_LDS u32x4*)d = u32x4{o[0], o[1], o[2], o[3]};
+    if (first) {
+      ksl[r] = sg;
+      ksl[r + 32] = sg;
+    }
   };
   auto put_bf16 = [&](MLA_LDS uint8_t* d0, MLA_LDS uint8_t* d1, const u32x4& w) {
     const uint2 b0 = e4m3x4_to_bf16x4(w[0]), b1 = e4m3x4_to_bf16x4(w[1]);
@@ -272,7 +314,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   };
   auto take = [&](const MLA_LDS uint8_t* src, int i, const WidenGeo& wg) {
     if constexpr (kLinear) {
-      if (i < 4 || (tid & 7) < 4) wr[i] = *(const MLA_LDS u32x4*)(src + wg.src + 128 * i);
+      if (ROPE || i < 4 || (tid & 7) < 4) wr[i] = *(const MLA_LDS u32x4*)(src + wg.src + 128 * i);
     } else {
       // the piece arithmetic is redone per call from an opaque copy of the thread id:
       // hoisted out of the stage loop it would hold registers the stage compute needs
@@ -282,9 +324,11 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
       if (i * NT + NT <= kRawPieces || tid + i * NT < kRawPieces) wr[i] = *(const MLA_LDS u32x4*)(src + c * 16);
     }
   };
-  auto put = [&](MLA_LDS uint8_t* dst, int i, const WidenGeo& wg) {
+  // ksl: the stage's scale slot (ROPE only)
+  auto put = [&](MLA_LDS uint8_t* dst, int i, const WidenGeo& wg, MLA_LDS float* ksl) {
     if constexpr (kLinear) {
-      if (i < 4 || (tid & 7) < 4) put_bf16(dst + wg.dst0 + 256 * i, dst + wg.dst1 + 256 * i, wr[i]);
+      if (ROPE && i == 4) put_rope(dst + wg.dstr, wr[i], ksl, tid >> 3, (tid & 7) == 0);
+      else if (ROPE || i < 4 || (tid & 7) < 4) put_bf16(dst + wg.dst0 + 256 * i, dst + wg.dst1 + 256 * i, wr[i]);
     } else {
       int tid_v = tid;
       asm volatile("" : "+v"(tid_v));
@@ -292,11 +336,14 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
       if (i * NT + NT <= kRawPieces || tid + i * NT < kRawPieces) {
         const int row = c / kRawPiecesPerRow, piece = c - row * kRawPiecesPerRow;
         MLA_LDS uint8_t* rowp = dst + row * kRowBytes;
-        put_bf16(rowp + swz_chunk(row, 2 * piece) * 16, rowp + swz_chunk(row, 2 * piece + 1) * 16, wr[i]);
+        if (ROPE && piece >= 32)
+          put_rope(rowp + swz_chunk(row, 64 + piece - 32) * 16, wr[i], ksl, row, piece == 32);
+        else
+          put_bf16(rowp + swz_chunk(row, 2 * piece) * 16, rowp + swz_chunk(row, 2 * piece + 1) * 16, wr[i]);
       }
     }
   };
-  static_assert(!kLinear || kWp == 5, "256 threads: 4.5 pieces each");
+  static_assert(!kLinear || kWp == 5, "256 threads: 4.5 (5 with ROPE) pieces each");
 
   // ---- prologue: stages 0 and 1 in flight, q, then stage 2 issued and stage 0 widened
   uint32_t m0 = issue(s_first, 0, 0), m1 = 0, m2 = 0, m3 = 0;
@@ -314,19 +361,33 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
       for (int ks = 0; ks < 18; ++ks) qf[hb][ks] = *(const bf16x8*)(qh + 32 * ks);
     }
   } else {
-    const uint8_t* qrow = a.q + (int64_t)t * a.q_tok + 8 * gq;
+    const uint8_t* qrow = a.q + (int64_t)t * a.q_tok;
+    const float qinv = ROPE ? 1.f / rope_scale(a.q_scale != nullptr ? ld_const(a.q_scale + t) : 1.f) : 1.f;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const uint8_t* qh = qrow + (int64_t)(h0 + 16 * hb + ln) * a.q_head;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        const uint2 w = *(const uint2*)(qh + 32 * ks);
-        const uint2 lo = e4m3x4_to_bf16x4(w.x), hi = e4m3x4_to_bf16x4(w.y);
-        qf[hb][ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        if (ROPE && ks >= 16) {
+          // rope values 32(ks - 16) + 8gq .. + 7 (bf16 after the 512 codes), over the scale
+          const uint4 w = *(const uint4*)(qh + 512 + 64 * (ks - 16) + 16 * gq);
+          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o[i] = (uint32_t)bf16_bits_rne(__builtin_bit_cast(float, ww[i] << 16) * qinv) |
+                   ((uint32_t)bf16_bits_rne(__builtin_bit_cast(float, ww[i] & 0xFFFF0000u) * qinv) << 16);
+          qf[hb][ks] = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+        } else {
+          const uint2 w = *(const uint2*)(qh + 32 * ks + 8 * gq);
+          const uint2 lo = e4m3x4_to_bf16x4(w.x), hi = e4m3x4_to_bf16x4(w.y);
+          qf[hb][ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
       }
     }
   }
-  const float q_scale = a.q_scale != nullptr ? ld_const(a.q_scale + t) : 1.f;
+  float q_scale = a.q_scale != nullptr ? ld_const(a.q_scale + t) : 1.f;
+  if (ROPE) q_scale = rope_scale(q_scale);
   const float scale_log2 = a.scale_log2 * q_scale;
   all_wait0();
   stage_barrier();
@@ -336,7 +397,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
 #pragma unroll
     for (int i = 0; i < kWp; ++i) {
       take(raw, i, wg);
-      put(tiles, i, wg);
+      put(tiles, i, wg, kscale);
     }
   }
   lgkm_wait0();
@@ -360,6 +421,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
     const bool next = k + 1 < nst;
     const MLA_LDS uint8_t* wsrc = raw + ((k + 1) % kSpRaw) * kRawStageBytes;
     MLA_LDS uint8_t* wdst = tiles + ((k + 1) % kSpTiles) * kStageBytes;
+    MLA_LDS float* wks = kscale + ((k + 1) % kSpScale) * 64;
     WidenGeo wg{0, 0, 0};
     auto hook = [&](int ks) {
       if (hook_issue) {
@@ -373,10 +435,10 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
       if (kLinear && ks == 0) wg = widen_geo();
       if (kTwoPhase) {
         if ((ks & 1) == 0 && ks / 2 < kWp) take(wsrc, ks / 2, wg);
-        if ((ks & 1) == 1 && ks / 2 < kWp) put(wdst, ks / 2, wg);
+        if ((ks & 1) == 1 && ks / 2 < kWp) put(wdst, ks / 2, wg, wks);
       } else if (ks < kWp) {
         take(wsrc, ks, wg);
-        put(wdst, ks, wg);
+        put(wdst, ks, wg, wks);
       }
     };
     // the lane geometry is rebuilt per stage from an opaque lane id: kept across the stage
@@ -410,7 +472,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
 
 // SMALL: balanced batch of at most 64 rows, no more rows than work-groups (planned per
 // wave, see plan_run).
-template <int HB, int NW, bool SMALL, bool DENSE, bool XTRA>
+template <int HB, int NW, bool SMALL, bool DENSE, bool XTRA, bool ROPE>
 __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs a, const SplitPlan plan) {
   // the widened tiles, then the fp8 landing buffers
   __shared__ __attribute__((aligned(1024))) uint8_t buf_raw[kSpLdsBytes];
@@ -432,7 +494,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs
         else if (lane < a.T) geo[lane] = RowGeo{lane, 0, sparse_len<XTRA>(a, lane)};
       },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
-        sparse_segment<HB, NW, DENSE, XTRA>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
+        sparse_segment<HB, NW, DENSE, XTRA, ROPE>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
       });
 }
 
@@ -459,15 +521,24 @@ template <int HB, int NW>
 static hipError_t launch_sparse_h(const SparseArgs& a, const SplitPlan& p, hipStream_t stream) {
   const dim3 grid(a.nparts >= 1 ? a.T * a.nparts : a.grid), block(NW * 64);
   const bool small = a.nparts == 0 && a.T <= 64 && a.T <= a.grid && (!a.dense || a.B <= 64);
-  if (a.dense) {
-    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, true, false>), grid, block, 0, stream, a, p);
-    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, true, false>), grid, block, 0, stream, a, p);
+  if (a.rope) {
+    if (a.xidx != nullptr || a.sink != nullptr) return hipErrorInvalidValue;  // refused by the host checks
+    if (a.dense) {
+      if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, true, false, true>), grid, block, 0, stream, a, p);
+      else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, true, false, true>), grid, block, 0, stream, a, p);
+    } else {
+      if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, false, false, true>), grid, block, 0, stream, a, p);
+      else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, false, false, true>), grid, block, 0, stream, a, p);
+    }
+  } else if (a.dense) {
+    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, true, false, false>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, true, false, false>), grid, block, 0, stream, a, p);
   } else if (a.xidx != nullptr || a.sink != nullptr) {
-    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, false, true>), grid, block, 0, stream, a, p);
-    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, false, true>), grid, block, 0, stream, a, p);
+    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, false, true, false>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, false, true, false>), grid, block, 0, stream, a, p);
   } else {
-    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, false, false>), grid, block, 0, stream, a, p);
-    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, false, false>), grid, block, 0, stream, a, p);
+    if (small) hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, true, false, false, false>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_sparse_kernel<HB, NW, false, false, false, false>), grid, block, 0, stream, a, p);
   }
   return hipGetLastError();
 }

@@ -14,11 +14,13 @@ patterns as uint16, "e4m3" arrays hold OCP FP8 E4M3 codes as uint8):
   page_table         int32 [B, max_pages]    entries past a sequence's pages are -1
   cache_lens         int32 [B]               valid cache rows, current tokens included
   input_row_offsets  uint32 [B + 1]          q rows of sequence b are [off[b], off[b+1])
+  rope-aware q8 / cache8  uint8 [..., 640]   512 e4m3 latent codes, then 64 bf16 rope
+                                             values (little-endian); see rope_aware()
 
 Draws: a Generator seeded with ``seed`` gives, in this order, the lengths / top-k
 counts, the page permutation and the sparse index lists; the large value arrays come
 from child streams of SeedSequence([seed, tag]) with tag 1 = q, 2 = cache, 3 = prefill
-k, 4 = prefill v (split into a fixed number of chunks, so the bytes never depend on
+k, 4 = prefill v, 11 / 12 = rope-aware q / cache rope values (split into a fixed number of chunks, so the bytes never depend on
 the host's thread count).
 """
 from __future__ import annotations
@@ -40,7 +42,7 @@ E4M3_NAN_CODE = 0x7F
 
 __all__ = [
     "HEAD_DIM", "LATENT_DIM", "ROPE_DIM", "PREFILL_QK_DIM", "PREFILL_V_DIM",
-    "PREFILL_NOPE_DIM", "BF16_NAN_BITS", "E4M3_NAN_CODE", "default_scale",
+    "PREFILL_NOPE_DIM", "BF16_NAN_BITS", "E4M3_NAN_CODE", "default_scale", "rope_aware",
     "bf16_bits", "e4m3_codes", "DecodeCase", "SparseCase", "PrefillCase",
     "make_decode_case", "make_sparse_case", "make_prefill_case", "config_case",
     "CONFIG_DESCRIPTIONS", "algorithmic_bytes", "algorithmic_flops",
@@ -251,6 +253,24 @@ def make_decode_case(seed, lens, num_heads, page_size, q_per_seq=1, mask="causal
     return DecodeCase(name=name, q=q, input_row_offsets=offsets, page_table=table,
                       cache_lens=lens, latent_cache=cache, page_size=page_size,
                       scale=default_scale(), mask=mask, window=window)
+
+
+def rope_aware(case, seed):
+    """The same fp8 case (DecodeCase or SparseCase) in the rope-aware layout: every 576-wide
+    q head and cache row becomes 640 bytes, its first 512 E4M3 codes (scales unchanged)
+    followed by 64 bfloat16 values (little-endian) drawn N(0,1).  Cache rows whose first
+    code is the NaN code (poisoned slots) get NaN rope values too."""
+    def convert(codes, tag):
+        lead = codes.shape[:-1]
+        rope = _normal_bf16(seed, tag, lead + (ROPE_DIM,))
+        bad = codes[..., 0] == E4M3_NAN_CODE
+        rope[bad] = BF16_NAN_BITS
+        out = np.empty(lead + (LATENT_DIM + 2 * ROPE_DIM,), dtype=np.uint8)
+        out[..., :LATENT_DIM] = codes[..., :LATENT_DIM]
+        out[..., LATENT_DIM:] = rope.astype("<u2").view(np.uint8).reshape(lead + (2 * ROPE_DIM,))
+        return out
+    return dataclasses.replace(case, name=case.name + "-rope", q8=convert(case.q8, 11),
+                               cache8=convert(case.cache8, 12))
 
 
 # --------------------------------------------------------------------------------------
@@ -480,14 +500,15 @@ def algorithmic_bytes(case) -> int:
                 lo = max(0, (L - n) - case.window + 1)
             rows += max(0, L - lo)
         if case.fp8:
-            row_bytes = HEAD_DIM + (4 if case.cache_scale is not None else 0)
+            # 576 (all e4m3) or 640 (rope-aware) bytes per row, plus its scale
+            row_bytes = int(case.cache8.shape[-1]) + (4 if case.cache_scale is not None else 0)
             qb = case.q8.size + (case.q_scale.size * 4 if case.q_scale is not None else 0)
             return rows * row_bytes + qb
         return rows * HEAD_DIM * 2 + case.q.size * 2
     if isinstance(case, SparseCase):
         listed = int(sum(int(np.count_nonzero(case.d_indices[t, :case.topk_lengths[t]] >= 0))
                          for t in range(case.total_q)))
-        row_bytes = HEAD_DIM + (4 if case.cache_scale is not None else 0)
+        row_bytes = int(case.cache8.shape[-1]) + (4 if case.cache_scale is not None else 0)
         qb = case.q8.size + (case.q_scale.size * 4 if case.q_scale is not None else 0)
         return listed * row_bytes + qb
     if isinstance(case, PrefillCase):

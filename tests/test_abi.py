@@ -152,6 +152,25 @@ def test_sparse_validation(over, status):
     assert msg
 
 
+@pytest.mark.parametrize("over,status", [
+    (dict(q=_t(FAKE, 1, (4, 16, 640))), 2),                 # rope-aware q, all-e4m3 cache
+    (dict(cache=_t(FAKE, 1, (10, 64, 640)), cs=_t(FAKE, 2, (10, 64))), 2),  # rope-aware cache only
+    (dict(q=_t(FAKE, 0, (4, 16, 640)), qs=None, cache=_t(FAKE, 1, (10, 64, 640))), 8),  # bf16 q
+    (dict(q=_t(FAKE, 1, (4, 16, 640)), cache=_t(FAKE, 1, (10, 64, 640), stride=(64 * 704, 704, 1))), 2),
+])
+def test_sparse_rope_aware_validation(over, status):
+    st, msg = call_sparse(sparse_args(**over))
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_sparse_rope_aware_empty_batch_is_a_no_op():
+    st, msg = call_sparse(sparse_args(q=_t(FAKE, 1, (0, 16, 640)), qs=_t(FAKE, 2, (0,)),
+                                      cache=_t(FAKE, 1, (10, 64, 640)), idx=_t(FAKE, 3, (0, 32)),
+                                      topk=_t(FAKE, 3, (0,)), out=_t(FAKE, 0, (0, 16, 512))))
+    assert st == 0, msg
+
+
 def test_sparse_empty_batch_is_a_no_op():
     st, _ = call_sparse(sparse_args(q=_t(FAKE, 1, (0, 16, 576)), qs=_t(FAKE, 2, (0,)),
                                     idx=_t(FAKE, 3, (0, 32)), topk=_t(FAKE, 3, (0,)),
@@ -235,6 +254,24 @@ def test_fp8_decode_validation(over, status):
     st, msg = call_fp8_decode(fp8_decode_args(**over))
     assert st == status, (st, msg)
     assert msg
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=_t(FAKE, 1, (4, 16, 640))), 2),                 # rope-aware q, all-e4m3 cache
+    (dict(cache=_t(FAKE, 1, (10, 64, 640))), 2),            # rope-aware cache, all-e4m3 q
+    (dict(q=_t(FAKE, 1, (4, 16, 640)), cache=_t(FAKE, 1, (10, 64, 640), stride=(64 * 704, 704, 1))), 2),
+    (dict(q=_t(FAKE, 1, (4, 16, 640)), cache=_t(FAKE, 1, (10, 64, 640)), cs=_t(FAKE, 2, (10, 32))), 2),
+])
+def test_fp8_decode_rope_aware_validation(over, status):
+    st, msg = call_fp8_decode(fp8_decode_args(**over))
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_fp8_decode_rope_aware_empty_batch_is_ok_without_gpu():
+    st, msg = call_fp8_decode(fp8_decode_args(q=_t(FAKE, 1, (0, 16, 640)), qs=_t(FAKE, 2, (0,)),
+                                              cache=_t(FAKE, 1, (10, 64, 640)), out=_t(FAKE, 0, (0, 16, 512))))
+    assert st == 0, msg
 
 
 def test_fp8_decode_empty_batch_is_ok_without_gpu():
@@ -395,3 +432,11 @@ def test_noalloc_refuses_oversized_calls_without_a_gpu():
                                       ctypes.c_float(a["scale"]), a["mask"], a["window"], a["parts"], ref(a["out"]),
                                       None)
     assert st == 6, lib.mla_last_error_message()
+
+
+def test_sparse_ext_refuses_rope_aware_with_a_sink_or_second_stream():
+    a = sparse_args(q=_t(FAKE, 1, (4, 16, 640)), cache=_t(FAKE, 1, (10, 64, 640)))
+    st, msg = call_sparse_ext(a, sink=_t(FAKE, 2, (16,)))
+    assert st == 5 and msg, (st, msg)
+    st, msg = call_sparse_ext(a, **_xstream())
+    assert st == 5 and msg, (st, msg)
