@@ -57,6 +57,13 @@ Readings of points the pages leave open (each also listed in the design notes):
     float32 scale multiplies the latent codes only, the rope values are taken as
     stored.  V is the dequantised latent part, as above.
 
+  * Shared index lists ([DEC] Parameters fold_shared_index, "read-once shared-index MTP
+    fold", with no formula): every query token of sequence b (rows off[b] .. off[b+1]-1
+    of input_row_offsets) attends to sequence b's one index list (row b of d_indices,
+    its first topk_lengths[b] entries, by the rules above), so the list's rows serve all
+    of the sequence's tokens.  The result is the sparse decode with each token given its
+    sequence's list.
+
   * Attention sink and second KV stream ([DEC] Args attn_sink_ptr, extra_k,
     extra_d_indices, extra_indices_stride, extra_topk_lengths, extra_scales_ptr; the
     page names them without a formula): the sink is one logit per head, shared by the
@@ -332,6 +339,22 @@ def decode_paged_fp8(q8, q_scale, input_row_offsets, page_table, cache_lens, cac
         q = q * np.asarray(q_scale, dtype=np.float64)[:, None, None]
     return decode_paged_f64(q, input_row_offsets, page_table, cache_lens, _LazyE4M3(cache8, cache_scale),
                             page_size, scale, mask, window, rows)
+
+
+def token_lists(input_row_offsets, d_indices_seq, topk_seq):
+    """Per-token index lists from per-sequence ones ([DEC] Parameters fold_shared_index):
+    token t of sequence b takes row b of the lists and its top-k length."""
+    off = np.asarray(input_row_offsets, dtype=np.int64)
+    seq_of = np.repeat(np.arange(len(off) - 1), np.diff(off))
+    return np.asarray(d_indices_seq)[seq_of], np.asarray(topk_seq)[seq_of]
+
+
+def decode_sparse_shared(q8, q_scale, input_row_offsets, cache8, cache_scale, d_indices_seq, topk_seq,
+                         page_size, scale, rows=None):
+    """Sparse FP8 decode where the query tokens of a sequence share its index list
+    (d_indices_seq [B, stride], topk_seq [B]); see token_lists."""
+    idx, topk = token_lists(input_row_offsets, d_indices_seq, topk_seq)
+    return decode_sparse(q8, q_scale, input_row_offsets, cache8, cache_scale, idx, topk, page_size, scale, rows)
 
 
 ROPE_ROW_BYTES = LATENT_DIM + 2 * ROPE_DIM  # 640

@@ -288,6 +288,37 @@ def pin_rope_aware_sparse():
             close(lse[t, h], l, 1e-12)
 
 
+def pin_shared_index_lists():
+    """Query tokens sharing their sequence's list, against attention_row over that list:
+    3 sequences with 2, 1 and 3 tokens, lists of different lengths with a pad inside."""
+    rng = np.random.default_rng(43)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    small = finite[(finite & 0x78) < 0x50]
+    H, ps, pages, stride = 2, 8, 5, 9
+    n_tokens = (2, 1, 3)
+    off = offsets_of(n_tokens)
+    T, B = int(off[-1]), len(n_tokens)
+    cache8 = rng.choice(finite, size=(pages, ps, D)).astype(np.uint8)
+    c_scale = rng.uniform(0.001, 0.01, size=(pages, ps)).astype(np.float32)
+    q8 = rng.choice(small, size=(T, H, D)).astype(np.uint8)
+    q_scale = rng.uniform(0.001, 0.01, size=T).astype(np.float32)
+    idx = rng.integers(0, pages * ps, size=(B, stride)).astype(np.int32)
+    idx[2, 1] = -1
+    topk = np.array([6, 2, 9], dtype=np.int32)
+    out, lse = O.decode_sparse_shared(q8, q_scale, off, cache8, c_scale, idx, topk, ps, SCALE)
+    kv = _torch_e4m3(cache8).reshape(pages * ps, D) * c_scale.reshape(-1).astype(np.float64)[:, None]
+    qv = _torch_e4m3(q8) * q_scale.astype(np.float64)[:, None, None]
+    t = 0
+    for b, n in enumerate(n_tokens):
+        keys = [kv[int(r)].tolist() for r in idx[b, :topk[b]] if r >= 0]
+        for _ in range(n):
+            for h in range(H):
+                o, l = attention_row(qv[t, h].tolist(), keys, [k[:DV] for k in keys], SCALE)
+                close(out[t, h], o, 1e-12)
+                close(lse[t, h], l, 1e-12)
+            t += 1
+
+
 def pin_p1_indexer():
     """The indexer against scalar brute force: scores by plain loops over heads and
     columns with math.fsum (torch's e4m3 widening), selection by a full sort of

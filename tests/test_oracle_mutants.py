@@ -217,13 +217,39 @@ def m_rope_unscaled_latent(mp):
     mp.setattr(O, "rope_aware_to_f64", lambda raw, scales: _rope_aware(raw, None))
 
 
+_token_lists = O.token_lists
+
+
+def m_shared_lists_by_token(mp):
+    """Token t takes list row t (clamped) instead of its sequence's row."""
+    def tl(off, idx, topk):
+        T = int(np.asarray(off)[-1])
+        r = np.minimum(np.arange(T), len(topk) - 1)
+        return np.asarray(idx)[r], np.asarray(topk)[r]
+    mp.setattr(O, "token_lists", tl)
+
+
+def m_shared_lists_first_token_only(mp):
+    """Only the first token of each sequence sees the list; the others see none."""
+    def tl(off, idx, topk):
+        i, k = _token_lists(off, idx, topk)
+        k = k.copy()
+        first = np.asarray(off, dtype=np.int64)[:-1]
+        keep = np.zeros(len(k), dtype=bool)
+        keep[first[first < len(k)]] = True
+        k[~keep] = 0
+        return i, k
+    mp.setattr(O, "token_lists", tl)
+
+
 MUTANTS = [m_scale_dropped, m_values_shifted, m_causal_off_by_one, m_token_order_reversed,
            m_page_slot_swapped, m_combine_unweighted, m_no_max_subtraction, m_softmax_over_heads,
            m_lse_without_max, m_e4m3_bias8, m_sparse_ignores_topk, m_sparse_keeps_pads,
            m_prefill_rope_at_query, m_bf16_low_half,
            m_indexer_unweighted_heads, m_indexer_ties_reversed, m_sink_dropped, m_sink_scaled,
            m_sink_in_numerator, m_extra_stream_ignored, m_extra_reads_main_cache,
-           m_rope_scaled, m_rope_big_endian, m_rope_unscaled_latent]
+           m_rope_scaled, m_rope_big_endian, m_rope_unscaled_latent, m_shared_lists_by_token,
+           m_shared_lists_first_token_only]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
