@@ -47,13 +47,14 @@ DESCRIPTIONS = {
     "M4": "M4: multi-token decode, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64) with 4 query tokens per sequence, causal within the new tokens, bf16",
     "D8": "D8: dense decode over a paged fp8 e4m3 cache, the C1 batch (B=64 H=128 lens U[1024,4096] PS=64), one float32 scale per cache row and per q token",
     "R8": "R8: dense decode in the rope-aware layout (640-byte rows: 512 e4m3 latent codes + 64 bf16 rope values, one float32 scale per cache row and q token on the codes), the C1 batch (B=64 H=128 lens U[1024,4096] PS=64)",
+    "S2": "S2: sparse decode with shared lists, the C4 batch (B=32 H=128, 16384 rows/seq PS=64, top-k U[1024,2048] of 2048 indices, fp8 e4m3) with 2 query tokens per sequence sharing its list",
     "X4": "X4: fp8 top-k indexer in front of C4, 32 sequences x 16384 cache rows PS=64, 1 query token each, 64 heads of width 128, top 2048, causal",
 }
 # multi-token workloads: (configuration they extend, query tokens per sequence)
 MULTI_TOKEN = {"M2": (1, 2), "M4": (1, 4)}
 KERNELS = {"C0": "mla_decode_kernel", "C1": "mla_decode2_kernel", "C2": "mla_decode2_kernel",
            "C3": "mla_prefill_kernel", "C4": "mla_sparse_kernel", "M2": "mla_decode_kernel",
-           "M4": "mla_decode_kernel", "D8": "mla_sparse_kernel", "R8": "mla_sparse_kernel",
+           "M4": "mla_decode_kernel", "D8": "mla_sparse_kernel", "R8": "mla_sparse_kernel", "S2": "mla_sparse_kernel",
            "X4": "mla_indexer_score_kernel + mla_indexer_select_kernel"}
 
 
@@ -169,6 +170,9 @@ def setup(workload, copies, num_partitions, dev):
     elif workload == "X4":
         from synth import indexer_config
         case = indexer_config()
+    elif workload == "S2":
+        from synth import make_shared_sparse_case
+        case = make_shared_sparse_case(355004, [2] * 32, 128, 16384, 64, (1024, 2048), 2048, name="S2")
     else:
         case = config_case(int(workload[1]))
 
@@ -230,6 +234,18 @@ def setup(workload, copies, num_partitions, dev):
             q, c = sets[i % len(sets)]
             m.decode_paged_sparse(q, qs, off, c, cs, idx, topk, case.scale,
                                   num_partitions=num_partitions, out=out)
+        return case, step, case.total_q
+    if workload == "S2":
+        q0, c0 = u8(case.q8), u8(case.cache8)
+        sets = [(q0, c0)] + [(q0.clone(), c0.clone()) for _ in range(n - 1)]
+        qs, cs = f32(case.q_scale), f32(case.cache_scale)
+        off, idx, topk = i32(case.input_row_offsets), i32(case.d_indices), i32(case.topk_lengths)
+        out = torch.empty((case.total_q, case.q8.shape[1], 512), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            q, c = sets[i % len(sets)]
+            m.decode_paged_sparse_shared(q, qs, off, c, cs, idx, topk, case.scale,
+                                         num_partitions=num_partitions, out=out)
         return case, step, case.total_q
     if workload == "C3":
         q0, k0, v0 = bf16(case.q), bf16(case.k), bf16(case.v)
@@ -390,7 +406,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "hbm_achieved_gbs": round(alg_bytes / (k_avg_ms * 1e-3) / 1e9, 2)}
-        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else 'fp8 ' if wl == 'D8' else 'fp8 rope-aware ' if wl == 'R8' else ''}decode GB/s, {wl}, 1 GPU"
+        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl in ('C4', 'S2') else 'fp8 ' if wl == 'D8' else 'fp8 rope-aware ' if wl == 'R8' else ''}decode GB/s, {wl}, 1 GPU"
         if wl == "X4":
             metric = "MLA fp8 top-k indexer GB/s (cache rows once per token), X4, 1 GPU"
         if wl in MULTI_TOKEN:
@@ -405,7 +421,7 @@ def main():
         achieved = alg_bytes / (k_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl)}
-        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl == 'C4' else 'fp8 ' if wl == 'D8' else 'fp8 rope-aware ' if wl == 'R8' else ''}decode GB/s, {wl}, 1 GPU"
+        metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl in ('C4', 'S2') else 'fp8 ' if wl == 'D8' else 'fp8 rope-aware ' if wl == 'R8' else ''}decode GB/s, {wl}, 1 GPU"
         if wl == "X4":
             metric = "MLA fp8 top-k indexer GB/s (cache rows once per token), X4, 1 GPU"
         if wl in MULTI_TOKEN:
@@ -429,13 +445,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 in, bf16 MFMA" if wl in ("C4", "D8") else "fp8-e4m3 + bf16 rope in, bf16 MFMA" if wl == "R8" else "fp8-e4m3 in, f32 scores" if wl == "X4" else "bf16",
+        "dtype": "fp8-e4m3 in, bf16 MFMA" if wl in ("C4", "D8", "S2") else "fp8-e4m3 + bf16 rope in, bf16 MFMA" if wl == "R8" else "fp8-e4m3 in, f32 scores" if wl == "X4" else "bf16",
         "data": "synthetic",
         "config": {
             "workload": DESCRIPTIONS[wl],
             "num_partitions": args.num_partitions if args.num_partitions > 0 else "library",
             "rotated_input_copies": args.copies,
-            "seed": 355000 + (MULTI_TOKEN[wl][0] if wl in MULTI_TOKEN else 1 if wl in ("D8", "R8") else 5 if wl == "X4" else int(wl[1])),
+            "seed": 355000 + (MULTI_TOKEN[wl][0] if wl in MULTI_TOKEN else 1 if wl in ("D8", "R8") else 5 if wl == "X4" else 4 if wl == "S2" else int(wl[1])),
         },
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

@@ -149,6 +149,31 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
                                    void* stream);
 
 /*
+ * Sparse MLA decode with shared index lists (generic_flare_mla_decode_kv_cache_ragged:
+ * Parameters sparse_mla, fold_shared_index; the page names a read-once shared-index fold
+ * for multi-token decode without a formula, so what follows is this library's reading).
+ * Every query token of sequence b (rows input_row_offsets[b] .. input_row_offsets[b+1]-1)
+ * attends to sequence b's one list, read by the rules of mla_decode_paged_sparse.  The
+ * tokens of a sequence are consecutive work of the split and land on the same XCD, so
+ * each listed cache row is fetched from HBM once for all of them and served to the
+ * others from that XCD's L2.
+ *
+ *   q, q_scale, latent_cache, cache_scale, scale, num_partitions, out
+ *                      as for mla_decode_paged_sparse
+ *   input_row_offsets  u32 [B + 1]: non-decreasing, from 0 to T (read on the device;
+ *                      malformed offsets set bit 2 of the device error word and leave
+ *                      their rows zero)
+ *   d_indices          i32 [B, indices_stride]: one list per sequence
+ *   topk_lengths       i32 [B]
+ */
+mla_status mla_decode_paged_sparse_shared(const mla_tensor* q, const mla_tensor* q_scale,
+                                          const mla_tensor* input_row_offsets,
+                                          const mla_tensor* latent_cache, const mla_tensor* cache_scale,
+                                          const mla_tensor* d_indices, const mla_tensor* topk_lengths,
+                                          float scale, int32_t num_partitions, mla_tensor* out,
+                                          void* stream);
+
+/*
  * Sparse MLA decode with an attention sink and a second KV stream
  * (generic_flare_mla_decode_kv_cache_ragged: Args attn_sink_ptr, extra_k,
  * extra_d_indices, extra_indices_stride, extra_topk_lengths, extra_scales_ptr; the page

@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "LIBRARY_PATH", "MlaError", "library", "decode_paged", "decode_paged_noalloc",
-    "decode_noalloc_scratch_bytes", "decode_paged_sparse",
+    "decode_noalloc_scratch_bytes", "decode_paged_sparse", "decode_paged_sparse_shared",
     "decode_paged_sparse_ext", "decode_paged_fp8", "indexer_paged_fp8", "prefill_paged", "decode_num_partitions",
     "decode_workspace_bytes", "reserve_workspace", "check_device_errors", "shutdown",
     "version", "profile_enable", "profile_read", "profile_read_each", "MASKS", "STATUS",
@@ -56,11 +56,12 @@ def library() -> ctypes.CDLL:
         lib.mla_decode_noalloc_scratch_bytes.argtypes = []
         lib.mla_decode_noalloc_scratch_bytes.restype = ctypes.c_size_t
         lib.mla_decode_paged_sparse.argtypes = [P, P, P, P, P, P, P, f32, i32, P, vp]
+        lib.mla_decode_paged_sparse_shared.argtypes = [P, P, P, P, P, P, P, f32, i32, P, vp]
         lib.mla_decode_paged_sparse_ext.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, f32, i32, P, vp]
         lib.mla_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, f32, i32, i32, i32, P, vp]
         lib.mla_indexer_paged_fp8.argtypes = [P, P, P, P, P, P, P, i32, i32, P, vp]
         lib.mla_prefill_paged.argtypes = [P, P, P, P, P, P, P, P, P, f32, i32, P, vp]
-        for fn in ("mla_decode_paged", "mla_decode_paged_noalloc", "mla_decode_paged_sparse", "mla_decode_paged_sparse_ext", "mla_decode_paged_fp8", "mla_indexer_paged_fp8", "mla_prefill_paged",
+        for fn in ("mla_decode_paged", "mla_decode_paged_noalloc", "mla_decode_paged_sparse", "mla_decode_paged_sparse_shared", "mla_decode_paged_sparse_ext", "mla_decode_paged_fp8", "mla_indexer_paged_fp8", "mla_prefill_paged",
                    "mla_reserve_workspace", "mla_check_device_errors"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_decode_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32, i32]
@@ -187,6 +188,22 @@ def decode_paged_sparse(q, q_scale, input_row_offsets, latent_cache, cache_scale
     if out is None:
         out = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
     _check(library().mla_decode_paged_sparse(
+        _desc(q), _desc(q_scale), _offsets(input_row_offsets), _desc(latent_cache),
+        _desc(cache_scale), _desc(d_indices), _desc(topk_lengths), float(scale),
+        int(num_partitions), _desc(out), _stream(stream)))
+    return out
+
+
+def decode_paged_sparse_shared(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices,
+                               topk_lengths, scale, num_partitions=0, out=None, stream=None):
+    """Sparse MLA decode where the query tokens of a sequence share its index list
+    (mla_decode_paged_sparse_shared): d_indices i32 [B, stride] and topk_lengths i32 [B],
+    one per sequence of input_row_offsets; otherwise as decode_paged_sparse."""
+    import torch
+    _on_gpu(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices, topk_lengths, out)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
+    _check(library().mla_decode_paged_sparse_shared(
         _desc(q), _desc(q_scale), _offsets(input_row_offsets), _desc(latent_cache),
         _desc(cache_scale), _desc(d_indices), _desc(topk_lengths), float(scale),
         int(num_partitions), _desc(out), _stream(stream)))

@@ -594,7 +594,7 @@ mla_status sparse_impl(const mla_tensor* q, const mla_tensor* q_scale, const mla
                        const mla_tensor* attn_sink, const mla_tensor* extra_cache,
                        const mla_tensor* extra_cache_scale, const mla_tensor* extra_d_indices,
                        const mla_tensor* extra_topk_lengths, float scale, int32_t num_partitions,
-                       mla_tensor* out, void* stream) {
+                       mla_tensor* out, void* stream, bool shared = false) {
   mla_status s;
   if (!q) return fail(MLA_ERR_NULL_ARG, "q: descriptor is NULL");
   const bool q_bf16 = q->dtype == MLA_DTYPE_BF16;
@@ -612,6 +612,10 @@ mla_status sparse_impl(const mla_tensor* q, const mla_tensor* q_scale, const mla
   }
   if ((s = check_tensor(input_row_offsets, "input_row_offsets", MLA_DTYPE_U32, 1, false)) != MLA_OK) return s;
   if (input_row_offsets->shape[0] < 2) return fail(MLA_ERR_SHAPE, "input_row_offsets: needs batch + 1 >= 2 entries");
+  // the rows of d_indices / topk_lengths: one per query row, or one per sequence (shared)
+  const int64_t B = input_row_offsets->shape[0] - 1;
+  const int64_t LR = shared ? B : T;
+  if (shared && B > kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "more than 2^24 sequences");
   if (latent_cache->dtype == MLA_DTYPE_BF16)
     return fail(MLA_ERR_UNSUPPORTED, "sparse decode reads an fp8 e4m3 cache; a bf16 cache is not supported");
   if ((s = check_tensor(latent_cache, "latent_cache", MLA_DTYPE_FP8_E4M3, 3, true)) != MLA_OK) return s;
@@ -629,11 +633,11 @@ mla_status sparse_impl(const mla_tensor* q, const mla_tensor* q_scale, const mla
       return fail(MLA_ERR_SHAPE, "cache_scale: shape must be [%lld, %lld]", (long long)NP, (long long)PS);
   }
   if ((s = check_tensor(d_indices, "d_indices", MLA_DTYPE_I32, 2, false)) != MLA_OK) return s;
-  if (d_indices->shape[0] != T) return fail(MLA_ERR_SHAPE, "d_indices: %lld rows, expected %lld", (long long)d_indices->shape[0], (long long)T);
+  if (d_indices->shape[0] != LR) return fail(MLA_ERR_SHAPE, "d_indices: %lld rows, expected %lld", (long long)d_indices->shape[0], (long long)LR);
   if (d_indices->shape[1] > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "d_indices: too many columns");
-  if (T > 1 && d_indices->stride[0] < d_indices->shape[1])
+  if (LR > 1 && d_indices->stride[0] < d_indices->shape[1])
     return fail(MLA_ERR_SHAPE, "d_indices: row stride below the row length");
-  if ((s = check_1d(topk_lengths, "topk_lengths", MLA_DTYPE_I32, T)) != MLA_OK) return s;
+  if ((s = check_1d(topk_lengths, "topk_lengths", MLA_DTYPE_I32, LR)) != MLA_OK) return s;
   if ((s = check_tensor(out, "out", MLA_DTYPE_BF16, 3, true)) != MLA_OK) return s;
   if (out->shape[0] != T || out->shape[1] != H || out->shape[2] != 512)
     return fail(MLA_ERR_SHAPE, "out: shape must be [%lld, %lld, 512]", (long long)T, (long long)H);
@@ -703,6 +707,11 @@ mla_status sparse_impl(const mla_tensor* q, const mla_tensor* q_scale, const mla
   a.PS = (int32_t)PS;
   a.flat = a.page_bytes == PS * RW && (cache_scale == nullptr || a.cs_page == PS) ? 1 : 0;
   a.rope = RW == 640 ? 1 : 0;
+  a.shared = shared ? 1 : 0;
+  if (shared) {
+    a.offsets = (const uint32_t*)input_row_offsets->data;
+    a.B = (int32_t)B;
+  }
   a.idx = (const int32_t*)d_indices->data;
   a.idx_row = d_indices->stride[0];
   a.idx_cols = (int32_t)d_indices->shape[1];
@@ -756,6 +765,16 @@ mla_status mla_decode_paged_sparse(const mla_tensor* q, const mla_tensor* q_scal
                                    void* stream) {
   return sparse_impl(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices, topk_lengths, nullptr,
                      nullptr, nullptr, nullptr, nullptr, scale, num_partitions, out, stream);
+}
+
+mla_status mla_decode_paged_sparse_shared(const mla_tensor* q, const mla_tensor* q_scale,
+                                          const mla_tensor* input_row_offsets,
+                                          const mla_tensor* latent_cache, const mla_tensor* cache_scale,
+                                          const mla_tensor* d_indices, const mla_tensor* topk_lengths,
+                                          float scale, int32_t num_partitions, mla_tensor* out,
+                                          void* stream) {
+  return sparse_impl(q, q_scale, input_row_offsets, latent_cache, cache_scale, d_indices, topk_lengths, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, scale, num_partitions, out, stream, true);
 }
 
 mla_status mla_decode_paged_sparse_ext(const mla_tensor* q, const mla_tensor* q_scale,

@@ -53,10 +53,13 @@ struct SparseArgs {
   int64_t num_rows;           // num_pages * PS: listed rows outside [0, num_rows) are skipped
   int32_t PS;
   int32_t flat;               // 1: row r is at byte r * (576 or 640) and its scale at element r
-  const int32_t* idx;         // [T, idx_row]
+  const int32_t* idx;         // [T, idx_row] ([B, idx_row] with shared lists)
   int64_t idx_row;            // element stride between index rows
   int32_t idx_cols;           // shape[1] of d_indices (topk is clamped to it)
-  const int32_t* topk;        // [T]
+  const int32_t* topk;        // [T] ([B] with shared lists)
+  // shared = 1 ([DEC] Parameters fold_shared_index): idx / topk hold one list per
+  // sequence, [B, idx_row] / [B], read by every query row of the sequence (offsets, B)
+  int32_t shared;
   // dense = 1: the rows of q row t are the visible positions of its sequence, physical
   // row page_table[b][pos / PS] * PS + pos % PS (idx and topk are unused)
   int32_t dense;

@@ -74,14 +74,44 @@ __device__ __forceinline__ int sparse_len(const SparseArgs& a, int t) {
   if (XTRA && a.xidx != nullptr) n += max(0, min(ld_const(a.xtopk + t), a.xidx_cols));
   return n;
 }
+// Row geometry: b = the row of d_indices / topk_lengths that query row t reads -- t itself,
+// or with shared lists ([DEC] Parameters fold_shared_index) the sequence of t in the
+// input_row_offsets (-1 with no visible entry for a row outside them) -- and the list
+// positions [0, n).
 template <bool XTRA>
 __device__ __forceinline__ RowGeo sparse_row_geo(const SparseArgs& a, int t) {
-  return RowGeo{t, 0, sparse_len<XTRA>(a, t)};
+  if (!a.shared) return RowGeo{t, 0, sparse_len<XTRA>(a, t)};
+  int lo = 0, hi = a.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int)ld_const(a.offsets + mid) <= t) lo = mid; else hi = mid;
+  }
+  const int o0 = (int)ld_const(a.offsets + lo), o1 = (int)ld_const(a.offsets + lo + 1);
+  if (t < o0 || t >= o1) return RowGeo{-1, 0, 0};
+  return RowGeo{lo, 0, sparse_main_len(a, lo)};
+}
+
+// Shared lists: sequence b (one thread or lane per sequence) writes the geometry of its
+// query rows; malformed offsets set kErrOffsets and leave their rows empty.
+__device__ __forceinline__ void sparse_fill_seq(const SparseArgs& a, RowGeo* geo, int b) {
+  const int o0 = (int)a.offsets[b], o1 = (int)a.offsets[b + 1];
+  if (o1 < o0 || o0 < 0 || o1 > a.T) {
+    atomicOr(a.err, kErrOffsets);
+    return;
+  }
+  const int n = sparse_main_len(a, b);
+  for (int t = o0; t < o1; ++t) geo[t] = RowGeo{b, 0, n};
 }
 
 template <int NT, bool XTRA>
 __device__ __forceinline__ void sparse_fill(const SparseArgs& a, PlanLds& L) {
-  for (int t = threadIdx.x; t < a.T; t += NT) L.geo[t] = RowGeo{t, 0, sparse_len<XTRA>(a, t)};
+  if (!a.shared) {
+    for (int t = threadIdx.x; t < a.T; t += NT) L.geo[t] = RowGeo{t, 0, sparse_len<XTRA>(a, t)};
+    return;
+  }
+  for (int t = threadIdx.x; t < a.T; t += NT) L.geo[t] = RowGeo{-1, 0, 0};
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.B; b += NT) sparse_fill_seq(a, L.geo, b);
 }
 
 // One row segment: list positions of tiles [ta, tc) of row t.
@@ -120,7 +150,7 @@ __device__ __forceinline__ void sparse_segment(const SparseArgs& a, MLA_LDS uint
   const int khi = __builtin_amdgcn_readfirstlane(min(g.hi, (first_tile + tc) * kTileKeys));
   const int s_first = klo / kStageKeys;
   const int nst = (khi - 1) / kStageKeys - s_first + 1;
-  const int32_t* ilist = a.idx + (int64_t)t * a.idx_row;
+  const int32_t* ilist = a.idx + (int64_t)g.b * a.idx_row;  // g.b: the list row of t
   // XTRA: positions from nmain on are the second list's (block-uniform)
   const int nmain = XTRA && a.xidx != nullptr ? __builtin_amdgcn_readfirstlane(sparse_main_len(a, t)) : INT32_MAX;
   const int32_t* xlist = XTRA ? a.xidx + (int64_t)t * a.xidx_row : nullptr;
@@ -490,8 +520,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs
         if constexpr (DENSE) return decode_row_geo(a, t); else return sparse_row_geo<XTRA>(a, t);
       },
       [&](RowGeo* geo, int lane) {
-        if constexpr (DENSE) decode_fill_wave(a, geo, lane);
-        else if (lane < a.T) geo[lane] = RowGeo{lane, 0, sparse_len<XTRA>(a, lane)};
+        if constexpr (DENSE) {
+          decode_fill_wave(a, geo, lane);
+        } else if (!a.shared) {
+          if (lane < a.T) geo[lane] = RowGeo{lane, 0, sparse_len<XTRA>(a, lane)};
+        } else {
+          if (lane < a.T) geo[lane] = RowGeo{-1, 0, 0};
+          if (lane < a.B) sparse_fill_seq(a, geo, lane);
+        }
       },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
         sparse_segment<HB, NW, DENSE, XTRA, ROPE>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
@@ -520,7 +556,7 @@ static SplitPlan plan_of(const SparseArgs& a) {
 template <int HB, int NW>
 static hipError_t launch_sparse_h(const SparseArgs& a, const SplitPlan& p, hipStream_t stream) {
   const dim3 grid(a.nparts >= 1 ? a.T * a.nparts : a.grid), block(NW * 64);
-  const bool small = a.nparts == 0 && a.T <= 64 && a.T <= a.grid && (!a.dense || a.B <= 64);
+  const bool small = a.nparts == 0 && a.T <= 64 && a.T <= a.grid && ((!a.dense && !a.shared) || a.B <= 64);
   if (a.rope) {
     if (a.xidx != nullptr || a.sink != nullptr) return hipErrorInvalidValue;  // refused by the host checks
     if (a.dense) {

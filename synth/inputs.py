@@ -44,7 +44,7 @@ __all__ = [
     "HEAD_DIM", "LATENT_DIM", "ROPE_DIM", "PREFILL_QK_DIM", "PREFILL_V_DIM",
     "PREFILL_NOPE_DIM", "BF16_NAN_BITS", "E4M3_NAN_CODE", "default_scale", "rope_aware",
     "bf16_bits", "e4m3_codes", "DecodeCase", "SparseCase", "PrefillCase",
-    "make_decode_case", "make_sparse_case", "make_prefill_case", "config_case",
+    "make_decode_case", "make_sparse_case", "make_shared_sparse_case", "make_prefill_case", "config_case",
     "CONFIG_DESCRIPTIONS", "algorithmic_bytes", "algorithmic_flops",
     "IndexerCase", "make_indexer_case", "indexer_config",
 ]
@@ -346,6 +346,20 @@ def make_sparse_case(seed, batch, num_heads, rows_per_seq, page_size, topk_range
                       rows_per_seq=rows_per_seq)
 
 
+def make_shared_sparse_case(seed, n_tokens, num_heads, rows_per_seq, page_size, topk_range, n_index,
+                            name="shared"):
+    """Sparse inputs with one index list per sequence shared by its query tokens: the
+    lists, cache and scales of make_sparse_case(seed, len(n_tokens), ...), and q drawn for
+    sum(n_tokens) tokens (with its per-token scales) from seed + 1.  input_row_offsets
+    gives the tokens of each sequence; d_indices / topk_lengths have one row per sequence."""
+    B, T = len(n_tokens), int(sum(n_tokens))
+    base = make_sparse_case(seed, B, num_heads, rows_per_seq, page_size, topk_range, n_index, name=name)
+    tok = make_sparse_case(seed + 1, T, num_heads, 64, 16, (1, 1), 1, name=name + "-q")
+    off = np.zeros(B + 1, dtype=np.uint32)
+    off[1:] = np.cumsum(n_tokens)
+    return dataclasses.replace(base, q8=tok.q8, q_scale=tok.q_scale, input_row_offsets=off)
+
+
 # --------------------------------------------------------------------------------------
 # FP8 top-k indexer
 # --------------------------------------------------------------------------------------
@@ -506,8 +520,9 @@ def algorithmic_bytes(case) -> int:
             return rows * row_bytes + qb
         return rows * HEAD_DIM * 2 + case.q.size * 2
     if isinstance(case, SparseCase):
-        listed = int(sum(int(np.count_nonzero(case.d_indices[t, :case.topk_lengths[t]] >= 0))
-                         for t in range(case.total_q)))
+        # every list's rows once (a list shared by a sequence's tokens is read once)
+        listed = int(sum(int(np.count_nonzero(case.d_indices[r, :case.topk_lengths[r]] >= 0))
+                         for r in range(case.d_indices.shape[0])))
         row_bytes = int(case.cache8.shape[-1]) + (4 if case.cache_scale is not None else 0)
         qb = case.q8.size + (case.q_scale.size * 4 if case.q_scale is not None else 0)
         return listed * row_bytes + qb
@@ -547,8 +562,12 @@ def algorithmic_flops(case) -> int:
                     pairs += max(0, hi - lo)
         return pairs * 2 * H * (HEAD_DIM + LATENT_DIM)
     if isinstance(case, SparseCase):
-        listed = int(sum(int(np.count_nonzero(case.d_indices[t, :case.topk_lengths[t]] >= 0))
-                         for t in range(case.total_q)))
+        per_list = [int(np.count_nonzero(case.d_indices[r, :case.topk_lengths[r]] >= 0))
+                    for r in range(case.d_indices.shape[0])]
+        if case.d_indices.shape[0] == case.total_q:
+            listed = sum(per_list)
+        else:  # shared lists: each token of sequence b attends to list b
+            listed = int(sum(n * c for n, c in zip(np.diff(case.input_row_offsets.astype(np.int64)), per_list)))
         return listed * 2 * case.num_heads * (HEAD_DIM + LATENT_DIM)
     if isinstance(case, PrefillCase):
         H = case.num_heads

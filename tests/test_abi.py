@@ -440,3 +440,32 @@ def test_sparse_ext_refuses_rope_aware_with_a_sink_or_second_stream():
     assert st == 5 and msg, (st, msg)
     st, msg = call_sparse_ext(a, **_xstream())
     assert st == 5 and msg, (st, msg)
+
+
+def call_sparse_shared(a):
+    lib = m.library()
+    ref = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    st = lib.mla_decode_paged_sparse_shared(ref(a["q"]), ref(a["qs"]), ref(a["off"]), ref(a["cache"]),
+                                            ref(a["cs"]), ref(a["idx"]), ref(a["topk"]),
+                                            ctypes.c_float(a["scale"]), a["parts"], ref(a["out"]), None)
+    return st, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(idx=_t(FAKE, 3, (4, 32))), 2),                    # one list per token, not per sequence
+    (dict(topk=_t(FAKE, 3, (4,))), 2),                      # topk per token
+    (dict(off=_t(FAKE, 4, (1,))), 2),                       # no sequence
+])
+def test_sparse_shared_validation(over, status):
+    a = sparse_args(off=_t(FAKE, 4, (3,)), idx=_t(FAKE, 3, (2, 32)), topk=_t(FAKE, 3, (2,)))
+    a.update(over)
+    st, msg = call_sparse_shared(a)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_sparse_shared_empty_batch_is_a_no_op():
+    a = sparse_args(q=_t(FAKE, 1, (0, 16, 576)), qs=_t(FAKE, 2, (0,)), off=_t(FAKE, 4, (3,)),
+                    idx=_t(FAKE, 3, (2, 32)), topk=_t(FAKE, 3, (2,)), out=_t(FAKE, 0, (0, 16, 512)))
+    st, msg = call_sparse_shared(a)
+    assert st == 0, msg
