@@ -23,9 +23,11 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  The batch decode keeps its running scores in ordinary registers
-# (the accumulation registers hold the output tile): its score MFMAs use the VGPR form.
-EXTRA = {"mla_decode2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The batch decode kernels keep their running scores in ordinary
+# registers (the accumulation registers hold the output tile): their score MFMAs use the
+# VGPR form.
+EXTRA = {"mla_decode2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "mla_fp8mma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

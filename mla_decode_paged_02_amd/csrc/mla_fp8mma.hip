@@ -1,0 +1,627 @@
+// Dense MLA decode over a paged fp8 e4m3 cache with the scores on fp8 MFMA (gfx950).
+//
+// What is computed follows generic_flare_mla_decode_kv_cache_ragged (summary; Args q,
+// q_scale_ptr, kv_collection, input_row_offsets, scale, output; Parameters mask_str,
+// local_window_size, per_token_scale_rope_aware): mla_decode_paged_fp8, whose general
+// kernel is mla_sparse.hip with dense = 1.  This kernel serves its balanced split of at
+// most 64 rows and sequences at 128 heads.
+//
+// Per work-group (4 waves, one per SIMD) and 32-key stage:
+//   scores    wave w computes S^T = K Q^T for heads 32w..32w+31 straight from the e4m3
+//             codes: v_mfma_f32_32x32x64_f8f6f4 over the 576 columns (9 k-steps), or with
+//             ROPE over the 512 latent columns (8 k-steps) plus v_mfma_f32_32x32x16_bf16 over
+//             the 64 bf16 rope columns (4 k-steps) into a second accumulator, so that the
+//             logit is scale * (sigma_q sigma_k S_latent + S_rope) exactly;
+//   values    the stage's 512 latent columns are widened to bf16 (exact) into a value tile
+//             while the matrix cores run the previous stage's values: wave w owns output
+//             columns 128w..128w+127 of all heads, O^T += V^T (P sigma_k)^T with the bf16
+//             weights of every head exchanged through LDS (the row scale rides on the weight,
+//             so V stays the bare codes and P keeps bf16 precision).
+// The stage pipeline is that of mla_decode2.hip: step k scores stage k while the vector
+// units run the online softmax of stage k-1, then adds the values of stage k-1.
+//
+// Layout of a stage's fp8 rows in LDS: chunk-major, 16-byte chunk c of row r at
+// (32 c + r) * 16.  A score operand (lane 32g + i: row i, bytes 64 ks + 32g .. + 31, two
+// chunks) is then two reads of 512 contiguous bytes per half-wave, and the stage loads put
+// chunk 2J + (lane >> 5) of row lane & 31 at load J: a per-lane constant plus 32 J bytes.
+// The operand layout of the fp8 MFMA (lane 32g + i holds 32 k-values of row i of A and of
+// column i of B, the halves g disjoint; D as for the bf16 32x32 MFMAs) was checked on
+// MI355X against exact products.
+#include <type_traits>
+
+#include "mla_device.h"
+#include "mla_kernels.h"
+#include "mla_plan.h"
+#include "mla_rows.h"
+#include "mla_stage.h"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kF8Raw = 3;                 // fp8 stage buffers: scores of k, k+1 landed, k+2 in flight
+constexpr int kF8PidWindow = 512;         // page ids of the segment held in LDS
+constexpr int kF8PBytes = 4 * 2 * 64 * 16;  // weights: [head block][value k-step][lane] x 16 B
+constexpr int kF8VBytes = 32 * kRowBytes;   // one bf16 value tile (rows of 1152 bytes, 1024 used)
+constexpr int kF8Loads = 5;               // row loads per wave and stage (the last may repeat one)
+constexpr int kF8Scales = 4;              // scale slots: stage k-1 (softmax), k, k+1, k+2 (loading)
+
+template <bool ROPE>
+struct F8Geo {
+  static constexpr int kRow = ROPE ? 640 : 576;        // bytes of a cache / q row
+  static constexpr int kChunks = kRow / 16;            // 40 / 36
+  static constexpr int kStage = kStageKeys * kRow;     // 20480 / 18432
+  static constexpr int kDma = kStage / 1024;           // 20 / 18 wave-wide loads
+  static constexpr int kKs8 = ROPE ? 8 : 9;            // fp8 k-steps of 64 columns
+  static_assert(kDma <= 4 * kF8Loads, "every stage load has a wave");
+};
+
+struct F8Lds {
+  RowGeo geo[256];            // per-wave planning tables (64 rows each)
+  int pids[kF8PidWindow];     // page-id window of the segment
+  float ksc[kF8Scales][64];   // the stages' row scales (lanes 32..63 repeat 0..31)
+};
+
+// LDS swizzle of the bf16 value tile (rows of 72 16-byte chunks, 64 used), the one the
+// transposing value reads of mla_decode2.hip were measured conflict-free with.
+__device__ __forceinline__ int f8_swz(int r) { return ((r >> 4) & 1) | (((r >> 1) & 1) << 1) | (((r ^ (r >> 2)) & 1) << 2); }
+
+__device__ __forceinline__ void mfma32_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// Wait states between the last write of a 16-pass MFMA into the accumulation registers
+// and other instructions reading them (24, above the 18 the longest such distance needs):
+// these MFMAs are inline assembly, which the compiler's hazard tracking does not see.
+__device__ __forceinline__ void fence_o(f32x16 (&o)[4][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]));
+#pragma unroll
+  for (int cb = 1; cb < 4; ++cb) asm volatile("" : "+a"(o[cb][0]), "+a"(o[cb][1]), "+a"(o[cb][2]), "+a"(o[cb][3]));
+}
+
+template <int KPAGES, bool ROPE>
+__device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint8_t* raw, MLA_LDS uint8_t* vt,
+                                               MLA_LDS uint8_t* xbuf, F8Lds& L, int t, const RowGeo& g, int ta,
+                                               int tc, bool full, int slot) {
+  using G = F8Geo<ROPE>;
+  constexpr int NT = 256;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = lane >> 5, li = lane & 31;
+  const int h0 = wave * 32;
+  MLA_LDS int* pids = (MLA_LDS int*)L.pids;
+  auto ksl = [&](int st) { return (MLA_LDS float*)L.ksc[st % kF8Scales]; };  // scale slot of stage st
+  MLA_LDS uint8_t* pbuf = xbuf;                                    // weights
+  MLA_LDS float* alpha_s = (MLA_LDS float*)(xbuf + kF8PBytes);     // [4][32]
+  MLA_LDS int* flag_s = (MLA_LDS int*)(xbuf + kF8PBytes + 512);    // [4]
+  MLA_LDS float* inv_s = (MLA_LDS float*)(xbuf + kF8PBytes + 1024);  // [128], after the loop
+
+  const int first_tile = __builtin_amdgcn_readfirstlane(g.lo / kTileKeys);
+  const int klo = __builtin_amdgcn_readfirstlane(max(g.lo, (first_tile + ta) * kTileKeys));
+  const int khi = __builtin_amdgcn_readfirstlane(min(g.hi, (first_tile + tc) * kTileKeys));
+  const int s_first = klo / kStageKeys;
+  const int nst = (khi - 1) / kStageKeys - s_first + 1;
+  const int32_t* pt = a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.pt_row;
+  const int p_last = (khi - 1) / a.PS;
+  const int npages32 = (int)min(a.num_rows / a.PS, (int64_t)INT32_MAX);
+
+  // every wave must be done with the buffers and window of anything before
+  all_wait0();
+  stage_barrier();
+
+  // ---- page-id window [pbase, pbase + kF8PidWindow) (entries past the segment are -1)
+  int pbase = klo / a.PS;
+  int pv[kF8PidWindow / NT];
+  auto window_load = [&]() {
+#pragma unroll
+    for (int i = 0; i < kF8PidWindow / NT; ++i) {
+      const int p = pbase + tid + i * NT;
+      pv[i] = p <= p_last ? pt[p] : -1;
+    }
+  };
+  auto window_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < kF8PidWindow / NT; ++i) pids[tid + i * NT] = pv[i];
+  };
+  // moves the window to start at page `base` (block-uniform call; drains the stage loads)
+  auto window_move = [&](int base) {
+    all_wait0();
+    stage_barrier();
+    pbase = base;
+    window_load();
+    all_wait0();
+    window_store();
+    lgkm_wait0();
+    stage_barrier();
+  };
+  if (KPAGES == 0) {
+    window_load();
+    all_wait0();
+    window_store();
+    lgkm_wait0();
+    stage_barrier();
+  }
+
+  bool bad_page = false;
+  // page of the stage last looked up, its id, and the id of the page after it (read from
+  // the window ahead of need; -1 past the window)
+  int lp_last = -1, pid_last = -1, pid_next_v = -1;
+  auto stage_page = [&](int st) {
+    const int kb0 = st * kStageKeys;  // consecutive stages: the page stays or advances by one
+    if (lp_last >= 0 && kb0 >= lp_last * a.PS && kb0 < (lp_last + 1) * a.PS) return pid_last;
+    if (lp_last >= 0 && kb0 >= (lp_last + 1) * a.PS && kb0 < (lp_last + 2) * a.PS &&
+        lp_last + 1 < pbase + kF8PidWindow) {
+      lp_last += 1;
+      pid_last = __builtin_amdgcn_readfirstlane(pid_next_v);
+    } else {
+      const int lp = kb0 / a.PS;
+      if (lp >= pbase + kF8PidWindow) window_move(lp);
+      lp_last = lp;
+      pid_last = __builtin_amdgcn_readfirstlane(pids[lp - pbase]);
+    }
+    const int nx = lp_last + 1 - pbase;
+    pid_next_v = nx < kF8PidWindow ? pids[nx] : -1;
+    return pid_last;
+  };
+  // a stage inside one valid page: the scalar base of its first row, else null
+  auto fast_base = [&](int st, int pa) -> const uint8_t* {
+    const int kbase = st * kStageKeys;
+    if (KPAGES != 0 && kbase >= klo && kbase + kStageKeys <= khi && pa >= 0 && pa < npages32)
+      return a.cache + (int64_t)pa * a.page_bytes + (int64_t)((uint32_t)kbase % (uint32_t)a.PS) * G::kRow;
+    return nullptr;
+  };
+  // load jj of this wave: global load J (the spare ones repeat the last, same bytes to the
+  // same place); lane -> row lane & 31, chunk 2J + (lane >> 5)
+  auto load_j = [&](int jj) { return min(jj * 4 + wave, G::kDma - 1); };
+  int lane_c = lane;
+  asm volatile("" : "+v"(lane_c));
+  const uint32_t doff0 = (uint32_t)((lane_c & 31) * G::kRow + 16 * (lane_c >> 5));
+  auto fast_load = [&](const uint8_t* base, MLA_LDS uint8_t* dst, int jj) {
+    const int J = load_j(jj);
+    dma16_base_nt(base, doff0 + 32 * J, dst + J * 1024);
+  };
+  // the stage's 32 row scales into its slot (every wave loads the same 32 floats)
+  auto scale_src_fast = [&](int st, int pa) -> const void* {
+    if (a.cache_scale == nullptr) return a.zero_row + kSparseOneOffset;
+    const int kbase = st * kStageKeys;
+    return a.cache_scale + (int64_t)pa * a.cs_page + ((uint32_t)kbase % (uint32_t)a.PS) + (lane_c & 31);
+  };
+  // pa: the stage's page id when a stage lies in one page (KPAGES), which the window may
+  // not hold yet (the prologue issues before it is stored)
+  auto issue_general = [&](int st, int bi, int pa) {
+    MLA_LDS uint8_t* dst = raw + bi * G::kStage;
+    const int kbase = st * kStageKeys;
+    if (KPAGES == 0) {
+      const int lp_hi = (min(kbase + kStageKeys, khi) - 1) / a.PS;
+      if (lp_hi >= pbase + kF8PidWindow) window_move(max(kbase, klo) / a.PS);
+    }
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int row = lane_v & 31, key = kbase + row;
+    const uint8_t* rsrc = nullptr;  // this lane's row, null: the zero row
+    const void* ssrc = a.zero_row;  // and its scale (0 for a key that does not count)
+    if (key >= klo && key < khi) {
+      const int lp = key / a.PS;
+      const int pid = KPAGES != 0 ? pa : pids[lp - pbase];
+      if (pid >= 0 && pid < npages32) {
+        rsrc = a.cache + (int64_t)pid * a.page_bytes + (int64_t)(key - lp * a.PS) * G::kRow;
+        ssrc = a.cache_scale == nullptr ? (const void*)(a.zero_row + kSparseOneOffset)
+                                        : (const void*)(a.cache_scale + (int64_t)pid * a.cs_page + (key - lp * a.PS));
+      } else {
+        bad_page = true;
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kF8Loads; ++jj) {
+      const int J = load_j(jj);
+      const int c = 2 * J + (lane_v >> 5);
+      dma16_nt((rsrc != nullptr ? rsrc : a.zero_row) + 16 * c, dst + J * 1024);
+    }
+    dma4(ssrc, ksl(st - s_first));
+  };
+  auto issue = [&](int st, int bi, int pa) {
+    const uint8_t* fb = fast_base(st, pa);
+    if (fb == nullptr) {
+      issue_general(st, bi, pa);
+      return;
+    }
+#pragma unroll
+    for (int jj = 0; jj < kF8Loads; ++jj) fast_load(fb, raw + bi * G::kStage, jj);
+    dma4(scale_src_fast(st, pa), ksl(st - s_first));
+  };
+
+  // ---- query fragments (B operand of S^T = K Q^T): lane 32g + i holds q[head h0 + i]
+  // bytes 64 ks + 32 g .. + 31 (e4m3), with ROPE also bf16 rope columns 16 kr + 8 g .. + 7
+  const uint8_t* qh = a.q + (int64_t)t * a.q_tok + (int64_t)(h0 + li) * a.q_head;
+  i32x8 qf[G::kKs8];
+#pragma unroll
+  for (int ks = 0; ks < G::kKs8; ++ks) {
+    const uint4 lo = *(const uint4*)(qh + 64 * ks + 32 * lg);
+    const uint4 hi = *(const uint4*)(qh + 64 * ks + 32 * lg + 16);
+    qf[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  bf16x8 qr[4];
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int kr = 0; kr < 4; ++kr) qr[kr] = *(const bf16x8*)(qh + 512 + 32 * kr + 16 * lg);
+  }
+  const float q_scale = a.q_scale != nullptr ? ld_const(a.q_scale + t) : 1.f;
+  const float qsl = a.scale_log2 * q_scale;  // logit units per code product (times sigma_k)
+
+  // ---- prologue: stages 0 and 1 (their page ids by scalar loads, which the full wait
+  // covers), the window for the loop, and zeros in the value tile "stage -1" uses
+  auto direct_page = [&](int st) { return ld_const(pt + st * kStageKeys / a.PS); };
+  const int pa0 = KPAGES != 0 ? direct_page(s_first) : 0;
+  const int pa1 = (KPAGES != 0 && nst > 1) ? direct_page(s_first + 1) : 0;
+  int pa_n = (KPAGES != 0 && nst > 2) ? direct_page(s_first + 2) : 0;
+  // stage "-1" reads a scale slot no load writes: zeros, so its weights are 0 x 0
+  for (int i = tid; i < kF8Scales * 64; i += NT) ((MLA_LDS float*)L.ksc)[i] = 0.f;
+  lgkm_wait0();
+  stage_barrier();
+  issue(s_first, 0, pa0);
+  if (nst > 1) issue(s_first + 1, 1, pa1);
+  if (KPAGES != 0) window_load();
+  {
+    MLA_LDS uint8_t* z = vt + kF8VBytes;
+    for (int i = tid; i < kF8VBytes / 16; i += NT) *(MLA_LDS u32x4*)(z + 16 * i) = u32x4{0, 0, 0, 0};
+  }
+  all_wait0();
+  if (KPAGES != 0) window_store();
+  lgkm_wait0();  // made visible to the other waves by the barrier at the loop top
+
+  f32x16 O[4][4];  // O^T tile (column block cb, head block hb), lane 32g+i: head 32hb + i
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      O[cb][hb] = f32x16{};
+      asm volatile("" : "+a"(O[cb][hb]));
+    }
+  float m = -INFINITY, l = 0.f;  // own head h0 + li (lanes i and 32 + i agree on m)
+  uint32_t pk[8];                // weights of the last scored stage (bf16 pairs)
+  float alpha = 1.f;             // its rescale factor of this head
+  int rflag = 0;                 // some head of this wave rescaled at that stage
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pk[i] = 0;
+
+  // Transposing value reads (the layout of mla_decode2.hip): lane 16G + 4r + q (G = 2g + c)
+  // reads row 16kp + 8h + 4g + r, chunk 16w + 4cb + 2c + (q >> 1); four per-lane bases.
+  int vb[2][2];
+  {
+    const int G2 = lane >> 4, gg = G2 >> 1, c = G2 & 1, r = (lane >> 2) & 3, q = lane & 3;
+    const int brow = 4 * gg + r;
+    const int X = (2 * c + (q >> 1)) ^ f8_swz(brow);
+    const int base = brow * kRowBytes + 256 * wave + 8 * (q & 1);
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) vb[kp][pp] = base + ((X ^ kp ^ (4 * pp)) << 4);
+  }
+  // widening: piece p = tid + 256 u (u < 4) is chunk p >> 5 (of the 32 latent chunks) of row
+  // p & 31; it becomes bf16 chunks 2c and 2c + 1 of that row of the value tile
+  int wdst[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int tid_v = tid;
+    asm volatile("" : "+v"(tid_v));
+    const int p = tid_v + 256 * u, c = p >> 5, r = p & 31, f = f8_swz(r);
+    wdst[u] = r * kRowBytes + ((((2 * c) & ~7) | (((2 * c) ^ f) & 7)) << 4);
+  }
+
+  // Step k scores stage k while the vector units turn the scores of stage k-1 into
+  // weights; once every wave has published its weights, it adds the values of stage k-1
+  // and widens the values of stage k.  Every step runs the whole stream: at k = 0 no key
+  // of "stage -1" is valid (zero weights on the zeroed value tile), and at k = nst the
+  // scores of a stale buffer are computed and dropped.
+  f32x16 Sp, Rp;  // scores of stage k-1: e4m3 products, and (ROPE) the bf16 rope products
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    Sp[e] = 0.f;
+    Rp[e] = 0.f;
+  }
+  auto pin = [](float& v) { asm volatile("" : "+v"(v)); };
+  auto pinu = [](uint32_t& v) { asm volatile("" : "+v"(v)); };
+#pragma unroll 1
+  for (int k = 0; k <= nst; ++k) {
+    // ---- stage k has landed (stage k+1 may still be in flight)
+    if (k < nst) {
+      if (k >= 1 && k + 1 < nst) vm_wait_imm<kF8Loads + 1>(); else vm_wait_imm<0>();
+    }
+    stage_barrier();  // also: every wave is done with stage k-1's raw buffer and tile k%2
+    const int kn = k + 2;
+    const uint8_t* fb = nullptr;
+    int pa_k = 0;
+    if (kn < nst) {
+      pa_k = pa_n;
+      fb = fast_base(s_first + kn, pa_n);
+      if (fb == nullptr) issue_general(s_first + kn, kn % kF8Raw, pa_n);
+      if (KPAGES != 0 && kn + 1 < nst) pa_n = stage_page(s_first + kn + 1);
+    }
+    MLA_LDS uint8_t* fdst = raw + (kn % kF8Raw) * G::kStage;
+    const MLA_LDS uint8_t* rs = raw + (k % kF8Raw) * G::kStage;     // stage k's rows
+    const MLA_LDS float* ksp = ksl(k + kF8Scales - 1);               // stage k-1's scales
+    const MLA_LDS uint8_t* vrd = vt + ((k + 1) & 1) * kF8VBytes;    // values of stage k-1
+    MLA_LDS uint8_t* vwr = vt + (k & 1) * kF8VBytes;                // values of stage k
+    auto kread = [&](int ks) {
+      const u32x4 lo = *(const MLA_LDS u32x4*)(rs + ((4 * ks + 2 * lg) * 32 + li) * 16);
+      const u32x4 hi = *(const MLA_LDS u32x4*)(rs + ((4 * ks + 2 * lg + 1) * 32 + li) * 16);
+      return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto rread = [&](int kr) { return *(const MLA_LDS bf16x8*)(rs + ((32 + 2 * kr + lg) * 32 + li) * 16); };
+
+    // ---- phase A: the score MFMAs of stage k, the online softmax of stage k-1 for heads
+    // h0 + i (lanes i and 32 + i: keys 8r + 4g + q of register 4r + q) in short pinned
+    // pieces between them, and the loads of stage k+2
+    f32x16 S, R;
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    {
+      const uint32_t valid = k == 0 ? 0u : range_bits((s_first + k - 1) * kStageKeys, klo, khi);
+      const uint32_t vbits = valid >> (4 * lg);
+      const bool all_valid = valid == 0xFFFFFFFFu;
+      // this lane's keys' row scales, times the query's logit scale
+      float ksc[16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const f32x4_t v = *(const MLA_LDS f32x4_t*)(ksp + 8 * r + 4 * lg);
+        ksc[4 * r] = v.x;
+        ksc[4 * r + 1] = v.y;
+        ksc[4 * r + 2] = v.z;
+        ksc[4 * r + 3] = v.w;
+      }
+      float x[16];
+      float lmax = -INFINITY, mx = 0.f, m_new = 0.f, ex = 0.f, mref = 0.f;
+      uint32_t hsw0 = 0, hsw1 = 0;
+      uint64_t rf = 0;
+      constexpr int KS = G::kKs8 + (ROPE ? 4 : 0);  // MFMA k-steps of the stage
+      i32x8 kf[G::kKs8];
+      bf16x8 rf8[4];
+      kf[0] = kread(0);
+      kf[1] = kread(1);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        // operands two k-steps ahead
+        {
+          const int n = i + 2;
+          if (n < G::kKs8) kf[n] = kread(n);
+          else if (ROPE && n < KS) rf8[n - G::kKs8] = rread(n - G::kKs8);
+        }
+        // softmax pieces: logits (k-steps 0, 1), running max (1, 2), the head's max over
+        // both lane halves and the lazy rescale (2..4), weights (4.., four pairs each)
+        if (i == 0 || i == 1) {
+#pragma unroll
+          for (int e = 8 * i; e < 8 * i + 8; ++e) {
+            float s0 = Sp[e], r0 = Rp[e];
+            pin(s0);
+            pin(r0);
+            float v = s0 * (ksc[e] * qsl);
+            if (ROPE) v = __builtin_fmaf(r0, a.scale_log2, v);
+            const int row = 8 * (e >> 2) + (e & 3);  // minus 4g, folded into vbits
+            x[e] = (all_valid || ((vbits >> row) & 1u)) ? v : -INFINITY;
+            pin(x[e]);
+          }
+        }
+        if (i == 1 || i == 2) {
+          pin(lmax);
+          const int e0 = 8 * (i - 1);
+          lmax = fmaxf(lmax, fmaxf(fmaxf(fmaxf(x[e0], x[e0 + 1]), fmaxf(x[e0 + 2], x[e0 + 3])),
+                                   fmaxf(fmaxf(x[e0 + 4], x[e0 + 5]), fmaxf(x[e0 + 6], x[e0 + 7]))));
+          pin(lmax);
+        }
+        if (i == 2) {
+          const uint32_t b = __builtin_bit_cast(uint32_t, lmax);
+          const auto hsw = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+          hsw0 = (uint32_t)hsw[0];
+          hsw1 = (uint32_t)hsw[1];
+          pinu(hsw0);
+          pinu(hsw1);
+        }
+        if (i == 3) {
+          mx = fmaxf(__builtin_bit_cast(float, hsw0), __builtin_bit_cast(float, hsw1));
+          pin(m);
+          m_new = mx > m + kRescaleSlack ? mx : m;
+          pin(m_new);
+        }
+        if (i == 4) {
+          ex = fast_exp2(m - m_new);  // 0 while m is -inf; unused unless m_new != m
+          // O is exactly zero while m is -inf: only a finite old maximum needs the rescale
+          rf = __builtin_amdgcn_ballot_w64(m_new != m && m != -INFINITY);
+          alpha = m_new != m ? ex : 1.f;
+          m = m_new;
+          mref = m == -INFINITY ? 0.f : m;
+          pin(alpha);
+          pin(mref);
+          pin(l);
+          l *= alpha;
+          pin(l);
+          rflag = rf != 0 ? 1 : 0;
+        }
+        if (i >= 5 && i < 9) {
+          // pairs 2(i-5), 2(i-5)+1: the weights p sigma_k as rounded for the MFMA; the
+          // denominator sums p (the value rows are the bare codes)
+          const int p0 = 2 * (i - 5);
+#pragma unroll
+          for (int pp = p0; pp < p0 + 2; ++pp) {
+            const int e = 2 * pp;
+            float a0 = x[e], a1 = x[e + 1];
+            pin(a0);
+            pin(a1);
+            const float e0 = fast_exp2(a0 - mref), e1 = fast_exp2(a1 - mref);
+            l += e0 + e1;
+            const bf16x2_t w = {(__bf16)(e0 * ksc[e]), (__bf16)(e1 * ksc[e + 1])};
+            pk[pp] = __builtin_bit_cast(uint32_t, w);
+            pinu(pk[pp]);
+            pin(l);
+          }
+        }
+        if (ROPE && i == KS - 1) {
+#pragma unroll
+          for (int pp = 0; pp < 8; ++pp) pinu(pk[pp]);  // (KS = 12: pairs are done by 9)
+        }
+        // the MFMA of k-step i
+        if (i < G::kKs8) {
+          S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], qf[i], i == 0 ? f32x16{} : S, 0, 0, 0, 0, 0, 0);
+        } else if constexpr (ROPE) {
+          const int kr = i - G::kKs8;
+          R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf8[kr], qr[kr], kr == 0 ? f32x16{} : R, 0, 0, 0);
+        }
+        // stage k+2's loads
+        if (i < kF8Loads && fb != nullptr) fast_load(fb, fdst, i);
+        if (i == kF8Loads && fb != nullptr) dma4(scale_src_fast(s_first + kn, pa_k), ksl(kn));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- publish the weights, rescale factor and flag of stage k-1 (own head block)
+    *(MLA_LDS u32x4*)(pbuf + wave * 2048 + lane * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    *(MLA_LDS u32x4*)(pbuf + wave * 2048 + 1024 + lane * 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    if (lg == 0) alpha_s[wave * 32 + li] = alpha;
+    if (lane == 0) flag_s[wave] = rflag;
+    auto vread = [&](int kp, int cb) {
+      const int o0 = 1152 * 16 * kp + 128 * (cb >> 1), o1 = o0 + 1152 * 8;
+      const bf16x4 a0 = ds_read_tr16(vrd + vb[kp][cb & 1] + o0);
+      const bf16x4 a1 = ds_read_tr16(vrd + vb[kp][cb & 1] + o1);
+      return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    };
+    auto pread = [&](int hb, int kp) { return *(const MLA_LDS bf16x8*)(pbuf + lane * 16 + hb * 2048 + kp * 1024); };
+    bf16x8 vf[8];  // V^T fragment 4kp + cb; at most two live
+    vf[0] = vread(0, 0);
+    lgkm_wait0();
+    stage_barrier();
+    bf16x8 pf0[4], pf1[4];  // P^T (kp, hb)
+    {
+      typedef int i32x4 __attribute__((ext_vector_type(4)));
+      const i32x4 fl = *(const MLA_LDS i32x4*)flag_s;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) pf0[hb] = pread(hb, 0);
+      // O holds the values of stages < k-1 relative to the maxima before stage k-1: bring
+      // the rescaled heads to their new maxima before stage k-1's values are added
+      if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0) {
+        fence_o(O);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          const float al = fl[hb] != 0 ? alpha_s[hb * 32 + li] : 1.f;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            O[cb][hb] *= al;
+            const int n = 4 * hb + cb + 1;
+            if (n < 16)
+              asm volatile("" : "+a"(O[cb][hb]), "+a"(O[n & 3][n >> 2]));
+            else
+              asm volatile("" : "+a"(O[cb][hb]));
+          }
+        }
+        asm volatile("s_nop 4" ::: "memory");
+      }
+    }
+
+    // ---- phase B: the values of stage k-1 (op j = 16kp + 4cb + hb) and the widening of
+    // stage k's 512 latent columns into the other value tile (piece u at ops 8u .. 8u + 2)
+    {
+      u32x4 wr[4];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int kp = j >> 4, cb = (j >> 2) & 3, hb = j & 3;
+        if (hb == 0 && j + 4 < 32) vf[(j >> 2) + 1] = vread((j + 4) >> 4, ((j + 4) >> 2) & 3);
+        mfma32_acc(O[cb][hb], vf[4 * kp + cb], kp == 0 ? pf0[hb] : pf1[hb]);
+        if (j >= 12 && j < 16) pf1[j - 12] = pread(j - 12, 1);
+        if ((j & 7) == 0) wr[j >> 3] = *(const MLA_LDS u32x4*)(rs + (tid + 256 * (j >> 3)) * 16);
+        if ((j & 7) == 2) {
+          const u32x4 w = wr[j >> 3];
+          const uint2 b0 = e4m3x4_to_bf16x4(w[0]), b1 = e4m3x4_to_bf16x4(w[1]);
+          const uint2 b2 = e4m3x4_to_bf16x4(w[2]), b3 = e4m3x4_to_bf16x4(w[3]);
+          MLA_LDS uint8_t* d = vwr + wdst[j >> 3];
+          *(MLA_LDS u32x4*)d = u32x4{b0.x, b0.y, b1.x, b1.y};
+          // chunk 2c + 1 sits next to chunk 2c: the swizzle flips bits 0..2 of the chunk
+          // index by s(r), and 2c ^ s(r) and (2c + 1) ^ s(r) differ in bit 0 only
+          *(MLA_LDS u32x4*)(vwr + (wdst[j >> 3] ^ 16)) = u32x4{b2.x, b2.y, b3.x, b3.y};
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    Sp = S;
+    if (ROPE) Rp = R;
+  }
+
+  if (bad_page) atomicOr(a.err, kErrPageId);
+
+  // ---- epilogue: each head's 1/l from its owner, then the wave's 128 columns of every
+  // head, normalised, through LDS to contiguous stores
+  {
+    const uint32_t lb = __builtin_bit_cast(uint32_t, l);
+    const auto hsw = __builtin_amdgcn_permlane32_swap(lb, lb, false, false);
+    const float l_tot = __builtin_bit_cast(float, (uint32_t)hsw[0]) + __builtin_bit_cast(float, (uint32_t)hsw[1]);
+    if (lg == 0) {
+      inv_s[h0 + li] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (!full) a.part_lse[(int64_t)slot * a.H + h0 + li] = l_tot > 0.f ? m + __log2f(l_tot) : -INFINITY;
+    }
+  }
+  fence_o(O);
+  lgkm_wait0();
+  stage_barrier();  // every wave is done with the stage buffers and has published 1/l
+  MLA_LDS uint8_t* st = vt + wave * 8192;  // [32 heads][256 bytes], chunk c of head h at c ^ (h >> 1)
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const float inv = inv_s[hb * 32 + li];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x16& o = O[cb][hb];
+        const uint32_t w0 = (uint32_t)bf16_bits_rne(o[4 * r] * inv) | ((uint32_t)bf16_bits_rne(o[4 * r + 1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)bf16_bits_rne(o[4 * r + 2] * inv) | ((uint32_t)bf16_bits_rne(o[4 * r + 3] * inv) << 16);
+        *(MLA_LDS u32x2*)(st + li * 256 + (((4 * cb + r) ^ (li >> 1)) << 4) + 8 * lg) = u32x2{w0, w1};
+      }
+    lgkm_wait0();
+    uint16_t* base = full ? a.out + (int64_t)t * a.o_tok + (int64_t)(hb * 32) * a.o_head
+                          : a.part_o + ((int64_t)slot * a.H + hb * 32) * kLatentDim;
+    const int64_t hstride = full ? a.o_head : kLatentDim;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int hl = 4 * i + (lane >> 4), c = lane & 15;
+      const u32x4 w = *(const MLA_LDS u32x4*)(st + hl * 256 + ((c ^ (hl >> 1)) << 4));
+      __builtin_nontemporal_store(w, (u32x4*)(base + hl * hstride + 128 * wave + 8 * c));
+    }
+    lgkm_wait0();  // the staging rows are rewritten for the next head block
+  }
+}
+
+template <int KPAGES, bool ROPE>
+__global__ __launch_bounds__(256, 1) void mla_fp8mma_kernel(const SparseArgs a, const SplitPlan plan) {
+  __shared__ __attribute__((aligned(1024))) uint8_t raw_b[kF8Raw * F8Geo<true>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt_b[2 * kF8VBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t xbuf_b[kF8PBytes + 1536];
+  __shared__ F8Lds L;
+  static_assert(2 * kF8VBytes >= 4 * 8192, "epilogue staging");
+  plan_run<256, true>(
+      plan, L, [&](F8Lds&) {}, [&](int) { return RowGeo{-1, 0, 0}; },
+      [&](RowGeo* geo, int lane) { decode_fill_wave(a, geo, lane); },
+      [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
+        fp8mma_segment<KPAGES, ROPE>(a, (MLA_LDS uint8_t*)raw_b, (MLA_LDS uint8_t*)vt_b, (MLA_LDS uint8_t*)xbuf_b, L,
+                                     r, g, ta, tc, full, slot);
+      });
+}
+
+}  // namespace
+
+// The dense fp8 decode's balanced split of at most 64 rows and sequences at 128 heads
+// (see launch_sparse).
+hipError_t launch_fp8mma(const SparseArgs& a, const SplitPlan& p, hipStream_t stream) {
+  const dim3 grid(a.grid), block(256);
+  const bool kp = a.PS % kStageKeys == 0;
+  if (a.rope) {
+    if (kp) hipLaunchKernelGGL((mla_fp8mma_kernel<1, true>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_fp8mma_kernel<0, true>), grid, block, 0, stream, a, p);
+  } else {
+    if (kp) hipLaunchKernelGGL((mla_fp8mma_kernel<1, false>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_fp8mma_kernel<0, false>), grid, block, 0, stream, a, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

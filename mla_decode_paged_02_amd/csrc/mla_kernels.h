@@ -182,6 +182,9 @@ hipError_t launch_combine(const SplitPlan& p, hipStream_t stream);
 // work-groups.
 hipError_t launch_decode2(const DecodeArgs& a, const SplitPlan& p, hipStream_t stream);
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream, const KernelTimer* timer);
+// The dense fp8 decode kernel with the scores on fp8 MFMA (mla_fp8mma.hip): 128 heads, the
+// balanced split of at most 64 rows and sequences, no more rows than work-groups, fp8 q.
+hipError_t launch_fp8mma(const SparseArgs& a, const SplitPlan& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, const KernelTimer* timer);
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const KernelTimer* timer);
 

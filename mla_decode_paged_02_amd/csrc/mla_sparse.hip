@@ -557,6 +557,7 @@ template <int HB, int NW>
 static hipError_t launch_sparse_h(const SparseArgs& a, const SplitPlan& p, hipStream_t stream) {
   const dim3 grid(a.nparts >= 1 ? a.T * a.nparts : a.grid), block(NW * 64);
   const bool small = a.nparts == 0 && a.T <= 64 && a.T <= a.grid && ((!a.dense && !a.shared) || a.B <= 64);
+  if (HB == 2 && NW == 4 && a.dense && small && !a.q_bf16) return launch_fp8mma(a, p, stream);
   if (a.rope) {
     if (a.xidx != nullptr || a.sink != nullptr) return hipErrorInvalidValue;  // refused by the host checks
     if (a.dense) {
