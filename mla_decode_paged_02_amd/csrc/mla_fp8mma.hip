@@ -310,26 +310,22 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     wdst[u] = r * kRowBytes + ((((2 * c) & ~7) | (((2 * c) ^ f) & 7)) << 4);
   }
 
-  // Step k scores stage k while the vector units turn the scores of stage k-1 into
-  // weights; once every wave has published its weights, it adds the values of stage k-1
-  // and widens the values of stage k.  Every step runs the whole stream: at k = 0 no key
-  // of "stage -1" is valid (zero weights on the zeroed value tile), and at k = nst the
-  // scores of a stale buffer are computed and dropped.
-  f32x16 Sp, Rp;  // scores of stage k-1: e4m3 products, and (ROPE) the bf16 rope products
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    Sp[e] = 0.f;
-    Rp[e] = 0.f;
-  }
+  // Step k publishes the weights of stage k-1, then runs the score MFMAs of stage k with
+  // the first value MFMAs of stage k-1 and the widening of stage k's values (phase A), then
+  // the other value MFMAs of stage k-1 while the vector units turn the scores of stage k
+  // into weights (phase B).  Every step runs the whole stream: at k = 0 the values of
+  // "stage -1" are zero weights on the zeroed value tile, and at k = nst the scores of a
+  // stale buffer are computed and masked out entirely.
+  auto pinv = [](f32x16& v) { asm volatile("" : "+v"(v)); };
   auto pin = [](float& v) { asm volatile("" : "+v"(v)); };
-  auto pinu = [](uint32_t& v) { asm volatile("" : "+v"(v)); };
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll 1
   for (int k = 0; k <= nst; ++k) {
     // ---- stage k has landed (stage k+1 may still be in flight)
     if (k < nst) {
       if (k >= 1 && k + 1 < nst) vm_wait_imm<kF8Loads + 1>(); else vm_wait_imm<0>();
     }
-    stage_barrier();  // also: every wave is done with stage k-1's raw buffer and tile k%2
+    stage_barrier();  // also: every wave is done with stage k-1's raw buffer, tile k%2, the weights
     const int kn = k + 2;
     const uint8_t* fb = nullptr;
     int pa_k = 0;
@@ -341,7 +337,7 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     }
     MLA_LDS uint8_t* fdst = raw + (kn % kF8Raw) * G::kStage;
     const MLA_LDS uint8_t* rs = raw + (k % kF8Raw) * G::kStage;     // stage k's rows
-    const MLA_LDS float* ksp = ksl(k + kF8Scales - 1);               // stage k-1's scales
+    const MLA_LDS float* ksp = ksl(k);                               // stage k's scales
     const MLA_LDS uint8_t* vrd = vt + ((k + 1) & 1) * kF8VBytes;    // values of stage k-1
     MLA_LDS uint8_t* vwr = vt + (k & 1) * kF8VBytes;                // values of stage k
     auto kread = [&](int ks) {
@@ -350,136 +346,6 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
       return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
     auto rread = [&](int kr) { return *(const MLA_LDS bf16x8*)(rs + ((32 + 2 * kr + lg) * 32 + li) * 16); };
-
-    // ---- phase A: the score MFMAs of stage k, the online softmax of stage k-1 for heads
-    // h0 + i (lanes i and 32 + i: keys 8r + 4g + q of register 4r + q) in short pinned
-    // pieces between them, and the loads of stage k+2
-    f32x16 S, R;
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    {
-      const uint32_t valid = k == 0 ? 0u : range_bits((s_first + k - 1) * kStageKeys, klo, khi);
-      const uint32_t vbits = valid >> (4 * lg);
-      const bool all_valid = valid == 0xFFFFFFFFu;
-      // this lane's keys' row scales, times the query's logit scale
-      float ksc[16];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        typedef float f32x4_t __attribute__((ext_vector_type(4)));
-        const f32x4_t v = *(const MLA_LDS f32x4_t*)(ksp + 8 * r + 4 * lg);
-        ksc[4 * r] = v.x;
-        ksc[4 * r + 1] = v.y;
-        ksc[4 * r + 2] = v.z;
-        ksc[4 * r + 3] = v.w;
-      }
-      float x[16];
-      float lmax = -INFINITY, mx = 0.f, m_new = 0.f, ex = 0.f, mref = 0.f;
-      uint32_t hsw0 = 0, hsw1 = 0;
-      uint64_t rf = 0;
-      constexpr int KS = G::kKs8 + (ROPE ? 4 : 0);  // MFMA k-steps of the stage
-      i32x8 kf[G::kKs8];
-      bf16x8 rf8[4];
-      kf[0] = kread(0);
-      kf[1] = kread(1);
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        // operands two k-steps ahead
-        {
-          const int n = i + 2;
-          if (n < G::kKs8) kf[n] = kread(n);
-          else if (ROPE && n < KS) rf8[n - G::kKs8] = rread(n - G::kKs8);
-        }
-        // softmax pieces: logits (k-steps 0, 1), running max (1, 2), the head's max over
-        // both lane halves and the lazy rescale (2..4), weights (4.., four pairs each)
-        if (i == 0 || i == 1) {
-#pragma unroll
-          for (int e = 8 * i; e < 8 * i + 8; ++e) {
-            float s0 = Sp[e], r0 = Rp[e];
-            pin(s0);
-            pin(r0);
-            float v = s0 * (ksc[e] * qsl);
-            if (ROPE) v = __builtin_fmaf(r0, a.scale_log2, v);
-            const int row = 8 * (e >> 2) + (e & 3);  // minus 4g, folded into vbits
-            x[e] = (all_valid || ((vbits >> row) & 1u)) ? v : -INFINITY;
-            pin(x[e]);
-          }
-        }
-        if (i == 1 || i == 2) {
-          pin(lmax);
-          const int e0 = 8 * (i - 1);
-          lmax = fmaxf(lmax, fmaxf(fmaxf(fmaxf(x[e0], x[e0 + 1]), fmaxf(x[e0 + 2], x[e0 + 3])),
-                                   fmaxf(fmaxf(x[e0 + 4], x[e0 + 5]), fmaxf(x[e0 + 6], x[e0 + 7]))));
-          pin(lmax);
-        }
-        if (i == 2) {
-          const uint32_t b = __builtin_bit_cast(uint32_t, lmax);
-          const auto hsw = __builtin_amdgcn_permlane32_swap(b, b, false, false);
-          hsw0 = (uint32_t)hsw[0];
-          hsw1 = (uint32_t)hsw[1];
-          pinu(hsw0);
-          pinu(hsw1);
-        }
-        if (i == 3) {
-          mx = fmaxf(__builtin_bit_cast(float, hsw0), __builtin_bit_cast(float, hsw1));
-          pin(m);
-          m_new = mx > m + kRescaleSlack ? mx : m;
-          pin(m_new);
-        }
-        if (i == 4) {
-          ex = fast_exp2(m - m_new);  // 0 while m is -inf; unused unless m_new != m
-          // O is exactly zero while m is -inf: only a finite old maximum needs the rescale
-          rf = __builtin_amdgcn_ballot_w64(m_new != m && m != -INFINITY);
-          alpha = m_new != m ? ex : 1.f;
-          m = m_new;
-          mref = m == -INFINITY ? 0.f : m;
-          pin(alpha);
-          pin(mref);
-          pin(l);
-          l *= alpha;
-          pin(l);
-          rflag = rf != 0 ? 1 : 0;
-        }
-        if (i >= 5 && i < 9) {
-          // pairs 2(i-5), 2(i-5)+1: the weights p sigma_k as rounded for the MFMA; the
-          // denominator sums p (the value rows are the bare codes)
-          const int p0 = 2 * (i - 5);
-#pragma unroll
-          for (int pp = p0; pp < p0 + 2; ++pp) {
-            const int e = 2 * pp;
-            float a0 = x[e], a1 = x[e + 1];
-            pin(a0);
-            pin(a1);
-            const float e0 = fast_exp2(a0 - mref), e1 = fast_exp2(a1 - mref);
-            l += e0 + e1;
-            const bf16x2_t w = {(__bf16)(e0 * ksc[e]), (__bf16)(e1 * ksc[e + 1])};
-            pk[pp] = __builtin_bit_cast(uint32_t, w);
-            pinu(pk[pp]);
-            pin(l);
-          }
-        }
-        if (ROPE && i == KS - 1) {
-#pragma unroll
-          for (int pp = 0; pp < 8; ++pp) pinu(pk[pp]);  // (KS = 12: pairs are done by 9)
-        }
-        // the MFMA of k-step i
-        if (i < G::kKs8) {
-          S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], qf[i], i == 0 ? f32x16{} : S, 0, 0, 0, 0, 0, 0);
-        } else if constexpr (ROPE) {
-          const int kr = i - G::kKs8;
-          R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf8[kr], qr[kr], kr == 0 ? f32x16{} : R, 0, 0, 0);
-        }
-        // stage k+2's loads
-        if (i < kF8Loads && fb != nullptr) fast_load(fb, fdst, i);
-        if (i == kF8Loads && fb != nullptr) dma4(scale_src_fast(s_first + kn, pa_k), ksl(kn));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // ---- publish the weights, rescale factor and flag of stage k-1 (own head block)
-    *(MLA_LDS u32x4*)(pbuf + wave * 2048 + lane * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-    *(MLA_LDS u32x4*)(pbuf + wave * 2048 + 1024 + lane * 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
-    if (lg == 0) alpha_s[wave * 32 + li] = alpha;
-    if (lane == 0) flag_s[wave] = rflag;
     auto vread = [&](int kp, int cb) {
       const int o0 = 1152 * 16 * kp + 128 * (cb >> 1), o1 = o0 + 1152 * 8;
       const bf16x4 a0 = ds_read_tr16(vrd + vb[kp][cb & 1] + o0);
@@ -487,6 +353,12 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
       return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     };
     auto pread = [&](int hb, int kp) { return *(const MLA_LDS bf16x8*)(pbuf + lane * 16 + hb * 2048 + kp * 1024); };
+
+    // ---- publish the weights, rescale factor and flag of stage k-1 (own head block)
+    *(MLA_LDS u32x4*)(pbuf + wave * 2048 + lane * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    *(MLA_LDS u32x4*)(pbuf + wave * 2048 + 1024 + lane * 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    if (lg == 0) alpha_s[wave * 32 + li] = alpha;
+    if (lane == 0) flag_s[wave] = rflag;
     bf16x8 vf[8];  // V^T fragment 4kp + cb; at most two live
     vf[0] = vread(0, 0);
     lgkm_wait0();
@@ -517,34 +389,145 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
         asm volatile("s_nop 4" ::: "memory");
       }
     }
+    // value op j = 16kp + 4cb + hb of stage k-1 (and the operand reads it needs next)
+    auto pv_op = [&](int j) {
+      const int kp = j >> 4, cb = (j >> 2) & 3, hb = j & 3;
+      if (hb == 0 && j + 4 < 32) vf[(j >> 2) + 1] = vread((j + 4) >> 4, ((j + 4) >> 2) & 3);
+      mfma32_acc(O[cb][hb], vf[4 * kp + cb], kp == 0 ? pf0[hb] : pf1[hb]);
+      if (j >= 12 && j < 16) pf1[j - 12] = pread(j - 12, 1);
+    };
 
-    // ---- phase B: the values of stage k-1 (op j = 16kp + 4cb + hb) and the widening of
-    // stage k's 512 latent columns into the other value tile (piece u at ops 8u .. 8u + 2)
+    // ---- phase A: the score MFMAs of stage k, value ops 0..7 of stage k-1, the widening
+    // of stage k's 512 latent columns (piece u: read at k-step u, converted and stored at
+    // u + 4), and the loads of stage k+2
+    f32x16 S, R;
+    constexpr int KS = G::kKs8 + (ROPE ? 4 : 0);  // MFMA k-steps of the stage
+    static_assert(KS >= 8 && KS > kF8Loads, "room for the value ops, the widening and the loads");
     {
+      i32x8 kf[G::kKs8];
+      bf16x8 rf8[4];
       u32x4 wr[4];
+      kf[0] = kread(0);
+      kf[1] = kread(1);
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
+      for (int i = 0; i < KS; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        const int kp = j >> 4, cb = (j >> 2) & 3, hb = j & 3;
-        if (hb == 0 && j + 4 < 32) vf[(j >> 2) + 1] = vread((j + 4) >> 4, ((j + 4) >> 2) & 3);
-        mfma32_acc(O[cb][hb], vf[4 * kp + cb], kp == 0 ? pf0[hb] : pf1[hb]);
-        if (j >= 12 && j < 16) pf1[j - 12] = pread(j - 12, 1);
-        if ((j & 7) == 0) wr[j >> 3] = *(const MLA_LDS u32x4*)(rs + (tid + 256 * (j >> 3)) * 16);
-        if ((j & 7) == 2) {
-          const u32x4 w = wr[j >> 3];
+        {
+          const int n = i + 2;
+          if (n < G::kKs8) kf[n] = kread(n);
+          else if (ROPE && n < KS) rf8[n - G::kKs8] = rread(n - G::kKs8);
+        }
+        if (i < 4) wr[i] = *(const MLA_LDS u32x4*)(rs + (tid + 256 * i) * 16);
+        if (i >= 4 && i < 8) {
+          const u32x4 w = wr[i - 4];
           const uint2 b0 = e4m3x4_to_bf16x4(w[0]), b1 = e4m3x4_to_bf16x4(w[1]);
           const uint2 b2 = e4m3x4_to_bf16x4(w[2]), b3 = e4m3x4_to_bf16x4(w[3]);
-          MLA_LDS uint8_t* d = vwr + wdst[j >> 3];
-          *(MLA_LDS u32x4*)d = u32x4{b0.x, b0.y, b1.x, b1.y};
+          *(MLA_LDS u32x4*)(vwr + wdst[i - 4]) = u32x4{b0.x, b0.y, b1.x, b1.y};
           // chunk 2c + 1 sits next to chunk 2c: the swizzle flips bits 0..2 of the chunk
           // index by s(r), and 2c ^ s(r) and (2c + 1) ^ s(r) differ in bit 0 only
-          *(MLA_LDS u32x4*)(vwr + (wdst[j >> 3] ^ 16)) = u32x4{b2.x, b2.y, b3.x, b3.y};
+          *(MLA_LDS u32x4*)(vwr + (wdst[i - 4] ^ 16)) = u32x4{b2.x, b2.y, b3.x, b3.y};
         }
+        if (i < G::kKs8) {
+          S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], qf[i], i == 0 ? f32x16{} : S, 0, 0, 0, 0, 0, 0);
+        } else if constexpr (ROPE) {
+          const int kr = i - G::kKs8;
+          R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf8[kr], qr[kr], kr == 0 ? f32x16{} : R, 0, 0, 0);
+        }
+        if (i < 8) pv_op(i);
+        if (i < kF8Loads && fb != nullptr) fast_load(fb, fdst, i);
+        if (i == kF8Loads && fb != nullptr) dma4(scale_src_fast(s_first + kn, pa_k), ksl(kn));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    Sp = S;
-    if (ROPE) Rp = R;
+
+    // ---- phase B: value ops 8..31 of stage k-1, with the online softmax of stage k for
+    // heads h0 + i (lanes i and 32 + i: keys 8r + 4g + q of register 4r + q) in pinned
+    // pieces between them: logits (ops 8..11), running max (9..12), the head's max over
+    // both lane halves and the lazy rescale (13..15), weights (16..23, two pairs each)
+    {
+      const uint32_t valid = k < nst ? range_bits((s_first + k) * kStageKeys, klo, khi) : 0u;
+      const uint32_t vbits = valid >> (4 * lg);
+      const bool all_valid = valid == 0xFFFFFFFFu;
+      float ksc[16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const f32x4_t v = *(const MLA_LDS f32x4_t*)(ksp + 8 * r + 4 * lg);
+        ksc[4 * r] = v.x;
+        ksc[4 * r + 1] = v.y;
+        ksc[4 * r + 2] = v.z;
+        ksc[4 * r + 3] = v.w;
+      }
+      float x[16];
+      float lmax = -INFINITY, mx = 0.f, m_new = 0.f, mref = 0.f;
+      uint32_t hsw0 = 0, hsw1 = 0;
+#pragma unroll
+      for (int j = 8; j < 32; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (j == 8) {
+          pinv(S);
+          if (ROPE) pinv(R);
+        }
+        if (j >= 8 && j < 12) {
+#pragma unroll
+          for (int e = 4 * (j - 8); e < 4 * (j - 8) + 4; ++e) {
+            float v = S[e] * (ksc[e] * qsl);
+            if (ROPE) v = __builtin_fmaf(R[e], a.scale_log2, v);
+            const int row = 8 * (e >> 2) + (e & 3);  // minus 4g, folded into vbits
+            x[e] = (all_valid || ((vbits >> row) & 1u)) ? v : -INFINITY;
+          }
+#pragma unroll
+          for (int e = 4 * (j - 8); e < 4 * (j - 8) + 4; ++e) pin(x[e]);
+        }
+        if (j >= 9 && j < 13) {
+          const int e0 = 4 * (j - 9);
+          pin(lmax);
+          lmax = fmaxf(lmax, fmaxf(fmaxf(x[e0], x[e0 + 1]), fmaxf(x[e0 + 2], x[e0 + 3])));
+          pin(lmax);
+        }
+        if (j == 13) {
+          const uint32_t bb = __builtin_bit_cast(uint32_t, lmax);
+          const auto hsw = __builtin_amdgcn_permlane32_swap(bb, bb, false, false);
+          hsw0 = (uint32_t)hsw[0];
+          hsw1 = (uint32_t)hsw[1];
+          asm volatile("" : "+v"(hsw0), "+v"(hsw1));
+        }
+        if (j == 14) {
+          mx = fmaxf(__builtin_bit_cast(float, hsw0), __builtin_bit_cast(float, hsw1));
+          pin(m);
+          m_new = mx > m + kRescaleSlack ? mx : m;
+          pin(m_new);
+        }
+        if (j == 15) {
+          const float ex = fast_exp2(m - m_new);  // 0 while m is -inf; unused unless m_new != m
+          // O is exactly zero while m is -inf: only a finite old maximum needs the rescale
+          const uint64_t rf = __builtin_amdgcn_ballot_w64(m_new != m && m != -INFINITY);
+          alpha = m_new != m ? ex : 1.f;
+          m = m_new;
+          mref = m == -INFINITY ? 0.f : m;
+          l *= alpha;
+          rflag = rf != 0 ? 1 : 0;
+          pin(mref);
+          pin(l);
+        }
+        if (j >= 16 && j < 24) {
+          // pair p = j - 16: the weights p sigma_k as rounded for the MFMA; the denominator
+          // sums p (the value rows are the bare codes)
+          const int e = 2 * (j - 16);
+          float a0 = x[e], a1 = x[e + 1];
+          pin(a0);
+          pin(a1);
+          const float e0 = fast_exp2(a0 - mref), e1 = fast_exp2(a1 - mref);
+          l += e0 + e1;
+          const bf16x2_t w = {(__bf16)(e0 * ksc[e]), (__bf16)(e1 * ksc[e + 1])};
+          pk[j - 16] = __builtin_bit_cast(uint32_t, w);
+          asm volatile("" : "+v"(pk[j - 16]));
+          pin(l);
+        }
+        pv_op(j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   if (bad_page) atomicOr(a.err, kErrPageId);
