@@ -27,8 +27,6 @@
 // The operand layout of the fp8 MFMA (lane 32g + i holds 32 k-values of row i of A and of
 // column i of B, the halves g disjoint; D as for the bf16 32x32 MFMAs) was checked on
 // MI355X against exact products.
-#include <type_traits>
-
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "mla_plan.h"
@@ -399,8 +397,9 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
 
     // ---- phase A: the score MFMAs of stage k, value ops 0..7 of stage k-1, the widening
     // of stage k's 512 latent columns (piece u: read at k-step u, converted and stored at
-    // u + 4), and the loads of stage k+2
+    // u + 4), stage k's key scales, and the loads of stage k+2
     f32x16 S, R;
+    float ksc[16], kq[16];  // stage k's key scales sigma and sigma * qsl, key 8r + 4g + q at 4r + q
     constexpr int KS = G::kKs8 + (ROPE ? 4 : 0);  // MFMA k-steps of the stage
     static_assert(KS >= 8 && KS > kF8Loads, "room for the value ops, the widening and the loads");
     {
@@ -427,6 +426,21 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
           // index by s(r), and 2c ^ s(r) and (2c + 1) ^ s(r) differ in bit 0 only
           *(MLA_LDS u32x4*)(vwr + (wdst[i - 4] ^ 16)) = u32x4{b2.x, b2.y, b3.x, b3.y};
         }
+        if (i < 4) {
+          typedef float f32x4_t __attribute__((ext_vector_type(4)));
+          const f32x4_t v = *(const MLA_LDS f32x4_t*)(ksp + 8 * i + 4 * lg);
+          ksc[4 * i] = v.x;
+          ksc[4 * i + 1] = v.y;
+          ksc[4 * i + 2] = v.z;
+          ksc[4 * i + 3] = v.w;
+        }
+        if (i >= 4 && i < 8) {
+#pragma unroll
+          for (int e = 4 * (i - 4); e < 4 * (i - 4) + 4; ++e) {
+            kq[e] = ksc[e] * qsl;
+            pin(kq[e]);
+          }
+        }
         if (i < G::kKs8) {
           S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], qf[i], i == 0 ? f32x16{} : S, 0, 0, 0, 0, 0, 0);
         } else if constexpr (ROPE) {
@@ -443,24 +457,35 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     // ---- phase B: value ops 8..31 of stage k-1, with the online softmax of stage k for
     // heads h0 + i (lanes i and 32 + i: keys 8r + 4g + q of register 4r + q) in pinned
     // pieces between them: logits (ops 8..11), running max (9..12), the head's max over
-    // both lane halves and the lazy rescale (13..15), weights (16..23, two pairs each)
+    // both lane halves and the lazy rescale (13..15), one power per op (16..31) and its
+    // weight and denominator term one op later.
+    // Only a segment's first and last stage (and the stale stage after the last) have keys
+    // to mask: the other stages branch around the mask.
     {
       const uint32_t valid = k < nst ? range_bits((s_first + k) * kStageKeys, klo, khi) : 0u;
+      const bool partial = valid != 0xFFFFFFFFu;
       const uint32_t vbits = valid >> (4 * lg);
-      const bool all_valid = valid == 0xFFFFFFFFu;
-      float ksc[16];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        typedef float f32x4_t __attribute__((ext_vector_type(4)));
-        const f32x4_t v = *(const MLA_LDS f32x4_t*)(ksp + 8 * r + 4 * lg);
-        ksc[4 * r] = v.x;
-        ksc[4 * r + 1] = v.y;
-        ksc[4 * r + 2] = v.z;
-        ksc[4 * r + 3] = v.w;
-      }
       float x[16];
       float lmax = -INFINITY, mx = 0.f, m_new = 0.f, mref = 0.f;
       uint32_t hsw0 = 0, hsw1 = 0;
+      float pw[16];  // powers, one op ahead of their weights
+      auto weigh = [&](int e) {
+        // the weight p sigma_k as rounded for the MFMA; the denominator sums p (the value
+        // rows are the bare codes)
+        float pe = pw[e];
+        pin(pe);
+        l += pe;
+        const float w = pe * ksc[e];
+        if (e & 1) {
+          const bf16x2_t w2 = {(__bf16)pw[e - 1], (__bf16)w};
+          pk[e >> 1] = __builtin_bit_cast(uint32_t, w2);
+          asm volatile("" : "+v"(pk[e >> 1]));
+        } else {
+          pw[e] = w;  // held until its pair is packed
+          pin(pw[e]);
+        }
+        pin(l);
+      };
 #pragma unroll
       for (int j = 8; j < 32; ++j) {
         __builtin_amdgcn_sched_barrier(0);
@@ -471,10 +496,16 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
         if (j >= 8 && j < 12) {
 #pragma unroll
           for (int e = 4 * (j - 8); e < 4 * (j - 8) + 4; ++e) {
-            float v = S[e] * (ksc[e] * qsl);
+            float v = S[e] * kq[e];
             if (ROPE) v = __builtin_fmaf(R[e], a.scale_log2, v);
-            const int row = 8 * (e >> 2) + (e & 3);  // minus 4g, folded into vbits
-            x[e] = (all_valid || ((vbits >> row) & 1u)) ? v : -INFINITY;
+            x[e] = v;
+          }
+          if (partial) {
+#pragma unroll
+            for (int e = 4 * (j - 8); e < 4 * (j - 8) + 4; ++e) {
+              const int row = 8 * (e >> 2) + (e & 3);  // minus 4g, folded into vbits
+              x[e] = ((vbits >> row) & 1u) ? x[e] : -INFINITY;
+            }
           }
 #pragma unroll
           for (int e = 4 * (j - 8); e < 4 * (j - 8) + 4; ++e) pin(x[e]);
@@ -510,23 +541,18 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
           pin(mref);
           pin(l);
         }
-        if (j >= 16 && j < 24) {
-          // pair p = j - 16: the weights p sigma_k as rounded for the MFMA; the denominator
-          // sums p (the value rows are the bare codes)
-          const int e = 2 * (j - 16);
-          float a0 = x[e], a1 = x[e + 1];
+        if (j >= 16) {
+          const int e = j - 16;
+          float a0 = x[e];
           pin(a0);
-          pin(a1);
-          const float e0 = fast_exp2(a0 - mref), e1 = fast_exp2(a1 - mref);
-          l += e0 + e1;
-          const bf16x2_t w = {(__bf16)(e0 * ksc[e]), (__bf16)(e1 * ksc[e + 1])};
-          pk[j - 16] = __builtin_bit_cast(uint32_t, w);
-          asm volatile("" : "+v"(pk[j - 16]));
-          pin(l);
+          pw[e] = fast_exp2(a0 - mref);
+          pin(pw[e]);
         }
+        if (j >= 17) weigh(j - 17);
         pv_op(j);
       }
       __builtin_amdgcn_sched_barrier(0);
+      weigh(15);
     }
   }
 
