@@ -1,10 +1,14 @@
-// Dense MLA decode over a paged fp8 e4m3 cache with the scores on fp8 MFMA (gfx950).
+// MLA decode over an fp8 e4m3 latent cache with the scores on fp8 MFMA (gfx950): the dense
+// decode over a paged cache and the sparse decode over index lists.
 //
 // What is computed follows generic_flare_mla_decode_kv_cache_ragged (summary; Args q,
-// q_scale_ptr, kv_collection, input_row_offsets, scale, output; Parameters mask_str,
-// local_window_size, per_token_scale_rope_aware): mla_decode_paged_fp8, whose general
-// kernel is mla_sparse.hip with dense = 1.  This kernel serves its balanced split of at
-// most 64 rows and sequences at 128 heads.
+// q_scale_ptr, kv_collection, input_row_offsets, scale, output, d_indices, indices_stride,
+// topk_lengths; Parameters mask_str, local_window_size, sparse_mla, fold_shared_index,
+// per_token_scale_rope_aware): mla_decode_paged_fp8 and mla_decode_paged_sparse(_shared),
+// whose general kernel is mla_sparse.hip.  This kernel serves their balanced split of at
+// most 64 rows (and sequences) at 128 heads, without a sink or second stream.  With SPARSE
+// the 32 keys of a stage are the rows its 32 list positions name, each gathered by its own
+// lane; otherwise they are 32 consecutive positions of the sequence through its page table.
 //
 // Per work-group (4 waves, one per SIMD) and 32-key stage:
 //   scores    wave w computes S^T = K Q^T for heads 32w..32w+31 straight from the e4m3
@@ -12,13 +16,13 @@
 //             ROPE over the 512 latent columns (8 k-steps) plus v_mfma_f32_32x32x16_bf16 over
 //             the 64 bf16 rope columns (4 k-steps) into a second accumulator, so that the
 //             logit is scale * (sigma_q sigma_k S_latent + S_rope) exactly;
-//   values    the stage's 512 latent columns are widened to bf16 (exact) into a value tile
-//             while the matrix cores run the previous stage's values: wave w owns output
-//             columns 128w..128w+127 of all heads, O^T += V^T (P sigma_k)^T with the bf16
-//             weights of every head exchanged through LDS (the row scale rides on the weight,
-//             so V stays the bare codes and P keeps bf16 precision).
-// The stage pipeline is that of mla_decode2.hip: step k scores stage k while the vector
-// units run the online softmax of stage k-1, then adds the values of stage k-1.
+//   values    the stage's 512 latent columns are widened to bf16 (exact) into a value tile:
+//             wave w owns output columns 128w..128w+127 of all heads, O^T += V^T (P sigma_k)^T
+//             with the bf16 weights of every head exchanged through LDS (the row scale rides
+//             on the weight, so V stays the bare codes and P keeps bf16 precision).
+// Step k publishes the weights of stage k-1; then the score MFMAs of stage k run with the
+// first value MFMAs of stage k-1 and the widening of stage k, and the other value MFMAs of
+// stage k-1 run while the vector units turn the scores of stage k into weights.
 //
 // Layout of a stage's fp8 rows in LDS: chunk-major, 16-byte chunk c of row r at
 // (32 c + r) * 16.  A score operand (lane 32g + i: row i, bytes 64 ks + 32g .. + 31, two
@@ -79,7 +83,7 @@ __device__ __forceinline__ void fence_o(f32x16 (&o)[4][4]) {
   for (int cb = 1; cb < 4; ++cb) asm volatile("" : "+a"(o[cb][0]), "+a"(o[cb][1]), "+a"(o[cb][2]), "+a"(o[cb][3]));
 }
 
-template <int KPAGES, bool ROPE>
+template <int KPAGES, bool ROPE, bool SPARSE>
 __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint8_t* raw, MLA_LDS uint8_t* vt,
                                                MLA_LDS uint8_t* xbuf, F8Lds& L, int t, const RowGeo& g, int ta,
                                                int tc, bool full, int slot) {
@@ -104,24 +108,41 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
   const int32_t* pt = a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.pt_row;
   const int p_last = (khi - 1) / a.PS;
   const int npages32 = (int)min(a.num_rows / a.PS, (int64_t)INT32_MAX);
+  // SPARSE: list row g.b of d_indices; list position p of the segment is key p
+  const int32_t* ilist = a.idx + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.idx_row;
+  static_assert(!SPARSE || KPAGES == 0, "the sparse rows are gathered one by one");
 
   // every wave must be done with the buffers and window of anything before
   all_wait0();
   stage_barrier();
 
-  // ---- page-id window [pbase, pbase + kF8PidWindow) (entries past the segment are -1)
-  int pbase = klo / a.PS;
+  // ---- page-id window [pbase, pbase + kF8PidWindow) (entries past the segment are -1);
+  // SPARSE: the listed rows of list positions [pbase, pbase + kF8PidWindow), checked against
+  // the pool as they are stored (-1 past the segment, for negative entries, which are
+  // skipped, and for rows past the end of the pool, which are skipped and flagged)
+  int pbase = SPARSE ? klo : klo / a.PS;
   int pv[kF8PidWindow / NT];
+  bool bad_idx = false;
   auto window_load = [&]() {
 #pragma unroll
     for (int i = 0; i < kF8PidWindow / NT; ++i) {
       const int p = pbase + tid + i * NT;
-      pv[i] = p <= p_last ? pt[p] : -1;
+      if (SPARSE)
+        pv[i] = p < khi ? ilist[p] : -1;
+      else
+        pv[i] = p <= p_last ? pt[p] : -1;
     }
   };
   auto window_store = [&]() {
 #pragma unroll
-    for (int i = 0; i < kF8PidWindow / NT; ++i) pids[tid + i * NT] = pv[i];
+    for (int i = 0; i < kF8PidWindow / NT; ++i) {
+      int r = pv[i];
+      if (SPARSE && (int64_t)r >= a.num_rows) {
+        bad_idx = true;
+        r = -1;
+      }
+      pids[tid + i * NT] = SPARSE && r < 0 ? -1 : r;
+    }
   };
   // moves the window to start at page `base` (block-uniform call; drains the stage loads)
   auto window_move = [&](int base) {
@@ -186,12 +207,28 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     const int kbase = st * kStageKeys;
     return a.cache_scale + (int64_t)pa * a.cs_page + ((uint32_t)kbase % (uint32_t)a.PS) + (lane_c & 31);
   };
+  // SPARSE: the place of listed row r (page * PS + slot, or r itself in a flat pool) and of
+  // its scale
+  auto sparse_row = [&](int r) -> const uint8_t* {
+    if (a.flat) return a.cache + (int64_t)r * G::kRow;
+    const int pg = r / a.PS;
+    return a.cache + (int64_t)pg * a.page_bytes + (int64_t)(r - pg * a.PS) * G::kRow;
+  };
+  auto sparse_scale = [&](int r) -> const void* {
+    if (a.cache_scale == nullptr) return a.zero_row + kSparseOneOffset;
+    if (a.flat) return a.cache_scale + r;
+    const int pg = r / a.PS;
+    return a.cache_scale + (int64_t)pg * a.cs_page + (r - pg * a.PS);
+  };
   // pa: the stage's page id when a stage lies in one page (KPAGES), which the window may
-  // not hold yet (the prologue issues before it is stored)
-  auto issue_general = [&](int st, int bi, int pa) {
+  // not hold yet (the prologue issues before it is stored).  Returns the stage's keys that
+  // count (SPARSE: the listed ones; else all, the range mask covers the rest).
+  auto issue_general = [&](int st, int bi, int pa) -> uint32_t {
     MLA_LDS uint8_t* dst = raw + bi * G::kStage;
     const int kbase = st * kStageKeys;
-    if (KPAGES == 0) {
+    if (SPARSE) {
+      if (min(kbase + kStageKeys, khi) - 1 >= pbase + kF8PidWindow) window_move(max(kbase, klo));
+    } else if (KPAGES == 0) {
       const int lp_hi = (min(kbase + kStageKeys, khi) - 1) / a.PS;
       if (lp_hi >= pbase + kF8PidWindow) window_move(max(kbase, klo) / a.PS);
     }
@@ -200,7 +237,13 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     const int row = lane_v & 31, key = kbase + row;
     const uint8_t* rsrc = nullptr;  // this lane's row, null: the zero row
     const void* ssrc = a.zero_row;  // and its scale (0 for a key that does not count)
-    if (key >= klo && key < khi) {
+    if (SPARSE) {
+      const int r = key >= klo && key < khi ? pids[key - pbase] : -1;
+      if (r >= 0) {
+        rsrc = sparse_row(r);
+        ssrc = sparse_scale(r);
+      }
+    } else if (key >= klo && key < khi) {
       const int lp = key / a.PS;
       const int pid = KPAGES != 0 ? pa : pids[lp - pbase];
       if (pid >= 0 && pid < npages32) {
@@ -218,16 +261,15 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
       dma16_nt((rsrc != nullptr ? rsrc : a.zero_row) + 16 * c, dst + J * 1024);
     }
     dma4(ssrc, ksl(st - s_first));
+    return SPARSE ? (uint32_t)__builtin_amdgcn_ballot_w64(lane_v < 32 && rsrc != nullptr) : ~0u;
   };
-  auto issue = [&](int st, int bi, int pa) {
+  auto issue = [&](int st, int bi, int pa) -> uint32_t {
     const uint8_t* fb = fast_base(st, pa);
-    if (fb == nullptr) {
-      issue_general(st, bi, pa);
-      return;
-    }
+    if (fb == nullptr) return issue_general(st, bi, pa);
 #pragma unroll
     for (int jj = 0; jj < kF8Loads; ++jj) fast_load(fb, raw + bi * G::kStage, jj);
     dma4(scale_src_fast(st, pa), ksl(st - s_first));
+    return ~0u;
   };
 
   // ---- query fragments (B operand of S^T = K Q^T): lane 32g + i holds q[head h0 + i]
@@ -258,8 +300,9 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
   for (int i = tid; i < kF8Scales * 64; i += NT) ((MLA_LDS float*)L.ksc)[i] = 0.f;
   lgkm_wait0();
   stage_barrier();
-  issue(s_first, 0, pa0);
-  if (nst > 1) issue(s_first + 1, 1, pa1);
+  // keys that count in stages k and k+1 (SPARSE; all otherwise)
+  uint32_t msk0 = issue(s_first, 0, pa0), msk1 = ~0u;
+  if (nst > 1) msk1 = issue(s_first + 1, 1, pa1);
   if (KPAGES != 0) window_load();
   {
     MLA_LDS uint8_t* z = vt + kF8VBytes;
@@ -327,10 +370,11 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     const int kn = k + 2;
     const uint8_t* fb = nullptr;
     int pa_k = 0;
+    uint32_t msk2 = ~0u;
     if (kn < nst) {
       pa_k = pa_n;
       fb = fast_base(s_first + kn, pa_n);
-      if (fb == nullptr) issue_general(s_first + kn, kn % kF8Raw, pa_n);
+      if (fb == nullptr) msk2 = issue_general(s_first + kn, kn % kF8Raw, pa_n);
       if (KPAGES != 0 && kn + 1 < nst) pa_n = stage_page(s_first + kn + 1);
     }
     MLA_LDS uint8_t* fdst = raw + (kn % kF8Raw) * G::kStage;
@@ -462,7 +506,7 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     // Only a segment's first and last stage (and the stale stage after the last) have keys
     // to mask: the other stages branch around the mask.
     {
-      const uint32_t valid = k < nst ? range_bits((s_first + k) * kStageKeys, klo, khi) : 0u;
+      const uint32_t valid = k < nst ? range_bits((s_first + k) * kStageKeys, klo, khi) & msk0 : 0u;
       const bool partial = valid != 0xFFFFFFFFu;
       const uint32_t vbits = valid >> (4 * lg);
       float x[16];
@@ -554,9 +598,12 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
       __builtin_amdgcn_sched_barrier(0);
       weigh(15);
     }
+    msk0 = msk1;
+    msk1 = msk2;
   }
 
   if (bad_page) atomicOr(a.err, kErrPageId);
+  if (SPARSE && __builtin_amdgcn_ballot_w64(bad_idx) != 0 && lane == 0) atomicOr(a.err, kErrSparseIndex);
 
   // ---- epilogue: each head's 1/l from its owner, then the wave's 128 columns of every
   // head, normalised, through LDS to contiguous stores
@@ -600,7 +647,7 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
   }
 }
 
-template <int KPAGES, bool ROPE>
+template <int KPAGES, bool ROPE, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void mla_fp8mma_kernel(const SparseArgs a, const SplitPlan plan) {
   __shared__ __attribute__((aligned(1024))) uint8_t raw_b[kF8Raw * F8Geo<true>::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t vt_b[2 * kF8VBytes];
@@ -609,26 +656,31 @@ __global__ __launch_bounds__(256, 1) void mla_fp8mma_kernel(const SparseArgs a, 
   static_assert(2 * kF8VBytes >= 4 * 8192, "epilogue staging");
   plan_run<256, true>(
       plan, L, [&](F8Lds&) {}, [&](int) { return RowGeo{-1, 0, 0}; },
-      [&](RowGeo* geo, int lane) { decode_fill_wave(a, geo, lane); },
+      [&](RowGeo* geo, int lane) {
+        if constexpr (SPARSE) sparse_fill_wave<false>(a, geo, lane); else decode_fill_wave(a, geo, lane);
+      },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
-        fp8mma_segment<KPAGES, ROPE>(a, (MLA_LDS uint8_t*)raw_b, (MLA_LDS uint8_t*)vt_b, (MLA_LDS uint8_t*)xbuf_b, L,
+        fp8mma_segment<KPAGES, ROPE, SPARSE>(a, (MLA_LDS uint8_t*)raw_b, (MLA_LDS uint8_t*)vt_b, (MLA_LDS uint8_t*)xbuf_b, L,
                                      r, g, ta, tc, full, slot);
       });
 }
 
 }  // namespace
 
-// The dense fp8 decode's balanced split of at most 64 rows and sequences at 128 heads
-// (see launch_sparse).
+// The balanced split of at most 64 rows at 128 heads, for the dense fp8 decode and the
+// sparse decode without a sink or second stream (see launch_sparse).
 hipError_t launch_fp8mma(const SparseArgs& a, const SplitPlan& p, hipStream_t stream) {
   const dim3 grid(a.grid), block(256);
   const bool kp = a.PS % kStageKeys == 0;
-  if (a.rope) {
-    if (kp) hipLaunchKernelGGL((mla_fp8mma_kernel<1, true>), grid, block, 0, stream, a, p);
-    else hipLaunchKernelGGL((mla_fp8mma_kernel<0, true>), grid, block, 0, stream, a, p);
+  if (!a.dense) {
+    if (a.rope) hipLaunchKernelGGL((mla_fp8mma_kernel<0, true, true>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_fp8mma_kernel<0, false, true>), grid, block, 0, stream, a, p);
+  } else if (a.rope) {
+    if (kp) hipLaunchKernelGGL((mla_fp8mma_kernel<1, true, false>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_fp8mma_kernel<0, true, false>), grid, block, 0, stream, a, p);
   } else {
-    if (kp) hipLaunchKernelGGL((mla_fp8mma_kernel<1, false>), grid, block, 0, stream, a, p);
-    else hipLaunchKernelGGL((mla_fp8mma_kernel<0, false>), grid, block, 0, stream, a, p);
+    if (kp) hipLaunchKernelGGL((mla_fp8mma_kernel<1, false, false>), grid, block, 0, stream, a, p);
+    else hipLaunchKernelGGL((mla_fp8mma_kernel<0, false, false>), grid, block, 0, stream, a, p);
   }
   return hipGetLastError();
 }

@@ -62,47 +62,6 @@ constexpr int kSpStageLds = kSpTiles * kStageBytes + kSpRaw * kRawStageBytesMax;
 constexpr int kSpLdsBytes = kSpStageLds > 4 * 32 * 1024 ? kSpStageLds : 4 * 32 * 1024;
 static_assert(sizeof(PlanLds::scan) == kIdxWindow * sizeof(int), "the window lives in the planning scratch");
 
-// Row t's list positions [0, n): its first min(topk[t], shape[1] of d_indices) entries,
-// then (EXT with a second stream) the first min(xtopk[t], its width) entries of its second
-// list.
-__device__ __forceinline__ int sparse_main_len(const SparseArgs& a, int t) {
-  return max(0, min(ld_const(a.topk + t), a.idx_cols));
-}
-template <bool XTRA>
-__device__ __forceinline__ int sparse_len(const SparseArgs& a, int t) {
-  int n = sparse_main_len(a, t);
-  if (XTRA && a.xidx != nullptr) n += max(0, min(ld_const(a.xtopk + t), a.xidx_cols));
-  return n;
-}
-// Row geometry: b = the row of d_indices / topk_lengths that query row t reads -- t itself,
-// or with shared lists ([DEC] Parameters fold_shared_index) the sequence of t in the
-// input_row_offsets (-1 with no visible entry for a row outside them) -- and the list
-// positions [0, n).
-template <bool XTRA>
-__device__ __forceinline__ RowGeo sparse_row_geo(const SparseArgs& a, int t) {
-  if (!a.shared) return RowGeo{t, 0, sparse_len<XTRA>(a, t)};
-  int lo = 0, hi = a.B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((int)ld_const(a.offsets + mid) <= t) lo = mid; else hi = mid;
-  }
-  const int o0 = (int)ld_const(a.offsets + lo), o1 = (int)ld_const(a.offsets + lo + 1);
-  if (t < o0 || t >= o1) return RowGeo{-1, 0, 0};
-  return RowGeo{lo, 0, sparse_main_len(a, lo)};
-}
-
-// Shared lists: sequence b (one thread or lane per sequence) writes the geometry of its
-// query rows; malformed offsets set kErrOffsets and leave their rows empty.
-__device__ __forceinline__ void sparse_fill_seq(const SparseArgs& a, RowGeo* geo, int b) {
-  const int o0 = (int)a.offsets[b], o1 = (int)a.offsets[b + 1];
-  if (o1 < o0 || o0 < 0 || o1 > a.T) {
-    atomicOr(a.err, kErrOffsets);
-    return;
-  }
-  const int n = sparse_main_len(a, b);
-  for (int t = o0; t < o1; ++t) geo[t] = RowGeo{b, 0, n};
-}
-
 template <int NT, bool XTRA>
 __device__ __forceinline__ void sparse_fill(const SparseArgs& a, PlanLds& L) {
   if (!a.shared) {
@@ -520,14 +479,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_sparse_kernel(const SparseArgs
         if constexpr (DENSE) return decode_row_geo(a, t); else return sparse_row_geo<XTRA>(a, t);
       },
       [&](RowGeo* geo, int lane) {
-        if constexpr (DENSE) {
-          decode_fill_wave(a, geo, lane);
-        } else if (!a.shared) {
-          if (lane < a.T) geo[lane] = RowGeo{lane, 0, sparse_len<XTRA>(a, lane)};
-        } else {
-          if (lane < a.T) geo[lane] = RowGeo{-1, 0, 0};
-          if (lane < a.B) sparse_fill_seq(a, geo, lane);
-        }
+        if constexpr (DENSE) decode_fill_wave(a, geo, lane); else sparse_fill_wave<XTRA>(a, geo, lane);
       },
       [&](int r, const RowGeo& g, int ta, int tc, bool full, int slot) {
         sparse_segment<HB, NW, DENSE, XTRA, ROPE>(a, tiles, land, ksc, (MLA_LDS int*)L.scan, r, g, ta, tc, full, slot);
@@ -557,7 +509,8 @@ template <int HB, int NW>
 static hipError_t launch_sparse_h(const SparseArgs& a, const SplitPlan& p, hipStream_t stream) {
   const dim3 grid(a.nparts >= 1 ? a.T * a.nparts : a.grid), block(NW * 64);
   const bool small = a.nparts == 0 && a.T <= 64 && a.T <= a.grid && ((!a.dense && !a.shared) || a.B <= 64);
-  if (HB == 2 && NW == 4 && a.dense && small && !a.q_bf16) return launch_fp8mma(a, p, stream);
+  if (HB == 2 && NW == 4 && small && !a.q_bf16 && a.xidx == nullptr && a.sink == nullptr)
+    return launch_fp8mma(a, p, stream);
   if (a.rope) {
     if (a.xidx != nullptr || a.sink != nullptr) return hipErrorInvalidValue;  // refused by the host checks
     if (a.dense) {

@@ -77,6 +77,30 @@ def test_many_rows_sampled(B, H, rows_per_seq, n_index):
         compare(got[rows], want, FP8_TOL, f"{B} rows x {H} heads P={P} (sampled)")
 
 
+def test_long_lists_window_refill():
+    """64 one-token rows at 128 heads whose lists hold up to 8192 entries, drawn with
+    repetition from 1024 rows of each sequence, one in 16 skipped: the library's split gives
+    each work-group segments of about 2000 list positions, so the window of listed rows the
+    balanced-batch kernel holds (512 positions) is refilled inside its segments.  Four rows
+    are compared with the oracle; the whole output is finite."""
+    m = need_gpu()
+    case = make_sparse_case(79, 64, 128, 1024, 64, (1024, 1024), 1024, name="sp-long")
+    rng = np.random.default_rng(79)
+    n = 8192
+    idx = np.empty((64, n), np.int32)
+    for b in range(64):
+        idx[b] = case.d_indices[b][rng.integers(0, 1024, size=n)]
+        idx[b, rng.random(n) < 1 / 16] = -1
+    topk = rng.integers(6000, n, endpoint=True, size=64).astype(np.int32)
+    rows = [0, 17, 40, 63]
+    want = oracle_of(case, d_indices=idx, topk=topk, rows=rows)
+    m.check_device_errors()
+    got = to_f64(sparse_on_gpu(m, case, d_indices=idx, topk=topk))
+    assert m.check_device_errors() == 0
+    assert np.all(np.isfinite(got))
+    compare(got[rows], want, FP8_TOL, "long lists (sampled)")
+
+
 def test_index_list_semantics():
     """Duplicates count twice, negative entries are skipped, entries past topk are never
     read (even when they name rows outside the pool), topk is clamped to the list width,

@@ -81,20 +81,26 @@ def test_c4_with_sink_and_second_stream():
 
 def test_without_sink_or_rows_is_the_plain_sparse_decode():
     """A sink of -inf everywhere, or a second stream whose lists count no row, gives the
-    same bits as mla_decode_paged_sparse."""
+    same bits as mla_decode_paged_sparse on the same split (num_partitions 3: one kernel
+    serves all three).  With the library's split the plain decode of this batch runs the
+    balanced-batch fp8-MFMA kernel: it agrees with them within the fp8 tolerance, and the
+    two extended forms still agree bit for bit."""
     m = need_gpu()
     case = make_sparse_case(405, 8, 128, 1000, 64, (1, 500), 500, name="ext-plain")
     import torch
-    plain = m.decode_paged_sparse(u8_dev(case.q8), f32_dev(case.q_scale), i32_dev(case.input_row_offsets),
-                                  u8_dev(case.cache8), f32_dev(case.cache_scale), i32_dev(case.d_indices),
-                                  i32_dev(case.topk_lengths), case.scale)
-    torch.cuda.synchronize()
-    a = bits_of(plain)
-    b = bits_of(ext_on_gpu(m, case, sink=np.full(128, -np.inf, dtype=np.float32)))
     c8, cs, idx, tk, ps = second_stream(406, 8, 16, 200, 50, (0, 50))
-    c = bits_of(ext_on_gpu(m, case, extra=(c8, cs, idx, np.zeros_like(tk), ps)))
-    assert np.array_equal(a, b)
-    assert np.array_equal(a, c)
+    for P in (3, 0):
+        plain = m.decode_paged_sparse(u8_dev(case.q8), f32_dev(case.q_scale), i32_dev(case.input_row_offsets),
+                                      u8_dev(case.cache8), f32_dev(case.cache_scale), i32_dev(case.d_indices),
+                                      i32_dev(case.topk_lengths), case.scale, num_partitions=P)
+        torch.cuda.synchronize()
+        b = ext_on_gpu(m, case, sink=np.full(128, -np.inf, dtype=np.float32), num_partitions=P)
+        c = ext_on_gpu(m, case, extra=(c8, cs, idx, np.zeros_like(tk), ps), num_partitions=P)
+        assert np.array_equal(bits_of(b), bits_of(c))
+        if P:
+            assert np.array_equal(bits_of(plain), bits_of(b))
+        else:
+            compare(to_f64(b), to_f64(plain), FP8_TOL, "extended forms vs plain, library split")
 
 
 def test_second_stream_poison_and_bad_rows():
