@@ -263,6 +263,28 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     dma4(ssrc, ksl(st - s_first));
     return SPARSE ? (uint32_t)__builtin_amdgcn_ballot_w64(lane_v < 32 && rsrc != nullptr) : ~0u;
   };
+  // SPARSE inside the stage loop: this lane's row and scale sources of stage st (the loads
+  // themselves are spread over the next score k-steps) and the stage's keys that count
+  struct Gather {
+    const uint8_t* row;  // the row's chunk for this lane's half (the zero row when skipped)
+    const void* scale;
+    uint32_t mask;
+  };
+  auto gather_prep = [&](int st) -> Gather {
+    const int kbase = st * kStageKeys;
+    if (min(kbase + kStageKeys, khi) - 1 >= pbase + kF8PidWindow) window_move(max(kbase, klo));
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int key = kbase + (lane_v & 31);
+    const int r = key >= klo && key < khi ? pids[key - pbase] : -1;
+    Gather gp{a.zero_row + 16 * (lane_v >> 5), a.zero_row, 0u};
+    if (r >= 0) {
+      gp.row = sparse_row(r) + 16 * (lane_v >> 5);
+      gp.scale = sparse_scale(r);
+    }
+    gp.mask = (uint32_t)__builtin_amdgcn_ballot_w64(lane_v < 32 && r >= 0);
+    return gp;
+  };
   auto issue = [&](int st, int bi, int pa) -> uint32_t {
     const uint8_t* fb = fast_base(st, pa);
     if (fb == nullptr) return issue_general(st, bi, pa);
@@ -371,7 +393,11 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     const uint8_t* fb = nullptr;
     int pa_k = 0;
     uint32_t msk2 = ~0u;
-    if (kn < nst) {
+    Gather gk{nullptr, nullptr, 0u};  // SPARSE: stage k+2's sources
+    if (kn < nst && SPARSE) {
+      gk = gather_prep(s_first + kn);
+      msk2 = gk.mask;
+    } else if (kn < nst) {
       pa_k = pa_n;
       fb = fast_base(s_first + kn, pa_n);
       if (fb == nullptr) msk2 = issue_general(s_first + kn, kn % kF8Raw, pa_n);
@@ -494,6 +520,10 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
         if (i < 8) pv_op(i);
         if (i < kF8Loads && fb != nullptr) fast_load(fb, fdst, i);
         if (i == kF8Loads && fb != nullptr) dma4(scale_src_fast(s_first + kn, pa_k), ksl(kn));
+        if (SPARSE && kn < nst) {
+          if (i < kF8Loads) dma16_nt(gk.row + 32 * load_j(i), fdst + load_j(i) * 1024);
+          if (i == kF8Loads) dma4(gk.scale, ksl(kn));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
