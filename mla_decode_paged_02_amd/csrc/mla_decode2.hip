@@ -537,19 +537,24 @@ __device__ __forceinline__ void decode2_segment(const DecodeArgs& a, MLA_LDS uin
   mfma32_fence_a(O);
   lgkm_wait0();
   stage_barrier();  // every wave is done with the stage buffers and has published 1/l
-  MLA_LDS uint8_t* st = tiles + wave * 8192;  // [32 heads][256 bytes], chunk c of head h at c ^ (h >> 1)
+  // two staging areas per wave, [32 heads][256 bytes] each (chunk c of head h at c ^ (h >> 1)),
+  // taken in turn: a head block's rows are written while the previous block's are stored
+  MLA_LDS uint8_t* st2 = tiles + wave * 16384;
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    MLA_LDS uint8_t* st = st2 + (hb & 1) * 8192;
     const float inv = inv_s[hb * 32 + li];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const f32x16& o = O[cb][hb];
-        const uint32_t w0 = (uint32_t)bf16_bits_rne(o[4 * r] * inv) | ((uint32_t)bf16_bits_rne(o[4 * r + 1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)bf16_bits_rne(o[4 * r + 2] * inv) | ((uint32_t)bf16_bits_rne(o[4 * r + 3] * inv) << 16);
+        const bf16x2_t p0 = {(__bf16)(o[4 * r] * inv), (__bf16)(o[4 * r + 1] * inv)};
+        const bf16x2_t p1 = {(__bf16)(o[4 * r + 2] * inv), (__bf16)(o[4 * r + 3] * inv)};
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, p0), w1 = __builtin_bit_cast(uint32_t, p1);
         *(MLA_LDS u32x2*)(st + li * 256 + (((4 * cb + r) ^ (li >> 1)) << 4) + 8 * lg) = u32x2{w0, w1};
       }
     lgkm_wait0();
@@ -562,7 +567,6 @@ __device__ __forceinline__ void decode2_segment(const DecodeArgs& a, MLA_LDS uin
       const u32x4 w = *(const MLA_LDS u32x4*)(st + hl * 256 + ((c ^ (hl >> 1)) << 4));
       __builtin_nontemporal_store(w, (u32x4*)(base + hl * hstride + 128 * wave + 8 * c));
     }
-    lgkm_wait0();  // the staging rows are rewritten for the next head block
   }
 }
 
@@ -571,7 +575,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode2_kernel(const DecodeArgs a,
   __shared__ __attribute__((aligned(1024))) uint8_t tiles_raw[kD2Bufs * kStageBytes];
   __shared__ __attribute__((aligned(256))) uint8_t xbuf_raw[kD2PBytes + kD2ABytes];
   __shared__ D2Lds L;
-  static_assert(kD2Bufs * kStageBytes >= 4 * 8192, "epilogue staging");
+  static_assert(kD2Bufs * kStageBytes >= 4 * 16384, "epilogue staging");
   MLA_LDS uint8_t* tiles = (MLA_LDS uint8_t*)tiles_raw;
   MLA_LDS uint8_t* xbuf = (MLA_LDS uint8_t*)xbuf_raw;
   plan_run<256, true>(

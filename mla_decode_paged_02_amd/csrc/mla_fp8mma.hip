@@ -649,18 +649,22 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
   fence_o(O);
   lgkm_wait0();
   stage_barrier();  // every wave is done with the stage buffers and has published 1/l
-  MLA_LDS uint8_t* st = vt + wave * 8192;  // [32 heads][256 bytes], chunk c of head h at c ^ (h >> 1)
+  // two staging areas per wave, [32 heads][256 bytes] each (chunk c of head h at c ^ (h >> 1)),
+  // taken in turn: a head block's rows are written while the previous block's are stored
+  MLA_LDS uint8_t* st2 = vt + wave * 16384;
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
+    MLA_LDS uint8_t* st = st2 + (hb & 1) * 8192;
     const float inv = inv_s[hb * 32 + li];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const f32x16& o = O[cb][hb];
-        const uint32_t w0 = (uint32_t)bf16_bits_rne(o[4 * r] * inv) | ((uint32_t)bf16_bits_rne(o[4 * r + 1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)bf16_bits_rne(o[4 * r + 2] * inv) | ((uint32_t)bf16_bits_rne(o[4 * r + 3] * inv) << 16);
+        const bf16x2_t p0 = {(__bf16)(o[4 * r] * inv), (__bf16)(o[4 * r + 1] * inv)};
+        const bf16x2_t p1 = {(__bf16)(o[4 * r + 2] * inv), (__bf16)(o[4 * r + 3] * inv)};
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, p0), w1 = __builtin_bit_cast(uint32_t, p1);
         *(MLA_LDS u32x2*)(st + li * 256 + (((4 * cb + r) ^ (li >> 1)) << 4) + 8 * lg) = u32x2{w0, w1};
       }
     lgkm_wait0();
@@ -673,7 +677,6 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
       const u32x4 w = *(const MLA_LDS u32x4*)(st + hl * 256 + ((c ^ (hl >> 1)) << 4));
       __builtin_nontemporal_store(w, (u32x4*)(base + hl * hstride + 128 * wave + 8 * c));
     }
-    lgkm_wait0();  // the staging rows are rewritten for the next head block
   }
 }
 
@@ -683,7 +686,7 @@ __global__ __launch_bounds__(256, 1) void mla_fp8mma_kernel(const SparseArgs a, 
   __shared__ __attribute__((aligned(1024))) uint8_t vt_b[2 * kF8VBytes];
   __shared__ __attribute__((aligned(256))) uint8_t xbuf_b[kF8PBytes + 1536];
   __shared__ F8Lds L;
-  static_assert(2 * kF8VBytes >= 4 * 8192, "epilogue staging");
+  static_assert(2 * kF8VBytes >= 4 * 16384, "epilogue staging");
   plan_run<256, true>(
       plan, L, [&](F8Lds&) {}, [&](int) { return RowGeo{-1, 0, 0}; },
       [&](RowGeo* geo, int lane) {
