@@ -34,6 +34,22 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode GB/s (% of HBM peak) + tokens/s, B=64 H=128 ctx≤4K, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+# fp8 workloads whose 128-head batches run the balanced fp8 kernel: the logits of these
+# many columns per key take fp8 MFMA, the rest of the logit (bf16 rope) and the 512 value
+# columns bf16 MFMA
+FP8_SCORE_COLS = {"C4": 576, "D8": 576, "S2": 576, "R8": 512}
+
+
+def mfma_peak(wl):
+    """Dense MFMA peak (TFLOP/s) of the workload's contraction mix: bf16, or for the fp8
+    workloads the time-weighted peak of fp8 scores and bf16 rope and values (576 + 512
+    flop columns per key and head, each at its own dtype's peak)."""
+    if wl not in FP8_SCORE_COLS:
+        return BF16_PEAK_TFLOPS
+    f8 = FP8_SCORE_COLS[wl]
+    bf = 576 - f8 + 512
+    return (f8 + bf) / (f8 / FP8_PEAK_TFLOPS + bf / BF16_PEAK_TFLOPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c1_traffic.txt")
 CSRC = os.path.join(ROOT, "mla_decode_paged_02_amd", "csrc")
 
@@ -53,8 +69,8 @@ DESCRIPTIONS = {
 # multi-token workloads: (configuration they extend, query tokens per sequence)
 MULTI_TOKEN = {"M2": (1, 2), "M4": (1, 4)}
 KERNELS = {"C0": "mla_decode_kernel", "C1": "mla_decode2_kernel", "C2": "mla_decode2_kernel",
-           "C3": "mla_prefill_kernel", "C4": "mla_sparse_kernel", "M2": "mla_decode_kernel",
-           "M4": "mla_decode_kernel", "D8": "mla_sparse_kernel", "R8": "mla_sparse_kernel", "S2": "mla_sparse_kernel",
+           "C3": "mla_prefill_kernel", "C4": "mla_fp8mma_kernel", "M2": "mla_decode_kernel",
+           "M4": "mla_decode_kernel", "D8": "mla_fp8mma_kernel", "R8": "mla_fp8mma_kernel", "S2": "mla_fp8mma_kernel",
            "X4": "mla_indexer_score_kernel + mla_indexer_select_kernel"}
 
 
@@ -398,14 +414,17 @@ def main():
 
     gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     tflops = alg_flops / (ms_step * 1e-3) / 1e12
-    # the roofline that bounds the kernel: bf16 MFMA when its arithmetic intensity is past
-    # the ridge (peak FLOP/s over peak bytes/s), else HBM
-    mfma_bound = alg_flops / alg_bytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    # the roofline that bounds the kernel: MFMA (bf16, or the fp8 / bf16 mix) when its
+    # arithmetic intensity is past the ridge (peak FLOP/s over peak bytes/s), else HBM
+    peak_mfma = mfma_peak(wl)
+    mfma_bound = alg_flops / alg_bytes > peak_mfma * 1e12 / (HBM_PEAK_GBS * 1e9)
     if mfma_bound and not prefill:
         achieved = alg_flops / (k_avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak_mfma, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / peak_mfma, 4), "traffic": None,
                 "hbm_achieved_gbs": round(alg_bytes / (k_avg_ms * 1e-3) / 1e9, 2)}
+        if wl in FP8_SCORE_COLS:
+            roof["peak_mix"] = f"fp8 scores over {FP8_SCORE_COLS[wl]} columns, bf16 for the rest and the values"
         metric = METRIC if wl == "C1" else f"MLA {'sparse ' if wl in ('C4', 'S2') else 'fp8 ' if wl == 'D8' else 'fp8 rope-aware ' if wl == 'R8' else ''}decode GB/s, {wl}, 1 GPU"
         if wl == "X4":
             metric = "MLA fp8 top-k indexer GB/s (cache rows once per token), X4, 1 GPU"
