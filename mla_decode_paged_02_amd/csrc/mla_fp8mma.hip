@@ -116,6 +116,23 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
   all_wait0();
   stage_barrier();
 
+  // ---- query fragments (B operand of S^T = K Q^T), loaded first so that their latency
+  // overlaps the window's: lane 32g + i holds q[head h0 + i]
+  // bytes 64 ks + 32 g .. + 31 (e4m3), with ROPE also bf16 rope columns 16 kr + 8 g .. + 7
+  const uint8_t* qh = a.q + (int64_t)t * a.q_tok + (int64_t)(h0 + li) * a.q_head;
+  i32x8 qf[G::kKs8];
+#pragma unroll
+  for (int ks = 0; ks < G::kKs8; ++ks) {
+    const uint4 lo = *(const uint4*)(qh + 64 * ks + 32 * lg);
+    const uint4 hi = *(const uint4*)(qh + 64 * ks + 32 * lg + 16);
+    qf[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  bf16x8 qr[4];
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int kr = 0; kr < 4; ++kr) qr[kr] = *(const bf16x8*)(qh + 512 + 32 * kr + 16 * lg);
+  }
+
   // ---- page-id window [pbase, pbase + kF8PidWindow) (entries past the segment are -1);
   // SPARSE: the listed rows of list positions [pbase, pbase + kF8PidWindow), checked against
   // the pool as they are stored (-1 past the segment, for negative entries, which are
@@ -294,24 +311,6 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     return ~0u;
   };
 
-  // ---- query fragments (B operand of S^T = K Q^T): lane 32g + i holds q[head h0 + i]
-  // bytes 64 ks + 32 g .. + 31 (e4m3), with ROPE also bf16 rope columns 16 kr + 8 g .. + 7
-  const uint8_t* qh = a.q + (int64_t)t * a.q_tok + (int64_t)(h0 + li) * a.q_head;
-  i32x8 qf[G::kKs8];
-#pragma unroll
-  for (int ks = 0; ks < G::kKs8; ++ks) {
-    const uint4 lo = *(const uint4*)(qh + 64 * ks + 32 * lg);
-    const uint4 hi = *(const uint4*)(qh + 64 * ks + 32 * lg + 16);
-    qf[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  }
-  bf16x8 qr[4];
-  if constexpr (ROPE) {
-#pragma unroll
-    for (int kr = 0; kr < 4; ++kr) qr[kr] = *(const bf16x8*)(qh + 512 + 32 * kr + 16 * lg);
-  }
-  const float q_scale = a.q_scale != nullptr ? ld_const(a.q_scale + t) : 1.f;
-  const float qsl = a.scale_log2 * q_scale;  // logit units per code product (times sigma_k)
-
   // ---- prologue: stages 0 and 1 (their page ids by scalar loads, which the full wait
   // covers), the window for the loop, and zeros in the value tile "stage -1" uses
   auto direct_page = [&](int st) { return ld_const(pt + st * kStageKeys / a.PS); };
@@ -322,6 +321,10 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
   for (int i = tid; i < kF8Scales * 64; i += NT) ((MLA_LDS float*)L.ksc)[i] = 0.f;
   lgkm_wait0();
   stage_barrier();
+  // the token scale after that wait, which drains the scalar loads too: its latency hides
+  // under the stage loads
+  const float q_scale = a.q_scale != nullptr ? ld_const(a.q_scale + t) : 1.f;
+  const float qsl = a.scale_log2 * q_scale;  // logit units per code product (times sigma_k)
   // keys that count in stages k and k+1 (SPARSE; all otherwise)
   uint32_t msk0 = issue(s_first, 0, pa0), msk1 = ~0u;
   if (nst > 1) msk1 = issue(s_first + 1, 1, pa1);
