@@ -101,12 +101,14 @@ def test_long_lists_window_refill():
     compare(got[rows], want, FP8_TOL, "long lists (sampled)")
 
 
-def test_index_list_semantics():
+# 128 heads: the balanced-batch fp8-MFMA kernel; the other head counts: the general kernel
+@pytest.mark.parametrize("H", [64, 128])
+def test_index_list_semantics(H):
     """Duplicates count twice, negative entries are skipped, entries past topk are never
     read (even when they name rows outside the pool), topk is clamped to the list width,
     and an empty list gives zeros -- none of this raises the device error bit."""
     m = need_gpu()
-    case = make_sparse_case(41, 5, 64, 512, 64, (100, 100), 120, name="sp-sem")
+    case = make_sparse_case(41, 5, H, 512, 64, (100, 100), 120, name="sp-sem")
     idx = case.d_indices.copy()
     topk = case.topk_lengths.copy()
     idx[0, 10] = idx[0, 3]          # duplicate
@@ -123,9 +125,10 @@ def test_index_list_semantics():
     assert np.all(got[4] == 0)
 
 
-def test_out_of_pool_index_is_flagged_and_skipped():
+@pytest.mark.parametrize("H", [32, 128])
+def test_out_of_pool_index_is_flagged_and_skipped(H):
     m = need_gpu()
-    case = make_sparse_case(42, 3, 32, 256, 64, (60, 60), 64, name="sp-oob")
+    case = make_sparse_case(42, 3, H, 256, 64, (60, 60), 64, name="sp-oob")
     idx = case.d_indices.copy()
     idx[1, 7] = 1 << 29              # inside topk, outside the pool
     m.check_device_errors()
@@ -185,12 +188,13 @@ def test_sparse_deterministic():
         assert np.array_equal(a, bits_of(sparse_on_gpu(m, case)))
 
 
-def test_strided_pages_and_scales():
+@pytest.mark.parametrize("H", [64, 128])
+def test_strided_pages_and_scales(H):
     """Pages and scale rows with padding between them (views of larger buffers) take the
     general loader, which derives each row's page and slot by division."""
     import torch
     m = need_gpu()
-    case = make_sparse_case(77, 4, 64, 700, 16, (100, 300), 300, name="sp-strided")
+    case = make_sparse_case(77, 4, H, 700, 16, (100, 300), 300, name="sp-strided")
     NP, PS = case.cache8.shape[0], case.page_size
     big = torch.full((NP, PS + 3, 576), 0x7F, dtype=torch.uint8, device="cuda:0")  # NaN padding
     big[:, :PS] = u8_dev(case.cache8)
@@ -202,12 +206,13 @@ def test_strided_pages_and_scales():
     assert np.array_equal(bits_of(sparse_on_gpu(m, case, cache8=big[:, :PS], cache_scale=sc[:, :PS])), flat)
 
 
-def test_empty_lists():
+@pytest.mark.parametrize("H", [16, 128])
+def test_empty_lists(H):
     """Rows whose lists are empty (top-k 0) or hold only skipped entries are zero; a batch
     with no listed row at all writes every row as zeros (over a NaN filled buffer)."""
     import torch
     m = need_gpu()
-    case = make_sparse_case(78, 4, 16, 300, 16, (50, 120), 120, name="sp-empty")
+    case = make_sparse_case(78, 4, H, 300, 16, (50, 120), 120, name="sp-empty")
     topk = case.topk_lengths.copy()
     topk[1] = 0
     idx = case.d_indices.copy()
@@ -217,7 +222,7 @@ def test_empty_lists():
     assert np.all(got[1] == 0) and np.all(got[2] == 0)
     zero = np.zeros_like(case.topk_lengths)
     for P in (0, 1, 3):
-        out = torch.full((4, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        out = torch.full((4, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda:0")
         qd = u8_dev(case.q8)
         res = m.decode_paged_sparse(qd, f32_dev(case.q_scale), i32_dev(case.input_row_offsets),
                                     u8_dev(case.cache8), f32_dev(case.cache_scale), i32_dev(case.d_indices),

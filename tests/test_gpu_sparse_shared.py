@@ -77,11 +77,13 @@ def test_equals_per_token_lists_bitwise():
     assert np.array_equal(bits_of(per_token), bits_of(shared_on_gpu(m, c)))
 
 
-def test_malformed_offsets_are_flagged():
+@pytest.mark.parametrize("H", [64, 128])
+def test_malformed_offsets_are_flagged(H):
     """Offsets that decrease set bit 2 of the device error word; the rows they cover stay
-    zero and every other row is still right."""
+    zero and every other row is still right (128 heads: the balanced-batch fp8-MFMA
+    kernel; 64: the general kernel)."""
     m = need_gpu()
-    c = shared_case(1540, [2, 2, 2], 64)
+    c = shared_case(1540, [2, 2, 2], H)
     bad = c["off"].copy()
     bad[2] = 1  # sequence 1 would end before it starts
     m.check_device_errors()       # clear
