@@ -109,7 +109,7 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
   const int p_last = (khi - 1) / a.PS;
   const int npages32 = (int)min(a.num_rows / a.PS, (int64_t)INT32_MAX);
   // SPARSE: list row g.b of d_indices; list position p of the segment is key p
-  const int32_t* ilist = a.idx + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.idx_row;
+  const int32_t* ilist = SPARSE ? a.idx + (int64_t)__builtin_amdgcn_readfirstlane(g.b) * a.idx_row : nullptr;
   static_assert(!SPARSE || KPAGES == 0, "the sparse rows are gathered one by one");
 
   // every wave must be done with the buffers and window of anything before
