@@ -20,9 +20,11 @@
 //             wave w owns output columns 128w..128w+127 of all heads, O^T += V^T (P sigma_k)^T
 //             with the bf16 weights of every head exchanged through LDS (the row scale rides
 //             on the weight, so V stays the bare codes and P keeps bf16 precision).
-// Step k publishes the weights of stage k-1; then the score MFMAs of stage k run with the
-// first value MFMAs of stage k-1 and the widening of stage k, and the other value MFMAs of
-// stage k-1 run while the vector units turn the scores of stage k into weights.
+// Step k: the score MFMAs of stage k run with the first value MFMAs of stage k-1 and the
+// widening of stage k, and the other value MFMAs of stage k-1 run while the vector units
+// turn the scores of stage k into weights, which every wave then publishes for its heads
+// in one of two LDS slots; the barrier at the top of the next step makes them visible, so
+// a step has one barrier.
 //
 // Layout of a stage's fp8 rows in LDS: chunk-major, 16-byte chunk c of row r at
 // (32 c + r) * 16.  A score operand (lane 32g + i: row i, bytes 64 ks + 32g .. + 31, two
@@ -95,10 +97,12 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
   const int h0 = wave * 32;
   MLA_LDS int* pids = (MLA_LDS int*)L.pids;
   auto ksl = [&](int st) { return (MLA_LDS float*)L.ksc[st % kF8Scales]; };  // scale slot of stage st
-  MLA_LDS uint8_t* pbuf = xbuf;                                    // weights
-  MLA_LDS float* alpha_s = (MLA_LDS float*)(xbuf + kF8PBytes);     // [4][32]
-  MLA_LDS int* flag_s = (MLA_LDS int*)(xbuf + kF8PBytes + 512);    // [4]
-  MLA_LDS float* inv_s = (MLA_LDS float*)(xbuf + kF8PBytes + 1024);  // [128], after the loop
+  // the weights, rescale factors [4][32] and flags [4] of a stage, in two slots (stage s in
+  // slot s & 1), and the epilogue's 1/l [128]
+  auto pbuf = [&](int sl) { return xbuf + sl * kF8PBytes; };
+  auto alpha_s = [&](int sl) { return (MLA_LDS float*)(xbuf + 2 * kF8PBytes + 512 * sl); };
+  auto flag_s = [&](int sl) { return (MLA_LDS int*)(xbuf + 2 * kF8PBytes + 1024 + 16 * sl); };
+  MLA_LDS float* inv_s = (MLA_LDS float*)(xbuf + 2 * kF8PBytes + 1024 + 64);
 
   const int first_tile = __builtin_amdgcn_readfirstlane(g.lo / kTileKeys);
   const int klo = __builtin_amdgcn_readfirstlane(max(g.lo, (first_tile + ta) * kTileKeys));
@@ -351,6 +355,15 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
   int rflag = 0;                 // some head of this wave rescaled at that stage
 #pragma unroll
   for (int i = 0; i < 8; ++i) pk[i] = 0;
+  // "stage -1": zero weights and no rescale, in slot 1 (visible after the barrier at the
+  // loop top)
+  {
+    MLA_LDS uint8_t* pw = pbuf(1) + wave * 2048 + lane * 16;
+    *(MLA_LDS u32x4*)pw = u32x4{0, 0, 0, 0};
+    *(MLA_LDS u32x4*)(pw + 1024) = u32x4{0, 0, 0, 0};
+    if (lg == 0) alpha_s(1)[wave * 32 + li] = 1.f;
+    if (lane == 0) flag_s(1)[wave] = 0;
+  }
 
   // Transposing value reads (the layout of mla_decode2.hip): lane 16G + 4r + q (G = 2g + c)
   // reads row 16kp + 8h + 4g + r, chunk 16w + 4cb + 2c + (q >> 1); four per-lane bases.
@@ -376,12 +389,12 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     wdst[u] = r * kRowBytes + ((((2 * c) & ~7) | (((2 * c) ^ f) & 7)) << 4);
   }
 
-  // Step k publishes the weights of stage k-1, then runs the score MFMAs of stage k with
-  // the first value MFMAs of stage k-1 and the widening of stage k's values (phase A), then
-  // the other value MFMAs of stage k-1 while the vector units turn the scores of stage k
-  // into weights (phase B).  Every step runs the whole stream: at k = 0 the values of
-  // "stage -1" are zero weights on the zeroed value tile, and at k = nst the scores of a
-  // stale buffer are computed and masked out entirely.
+  // Step k runs the score MFMAs of stage k with the first value MFMAs of stage k-1 and the
+  // widening of stage k's values (phase A), then the other value MFMAs of stage k-1 while
+  // the vector units turn the scores of stage k into weights (phase B), and publishes
+  // them.  Every step runs the whole stream: at k = 0 the values of "stage -1" are zero
+  // weights on the zeroed value tile, and at k = nst the scores of a stale buffer are
+  // computed and masked out entirely.
   auto pinv = [](f32x16& v) { asm volatile("" : "+v"(v)); };
   auto pin = [](float& v) { asm volatile("" : "+v"(v)); };
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -391,7 +404,8 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
     if (k < nst) {
       if (k >= 1 && k + 1 < nst) vm_wait_imm<kF8Loads + 1>(); else vm_wait_imm<0>();
     }
-    stage_barrier();  // also: every wave is done with stage k-1's raw buffer, tile k%2, the weights
+    lgkm_wait0();     // this wave's weights of stage k-1 are in LDS
+    stage_barrier();  // also: every wave is done with step k-1 (its buffers and weight slot)
     const int kn = k + 2;
     const uint8_t* fb = nullptr;
     int pa_k = 0;
@@ -423,21 +437,19 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
       const bf16x4 a1 = ds_read_tr16(vrd + vb[kp][cb & 1] + o1);
       return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     };
-    auto pread = [&](int hb, int kp) { return *(const MLA_LDS bf16x8*)(pbuf + lane * 16 + hb * 2048 + kp * 1024); };
+    auto pread = [&](int hb, int kp) {
+      return *(const MLA_LDS bf16x8*)(pbuf((k + 1) & 1) + lane * 16 + hb * 2048 + kp * 1024);
+    };
 
-    // ---- publish the weights, rescale factor and flag of stage k-1 (own head block)
-    *(MLA_LDS u32x4*)(pbuf + wave * 2048 + lane * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-    *(MLA_LDS u32x4*)(pbuf + wave * 2048 + 1024 + lane * 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
-    if (lg == 0) alpha_s[wave * 32 + li] = alpha;
-    if (lane == 0) flag_s[wave] = rflag;
+    // ---- the weights, rescale factors and flags of stage k-1 (published by every wave at
+    // the end of step k-1, visible since the barrier)
+    const int slp = (k + 1) & 1;
     bf16x8 vf[8];  // V^T fragment 4kp + cb; at most two live
     vf[0] = vread(0, 0);
-    lgkm_wait0();
-    stage_barrier();
     bf16x8 pf0[4], pf1[4];  // P^T (kp, hb)
     {
       typedef int i32x4 __attribute__((ext_vector_type(4)));
-      const i32x4 fl = *(const MLA_LDS i32x4*)flag_s;
+      const i32x4 fl = *(const MLA_LDS i32x4*)flag_s(slp);
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) pf0[hb] = pread(hb, 0);
       // O holds the values of stages < k-1 relative to the maxima before stage k-1: bring
@@ -446,7 +458,7 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
         fence_o(O);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
-          const float al = fl[hb] != 0 ? alpha_s[hb * 32 + li] : 1.f;
+          const float al = fl[hb] != 0 ? alpha_s(slp)[hb * 32 + li] : 1.f;
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             O[cb][hb] *= al;
@@ -631,6 +643,15 @@ __device__ __forceinline__ void fp8mma_segment(const SparseArgs& a, MLA_LDS uint
       __builtin_amdgcn_sched_barrier(0);
       weigh(15);
     }
+    // ---- publish the weights, rescale factor and flag of stage k (own head block) into
+    // slot k & 1: every wave is done with that slot's stage k-2 since the barrier above
+    {
+      MLA_LDS uint8_t* pw = pbuf(k & 1) + wave * 2048 + lane * 16;
+      *(MLA_LDS u32x4*)pw = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      *(MLA_LDS u32x4*)(pw + 1024) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+      if (lg == 0) alpha_s(k & 1)[wave * 32 + li] = alpha;
+      if (lane == 0) flag_s(k & 1)[wave] = rflag;
+    }
     msk0 = msk1;
     msk1 = msk2;
   }
@@ -687,7 +708,7 @@ template <int KPAGES, bool ROPE, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void mla_fp8mma_kernel(const SparseArgs a, const SplitPlan plan) {
   __shared__ __attribute__((aligned(1024))) uint8_t raw_b[kF8Raw * F8Geo<true>::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t vt_b[2 * kF8VBytes];
-  __shared__ __attribute__((aligned(256))) uint8_t xbuf_b[kF8PBytes + 1536];
+  __shared__ __attribute__((aligned(256))) uint8_t xbuf_b[2 * kF8PBytes + 1600];
   __shared__ F8Lds L;
   static_assert(2 * kF8VBytes >= 4 * 16384, "epilogue staging");
   plan_run<256, true>(
