@@ -20,13 +20,15 @@
 //           64-bit key (order-preserving score bits, then the inverted position, so every
 //           key is distinct) to a workspace row of the token;
 //   select: one work-group of 1024 threads per token loads its keys (at most
-//           kIdxMaxKeys) into LDS; a radix select (eight 8-bit digits, most significant
-//           first, histograms in LDS) finds the top_k-th largest key.  Once the bin that
-//           holds it has at most kIdxCand keys, one pass moves the keys above that bin to
-//           the output list and the bin's keys to a candidate list, and the remaining
-//           digits scan the candidates only.  A bitonic sort (in registers and lane
-//           shuffles up to distance 64, LDS beyond) orders the top_k, and they are written
-//           out.
+//           kIdxMaxKeys) into LDS; a radix select (8-bit digits, most significant first,
+//           histograms in LDS) finds the top_k-th largest key, stopping at the first
+//           digit whose whole bin is needed.  Once the bin that holds it has at most
+//           kIdxCand keys, one pass lists the keys above that bin and moves the bin's keys
+//           to a candidate list, and the remaining digits scan the candidates only.  The
+//           listed keys are then ordered without a sort network: kIdxBuckets buckets of
+//           equal key width between the threshold and the largest key, a scan of the
+//           bucket counts, and within a bucket a count of the larger keys give each key
+//           its output slot.
 #include <stdint.h>
 
 #include "mla_device.h"
@@ -37,6 +39,10 @@ namespace mla {
 constexpr int kIdxThreads = 256;      // scoring work-group
 constexpr int kIdxSelThreads = 1024;  // selection work-group
 constexpr int kIdxCand = 1024;        // candidate list of the radix select
+constexpr int kIdxBucketBits = 12;    // buckets of the listing order
+constexpr int kIdxBuckets = 1 << kIdxBucketBits;
+static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxBuckets * 4 + kIdxMaxTopK * 8 <= kIdxMaxKeys * 8,
+              "bucket counts and grouped keys fit in the key buffer");
 
 // The four e4m3 codes of a dword as floats (exact), byte e -> f[e], through the OCP
 // conversion the sparse decode uses (e4m3x4_to_bf16x4).
@@ -52,94 +58,6 @@ __device__ __forceinline__ void e4m3x4_f32(uint32_t w, float (&f)[4]) {
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// The value of lane (lane ^ M): DPP quad permutes for M = 1, 2, a bitmask-mode swizzle
-// (lane ^ M within 32 lanes) for M = 4 .. 16, a bpermute for M = 32.
-template <int M>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane distance");
-  if constexpr (M == 1)
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-  else if constexpr (M == 2)
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-  else if constexpr (M < 32)
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));  // and 0x1F, xor M
-  else
-    return (uint32_t)__shfl_xor((unsigned)v, M);
-}
-
-// One compare-exchange stage at element distance J (2 .. 64) on the thread's two keys
-// (elements e0 and e0 + 1), partners J / 2 lanes away.
-template <int J>
-__device__ __forceinline__ void lane_stage(uint64_t (&x)[2], int e0, int k) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = e0 + u;
-    const uint32_t lo = lane_xor<J / 2>((uint32_t)x[u]), hi = lane_xor<J / 2>((uint32_t)(x[u] >> 32));
-    const uint64_t y = ((uint64_t)hi << 32) | lo;
-    // the lower element of a descending pair keeps the larger key
-    const bool keep_max = ((e & J) == 0) == ((e & k) == 0);
-    x[u] = keep_max ? (x[u] > y ? x[u] : y) : (x[u] < y ? x[u] : y);
-  }
-}
-
-// Bitonic sort of n (a power of two, n <= 2 * kIdxSelThreads) keys in LDS into descending
-// order.  Thread tid holds elements 2 tid and 2 tid + 1 in registers: compare-exchange at
-// distance 1 stays in the thread, and distances 2 .. 64 pair lanes 1 .. 32 apart within
-// the wave (the partner of element e is e ^ jdist, in thread tid ^ jdist / 2), so neither
-// needs a barrier.  Distances of 128 and more go through LDS, one barrier per stage.
-__device__ __forceinline__ void bitonic_desc(uint64_t* v, int n) {
-  static_assert(kIdxMaxTopK <= 2 * kIdxSelThreads, "two keys per thread");
-  const int tid = threadIdx.x, e0 = 2 * tid;
-  uint64_t x[2] = {0, 0};
-  if (e0 < n) {
-    x[0] = v[e0];
-    x[1] = v[e0 + 1];
-  }
-  for (int k = 2; k <= n; k <<= 1) {
-    if ((k >> 1) >= 128) {
-      if (e0 < n) {
-        v[e0] = x[0];
-        v[e0 + 1] = x[1];
-      }
-      __syncthreads();
-      for (int jdist = k >> 1; jdist >= 128; jdist >>= 1) {
-        for (int j = tid; j < (n >> 1); j += kIdxSelThreads) {
-          const int i = ((j & ~(jdist - 1)) << 1) | (j & (jdist - 1)), p = i + jdist;
-          const uint64_t lo = v[i], hi = v[p];
-          if ((i & k) == 0 ? lo < hi : lo > hi) {
-            v[i] = hi;
-            v[p] = lo;
-          }
-        }
-        __syncthreads();
-      }
-      if (e0 < n) {
-        x[0] = v[e0];
-        x[1] = v[e0 + 1];
-      }
-    }
-    switch (min(k >> 1, 64)) {  // distances min(k / 2, 64) down to 2
-      case 64: lane_stage<64>(x, e0, k); [[fallthrough]];
-      case 32: lane_stage<32>(x, e0, k); [[fallthrough]];
-      case 16: lane_stage<16>(x, e0, k); [[fallthrough]];
-      case 8: lane_stage<8>(x, e0, k); [[fallthrough]];
-      case 4: lane_stage<4>(x, e0, k); [[fallthrough]];
-      case 2: lane_stage<2>(x, e0, k); [[fallthrough]];
-      default: break;
-    }
-    if ((e0 & k) == 0 ? x[0] < x[1] : x[0] > x[1]) {
-      const uint64_t tmp = x[0];
-      x[0] = x[1];
-      x[1] = tmp;
-    }
-  }
-  if (e0 < n) {
-    v[e0] = x[0];
-    v[e0 + 1] = x[1];
-  }
-  __syncthreads();
 }
 
 // The token's sequence (binary search of the offsets) and its visible rows [vlo, vhi).
@@ -290,37 +208,48 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
   if (bad) atomicOr(a.err, kErrPageId);
 }
 
+// Slot of this lane's entry in a list that grows at *count, when `take`: one LDS atomic
+// per wave reserves the wave's entries, and a lane's slot follows the taking lanes below
+// it.  All 64 lanes of the wave must be active.
+__device__ __forceinline__ int wave_slot(bool take, int* count) {
+  const uint64_t b = __builtin_amdgcn_ballot_w64(take);
+  int base = 0;
+  if ((threadIdx.x & 63) == 0 && b != 0) base = atomicAdd(count, (int)__popcll(b));
+  base = __builtin_amdgcn_readfirstlane(base);
+  return base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
 __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(const IndexerArgs a) {
-  __shared__ uint64_t keys[kIdxMaxKeys];
+  __shared__ __align__(16) uint64_t keys[kIdxMaxKeys];
   __shared__ uint64_t top[kIdxMaxTopK];
   __shared__ uint64_t cand[kIdxCand];
   __shared__ int hist[256];
-  __shared__ int wave_tot[4];
+  __shared__ int wave_tot[kIdxSelThreads / 64];
   __shared__ int sel_digit, sel_count, sel_bin, n_top, n_cand;
-  const int t = blockIdx.x, tid = threadIdx.x;
+  __shared__ unsigned long long kmax;
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave0 = tid & ~63;
   const TokenRows tr = token_rows(a, t, false);
   const int nvis = tr.vhi - tr.vlo;
-  const int32_t* prow = a.page_table + (int64_t)tr.b * a.pt_row;
   const uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
-#pragma unroll
-  for (int r = 0; r < kIdxMaxKeys / kIdxSelThreads; ++r) {
-    const int i = tid + r * kIdxSelThreads;
-    if (i < nvis) keys[i] = krow[i];
-  }
-  if (tid == 0) {
-    n_top = 0;
-    n_cand = 0;
-  }
-  __syncthreads();
-
-  // ---- the nsel largest keys into top[0 .. nsel), unordered
   const int nsel = min(a.top_k, nvis);
-  if (nsel == nvis) {
-    for (int i = tid; i < nvis; i += kIdxSelThreads) top[i] = keys[i];
-  } else if (nsel > 0) {
-    // radix select of the nsel-th largest key: `prefix` holds its digits found so far,
-    // the keys still in play are src[0 .. nsrc)
-    uint64_t prefix = 0;
+  uint64_t prefix = 0;  // a lower bound of the listed keys once they are listed
+  if (nsel == nvis) {   // block-uniform: every visible row is listed
+    for (int i = tid; i < nvis; i += kIdxSelThreads) top[i] = krow[i];
+  } else {
+#pragma unroll
+    for (int r = 0; r < kIdxMaxKeys / kIdxSelThreads; ++r) {
+      const int i = tid + r * kIdxSelThreads;
+      if (i < nvis) keys[i] = krow[i];
+    }
+    if (tid == 0) {
+      n_top = 0;
+      n_cand = 0;
+    }
+    __syncthreads();
+
+    // ---- the nsel largest keys into top[0 .. nsel), unordered: a radix select of the
+    // nsel-th largest key, `prefix` holding its digits found so far; the keys still in
+    // play are src[0 .. nsrc)
     int need = nsel;  // how many keys at or above the threshold are still to be placed
     const uint64_t* src = keys;
     int nsrc = nvis;
@@ -346,9 +275,9 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           const int up = __shfl_up(incl, off);
-          if ((tid & 63) >= off) incl += up;
+          if (lane >= off) incl += up;
         }
-        if ((tid & 63) == 63) wave_tot[tid >> 6] = incl;
+        if (lane == 63) wave_tot[tid >> 6] = incl;
       }
       __syncthreads();
       if (tid < 256) {
@@ -364,49 +293,108 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
       need = sel_count;
       const int bin = sel_bin;
       __syncthreads();
+      // All keys of the bin are needed: the keys at or above `prefix` (lower digits
+      // zero) are exactly the nsel largest, so the remaining digits change nothing.
+      if (need == bin) break;
       if (src == keys && shift > 0 && bin <= kIdxCand) {
-        // keys above the prefix on the digits found are in the top for sure; the keys
-        // equal to it there become the candidates for the remaining digits
+        // keys above the prefix on the digits found are listed for sure; the keys equal
+        // to it there become the candidates for the remaining digits
         const uint64_t m = ~0ull << shift;
-#pragma unroll 4
-        for (int i = tid; i < nvis; i += kIdxSelThreads) {
-          const uint64_t k = keys[i], km = k & m;
-          if (km > prefix) top[atomicAdd(&n_top, 1)] = k;
-          else if (km == prefix) cand[atomicAdd(&n_cand, 1)] = k;
+        for (int i0 = wave0; i0 < nvis; i0 += kIdxSelThreads) {  // whole waves
+          const int i = i0 + lane;
+          const uint64_t k = i < nvis ? keys[i] : 0, km = k & m;
+          const bool above = i < nvis && km > prefix, equal = i < nvis && km == prefix;
+          const int sa = wave_slot(above, &n_top), se = wave_slot(equal, &n_cand);
+          if (above) top[sa] = k;
+          if (equal) cand[se] = k;
         }
         __syncthreads();
         src = cand;
         nsrc = bin;
       }
     }
-    // keys are distinct: exactly nsel keys are >= the threshold `prefix`, those of
-    // src[0 .. nsrc) not yet in top
-    for (int i = tid; i < nsrc; i += kIdxSelThreads) {
-      const uint64_t k = src[i];
-      if (k >= prefix) top[atomicAdd(&n_top, 1)] = k;
+    // keys are distinct: exactly nsel keys are >= `prefix`, those of src[0 .. nsrc) not
+    // yet listed
+    for (int i0 = wave0; i0 < nsrc; i0 += kIdxSelThreads) {
+      const int i = i0 + lane;
+      const uint64_t k = i < nsrc ? src[i] : 0;
+      const bool take = i < nsrc && k >= prefix;
+      const int s = wave_slot(take, &n_top);
+      if (take) top[s] = k;
+    }
+  }
+  if (tid == 0) kmax = 0;
+  __syncthreads();  // top[0 .. nsel) complete; keys[] is free from here on
+
+  // ---- listing order.  The keys lie in [prefix, kmax]; bucket (k - prefix) >> sh
+  // (kIdxBuckets of them, larger keys in higher buckets) groups them, a scan from the top
+  // bucket gives each bucket's first output slot, and a key's slot is that plus the
+  // number of larger keys in its own bucket.  Keys are distinct, so the slots are
+  // 0 .. nsel - 1 once each, by descending key.
+  uint32_t* bfirst = (uint32_t*)keys;                 // [kIdxBuckets]
+  uint64_t* grouped = keys + kIdxBuckets / 2;         // [kIdxMaxTopK], by bucket
+  uint64_t mx = 0;
+  for (int i = tid; i < nsel; i += kIdxSelThreads) mx = max(mx, top[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint64_t)__shfl_xor((unsigned long long)mx, off));
+  if (lane == 0 && mx) atomicMax(&kmax, (unsigned long long)mx);
+#pragma unroll
+  for (int u = 0; u < kIdxBuckets / kIdxSelThreads; ++u) bfirst[tid * (kIdxBuckets / kIdxSelThreads) + u] = 0;
+  __syncthreads();
+  const uint64_t range = kmax > prefix ? kmax - prefix : 0;
+  const int sh = max(0, 64 - __clzll(range) - kIdxBucketBits);  // range >> sh < kIdxBuckets
+  for (int i = tid; i < nsel; i += kIdxSelThreads) atomicAdd(&bfirst[(int)((top[i] - prefix) >> sh)], 1u);
+  __syncthreads();
+  {
+    // exclusive scan from the top bucket: thread tid holds buckets
+    // kIdxBuckets - 1 - BPT * tid - u, u = 0 .. BPT - 1 (descending)
+    constexpr int BPT = kIdxBuckets / kIdxSelThreads;
+    uint32_t c[BPT], run = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      c[u] = bfirst[kIdxBuckets - 1 - BPT * tid - u];
+      run += c[u];
+    }
+    uint32_t incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t up = __shfl_up(incl, off);
+      if (lane >= off) incl += up;
+    }
+    if (lane == 63) wave_tot[tid >> 6] = (int)incl;
+    __syncthreads();
+    uint32_t first = incl - run;
+    for (int w = 0; w < (tid >> 6); ++w) first += (uint32_t)wave_tot[w];
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      bfirst[kIdxBuckets - 1 - BPT * tid - u] = first;
+      first += c[u];
     }
   }
   __syncthreads();
-
-  // ---- order them: bitonic sort over the next power of two (padding keys 0 sort last)
-  int npow = 1;
-  while (npow < nsel) npow <<= 1;
-  for (int i = nsel + tid; i < npow; i += kIdxSelThreads) top[i] = 0;
+  // grouped by bucket; afterwards bfirst[b] is the end of bucket b, which is the first
+  // slot of bucket b - 1
+  for (int i = tid; i < nsel; i += kIdxSelThreads) {
+    const uint64_t k = top[i];
+    grouped[atomicAdd(&bfirst[(int)((k - prefix) >> sh)], 1u)] = k;
+  }
   __syncthreads();
-  bitonic_desc(top, npow);
 
-  // ---- the top_k as physical rows, then -1
+  // ---- the top_k as physical rows in slot order, then -1
+  const int32_t* prow = a.page_table + (int64_t)tr.b * a.pt_row;
   int32_t* orow = a.out + (int64_t)t * a.out_row;
-  for (int i = tid; i < a.top_k; i += kIdxSelThreads) {
-    int32_t v = -1;
-    if (i < nsel) {
-      const int pos = (int)(0xFFFFFFFFu - (uint32_t)(top[i] & 0xFFFFFFFFu));
-      const int lp = pos / a.PS, slot = pos - lp * a.PS;
-      const int pid = prow[lp];
-      v = (pid >= 0 && (int64_t)pid < a.num_pages) ? pid * a.PS + slot : -1;
-    }
-    orow[i] = v;
+  for (int p = tid; p < nsel; p += kIdxSelThreads) {
+    const uint64_t k = grouped[p];
+    const int bk = (int)((k - prefix) >> sh);
+    const int s0 = bk == kIdxBuckets - 1 ? 0 : (int)bfirst[bk + 1], s1 = (int)bfirst[bk];
+    int rank = s0;
+    for (int q = s0; q < s1; ++q) rank += grouped[q] > k;
+    const int pos = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
+    const int lp = pos / a.PS, slot = pos - lp * a.PS;
+    const int pid = prow[lp];
+    orow[rank] = (pid >= 0 && (int64_t)pid < a.num_pages) ? pid * a.PS + slot : -1;
   }
+  for (int i = nsel + tid; i < a.top_k; i += kIdxSelThreads) orow[i] = -1;
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const KernelTimer* timer) {
