@@ -39,10 +39,13 @@ namespace mla {
 constexpr int kIdxThreads = 256;      // scoring work-group
 constexpr int kIdxSelThreads = 1024;  // selection work-group
 constexpr int kIdxCand = 1024;        // candidate list of the radix select
+constexpr int kIdxHistCopies = 16;   // radix histogram copies while all keys are in play
 constexpr int kIdxBucketBits = 12;    // buckets of the listing order
 constexpr int kIdxBuckets = 1 << kIdxBucketBits;
 static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxBuckets * 4 + kIdxMaxTopK * 8 <= kIdxMaxKeys * 8,
               "bucket counts and grouped keys fit in the key buffer");
+static_assert(256 * kIdxHistCopies * 4 <= kIdxMaxTopK * 8 && (256 * kIdxHistCopies) % kIdxSelThreads == 0,
+              "the histogram copies fit in the top-k list");
 
 // The four e4m3 codes of a dword as floats (exact), byte e -> f[e], through the OCP
 // conversion the sparse decode uses (e4m3x4_to_bf16x4).
@@ -221,7 +224,7 @@ __device__ __forceinline__ int wave_slot(bool take, int* count) {
 
 __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(const IndexerArgs a) {
   __shared__ __align__(16) uint64_t keys[kIdxMaxKeys];
-  __shared__ uint64_t top[kIdxMaxTopK];
+  __shared__ __align__(16) uint64_t top[kIdxMaxTopK];
   __shared__ uint64_t cand[kIdxCand];
   __shared__ int hist[256];
   __shared__ int wave_tot[kIdxSelThreads / 64];
@@ -236,14 +239,31 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   if (nsel == nvis) {   // block-uniform: every visible row is listed
     for (int i = tid; i < nvis; i += kIdxSelThreads) top[i] = krow[i];
   } else {
+    // Until the first compaction, histograms over all keys have kIdxHistCopies copies,
+    // lane l counting into copy l % kIdxHistCopies (keys crowd into a few bins there),
+    // kept in top[], which holds nothing before then.  The first digit is counted as the
+    // keys arrive.
+    int* hwide = (int*)top;
 #pragma unroll
-    for (int r = 0; r < kIdxMaxKeys / kIdxSelThreads; ++r) {
-      const int i = tid + r * kIdxSelThreads;
-      if (i < nvis) keys[i] = krow[i];
-    }
+    for (int u = 0; u < 256 * kIdxHistCopies / kIdxSelThreads; ++u) hwide[tid + u * kIdxSelThreads] = 0;
     if (tid == 0) {
       n_top = 0;
       n_cand = 0;
+    }
+    __syncthreads();
+    const int copy = lane % kIdxHistCopies;
+    // all loads in flight at once: indices past the last key re-read it (nvis > nsel >= 0)
+    constexpr int KPT = kIdxMaxKeys / kIdxSelThreads;
+    uint64_t kv[KPT];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) kv[r] = krow[min(tid + r * kIdxSelThreads, nvis - 1)];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int i = tid + r * kIdxSelThreads;
+      if (i < nvis) {
+        keys[i] = kv[r];
+        atomicAdd(&hwide[(int)(kv[r] >> 56) * kIdxHistCopies + copy], 1);
+      }
     }
     __syncthreads();
 
@@ -254,15 +274,30 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
     const uint64_t* src = keys;
     int nsrc = nvis;
     for (int shift = 56; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      const uint64_t hi_mask = shift == 56 ? 0 : ~0ull << (shift + 8);
+      const bool wide = src == keys;
+      if (shift < 56) {
+        if (wide) {
+#pragma unroll
+          for (int u = 0; u < 256 * kIdxHistCopies / kIdxSelThreads; ++u) hwide[tid + u * kIdxSelThreads] = 0;
+        } else if (tid < 256) {
+          hist[tid] = 0;
+        }
+        __syncthreads();
+        const uint64_t hi_mask = ~0ull << (shift + 8);
+        if (wide) {
 #pragma unroll 4
-      for (int i = tid; i < nsrc; i += kIdxSelThreads) {
-        const uint64_t k = src[i];
-        if ((k & hi_mask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 0xFF)], 1);
+          for (int i = tid; i < nsrc; i += kIdxSelThreads) {
+            const uint64_t k = src[i];
+            if ((k & hi_mask) == prefix) atomicAdd(&hwide[(int)((k >> shift) & 0xFF) * kIdxHistCopies + copy], 1);
+          }
+        } else {
+          for (int i = tid; i < nsrc; i += kIdxSelThreads) {
+            const uint64_t k = src[i];
+            if ((k & hi_mask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 0xFF)], 1);
+          }
+        }
+        __syncthreads();
       }
-      __syncthreads();
       // the digit where the count from the top reaches `need`: thread tid < 256 takes
       // digit 255 - tid, so a prefix sum over those threads is the count of keys with a
       // digit at or above it; the one thread where that count first reaches `need`
@@ -270,7 +305,15 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
       const int d = 255 - tid;
       int c = 0, incl = 0;
       if (tid < 256) {
-        c = hist[d];
+        if (wide) {
+#pragma unroll
+          for (int u = 0; u < kIdxHistCopies; u += 4) {
+            const int4 v = *(const int4*)&hwide[d * kIdxHistCopies + u];
+            c += v.x + v.y + v.z + v.w;
+          }
+        } else {
+          c = hist[d];
+        }
         incl = c;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
