@@ -947,11 +947,16 @@ mla_status mla_indexer_paged_fp8(const mla_tensor* q, const mla_tensor* q_s,
   if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
   void* ws = nullptr;
   const int64_t keys_row = page_table->shape[1] * PS;
-  if ((s = grow_workspace(current_device(), stream, (size_t)(T * keys_row) * sizeof(uint64_t), cap, &ws)) != MLA_OK)
+  const int64_t hist_row = 512 * ((keys_row + mla::kIdxSlice - 1) / mla::kIdxSlice);
+  const size_t key_bytes = (size_t)(T * keys_row) * sizeof(uint64_t);
+  if ((s = grow_workspace(current_device(), stream, key_bytes + (size_t)(T * hist_row) * sizeof(uint32_t), cap, &ws)) !=
+      MLA_OK)
     return s;
   mla::IndexerArgs a{};
   a.keys = (uint64_t*)((char*)ws + kHeaderBytes);
   a.keys_row = keys_row;
+  a.slice_hist = (uint32_t*)((char*)ws + kHeaderBytes + key_bytes);
+  a.hist_row = hist_row;
   a.q = (const uint8_t*)q->data;
   a.q_tok = q->stride[0];
   a.q_head = q->stride[1];

@@ -16,19 +16,19 @@
 // float32 query row qf[d] = sum_h q_s[t, h] * e4m3(q[t, h, d]) (a fixed order), then
 // scores every visible row with one dot product of `depth` terms in float32.  Two
 // kernels:
-//   score:  one work-group per (token, slice of kIdxSlice visible rows) writes each row's
-//           64-bit key (order-preserving score bits, then the inverted position, so every
-//           key is distinct) to a workspace row of the token;
-//   select: one work-group of 1024 threads per token loads its keys (at most
-//           kIdxMaxKeys) into LDS; a radix select (8-bit digits, most significant first,
-//           histograms in LDS) finds the top_k-th largest key, stopping at the first
-//           digit whose whole bin is needed.  Once the bin that holds it has at most
-//           kIdxCand keys, one pass lists the keys above that bin and moves the bin's keys
-//           to a candidate list, and the remaining digits scan the candidates only.  The
-//           listed keys are then ordered without a sort network: kIdxBuckets buckets of
-//           equal key width between the threshold and the largest key, a scan of the
-//           bucket counts, and within a bucket a count of the larger keys give each key
-//           its output slot.
+//   score:  one work-group per (token, slice of kIdxSlice visible rows) computes each
+//           row's 64-bit key (order-preserving score bits, then the inverted position, so
+//           every key is distinct) and writes the slice's keys to its part of the token's
+//           workspace row grouped by top 8-bit digit, digits descending (a counting sort
+//           in LDS), with the size and start of each digit's run;
+//   select: one work-group of 1024 threads per token.  The slices' run tables give the
+//           threshold's top digit directly; the runs above it are listed and the runs of
+//           it are loaded into LDS (the runs below are never read).  A radix select over
+//           those keys (8-bit digits, histograms in LDS) follows until the threshold's
+//           bin holds at most kIdxFinish keys, which one wave ranks.  The listed keys are
+//           then ordered without a sort network: kIdxBuckets buckets of equal key width
+//           between the threshold and the largest key, a scan of the bucket counts, and
+//           within a bucket a count of the larger keys give each key its output slot.
 #include <stdint.h>
 
 #include "mla_device.h"
@@ -38,14 +38,14 @@ namespace mla {
 
 constexpr int kIdxThreads = 256;      // scoring work-group
 constexpr int kIdxSelThreads = 1024;  // selection work-group
-constexpr int kIdxCand = 1024;        // candidate list of the radix select
+constexpr int kIdxFinish = 64;        // a bin this small is ranked by one wave
 constexpr int kIdxHistCopies = 16;   // radix histogram copies while all keys are in play
 constexpr int kIdxBucketBits = 12;    // buckets of the listing order
 constexpr int kIdxBuckets = 1 << kIdxBucketBits;
 static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxBuckets * 4 + kIdxMaxTopK * 8 <= kIdxMaxKeys * 8,
               "bucket counts and grouped keys fit in the key buffer");
-static_assert(256 * kIdxHistCopies * 4 <= kIdxMaxTopK * 8 && (256 * kIdxHistCopies) % kIdxSelThreads == 0,
-              "the histogram copies fit in the top-k list");
+static_assert(kIdxThreads == 256 && (256 * kIdxHistCopies) % kIdxThreads == 0, "one scoring thread per digit");
+static_assert(kIdxMaxKeys / kIdxSlice <= kIdxSelThreads / 64, "one selecting wave per key slice");
 
 // The four e4m3 codes of a dword as floats (exact), byte e -> f[e], through the OCP
 // conversion the sparse decode uses (e4m3x4_to_bf16x4).
@@ -114,11 +114,15 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
   static_assert(R % RF == 0, "rows per thread in whole groups");
   __shared__ __align__(16) float qf[kIdxMaxDepth];
   __shared__ float part[kIdxThreads];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  __shared__ __align__(16) int dcnt[256 * kIdxHistCopies];  // [digit][copy]
+  __shared__ int wave_sum[kIdxThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const TokenRows tr = token_rows(a, t, blockIdx.y == 0 && tid == 0);
   const int vlo = tr.vlo, nvis = tr.vhi - tr.vlo, b = tr.b;
   const int i0 = blockIdx.y * kIdxSlice, i1 = min(nvis, i0 + kIdxSlice);
   if (i0 >= i1) return;  // block-uniform, before any barrier
+#pragma unroll
+  for (int u = 0; u < 256 * kIdxHistCopies / kIdxThreads; ++u) dcnt[tid + u * kIdxThreads] = 0;
 
   // ---- the page ids of this thread's rows (rows i0 + tid + r * kIdxThreads)
   const int32_t* prow = a.page_table + (int64_t)b * a.pt_row;
@@ -156,6 +160,7 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
   // ---- scores of this slice's rows as distinct keys, RF rows in flight
   uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
   bool bad = false;
+  uint64_t key[R];  // row i0 + tid + r * kIdxThreads, if below i1
 #pragma unroll
   for (int r0 = 0; r0 < R; r0 += RF) {
     uint4 v[RF][NC];
@@ -205,10 +210,63 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
         if (s != s) s = -INFINITY;  // a NaN score (NaN data) ranks last
       }
       // the score's order bits, then the inverted position (equal scores: lower first)
-      krow[i] = ((uint64_t)order_key(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)pos[u]);
+      key[r0 + u] = ((uint64_t)order_key(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)pos[u]);
     }
   }
   if (bad) atomicOr(a.err, kErrPageId);
+
+  // ---- the slice's keys into krow[i0 .. i1) grouped by top digit, digits descending,
+  // and the slice's digit counts: a counting sort whose counters have kIdxHistCopies
+  // copies per digit, lane l using copy l % kIdxHistCopies (the keys crowd into a few
+  // digits, and lanes of one copy share a counter)
+  const int copy = lane % kIdxHistCopies;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (i0 + tid + r * kIdxThreads < i1) atomicAdd(&dcnt[(int)(key[r] >> 56) * kIdxHistCopies + copy], 1);
+  __syncthreads();
+  {
+    // thread tid takes digit 255 - tid: its copies' first slots follow the counts of
+    // the higher digits (an exclusive scan in thread order) and of its lower copies
+    const int d = 255 - tid;
+    int c[kIdxHistCopies], tot = 0;
+#pragma unroll
+    for (int u = 0; u < kIdxHistCopies; u += 4) {
+      const int4 v = *(const int4*)&dcnt[d * kIdxHistCopies + u];
+      c[u] = v.x;
+      c[u + 1] = v.y;
+      c[u + 2] = v.z;
+      c[u + 3] = v.w;
+      tot += v.x + v.y + v.z + v.w;
+    }
+    int incl = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int up = __shfl_up(incl, off);
+      if (lane >= off) incl += up;
+    }
+    if (lane == 63) wave_sum[tid >> 6] = incl;
+    __syncthreads();
+    int first = incl - tot;
+    for (int w = 0; w < (tid >> 6); ++w) first += wave_sum[w];
+    uint32_t* hs = a.slice_hist + (int64_t)t * a.hist_row + blockIdx.y * 512;
+    hs[d] = (uint32_t)tot;          // keys of digit d
+    hs[256 + d] = (uint32_t)first;  // keys of higher digits: where digit d's run starts
+#pragma unroll
+    for (int u = 0; u < kIdxHistCopies; ++u) {
+      dcnt[d * kIdxHistCopies + u] = first;
+      first += c[u];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (i0 + tid + r * kIdxThreads < i1)
+      krow[i0 + atomicAdd(&dcnt[(int)(key[r] >> 56) * kIdxHistCopies + copy], 1)] = key[r];
+}
+
+// The number of set bits of a wave-wide mask below this lane.
+__device__ __forceinline__ int lane_rank(uint64_t b) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
 }
 
 // Slot of this lane's entry in a list that grows at *count, when `take`: one LDS atomic
@@ -219,18 +277,19 @@ __device__ __forceinline__ int wave_slot(bool take, int* count) {
   int base = 0;
   if ((threadIdx.x & 63) == 0 && b != 0) base = atomicAdd(count, (int)__popcll(b));
   base = __builtin_amdgcn_readfirstlane(base);
-  return base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+  return base + lane_rank(b);
 }
 
 __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(const IndexerArgs a) {
+  constexpr int NSL = kIdxMaxKeys / kIdxSlice;  // key slices at most, one wave each
   __shared__ __align__(16) uint64_t keys[kIdxMaxKeys];
   __shared__ __align__(16) uint64_t top[kIdxMaxTopK];
-  __shared__ uint64_t cand[kIdxCand];
+  __shared__ uint64_t cand[kIdxFinish];
   __shared__ int hist[256];
-  __shared__ int wave_tot[kIdxSelThreads / 64];
+  __shared__ int wave_tot[kIdxSelThreads / 64], slice_above[NSL], slice_equal[NSL];
   __shared__ int sel_digit, sel_count, sel_bin, n_top, n_cand;
-  __shared__ unsigned long long kmax;
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave0 = tid & ~63;
+  __shared__ unsigned long long kmax, sel_key;
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const TokenRows tr = token_rows(a, t, false);
   const int nvis = tr.vhi - tr.vlo;
   const uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
@@ -239,132 +298,161 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   if (nsel == nvis) {   // block-uniform: every visible row is listed
     for (int i = tid; i < nvis; i += kIdxSelThreads) top[i] = krow[i];
   } else {
-    // Until the first compaction, histograms over all keys have kIdxHistCopies copies,
-    // lane l counting into copy l % kIdxHistCopies (keys crowd into a few bins there),
-    // kept in top[], which holds nothing before then.  The first digit is counted as the
-    // keys arrive.
-    int* hwide = (int*)top;
+    // ---- the nsel largest keys into top[0 .. nsel), unordered.  A radix select (8-bit
+    // digits, most significant first) finds the threshold: `prefix` holds its digits
+    // found so far, `need` how many keys at or above it are still to be listed.
+    //
+    // First digit, from the scoring kernel's counts: it wrote each slice's keys grouped
+    // by top digit, digits descending, with the size and start of each digit's run.
+    // Thread d < 256 sums digit d over the slices: A keys above it, H of it.  The digit
+    // where A < nsel <= A + H is the threshold's.
+    const int nsl = (nvis + kIdxSlice - 1) / kIdxSlice;  // 1 .. NSL
+    if (tid < 256) {
+      hist[tid] = 0;
+      const uint32_t* hs = a.slice_hist + (int64_t)t * a.hist_row + tid;
+      uint32_t cnt[NSL], st[NSL];
 #pragma unroll
-    for (int u = 0; u < 256 * kIdxHistCopies / kIdxSelThreads; ++u) hwide[tid + u * kIdxSelThreads] = 0;
-    if (tid == 0) {
-      n_top = 0;
-      n_cand = 0;
-    }
-    __syncthreads();
-    const int copy = lane % kIdxHistCopies;
-    // all loads in flight at once: indices past the last key re-read it (nvis > nsel >= 0)
-    constexpr int KPT = kIdxMaxKeys / kIdxSelThreads;
-    uint64_t kv[KPT];
+      for (int sl = 0; sl < NSL; ++sl) {
+        const int s2 = min(sl, nsl - 1) * 512;
+        cnt[sl] = hs[s2];
+        st[sl] = hs[s2 + 256];
+      }
+      int A = 0, H = 0;
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) kv[r] = krow[min(tid + r * kIdxSelThreads, nvis - 1)];
+      for (int sl = 0; sl < NSL; ++sl)
+        if (sl < nsl) {
+          A += (int)st[sl];
+          H += (int)cnt[sl];
+        }
+      if (A < nsel && nsel <= A + H) {  // exactly one digit (distinct keys, 0 < nsel < nvis)
+        sel_digit = tid;
+        sel_count = nsel - A;
+        sel_bin = H;
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int i = tid + r * kIdxSelThreads;
-      if (i < nvis) {
-        keys[i] = kv[r];
-        atomicAdd(&hwide[(int)(kv[r] >> 56) * kIdxHistCopies + copy], 1);
+        for (int sl = 0; sl < NSL; ++sl)
+          if (sl < nsl) {
+            slice_above[sl] = (int)st[sl];
+            slice_equal[sl] = (int)cnt[sl];
+          }
       }
     }
+    if (tid == 0) n_cand = 0;
+    __syncthreads();
+    prefix = (uint64_t)sel_digit << 56;
+    int need = sel_count;
+    const int nw = sel_bin;  // keys[0 .. nw) will hold the keys of the first digit
+    int n_above = 0;
+    for (int sl = 0; sl < nsl; ++sl) n_above += slice_above[sl];
+    // Wave w takes slice w: its run above the digit is listed, its run of the digit goes
+    // to keys[] (counting the next digit on the way), the rest is never read.
+    if (wave < nsl) {
+      int oa = 0, oe = 0;
+      for (int w = 0; w < wave; ++w) {
+        oa += slice_above[w];
+        oe += slice_equal[w];
+      }
+      const int na = slice_above[wave], n = na + slice_equal[wave];
+      const uint64_t* sk = krow + wave * kIdxSlice;
+      uint64_t v[kIdxSlice / 64];
+#pragma unroll
+      for (int u = 0; u < kIdxSlice / 64; ++u)
+        if (u * 64 < n) v[u] = sk[min(u * 64 + lane, n - 1)];  // all loads in flight
+#pragma unroll
+      for (int u = 0; u < kIdxSlice / 64; ++u) {
+        const int j = u * 64 + lane;
+        if (u * 64 < n) {
+          if (j < na) {
+            top[oa + j] = v[u];
+          } else if (j < n) {
+            keys[oe + j - na] = v[u];
+            atomicAdd(&hist[(int)((v[u] >> 48) & 0xFF)], 1);
+          }
+        }
+      }
+    }
+    if (tid == 0) n_top = n_above;
     __syncthreads();
 
-    // ---- the nsel largest keys into top[0 .. nsel), unordered: a radix select of the
-    // nsel-th largest key, `prefix` holding its digits found so far; the keys still in
-    // play are src[0 .. nsrc)
-    int need = nsel;  // how many keys at or above the threshold are still to be placed
-    const uint64_t* src = keys;
-    int nsrc = nvis;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      const bool wide = src == keys;
-      if (shift < 56) {
-        if (wide) {
-#pragma unroll
-          for (int u = 0; u < 256 * kIdxHistCopies / kIdxSelThreads; ++u) hwide[tid + u * kIdxSelThreads] = 0;
-        } else if (tid < 256) {
-          hist[tid] = 0;
-        }
-        __syncthreads();
-        const uint64_t hi_mask = ~0ull << (shift + 8);
-        if (wide) {
+    // Remaining digits over keys[0 .. nw), until the bin of the threshold's digits holds
+    // at most kIdxFinish keys; `thr` is then the threshold key itself, or a lower bound
+    // with exactly nsel keys at or above it.
+    uint64_t thr = prefix;
+    if (need < nw) {
+      for (int shift = 48;; shift -= 8) {
+        if (shift < 48) {
+          if (tid < 256) hist[tid] = 0;
+          __syncthreads();
+          const uint64_t hi_mask = ~0ull << (shift + 8);
 #pragma unroll 4
-          for (int i = tid; i < nsrc; i += kIdxSelThreads) {
-            const uint64_t k = src[i];
-            if ((k & hi_mask) == prefix) atomicAdd(&hwide[(int)((k >> shift) & 0xFF) * kIdxHistCopies + copy], 1);
-          }
-        } else {
-          for (int i = tid; i < nsrc; i += kIdxSelThreads) {
-            const uint64_t k = src[i];
+          for (int i = tid; i < nw; i += kIdxSelThreads) {
+            const uint64_t k = keys[i];
             if ((k & hi_mask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 0xFF)], 1);
           }
+          __syncthreads();
         }
-        __syncthreads();
-      }
-      // the digit where the count from the top reaches `need`: thread tid < 256 takes
-      // digit 255 - tid, so a prefix sum over those threads is the count of keys with a
-      // digit at or above it; the one thread where that count first reaches `need`
-      // writes the digit
-      const int d = 255 - tid;
-      int c = 0, incl = 0;
-      if (tid < 256) {
-        if (wide) {
+        // the digit where the count from the top reaches `need`: thread tid < 256 takes
+        // digit 255 - tid, so a prefix sum over those threads is the count of keys with
+        // a digit at or above it; the one thread where that count first reaches `need`
+        // publishes the digit, the count still needed within it and its size
+        {
+          const int c = tid < 256 ? hist[255 - tid] : 0;
+          int incl = c;
 #pragma unroll
-          for (int u = 0; u < kIdxHistCopies; u += 4) {
-            const int4 v = *(const int4*)&hwide[d * kIdxHistCopies + u];
-            c += v.x + v.y + v.z + v.w;
+          for (int off = 1; off < 64; off <<= 1) {
+            const int up = __shfl_up(incl, off);
+            if (lane >= off) incl += up;
           }
-        } else {
-          c = hist[d];
+          if (tid < 256 && lane == 63) wave_tot[wave] = incl;
+          __syncthreads();
+          if (tid < 256) {
+            for (int w = 0; w < wave; ++w) incl += wave_tot[w];
+            if (c > 0 && incl >= need && incl - c < need) {
+              sel_digit = 255 - tid;
+              sel_count = need - (incl - c);
+              sel_bin = c;
+            }
+          }
+          __syncthreads();
         }
-        incl = c;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int up = __shfl_up(incl, off);
-          if (lane >= off) incl += up;
-        }
-        if (lane == 63) wave_tot[tid >> 6] = incl;
-      }
-      __syncthreads();
-      if (tid < 256) {
-        for (int w = 0; w < (tid >> 6); ++w) incl += wave_tot[w];
-        if (c > 0 && incl >= need && incl - c < need) {
-          sel_digit = d;
-          sel_count = need - (incl - c);  // still needed within digit d
-          sel_bin = c;                    // keys whose digits so far equal the new prefix
-        }
-      }
-      __syncthreads();
-      prefix |= (uint64_t)sel_digit << shift;
-      need = sel_count;
-      const int bin = sel_bin;
-      __syncthreads();
-      // All keys of the bin are needed: the keys at or above `prefix` (lower digits
-      // zero) are exactly the nsel largest, so the remaining digits change nothing.
-      if (need == bin) break;
-      if (src == keys && shift > 0 && bin <= kIdxCand) {
-        // keys above the prefix on the digits found are listed for sure; the keys equal
-        // to it there become the candidates for the remaining digits
-        const uint64_t m = ~0ull << shift;
-        for (int i0 = wave0; i0 < nvis; i0 += kIdxSelThreads) {  // whole waves
-          const int i = i0 + lane;
-          const uint64_t k = i < nvis ? keys[i] : 0, km = k & m;
-          const bool above = i < nvis && km > prefix, equal = i < nvis && km == prefix;
-          const int sa = wave_slot(above, &n_top), se = wave_slot(equal, &n_cand);
-          if (above) top[sa] = k;
-          if (equal) cand[se] = k;
-        }
+        prefix |= (uint64_t)sel_digit << shift;
+        need = sel_count;
+        const int bin = sel_bin;
         __syncthreads();
-        src = cand;
-        nsrc = bin;
+        thr = prefix;
+        if (need == bin || shift == 0) break;  // all of the bin needed, or prefix exact
+        if (bin <= kIdxFinish) {
+          // the bin's keys to cand[], then one wave ranks them: the one with `need` - 1
+          // larger is the threshold (keys are distinct)
+          const uint64_t m = ~0ull << shift;
+          for (int i0 = wave * 64; i0 < nw; i0 += kIdxSelThreads) {  // whole waves
+            const int i = i0 + lane;
+            const uint64_t k = i < nw ? keys[i] : 0;
+            const bool in_bin = i < nw && (k & m) == prefix;
+            const int sl = wave_slot(in_bin, &n_cand);
+            if (in_bin) cand[sl] = k;
+          }
+          __syncthreads();
+          if (wave == 0) {
+            const uint64_t k = lane < bin ? cand[lane] : 0;
+            int rank = 0;
+            for (int j = 0; j < bin; ++j) rank += cand[j] > k;
+            if (lane < bin && rank == need - 1) sel_key = k;
+          }
+          __syncthreads();
+          thr = sel_key;
+          break;
+        }
       }
     }
-    // keys are distinct: exactly nsel keys are >= `prefix`, those of src[0 .. nsrc) not
-    // yet listed
-    for (int i0 = wave0; i0 < nsrc; i0 += kIdxSelThreads) {
+    // the keys of the first digit at or above the threshold join the list
+    for (int i0 = wave * 64; i0 < nw; i0 += kIdxSelThreads) {
       const int i = i0 + lane;
-      const uint64_t k = i < nsrc ? src[i] : 0;
-      const bool take = i < nsrc && k >= prefix;
-      const int s = wave_slot(take, &n_top);
-      if (take) top[s] = k;
+      const uint64_t k = i < nw ? keys[i] : 0;
+      const bool take = i < nw && k >= thr;
+      const int sl = wave_slot(take, &n_top);
+      if (take) top[sl] = k;
     }
+    prefix = thr;
   }
   if (tid == 0) kmax = 0;
   __syncthreads();  // top[0 .. nsel) complete; keys[] is free from here on

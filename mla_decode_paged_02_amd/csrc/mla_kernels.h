@@ -149,6 +149,9 @@ struct IndexerArgs {
   int64_t out_row;
   uint64_t* keys;             // workspace [T, keys_row]: the scored rows' sort keys
   int64_t keys_row;           // max_pages * PS
+  uint32_t* slice_hist;       // workspace [T, hist_row]: per key slice, the size and start
+                              // of each top digit's run of keys
+  int64_t hist_row;           // 512 * slices, slices = ceil(keys_row / kIdxSlice)
   uint32_t* err;
 };
 

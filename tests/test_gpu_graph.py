@@ -113,7 +113,7 @@ def test_graph_indexer():
     def make_out():
         return torch.empty(T, top_k, dtype=torch.int32, device="cuda")
 
-    ws = T * keys_row * 8 + (1 << 20)
+    ws = T * keys_row * 8 + T * 512 * 4 * -(-keys_row // 1024) + (1 << 20)  # keys, slice digit counts
     check_replays(m, variants, call, make_out, -7, ws, "indexer")
 
 
