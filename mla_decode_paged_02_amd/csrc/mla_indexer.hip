@@ -24,8 +24,8 @@
 //   select: one work-group of 1024 threads per token.  The slices' run tables give the
 //           threshold's top digit directly; the runs above it are listed and the runs of
 //           it are loaded into LDS (the runs below are never read).  A radix select over
-//           those keys (8-bit digits, histograms in LDS) follows until the threshold's
-//           bin holds at most kIdxFinish keys, which one wave ranks.  The listed keys are
+//           those keys (8-bit digits, histograms in LDS) follows until all keys of the
+//           threshold's bin are needed.  The listed keys are
 //           then ordered without a sort network: kIdxBuckets buckets of equal key width
 //           between the threshold and the largest key, a scan of the bucket counts, and
 //           within a bucket a count of the larger keys give each key its output slot.
@@ -38,13 +38,11 @@ namespace mla {
 
 constexpr int kIdxThreads = 256;      // scoring work-group
 constexpr int kIdxSelThreads = 1024;  // selection work-group
-constexpr int kIdxFinish = 64;        // a bin this small is ranked by one wave
 constexpr int kIdxHistCopies = 16;   // radix histogram copies while all keys are in play
-constexpr int kIdxBucketBits = 12;    // buckets of the listing order
+constexpr int kIdxBucketBits = 11;    // buckets of the listing order
 constexpr int kIdxBuckets = 1 << kIdxBucketBits;
-static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxBuckets * 4 + kIdxMaxTopK * 8 <= kIdxMaxKeys * 8,
-              "bucket counts and grouped keys fit in the key buffer");
-static_assert(kIdxThreads == 256 && (256 * kIdxHistCopies) % kIdxThreads == 0, "one scoring thread per digit");
+static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxMaxTopK <= kIdxMaxKeys, "bucket scan, grouped keys");
+static_assert(kIdxThreads == 256 && (256 * kIdxHistCopies) % (4 * kIdxThreads) == 0, "one scoring thread per digit");
 static_assert(kIdxMaxKeys / kIdxSlice <= kIdxSelThreads / 64, "one selecting wave per key slice");
 
 // The four e4m3 codes of a dword as floats (exact), byte e -> f[e], through the OCP
@@ -115,6 +113,7 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
   __shared__ __align__(16) float qf[kIdxMaxDepth];
   __shared__ float part[kIdxThreads];
   __shared__ __align__(16) int dcnt[256 * kIdxHistCopies];  // [digit][copy]
+  __shared__ __align__(16) uint64_t grouped[kIdxSlice];
   __shared__ int wave_sum[kIdxThreads / 64];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const TokenRows tr = token_rows(a, t, blockIdx.y == 0 && tid == 0);
@@ -122,7 +121,8 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
   const int i0 = blockIdx.y * kIdxSlice, i1 = min(nvis, i0 + kIdxSlice);
   if (i0 >= i1) return;  // block-uniform, before any barrier
 #pragma unroll
-  for (int u = 0; u < 256 * kIdxHistCopies / kIdxThreads; ++u) dcnt[tid + u * kIdxThreads] = 0;
+  for (int u = 0; u < 256 * kIdxHistCopies / (4 * kIdxThreads); ++u)
+    *(int4*)&dcnt[4 * (tid + u * kIdxThreads)] = make_int4(0, 0, 0, 0);
 
   // ---- the page ids of this thread's rows (rows i0 + tid + r * kIdxThreads)
   const int32_t* prow = a.page_table + (int64_t)b * a.pt_row;
@@ -260,8 +260,13 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    if (i0 + tid + r * kIdxThreads < i1)
-      krow[i0 + atomicAdd(&dcnt[(int)(key[r] >> 56) * kIdxHistCopies + copy], 1)] = key[r];
+    if (i0 + tid + r * kIdxThreads < i1) grouped[atomicAdd(&dcnt[(int)(key[r] >> 56) * kIdxHistCopies + copy], 1)] = key[r];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {  // the grouped slice out in whole rows
+    const int j = tid + r * kIdxThreads;
+    if (i0 + j < i1) krow[i0 + j] = grouped[j];
+  }
 }
 
 // The number of set bits of a wave-wide mask below this lane.
@@ -284,29 +289,71 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   constexpr int NSL = kIdxMaxKeys / kIdxSlice;  // key slices at most, one wave each
   __shared__ __align__(16) uint64_t keys[kIdxMaxKeys];
   __shared__ __align__(16) uint64_t top[kIdxMaxTopK];
-  __shared__ uint64_t cand[kIdxFinish];
-  __shared__ int hist[256];
+  __shared__ uint32_t bfirst[kIdxBuckets];
+  __shared__ __align__(16) int hist[256];
   __shared__ int wave_tot[kIdxSelThreads / 64], slice_above[NSL], slice_equal[NSL];
-  __shared__ int sel_digit, sel_count, sel_bin, n_top, n_cand;
-  __shared__ unsigned long long kmax, sel_key;
+  __shared__ uint64_t wave_max[kIdxSelThreads / 64], wave_min[kIdxSelThreads / 64];
+  __shared__ int sel_digit, sel_count, sel_bin, n_top;
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const TokenRows tr = token_rows(a, t, false);
   const int nvis = tr.vhi - tr.vlo;
   const uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
   const int nsel = min(a.top_k, nvis);
-  uint64_t prefix = 0;  // a lower bound of the listed keys once they are listed
-  if (nsel == nvis) {   // block-uniform: every visible row is listed
-    for (int i = tid; i < nvis; i += kIdxSelThreads) top[i] = krow[i];
+#pragma unroll
+  for (int u = 0; u < kIdxBuckets / kIdxSelThreads; ++u) bfirst[tid + u * kIdxSelThreads] = 0;
+  auto wave_max_u64 = [&](uint64_t x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint64_t)__shfl_xor((unsigned long long)x, off));
+    return x;
+  };
+  auto wave_min_u64 = [&](uint64_t x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = min(x, (uint64_t)__shfl_xor((unsigned long long)x, off));
+    return x;
+  };
+  // ---- the nsel largest keys into top[0 .. nsel), unordered, and bounds lo <= every
+  // listed key <= hi; bfirst[] then holds how many fall in each ordering bucket
+  // (k - lo) >> sh (bucket_of below)
+  uint64_t lo, hi;
+  int sh;
+  auto bucket_of = [&](uint64_t k) { return (int)((k - lo) >> sh); };
+  auto set_buckets = [&]() {
+    const uint64_t range = hi - lo;
+    sh = max(0, 64 - __clzll(range) - kIdxBucketBits);  // range >> sh < kIdxBuckets
+  };
+  if (nsel == nvis) {  // block-uniform: every visible row is listed
+    uint64_t mx = 0, mn = ~0ull;
+    for (int i = tid; i < nvis; i += kIdxSelThreads) {
+      const uint64_t k = krow[i];
+      top[i] = k;
+      mx = max(mx, k);
+      mn = min(mn, k);
+    }
+    mx = wave_max_u64(mx);
+    mn = wave_min_u64(mn);
+    if (lane == 0) {
+      wave_max[wave] = mx;
+      wave_min[wave] = mn;
+    }
+    __syncthreads();
+    hi = 0;
+    lo = ~0ull;
+    for (int w = 0; w < kIdxSelThreads / 64; ++w) {
+      hi = max(hi, wave_max[w]);
+      lo = min(lo, wave_min[w]);
+    }
+    if (nvis == 0) lo = hi = 0;
+    set_buckets();
+    for (int i = tid; i < nvis; i += kIdxSelThreads) atomicAdd(&bfirst[bucket_of(top[i])], 1u);
   } else {
-    // ---- the nsel largest keys into top[0 .. nsel), unordered.  A radix select (8-bit
-    // digits, most significant first) finds the threshold: `prefix` holds its digits
-    // found so far, `need` how many keys at or above it are still to be listed.
+    // A radix select (8-bit digits, most significant first) finds the threshold:
+    // `prefix` holds its digits found so far, `need` how many keys at or above it are
+    // still to be listed.
     //
-    // First digit, from the scoring kernel's counts: it wrote each slice's keys grouped
-    // by top digit, digits descending, with the size and start of each digit's run.
-    // Thread d < 256 sums digit d over the slices: A keys above it, H of it.  The digit
-    // where A < nsel <= A + H is the threshold's.
     const int nsl = (nvis + kIdxSlice - 1) / kIdxSlice;  // 1 .. NSL
+    // First digit, from the scoring kernel's run tables (the size and start of each
+    // digit's run in each slice).  Thread d < 256 sums digit d over the slices: A keys
+    // above it, H of it.  The digit where A < nsel <= A + H is the threshold's.
     if (tid < 256) {
       hist[tid] = 0;
       const uint32_t* hs = a.slice_hist + (int64_t)t * a.hist_row + tid;
@@ -336,46 +383,50 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
           }
       }
     }
-    if (tid == 0) n_cand = 0;
     __syncthreads();
-    prefix = (uint64_t)sel_digit << 56;
+    uint64_t prefix = (uint64_t)sel_digit << 56;
     int need = sel_count;
     const int nw = sel_bin;  // keys[0 .. nw) will hold the keys of the first digit
     int n_above = 0;
     for (int sl = 0; sl < nsl; ++sl) n_above += slice_above[sl];
     // Wave w takes slice w: its run above the digit is listed, its run of the digit goes
     // to keys[] (counting the next digit on the way), the rest is never read.
+    uint64_t mx = 0;
     if (wave < nsl) {
+      const uint64_t* sk = krow + wave * kIdxSlice;
+      uint64_t v[kIdxSlice / 64];
       int oa = 0, oe = 0;
       for (int w = 0; w < wave; ++w) {
         oa += slice_above[w];
         oe += slice_equal[w];
       }
       const int na = slice_above[wave], n = na + slice_equal[wave];
-      const uint64_t* sk = krow + wave * kIdxSlice;
-      uint64_t v[kIdxSlice / 64];
 #pragma unroll
-      for (int u = 0; u < kIdxSlice / 64; ++u)
-        if (u * 64 < n) v[u] = sk[min(u * 64 + lane, n - 1)];  // all loads in flight
+      for (int u = 0; u < kIdxSlice / 64; ++u)  // all loads in flight
+        if (u * 64 < n) v[u] = sk[min(u * 64 + lane, n - 1)];
 #pragma unroll
       for (int u = 0; u < kIdxSlice / 64; ++u) {
         const int j = u * 64 + lane;
         if (u * 64 < n) {
           if (j < na) {
             top[oa + j] = v[u];
+            mx = max(mx, v[u]);
           } else if (j < n) {
             keys[oe + j - na] = v[u];
+            mx = max(mx, v[u]);
             atomicAdd(&hist[(int)((v[u] >> 48) & 0xFF)], 1);
           }
         }
       }
     }
+    mx = wave_max_u64(mx);
+    if (lane == 0) wave_max[wave] = mx;
     if (tid == 0) n_top = n_above;
     __syncthreads();
 
-    // Remaining digits over keys[0 .. nw), until the bin of the threshold's digits holds
-    // at most kIdxFinish keys; `thr` is then the threshold key itself, or a lower bound
-    // with exactly nsel keys at or above it.
+    // Remaining digits over keys[0 .. nw), until all keys of the threshold's bin are
+    // needed; `thr` is then a lower bound (lower digits zero) with exactly nsel keys at or
+    // above it, or the threshold key itself after the last digit.
     uint64_t thr = prefix;
     if (need < nw) {
       for (int shift = 48;; shift -= 8) {
@@ -390,92 +441,64 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
           }
           __syncthreads();
         }
-        // the digit where the count from the top reaches `need`: thread tid < 256 takes
-        // digit 255 - tid, so a prefix sum over those threads is the count of keys with
-        // a digit at or above it; the one thread where that count first reaches `need`
-        // publishes the digit, the count still needed within it and its size
-        {
-          const int c = tid < 256 ? hist[255 - tid] : 0;
-          int incl = c;
+        // the digit where the count from the top reaches `need`, by wave 0: lane l takes
+        // digits 255 - 4 l .. 252 - 4 l, so a prefix sum over the lanes counts the keys
+        // at or above each; the digit where that count first reaches `need` is published
+        // with the count still needed within it and its size
+        if (wave == 0) {
+          const int4 h4 = *(const int4*)&hist[252 - 4 * lane];  // digits 252 - 4 l .. 255 - 4 l
+          const int c[4] = {h4.w, h4.z, h4.y, h4.x};            // descending digits
+          const int run = c[0] + c[1] + c[2] + c[3];
+          int incl = run;
 #pragma unroll
           for (int off = 1; off < 64; off <<= 1) {
             const int up = __shfl_up(incl, off);
             if (lane >= off) incl += up;
           }
-          if (tid < 256 && lane == 63) wave_tot[wave] = incl;
-          __syncthreads();
-          if (tid < 256) {
-            for (int w = 0; w < wave; ++w) incl += wave_tot[w];
-            if (c > 0 && incl >= need && incl - c < need) {
-              sel_digit = 255 - tid;
-              sel_count = need - (incl - c);
-              sel_bin = c;
+          int above = incl - run;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (c[u] > 0 && above < need && above + c[u] >= need) {
+              sel_digit = 255 - 4 * lane - u;
+              sel_count = need - above;
+              sel_bin = c[u];
             }
+            above += c[u];
           }
-          __syncthreads();
         }
+        __syncthreads();
         prefix |= (uint64_t)sel_digit << shift;
         need = sel_count;
         const int bin = sel_bin;
-        __syncthreads();
         thr = prefix;
         if (need == bin || shift == 0) break;  // all of the bin needed, or prefix exact
-        if (bin <= kIdxFinish) {
-          // the bin's keys to cand[], then one wave ranks them: the one with `need` - 1
-          // larger is the threshold (keys are distinct)
-          const uint64_t m = ~0ull << shift;
-          for (int i0 = wave * 64; i0 < nw; i0 += kIdxSelThreads) {  // whole waves
-            const int i = i0 + lane;
-            const uint64_t k = i < nw ? keys[i] : 0;
-            const bool in_bin = i < nw && (k & m) == prefix;
-            const int sl = wave_slot(in_bin, &n_cand);
-            if (in_bin) cand[sl] = k;
-          }
-          __syncthreads();
-          if (wave == 0) {
-            const uint64_t k = lane < bin ? cand[lane] : 0;
-            int rank = 0;
-            for (int j = 0; j < bin; ++j) rank += cand[j] > k;
-            if (lane < bin && rank == need - 1) sel_key = k;
-          }
-          __syncthreads();
-          thr = sel_key;
-          break;
-        }
       }
     }
-    // the keys of the first digit at or above the threshold join the list
+    hi = 0;
+    for (int w = 0; w < kIdxSelThreads / 64; ++w) hi = max(hi, wave_max[w]);
+    lo = thr;
+    set_buckets();
+    // the keys of the first digit at or above the threshold join the list; every listed
+    // key is counted in its bucket
     for (int i0 = wave * 64; i0 < nw; i0 += kIdxSelThreads) {
       const int i = i0 + lane;
       const uint64_t k = i < nw ? keys[i] : 0;
       const bool take = i < nw && k >= thr;
       const int sl = wave_slot(take, &n_top);
-      if (take) top[sl] = k;
+      if (take) {
+        top[sl] = k;
+        atomicAdd(&bfirst[bucket_of(k)], 1u);
+      }
     }
-    prefix = thr;
+    for (int i = tid; i < n_above; i += kIdxSelThreads) atomicAdd(&bfirst[bucket_of(top[i])], 1u);
   }
-  if (tid == 0) kmax = 0;
-  __syncthreads();  // top[0 .. nsel) complete; keys[] is free from here on
+  __syncthreads();  // top[0 .. nsel) and the bucket counts complete; keys[] is free
 
-  // ---- listing order.  The keys lie in [prefix, kmax]; bucket (k - prefix) >> sh
-  // (kIdxBuckets of them, larger keys in higher buckets) groups them, a scan from the top
-  // bucket gives each bucket's first output slot, and a key's slot is that plus the
-  // number of larger keys in its own bucket.  Keys are distinct, so the slots are
-  // 0 .. nsel - 1 once each, by descending key.
-  uint32_t* bfirst = (uint32_t*)keys;                 // [kIdxBuckets]
-  uint64_t* grouped = keys + kIdxBuckets / 2;         // [kIdxMaxTopK], by bucket
-  uint64_t mx = 0;
-  for (int i = tid; i < nsel; i += kIdxSelThreads) mx = max(mx, top[i]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint64_t)__shfl_xor((unsigned long long)mx, off));
-  if (lane == 0 && mx) atomicMax(&kmax, (unsigned long long)mx);
-#pragma unroll
-  for (int u = 0; u < kIdxBuckets / kIdxSelThreads; ++u) bfirst[tid * (kIdxBuckets / kIdxSelThreads) + u] = 0;
-  __syncthreads();
-  const uint64_t range = kmax > prefix ? kmax - prefix : 0;
-  const int sh = max(0, 64 - __clzll(range) - kIdxBucketBits);  // range >> sh < kIdxBuckets
-  for (int i = tid; i < nsel; i += kIdxSelThreads) atomicAdd(&bfirst[(int)((top[i] - prefix) >> sh)], 1u);
-  __syncthreads();
+  // ---- listing order.  The buckets are of equal key width between lo and hi, larger
+  // keys in higher buckets; a scan from the top bucket gives each bucket's first output
+  // slot, and a key's slot is that plus the number of larger keys in its own bucket.
+  // Keys are distinct, so the slots are 0 .. nsel - 1 once each, by descending key.
+  uint64_t* grouped = keys;  // [kIdxMaxTopK], by bucket
   {
     // exclusive scan from the top bucket: thread tid holds buckets
     // kIdxBuckets - 1 - BPT * tid - u, u = 0 .. BPT - 1 (descending)
@@ -492,10 +515,10 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
       const uint32_t up = __shfl_up(incl, off);
       if (lane >= off) incl += up;
     }
-    if (lane == 63) wave_tot[tid >> 6] = (int)incl;
+    if (lane == 63) wave_tot[wave] = (int)incl;
     __syncthreads();
     uint32_t first = incl - run;
-    for (int w = 0; w < (tid >> 6); ++w) first += (uint32_t)wave_tot[w];
+    for (int w = 0; w < wave; ++w) first += (uint32_t)wave_tot[w];
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
       bfirst[kIdxBuckets - 1 - BPT * tid - u] = first;
@@ -507,7 +530,7 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   // slot of bucket b - 1
   for (int i = tid; i < nsel; i += kIdxSelThreads) {
     const uint64_t k = top[i];
-    grouped[atomicAdd(&bfirst[(int)((k - prefix) >> sh)], 1u)] = k;
+    grouped[atomicAdd(&bfirst[bucket_of(k)], 1u)] = k;
   }
   __syncthreads();
 
@@ -516,13 +539,13 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   int32_t* orow = a.out + (int64_t)t * a.out_row;
   for (int p = tid; p < nsel; p += kIdxSelThreads) {
     const uint64_t k = grouped[p];
-    const int bk = (int)((k - prefix) >> sh);
+    const int pos = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
+    const int lp = pos / a.PS, slot = pos - lp * a.PS;
+    const int pid = prow[lp];  // in flight during the count below
+    const int bk = bucket_of(k);
     const int s0 = bk == kIdxBuckets - 1 ? 0 : (int)bfirst[bk + 1], s1 = (int)bfirst[bk];
     int rank = s0;
     for (int q = s0; q < s1; ++q) rank += grouped[q] > k;
-    const int pos = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
-    const int lp = pos / a.PS, slot = pos - lp * a.PS;
-    const int pid = prow[lp];
     orow[rank] = (pid >= 0 && (int64_t)pid < a.num_pages) ? pid * a.PS + slot : -1;
   }
   for (int i = nsel + tid; i < a.top_k; i += kIdxSelThreads) orow[i] = -1;
