@@ -269,31 +269,15 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
   }
 }
 
-// The number of set bits of a wave-wide mask below this lane.
-__device__ __forceinline__ int lane_rank(uint64_t b) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-}
-
-// Slot of this lane's entry in a list that grows at *count, when `take`: one LDS atomic
-// per wave reserves the wave's entries, and a lane's slot follows the taking lanes below
-// it.  All 64 lanes of the wave must be active.
-__device__ __forceinline__ int wave_slot(bool take, int* count) {
-  const uint64_t b = __builtin_amdgcn_ballot_w64(take);
-  int base = 0;
-  if ((threadIdx.x & 63) == 0 && b != 0) base = atomicAdd(count, (int)__popcll(b));
-  base = __builtin_amdgcn_readfirstlane(base);
-  return base + lane_rank(b);
-}
-
 __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(const IndexerArgs a) {
   constexpr int NSL = kIdxMaxKeys / kIdxSlice;  // key slices at most, one wave each
   __shared__ __align__(16) uint64_t keys[kIdxMaxKeys];
-  __shared__ __align__(16) uint64_t top[kIdxMaxTopK];
+  __shared__ __align__(16) uint64_t grouped[kIdxMaxTopK];
   __shared__ uint32_t bfirst[kIdxBuckets];
   __shared__ __align__(16) int hist[256];
   __shared__ int wave_tot[kIdxSelThreads / 64], slice_above[NSL], slice_equal[NSL];
   __shared__ uint64_t wave_max[kIdxSelThreads / 64], wave_min[kIdxSelThreads / 64];
-  __shared__ int sel_digit, sel_count, sel_bin, n_top;
+  __shared__ int sel_digit, sel_count, sel_bin;
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const TokenRows tr = token_rows(a, t, false);
   const int nvis = tr.vhi - tr.vlo;
@@ -301,36 +285,23 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   const int nsel = min(a.top_k, nvis);
 #pragma unroll
   for (int u = 0; u < kIdxBuckets / kIdxSelThreads; ++u) bfirst[tid + u * kIdxSelThreads] = 0;
-  auto wave_max_u64 = [&](uint64_t x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint64_t)__shfl_xor((unsigned long long)x, off));
-    return x;
-  };
-  auto wave_min_u64 = [&](uint64_t x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = min(x, (uint64_t)__shfl_xor((unsigned long long)x, off));
-    return x;
-  };
-  // ---- the nsel largest keys into top[0 .. nsel), unordered, and bounds lo <= every
-  // listed key <= hi; bfirst[] then holds how many fall in each ordering bucket
-  // (k - lo) >> sh (bucket_of below)
-  uint64_t lo, hi;
-  int sh;
-  auto bucket_of = [&](uint64_t k) { return (int)((k - lo) >> sh); };
-  auto set_buckets = [&]() {
-    const uint64_t range = hi - lo;
-    sh = max(0, 64 - __clzll(range) - kIdxBucketBits);  // range >> sh < kIdxBuckets
-  };
+  // ---- The listed keys are keys[nw .. nw + nab) and those of keys[0 .. nw) at or above
+  // thr, exactly nsel in all; lo <= each listed key <= hi.
+  int nw, nab;
+  uint64_t thr, lo, hi;
   if (nsel == nvis) {  // block-uniform: every visible row is listed
     uint64_t mx = 0, mn = ~0ull;
     for (int i = tid; i < nvis; i += kIdxSelThreads) {
       const uint64_t k = krow[i];
-      top[i] = k;
+      keys[i] = k;
       mx = max(mx, k);
       mn = min(mn, k);
     }
-    mx = wave_max_u64(mx);
-    mn = wave_min_u64(mn);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mx = max(mx, (uint64_t)__shfl_xor((unsigned long long)mx, off));
+      mn = min(mn, (uint64_t)__shfl_xor((unsigned long long)mn, off));
+    }
     if (lane == 0) {
       wave_max[wave] = mx;
       wave_min[wave] = mn;
@@ -343,17 +314,19 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
       lo = min(lo, wave_min[w]);
     }
     if (nvis == 0) lo = hi = 0;
-    set_buckets();
-    for (int i = tid; i < nvis; i += kIdxSelThreads) atomicAdd(&bfirst[bucket_of(top[i])], 1u);
+    nw = 0;
+    nab = nvis;
+    thr = 0;
   } else {
     // A radix select (8-bit digits, most significant first) finds the threshold:
     // `prefix` holds its digits found so far, `need` how many keys at or above it are
     // still to be listed.
     //
-    const int nsl = (nvis + kIdxSlice - 1) / kIdxSlice;  // 1 .. NSL
     // First digit, from the scoring kernel's run tables (the size and start of each
     // digit's run in each slice).  Thread d < 256 sums digit d over the slices: A keys
-    // above it, H of it.  The digit where A < nsel <= A + H is the threshold's.
+    // above it, H of it.  The digit where A < nsel <= A + H is the threshold's.  The
+    // highest digit with keys bounds them all from above.
+    const int nsl = (nvis + kIdxSlice - 1) / kIdxSlice;  // 1 .. NSL
     if (tid < 256) {
       hist[tid] = 0;
       const uint32_t* hs = a.slice_hist + (int64_t)t * a.hist_row + tid;
@@ -382,25 +355,29 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
             slice_equal[sl] = (int)cnt[sl];
           }
       }
+      const uint64_t nz = __builtin_amdgcn_ballot_w64(H > 0);
+      if (lane == 0) wave_tot[wave] = nz ? wave * 64 + 63 - __clzll(nz) : -1;
     }
     __syncthreads();
     uint64_t prefix = (uint64_t)sel_digit << 56;
     int need = sel_count;
-    const int nw = sel_bin;  // keys[0 .. nw) will hold the keys of the first digit
-    int n_above = 0;
-    for (int sl = 0; sl < nsl; ++sl) n_above += slice_above[sl];
-    // Wave w takes slice w: its run above the digit is listed, its run of the digit goes
-    // to keys[] (counting the next digit on the way), the rest is never read.
-    uint64_t mx = 0;
+    nw = sel_bin;  // keys[0 .. nw): the keys of the first digit
+    const int dmax = max(max(wave_tot[0], wave_tot[1]), max(wave_tot[2], wave_tot[3]));
+    hi = dmax == 255 ? ~0ull : ((uint64_t)(dmax + 1) << 56) - 1;
+    nab = 0;
+    for (int sl = 0; sl < nsl; ++sl) nab += slice_above[sl];
+    // Wave w takes slice w: its run above the digit goes to keys[nw ..), its run of the
+    // digit to keys[0 .. nw) (counting the next digit on the way); the rest is never
+    // read.
     if (wave < nsl) {
-      const uint64_t* sk = krow + wave * kIdxSlice;
-      uint64_t v[kIdxSlice / 64];
-      int oa = 0, oe = 0;
+      int oa = nw, oe = 0;
       for (int w = 0; w < wave; ++w) {
         oa += slice_above[w];
         oe += slice_equal[w];
       }
       const int na = slice_above[wave], n = na + slice_equal[wave];
+      const uint64_t* sk = krow + wave * kIdxSlice;
+      uint64_t v[kIdxSlice / 64];
 #pragma unroll
       for (int u = 0; u < kIdxSlice / 64; ++u)  // all loads in flight
         if (u * 64 < n) v[u] = sk[min(u * 64 + lane, n - 1)];
@@ -409,25 +386,20 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
         const int j = u * 64 + lane;
         if (u * 64 < n) {
           if (j < na) {
-            top[oa + j] = v[u];
-            mx = max(mx, v[u]);
+            keys[oa + j] = v[u];
           } else if (j < n) {
             keys[oe + j - na] = v[u];
-            mx = max(mx, v[u]);
             atomicAdd(&hist[(int)((v[u] >> 48) & 0xFF)], 1);
           }
         }
       }
     }
-    mx = wave_max_u64(mx);
-    if (lane == 0) wave_max[wave] = mx;
-    if (tid == 0) n_top = n_above;
     __syncthreads();
 
     // Remaining digits over keys[0 .. nw), until all keys of the threshold's bin are
-    // needed; `thr` is then a lower bound (lower digits zero) with exactly nsel keys at or
+    // needed; thr is then a lower bound (lower digits zero) with exactly nsel keys at or
     // above it, or the threshold key itself after the last digit.
-    uint64_t thr = prefix;
+    thr = prefix;
     if (need < nw) {
       for (int shift = 48;; shift -= 8) {
         if (shift < 48) {
@@ -474,31 +446,22 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
         if (need == bin || shift == 0) break;  // all of the bin needed, or prefix exact
       }
     }
-    hi = 0;
-    for (int w = 0; w < kIdxSelThreads / 64; ++w) hi = max(hi, wave_max[w]);
     lo = thr;
-    set_buckets();
-    // the keys of the first digit at or above the threshold join the list; every listed
-    // key is counted in its bucket
-    for (int i0 = wave * 64; i0 < nw; i0 += kIdxSelThreads) {
-      const int i = i0 + lane;
-      const uint64_t k = i < nw ? keys[i] : 0;
-      const bool take = i < nw && k >= thr;
-      const int sl = wave_slot(take, &n_top);
-      if (take) {
-        top[sl] = k;
-        atomicAdd(&bfirst[bucket_of(k)], 1u);
-      }
-    }
-    for (int i = tid; i < n_above; i += kIdxSelThreads) atomicAdd(&bfirst[bucket_of(top[i])], 1u);
   }
-  __syncthreads();  // top[0 .. nsel) and the bucket counts complete; keys[] is free
+  const int nall = nw + nab;
+  auto listed = [&](int i, uint64_t k) { return i >= nw || k >= thr; };
 
-  // ---- listing order.  The buckets are of equal key width between lo and hi, larger
-  // keys in higher buckets; a scan from the top bucket gives each bucket's first output
-  // slot, and a key's slot is that plus the number of larger keys in its own bucket.
-  // Keys are distinct, so the slots are 0 .. nsel - 1 once each, by descending key.
-  uint64_t* grouped = keys;  // [kIdxMaxTopK], by bucket
+  // ---- listing order.  Buckets of equal key width between lo and hi, larger keys in
+  // higher buckets: a scan from the top bucket gives each bucket's first output slot,
+  // and a key's slot is that plus the number of larger keys in its own bucket.  Keys are
+  // distinct, so the slots are 0 .. nsel - 1 once each, by descending key.
+  const int sh = max(0, 64 - __clzll(hi - lo) - kIdxBucketBits);  // (hi - lo) >> sh < kIdxBuckets
+  auto bucket_of = [&](uint64_t k) { return (int)((k - lo) >> sh); };
+  for (int i = tid; i < nall; i += kIdxSelThreads) {
+    const uint64_t k = keys[i];
+    if (listed(i, k)) atomicAdd(&bfirst[bucket_of(k)], 1u);
+  }
+  __syncthreads();
   {
     // exclusive scan from the top bucket: thread tid holds buckets
     // kIdxBuckets - 1 - BPT * tid - u, u = 0 .. BPT - 1 (descending)
@@ -528,9 +491,9 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   __syncthreads();
   // grouped by bucket; afterwards bfirst[b] is the end of bucket b, which is the first
   // slot of bucket b - 1
-  for (int i = tid; i < nsel; i += kIdxSelThreads) {
-    const uint64_t k = top[i];
-    grouped[atomicAdd(&bfirst[bucket_of(k)], 1u)] = k;
+  for (int i = tid; i < nall; i += kIdxSelThreads) {
+    const uint64_t k = keys[i];
+    if (listed(i, k)) grouped[atomicAdd(&bfirst[bucket_of(k)], 1u)] = k;
   }
   __syncthreads();
 
