@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
   constexpr int R = kIdxSlice / kIdxThreads;  // rows per thread
   static_assert(R % RF == 0, "rows per thread in whole groups");
   __shared__ __align__(16) float qf[kIdxMaxDepth];
-  __shared__ float part[kIdxThreads];
+  __shared__ __align__(16) float part[4 * kIdxThreads];  // [group][d] partial sums of the fold
   __shared__ __align__(16) int dcnt[256 * kIdxHistCopies];  // [digit][copy]
   __shared__ __align__(16) uint64_t grouped[kIdxSlice];
   __shared__ int wave_sum[kIdxThreads / 64];
@@ -133,27 +133,53 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
     pid[r] = i < i1 ? prow[(vlo + i) / a.PS] : 0;
   }
 
-  // ---- heads folded into one float32 query row: G groups of `depth` threads, group g
-  // summing heads g, g + G, ...; the groups' sums are then added in group order
-  const int G = kIdxThreads / a.depth;
-  if (tid < G * a.depth) {
-    const int g = tid / a.depth, d = tid - g * a.depth;
-    const uint8_t* qt = a.q + (int64_t)t * a.q_tok + d;
-    const float* qst = a.q_s + (int64_t)t * a.qs_tok;
-    float acc = 0.f;
+  // ---- heads folded into one float32 query row, qf[d] = sum_h q_s[h] * q[h, d]: G
+  // groups of threads, group g summing heads g, g + G, ...; the groups' sums are then
+  // added in group order.  With q 4-byte aligned a thread takes 4 consecutive d of each
+  // of its heads (one dword load per head, all of them in flight), else one d.
+  const float* qst = a.q_s + (int64_t)t * a.qs_tok;
+  if ((((uintptr_t)a.q | (uintptr_t)a.q_tok | (uintptr_t)a.q_head) & 3) == 0) {  // block-uniform
+    const int C4 = a.depth >> 2, G = kIdxThreads / C4;
+    if (tid < G * C4) {
+      const int g = tid / C4, c = tid - g * C4;
+      const uint8_t* qt = a.q + (int64_t)t * a.q_tok + 4 * c;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-    for (int h = g; h < a.NH; h += G) {
-      float f[4];
-      e4m3x4_f32(qt[(int64_t)h * a.q_head], f);
-      acc += qst[h] * f[0];
+      for (int h = g; h < a.NH; h += G) {
+        float f[4];
+        e4m3x4_f32(*(const uint32_t*)(qt + (int64_t)h * a.q_head), f);
+        const float w = qst[h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += w * f[e];
+      }
+      *(float4*)&part[g * a.depth + 4 * c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
-    part[tid] = acc;
-  }
-  __syncthreads();
-  if (tid < a.depth) {
-    float acc = 0.f;
-    for (int g = 0; g < G; ++g) acc += part[g * a.depth + tid];
-    qf[tid] = acc;
+    __syncthreads();
+    if (tid < a.depth) {
+      float acc = 0.f;
+      for (int g = 0; g < G; ++g) acc += part[g * a.depth + tid];
+      qf[tid] = acc;
+    }
+  } else {
+    const int G = kIdxThreads / a.depth;
+    if (tid < G * a.depth) {
+      const int g = tid / a.depth, d = tid - g * a.depth;
+      const uint8_t* qt = a.q + (int64_t)t * a.q_tok + d;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int h = g; h < a.NH; h += G) {
+        float f[4];
+        e4m3x4_f32(qt[(int64_t)h * a.q_head], f);
+        acc += qst[h] * f[0];
+      }
+      part[tid] = acc;
+    }
+    __syncthreads();
+    if (tid < a.depth) {
+      float acc = 0.f;
+      for (int g = 0; g < G; ++g) acc += part[g * a.depth + tid];
+      qf[tid] = acc;
+    }
   }
   __syncthreads();
 
