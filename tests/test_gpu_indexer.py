@@ -165,6 +165,29 @@ def test_indexer_widths(num_heads, depth):
     assert differ <= max(total // 100, 8)
 
 
+def test_indexer_unaligned_q():
+    """q as a view into rows one byte wider (head stride D + 1, not a multiple of 4 bytes):
+    the head fold reads it a byte at a time instead of a dword; the result meets the same
+    checks over sequences of several 1024-row slices."""
+    import torch
+    m = need_gpu()
+    c = make_indexer_case(47, [700, 2500, 1024], 8, 128, 64, 512, q_per_seq=[1, 2, 1], name="idx-uq")
+    T, NH, D = c.q8.shape
+    wide = torch.zeros((T, NH, D + 1), dtype=torch.uint8, device="cuda")
+    wide[:, :, :D] = u8_dev(c.q8)
+    q_view = wide[:, :, :D]
+    assert q_view.stride(1) % 4 != 0
+    out = m.indexer_paged_fp8(q_view, f32_dev(c.q_s), i32_dev(c.input_row_offsets), i32_dev(c.page_table),
+                              i32_dev(c.cache_lens), u8_dev(c.k8), f32_dev(c.k_scale), c.top_k, mask=c.mask,
+                              local_window_size=c.window)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.int64)
+    differ = check_indexer(got, c, "unaligned q")
+    assert differ <= max(c.total_q * c.top_k // 100, 8)
+    aligned = run_indexer(m, c)
+    assert check_indexer(aligned, c, "aligned q") <= max(c.total_q * c.top_k // 100, 8)
+
+
 @pytest.mark.parametrize("top_k", [1, 700, 2048])
 def test_indexer_ties_exact(top_k):
     """Cache rows drawn from three patterns with one shared scale: scores tie exactly in
