@@ -38,7 +38,7 @@ namespace mla {
 
 constexpr int kIdxThreads = 256;      // scoring work-group
 constexpr int kIdxSelThreads = 1024;  // selection work-group
-constexpr int kIdxHistCopies = 16;   // radix histogram copies while all keys are in play
+constexpr int kIdxHistCopies = 4;    // copies of each digit counter in the scoring kernel
 constexpr int kIdxBucketBits = 11;    // buckets of the listing order
 constexpr int kIdxBuckets = 1 << kIdxBucketBits;
 static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxMaxTopK <= kIdxMaxKeys, "bucket scan, grouped keys");
