@@ -957,6 +957,7 @@ mla_status mla_indexer_paged_fp8(const mla_tensor* q, const mla_tensor* q_s,
   a.keys_row = keys_row;
   a.slice_hist = (uint32_t*)((char*)ws + kHeaderBytes + key_bytes);
   a.hist_row = hist_row;
+  a.zero_row = (const uint8_t*)ws;  // the header's zero row
   a.q = (const uint8_t*)q->data;
   a.q_tok = q->stride[0];
   a.q_head = q->stride[1];

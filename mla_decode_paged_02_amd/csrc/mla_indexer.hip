@@ -39,6 +39,7 @@ namespace mla {
 constexpr int kIdxThreads = 256;      // scoring work-group
 constexpr int kIdxSelThreads = 1024;  // selection work-group
 constexpr int kIdxHistCopies = 4;    // copies of each digit counter in the scoring kernel
+constexpr int kFoldHeads = 8;        // heads per fold thread whose q loads go out before the rows
 constexpr int kIdxBucketBits = 11;    // buckets of the listing order
 constexpr int kIdxBuckets = 1 << kIdxBucketBits;
 static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxMaxTopK <= kIdxMaxKeys, "bucket scan, grouped keys");
@@ -105,8 +106,9 @@ __device__ __forceinline__ TokenRows token_rows(const IndexerArgs& a, int t, boo
 }
 
 // NC: 16-byte chunks of a cache row held in registers (depth <= 16 * NC); RF: rows a
-// thread has in flight at once.
-template <int NC, int RF>
+// thread has in flight at once; PRE: q 4-byte aligned with at most kFoldHeads heads per
+// fold thread, so the fold's q loads and the first row group go out together.
+template <int NC, int RF, bool PRE>
 __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const IndexerArgs a) {
   constexpr int R = kIdxSlice / kIdxThreads;  // rows per thread
   static_assert(R % RF == 0, "rows per thread in whole groups");
@@ -133,13 +135,107 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
     pid[r] = i < i1 ? prow[(vlo + i) / a.PS] : 0;
   }
 
+  // ---- row groups: RF rows of this thread (rows i0 + tid + (r0 + u) * kIdxThreads),
+  // their 16-byte chunks loaded at once, then scored into distinct keys
+  uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
+  bool bad = false;
+  uint64_t key[R];  // row i0 + tid + r * kIdxThreads, if below i1
+  struct Rows {
+    uint4 v[RF][NC];
+    bool ok[RF];
+    int pos[RF];
+    float ks[RF];
+  };
+  auto load_rows = [&](int r0, Rows& g) {
+#pragma unroll
+    for (int u = 0; u < RF; ++u) {
+      const int i = i0 + tid + (r0 + u) * kIdxThreads;
+      g.pos[u] = vlo + i;
+      const int lp = g.pos[u] / a.PS, slot = g.pos[u] - lp * a.PS, p = pid[r0 + u];
+      g.ok[u] = p >= 0 && (int64_t)p < a.num_pages;
+      if (i < i1 && !g.ok[u]) bad = true;
+      g.ok[u] = g.ok[u] && i < i1;
+      // no branch around the loads (rows that do not count read the zero row, chunks past
+      // the width re-read the last one), so the compiler can count them in its waits
+      const int64_t pc = g.ok[u] ? p : 0;
+      const uint8_t* row = g.ok[u] ? a.k + pc * a.page_bytes + (int64_t)slot * a.depth : a.zero_row;
+      const int nc = a.depth >> 4;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) g.v[u][c] = *(const uint4*)(row + min(c, nc - 1) * 16);
+      const float* sp = g.ok[u] && a.k_s ? a.k_s + pc * a.ks_page + slot : (const float*)a.zero_row;
+      g.ks[u] = *sp;  // used (or replaced by 1) when the row is scored
+    }
+  };
+  auto score_rows = [&](int r0, const Rows& g) {
+#pragma unroll
+    for (int u = 0; u < RF; ++u) {
+      const int i = i0 + tid + (r0 + u) * kIdxThreads;
+      if (i >= i1) continue;
+      float s = -INFINITY;
+      if (g.ok[u]) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          if (c * 16 >= a.depth) break;
+          const uint32_t w[4] = {g.v[u][c].x, g.v[u][c].y, g.v[u][c].z, g.v[u][c].w};
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            float f[4];
+            e4m3x4_f32(w[e4], f);
+            const float4 qv = *(const float4*)&qf[c * 16 + 4 * e4];
+            acc += qv.x * f[0];
+            acc += qv.y * f[1];
+            acc += qv.z * f[2];
+            acc += qv.w * f[3];
+          }
+        }
+        s = acc * (a.k_s ? g.ks[u] : 1.f);
+        if (s != s) s = -INFINITY;  // a NaN score (NaN data) ranks last
+      }
+      // the score's order bits, then the inverted position (equal scores: lower first)
+      key[r0 + u] = ((uint64_t)order_key(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)g.pos[u]);
+    }
+  };
+  Rows first;  // the first row group, in flight during the fold
+
   // ---- heads folded into one float32 query row, qf[d] = sum_h q_s[h] * q[h, d]: G
   // groups of threads, group g summing heads g, g + G, ...; the groups' sums are then
   // added in group order.  With q 4-byte aligned a thread takes 4 consecutive d of each
-  // of its heads (one dword load per head, all of them in flight), else one d.
+  // of its heads (one dword load per head); when a thread has at most kFoldHeads heads
+  // their loads go out before those of the first row group, so the fold's wait for them
+  // does not also wait for the rows (loads complete in issue order).  Otherwise one d, a
+  // byte at a time.
   const float* qst = a.q_s + (int64_t)t * a.qs_tok;
-  if ((((uintptr_t)a.q | (uintptr_t)a.q_tok | (uintptr_t)a.q_head) & 3) == 0) {  // block-uniform
-    const int C4 = a.depth >> 2, G = kIdxThreads / C4;
+  const bool q4 = (((uintptr_t)a.q | (uintptr_t)a.q_tok | (uintptr_t)a.q_head) & 3) == 0;
+  const int G = q4 ? kIdxThreads / (a.depth >> 2) : kIdxThreads / a.depth;
+  if constexpr (PRE) {  // q 4-byte aligned and NH <= kFoldHeads * G (checked on the host)
+    const int C4 = a.depth >> 2;
+    const bool active = tid < G * C4;
+    const int g = active ? tid / C4 : 0, c = active ? tid - g * C4 : 0;
+    const uint8_t* qt = a.q + (int64_t)t * a.q_tok + 4 * c;
+    uint32_t qw[kFoldHeads];
+    float qw_s[kFoldHeads];
+#pragma unroll
+    for (int j = 0; j < kFoldHeads; ++j) {  // heads past NH read head NH - 1 with weight 0
+      const int h = min(g + j * G, a.NH - 1);
+      qw[j] = *(const uint32_t*)(qt + (int64_t)h * a.q_head);
+      qw_s[j] = qst[h];
+    }
+    load_rows(0, first);
+    if (active) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kFoldHeads; ++j) {
+        float f[4];
+        e4m3x4_f32(qw[j], f);
+        const float w = g + j * G < a.NH ? qw_s[j] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += w * f[e];
+      }
+      *(float4*)&part[g * a.depth + 4 * c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+  } else if (q4) {
+    const int C4 = a.depth >> 2;
     if (tid < G * C4) {
       const int g = tid / C4, c = tid - g * C4;
       const uint8_t* qt = a.q + (int64_t)t * a.q_tok + 4 * c;
@@ -154,14 +250,7 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
       }
       *(float4*)&part[g * a.depth + 4 * c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
-    __syncthreads();
-    if (tid < a.depth) {
-      float acc = 0.f;
-      for (int g = 0; g < G; ++g) acc += part[g * a.depth + tid];
-      qf[tid] = acc;
-    }
   } else {
-    const int G = kIdxThreads / a.depth;
     if (tid < G * a.depth) {
       const int g = tid / a.depth, d = tid - g * a.depth;
       const uint8_t* qt = a.q + (int64_t)t * a.q_tok + d;
@@ -174,70 +263,23 @@ __global__ __launch_bounds__(kIdxThreads) void mla_indexer_score_kernel(const In
       }
       part[tid] = acc;
     }
-    __syncthreads();
-    if (tid < a.depth) {
-      float acc = 0.f;
-      for (int g = 0; g < G; ++g) acc += part[g * a.depth + tid];
-      qf[tid] = acc;
-    }
   }
   __syncthreads();
+  if (tid < a.depth) {
+    float acc = 0.f;
+    for (int g = 0; g < G; ++g) acc += part[g * a.depth + tid];
+    qf[tid] = acc;
+  }
+  __syncthreads();
+  if constexpr (!PRE) load_rows(0, first);
 
   // ---- scores of this slice's rows as distinct keys, RF rows in flight
-  uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
-  bool bad = false;
-  uint64_t key[R];  // row i0 + tid + r * kIdxThreads, if below i1
+  score_rows(0, first);
 #pragma unroll
-  for (int r0 = 0; r0 < R; r0 += RF) {
-    uint4 v[RF][NC];
-    bool ok[RF];
-    int pos[RF];
-    float ks[RF];
-#pragma unroll
-    for (int u = 0; u < RF; ++u) {
-      const int i = i0 + tid + (r0 + u) * kIdxThreads;
-      pos[u] = vlo + i;
-      const int lp = pos[u] / a.PS, slot = pos[u] - lp * a.PS, p = pid[r0 + u];
-      ok[u] = p >= 0 && (int64_t)p < a.num_pages;
-      if (i < i1 && !ok[u]) bad = true;
-      ok[u] = ok[u] && i < i1;
-      ks[u] = 1.f;
-      if (ok[u]) {
-        const uint8_t* row = a.k + (int64_t)p * a.page_bytes + (int64_t)slot * a.depth;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          if (c * 16 < a.depth) v[u][c] = *(const uint4*)(row + c * 16);
-        if (a.k_s) ks[u] = a.k_s[(int64_t)p * a.ks_page + slot];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < RF; ++u) {
-      const int i = i0 + tid + (r0 + u) * kIdxThreads;
-      if (i >= i1) continue;
-      float s = -INFINITY;
-      if (ok[u]) {
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          if (c * 16 >= a.depth) break;
-          const uint32_t w[4] = {v[u][c].x, v[u][c].y, v[u][c].z, v[u][c].w};
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            float f[4];
-            e4m3x4_f32(w[e4], f);
-            const float4 qv = *(const float4*)&qf[c * 16 + 4 * e4];
-            acc += qv.x * f[0];
-            acc += qv.y * f[1];
-            acc += qv.z * f[2];
-            acc += qv.w * f[3];
-          }
-        }
-        s = acc * ks[u];
-        if (s != s) s = -INFINITY;  // a NaN score (NaN data) ranks last
-      }
-      // the score's order bits, then the inverted position (equal scores: lower first)
-      key[r0 + u] = ((uint64_t)order_key(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)pos[u]);
-    }
+  for (int r0 = RF; r0 < R; r0 += RF) {
+    Rows g;
+    load_rows(r0, g);
+    score_rows(r0, g);
   }
   if (bad) atomicOr(a.err, kErrPageId);
 
@@ -545,10 +587,19 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const Kernel
   if (timer && (e = hipEventRecord(timer->start, stream)) != hipSuccess) return e;
   const int slices = (int)((a.keys_row + kIdxSlice - 1) / kIdxSlice);
   const dim3 sgrid(a.T, slices > 0 ? slices : 1);
-  if (a.depth <= 128)
-    hipLaunchKernelGGL((mla_indexer_score_kernel<8, 2>), sgrid, dim3(kIdxThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((mla_indexer_score_kernel<16, 1>), sgrid, dim3(kIdxThreads), 0, stream, a);
+  const bool q4 = (((uintptr_t)a.q | (uintptr_t)a.q_tok | (uintptr_t)a.q_head) & 3) == 0;
+  const bool pre = q4 && a.NH <= kFoldHeads * (kIdxThreads / (a.depth >> 2));
+  if (a.depth <= 128) {
+    if (pre)
+      hipLaunchKernelGGL((mla_indexer_score_kernel<8, 2, true>), sgrid, dim3(kIdxThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((mla_indexer_score_kernel<8, 2, false>), sgrid, dim3(kIdxThreads), 0, stream, a);
+  } else {
+    if (pre)
+      hipLaunchKernelGGL((mla_indexer_score_kernel<16, 1, true>), sgrid, dim3(kIdxThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((mla_indexer_score_kernel<16, 1, false>), sgrid, dim3(kIdxThreads), 0, stream, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(mla_indexer_select_kernel, dim3(a.T), dim3(kIdxSelThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

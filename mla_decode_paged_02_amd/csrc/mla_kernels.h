@@ -153,6 +153,7 @@ struct IndexerArgs {
                               // of each top digit's run of keys
   int64_t hist_row;           // 512 * slices, slices = ceil(keys_row / kIdxSlice)
   uint32_t* err;
+  const uint8_t* zero_row;    // >= 256 zero bytes (the workspace header), read in place of rows that do not count
 };
 
 // Where the decode kernels put split rows' parts (mla_plan.h).

@@ -151,11 +151,12 @@ def test_indexer_feeds_sparse_decode():
     compare(to_f64(out), want, FP8_TOL, "indexer -> sparse decode")
 
 
-@pytest.mark.parametrize("num_heads,depth", [(3, 16), (5, 48), (64, 128), (7, 208), (2, 256)])
+@pytest.mark.parametrize("num_heads,depth", [(3, 16), (5, 48), (64, 128), (7, 208), (2, 256), (48, 256)])
 def test_indexer_widths(num_heads, depth):
     """Head widths from 16 to 256 (rows held in registers in 8 or 16 chunks) and head counts
-    that leave some fold groups empty; lengths over several 1024-row slices, top_k below,
-    at and above the visible count."""
+    that leave some fold groups empty, or give a fold thread more heads than it preloads
+    (48 heads of 256); lengths over several 1024-row slices, top_k below, at and above the
+    visible count."""
     m = need_gpu()
     c = make_indexer_case(44 + depth, [1, 1023, 1024, 2500, 4097], num_heads, depth, 64, 1024,
                           q_per_seq=[1, 2, 1, 3, 1], name=f"idx-w{depth}")
