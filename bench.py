@@ -280,8 +280,7 @@ def setup(workload, copies, num_partitions, dev):
 def graph_workspace_bytes(m, wl, case, num_partitions):
     """Workspace a captured step needs: reserved on the capture stream before capturing."""
     if wl == "X4":
-        keys_row = case.page_table.shape[1] * case.page_size
-        return case.total_q * (keys_row * 8 + 512 * 4 * -(-keys_row // 1024)) + (1 << 20)  # keys, slice digit counts
+        return m.indexer_workspace_bytes(case.total_q, case.page_table.shape[1], case.page_size)
     if wl == "C3":
         return 1 << 20
     heads = case.num_heads if hasattr(case, "num_heads") else int(case.q8.shape[1])

@@ -15,7 +15,7 @@ __all__ = [
     "LIBRARY_PATH", "MlaError", "library", "decode_paged", "decode_paged_noalloc",
     "decode_noalloc_scratch_bytes", "decode_paged_sparse", "decode_paged_sparse_shared",
     "decode_paged_sparse_ext", "decode_paged_fp8", "indexer_paged_fp8", "prefill_paged", "decode_num_partitions",
-    "decode_workspace_bytes", "reserve_workspace", "check_device_errors", "shutdown",
+    "decode_workspace_bytes", "indexer_workspace_bytes", "reserve_workspace", "check_device_errors", "shutdown",
     "version", "profile_enable", "profile_read", "profile_read_each", "MASKS", "STATUS",
 ]
 
@@ -66,6 +66,8 @@ def library() -> ctypes.CDLL:
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_decode_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32, i32]
         lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.mla_indexer_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32]
+        lib.mla_indexer_workspace_bytes.restype = ctypes.c_size_t
         lib.mla_reserve_workspace.argtypes = [i32, vp, ctypes.c_size_t]
         lib.mla_check_device_errors.argtypes = [i32, vp, ctypes.POINTER(ctypes.c_uint32)]
         lib.mla_profile_enable.argtypes = [i32]
@@ -292,6 +294,10 @@ def decode_num_partitions(batch, num_heads, max_pages, page_size) -> int:
 def decode_workspace_bytes(total_q, num_heads, num_partitions=0, device=-1) -> int:
     return int(library().mla_decode_workspace_bytes(int(total_q), int(num_heads),
                                                     int(num_partitions), int(device)))
+
+
+def indexer_workspace_bytes(total_q, max_pages, page_size) -> int:
+    return int(library().mla_indexer_workspace_bytes(int(total_q), int(max_pages), int(page_size)))
 
 
 def reserve_workspace(nbytes, device=-1, stream=None) -> None:

@@ -321,6 +321,26 @@ const char* mla_status_string(mla_status s) {
 
 const char* mla_last_error_message(void) { return g_msg; }
 
+// The indexer's workspace past the header: the keys [T, keys_row], then the run tables
+// [T, hist_row].
+struct IndexerLayout {
+  int64_t keys_row, hist_row;
+  size_t key_bytes, total;
+};
+static IndexerLayout indexer_layout(int64_t T, int64_t max_pages, int64_t PS) {
+  IndexerLayout L;
+  L.keys_row = max_pages * PS;
+  L.hist_row = 512 * ((L.keys_row + mla::kIdxSlice - 1) / mla::kIdxSlice);
+  L.key_bytes = (size_t)(T * L.keys_row) * sizeof(uint64_t);
+  L.total = L.key_bytes + (size_t)(T * L.hist_row) * sizeof(uint32_t);
+  return L;
+}
+
+size_t mla_indexer_workspace_bytes(int64_t total_q, int32_t max_pages, int32_t page_size) {
+  if (total_q < 0 || max_pages < 0 || page_size < 0) return 0;
+  return indexer_layout(total_q, max_pages, page_size).total + kHeaderBytes;
+}
+
 size_t mla_decode_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t num_partitions, int32_t device) {
   const int dev = device < 0 ? current_device() : device;
   const int grid = cu_count(dev);
@@ -946,17 +966,13 @@ mla_status mla_indexer_paged_fp8(const mla_tensor* q, const mla_tensor* q_s,
   bool cap = false;
   if ((s = stream_capturing(stream, &cap)) != MLA_OK) return s;
   void* ws = nullptr;
-  const int64_t keys_row = page_table->shape[1] * PS;
-  const int64_t hist_row = 512 * ((keys_row + mla::kIdxSlice - 1) / mla::kIdxSlice);
-  const size_t key_bytes = (size_t)(T * keys_row) * sizeof(uint64_t);
-  if ((s = grow_workspace(current_device(), stream, key_bytes + (size_t)(T * hist_row) * sizeof(uint32_t), cap, &ws)) !=
-      MLA_OK)
-    return s;
+  const IndexerLayout L = indexer_layout(T, page_table->shape[1], PS);
+  if ((s = grow_workspace(current_device(), stream, L.total, cap, &ws)) != MLA_OK) return s;
   mla::IndexerArgs a{};
   a.keys = (uint64_t*)((char*)ws + kHeaderBytes);
-  a.keys_row = keys_row;
-  a.slice_hist = (uint32_t*)((char*)ws + kHeaderBytes + key_bytes);
-  a.hist_row = hist_row;
+  a.keys_row = L.keys_row;
+  a.slice_hist = (uint32_t*)((char*)ws + kHeaderBytes + L.key_bytes);
+  a.hist_row = L.hist_row;
   a.zero_row = (const uint8_t*)ws;  // the header's zero row
   a.q = (const uint8_t*)q->data;
   a.q_tok = q->stride[0];

@@ -107,6 +107,17 @@ def test_workspace_size_grows_with_partitions():
     assert m.decode_workspace_bytes(64, 128, 0) >= 2 * 256 * 128 * 512 * 2
 
 
+def test_indexer_workspace_size():
+    """The indexer keeps 8 bytes per page-table row and 2 KiB per 1,024-row slice for each
+    query token, plus the fixed header."""
+    base = m.indexer_workspace_bytes(0, 256, 64)
+    one = m.indexer_workspace_bytes(1, 256, 64)
+    assert one - base == 16384 * 8 + 16 * 2048
+    assert m.indexer_workspace_bytes(32, 256, 64) - base == 32 * (one - base)
+    # a partial last slice still has its table row
+    assert m.indexer_workspace_bytes(1, 3, 500) - base == 1500 * 8 + 2 * 2048
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros((1, 16, 576), dtype=torch.bfloat16)

@@ -105,7 +105,6 @@ def test_graph_indexer():
                          "pt": i32_dev(c.page_table), "lens": i32_dev(c.cache_lens), "k": u8_dev(c.k8),
                          "ks": f32_dev(c.k_scale)})
     T = c.total_q
-    keys_row = c.page_table.shape[1] * c.page_size
 
     def call(b, out):
         m.indexer_paged_fp8(b["q"], b["qs"], b["off"], b["pt"], b["lens"], b["k"], b["ks"], top_k, out=out)
@@ -113,7 +112,7 @@ def test_graph_indexer():
     def make_out():
         return torch.empty(T, top_k, dtype=torch.int32, device="cuda")
 
-    ws = T * keys_row * 8 + T * 512 * 4 * -(-keys_row // 1024) + (1 << 20)  # keys, slice digit counts
+    ws = m.indexer_workspace_bytes(T, c.page_table.shape[1], c.page_size)
     check_replays(m, variants, call, make_out, -7, ws, "indexer")
 
 
