@@ -42,7 +42,8 @@ constexpr int kIdxHistCopies = 4;    // copies of each digit counter in the scor
 constexpr int kFoldHeads = 8;        // heads per fold thread whose q loads go out before the rows
 constexpr int kIdxBucketBits = 11;    // buckets of the listing order
 constexpr int kIdxBuckets = 1 << kIdxBucketBits;
-static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxMaxTopK <= kIdxMaxKeys, "bucket scan, grouped keys");
+static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxMaxTopK <= kIdxMaxKeys && kIdxMaxTopK % kIdxSelThreads == 0,
+              "bucket scan, grouped keys, listed keys per thread");
 static_assert(kIdxThreads == 256 && (256 * kIdxHistCopies) % (4 * kIdxThreads) == 0, "one scoring thread per digit");
 static_assert(kIdxMaxKeys / kIdxSlice <= kIdxSelThreads / 64, "one selecting wave per key slice");
 
@@ -568,16 +569,29 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   // ---- the top_k as physical rows in slot order, then -1
   const int32_t* prow = a.page_table + (int64_t)tr.b * a.pt_row;
   int32_t* orow = a.out + (int64_t)t * a.out_row;
-  for (int p = tid; p < nsel; p += kIdxSelThreads) {
-    const uint64_t k = grouped[p];
-    const int pos = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
-    const int lp = pos / a.PS, slot = pos - lp * a.PS;
-    const int pid = prow[lp];  // in flight during the count below
-    const int bk = bucket_of(k);
-    const int s0 = bk == kIdxBuckets - 1 ? 0 : (int)bfirst[bk + 1], s1 = (int)bfirst[bk];
-    int rank = s0;
-    for (int q = s0; q < s1; ++q) rank += grouped[q] > k;
-    orow[rank] = (pid >= 0 && (int64_t)pid < a.num_pages) ? pid * a.PS + slot : -1;
+  constexpr int OPT = kIdxMaxTopK / kIdxSelThreads;  // listed keys per thread at most
+  if (nsel > 0) {                                    // block-uniform
+    // both page-id loads in flight before either count (slots past nsel re-read the last
+    // key, so there is no branch around the loads)
+    uint64_t k[OPT];
+    int pid[OPT], slot[OPT];
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      k[u] = grouped[min(tid + u * kIdxSelThreads, nsel - 1)];
+      const int pos = (int)(0xFFFFFFFFu - (uint32_t)(k[u] & 0xFFFFFFFFu));
+      const int lp = pos / a.PS;
+      slot[u] = pos - lp * a.PS;
+      pid[u] = prow[lp];
+    }
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      if (tid + u * kIdxSelThreads >= nsel) break;
+      const int bk = bucket_of(k[u]);
+      const int s0 = bk == kIdxBuckets - 1 ? 0 : (int)bfirst[bk + 1], s1 = (int)bfirst[bk];
+      int rank = s0;
+      for (int q = s0; q < s1; ++q) rank += grouped[q] > k[u];
+      orow[rank] = (pid[u] >= 0 && (int64_t)pid[u] < a.num_pages) ? pid[u] * a.PS + slot[u] : -1;
+    }
   }
   for (int i = nsel + tid; i < a.top_k; i += kIdxSelThreads) orow[i] = -1;
 }
