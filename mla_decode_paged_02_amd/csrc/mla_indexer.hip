@@ -63,21 +63,41 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// The token's sequence (binary search of the offsets) and its visible rows [vlo, vhi).
+// The token's sequence and its visible rows [vlo, vhi).  The sequence is the last b < B
+// with offsets[b] <= t: each lane of a wave tests one offset and a ballot counts them, 64
+// offsets per round (non-decreasing offsets; others are caught by the range check below).
+// Lane i also loads sequence i's offsets and length, so a batch of at most 64 sequences
+// costs one load round trip.
 struct TokenRows {
   int b, vlo, vhi;
 };
 
 __device__ __forceinline__ TokenRows token_rows(const IndexerArgs& a, int t, bool report) {
-  int lo_b = 0, hi_b = a.B;
-  while (hi_b - lo_b > 1) {
-    const int mid = (lo_b + hi_b) >> 1;
-    if ((int)ld_const(a.offsets + mid) <= t) lo_b = mid; else hi_b = mid;
+  const int lane = (int)(threadIdx.x & 63);
+  int below = 0;  // offsets[0 .. B) at or below t
+  // lane i also loads sequence i's end offset and length, for a batch of at most 64
+  const int i0 = min(lane, a.B - 1);
+  const uint32_t own0 = a.offsets[i0], own1 = a.offsets[i0 + 1];
+  const int32_t own_len = a.cache_lens[i0];
+  for (int base = 0; base < a.B; base += 64) {  // wave-uniform
+    const int i = base + lane;
+    const uint32_t oi = base == 0 ? own0 : a.offsets[min(i, a.B - 1)];
+    below += (int)__popcll(__builtin_amdgcn_ballot_w64(i < a.B && (int64_t)oi <= (int64_t)t));
   }
+  const int lo_b = __builtin_amdgcn_readfirstlane(max(below - 1, 0));
   TokenRows r{lo_b, 0, 0};
-  const int o0 = (int)ld_const(a.offsets + lo_b), o1 = (int)ld_const(a.offsets + lo_b + 1);
+  int o0, o1;
+  long long L;
+  if (lo_b < 64) {  // wave-uniform
+    o0 = (int)__builtin_amdgcn_readlane((int)own0, lo_b);
+    o1 = (int)__builtin_amdgcn_readlane((int)own1, lo_b);
+    L = __builtin_amdgcn_readlane(own_len, lo_b);
+  } else {
+    o0 = (int)ld_const(a.offsets + lo_b);
+    o1 = (int)ld_const(a.offsets + lo_b + 1);
+    L = ld_const(a.cache_lens + lo_b);
+  }
   if (t >= o0 && t < o1) {
-    long long L = ld_const(a.cache_lens + lo_b);
     const long long Lmax = (long long)a.max_pages * a.PS;
     if (L > Lmax) {
       if (report) atomicOr(a.err, kErrCacheLen);
@@ -348,6 +368,20 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
   __shared__ uint64_t wave_max[kIdxSelThreads / 64], wave_min[kIdxSelThreads / 64];
   __shared__ int sel_digit, sel_count, sel_bin;
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The scoring kernel's run tables (per slice, the size and start of each top digit's
+  // run), loaded before the token's rows are known: thread d < 256 takes digit d of every
+  // slice the tables hold (slices past the token's last are masked below).
+  uint32_t cnt[NSL], st[NSL];
+  if (tid < 256) {
+    const int nsl_tab = (int)(a.hist_row / 512);
+    const uint32_t* hs = a.slice_hist + (int64_t)t * a.hist_row + tid;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int s2 = min(sl, nsl_tab - 1) * 512;
+      cnt[sl] = hs[s2];
+      st[sl] = hs[s2 + 256];
+    }
+  }
   const TokenRows tr = token_rows(a, t, false);
   const int nvis = tr.vhi - tr.vlo;
   const uint64_t* krow = a.keys + (int64_t)t * a.keys_row;
@@ -391,21 +425,12 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
     // `prefix` holds its digits found so far, `need` how many keys at or above it are
     // still to be listed.
     //
-    // First digit, from the scoring kernel's run tables (the size and start of each
-    // digit's run in each slice).  Thread d < 256 sums digit d over the slices: A keys
-    // above it, H of it.  The digit where A < nsel <= A + H is the threshold's.  The
+    // First digit, from the run tables.  Thread d < 256 sums digit d over the slices: A
+    // keys above it, H of it.  The digit where A < nsel <= A + H is the threshold's.  The
     // highest digit with keys bounds them all from above.
     const int nsl = (nvis + kIdxSlice - 1) / kIdxSlice;  // 1 .. NSL
     if (tid < 256) {
       hist[tid] = 0;
-      const uint32_t* hs = a.slice_hist + (int64_t)t * a.hist_row + tid;
-      uint32_t cnt[NSL], st[NSL];
-#pragma unroll
-      for (int sl = 0; sl < NSL; ++sl) {
-        const int s2 = min(sl, nsl - 1) * 512;
-        cnt[sl] = hs[s2];
-        st[sl] = hs[s2 + 256];
-      }
       int A = 0, H = 0;
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl)
