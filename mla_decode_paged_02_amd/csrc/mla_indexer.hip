@@ -496,9 +496,7 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
     thr = prefix;
     if (need < nw) {
       for (int shift = 48;; shift -= 8) {
-        if (shift < 48) {
-          if (tid < 256) hist[tid] = 0;
-          __syncthreads();
+        if (shift < 48) {  // hist[] was cleared by the previous digit's search
           const uint64_t hi_mask = ~0ull << (shift + 8);
 #pragma unroll 4
           for (int i = tid; i < nw; i += kIdxSelThreads) {
@@ -510,9 +508,11 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
         // the digit where the count from the top reaches `need`, by wave 0: lane l takes
         // digits 255 - 4 l .. 252 - 4 l, so a prefix sum over the lanes counts the keys
         // at or above each; the digit where that count first reaches `need` is published
-        // with the count still needed within it and its size
+        // with the count still needed within it and its size.  The bins are cleared for
+        // the next digit as they are read.
         if (wave == 0) {
           const int4 h4 = *(const int4*)&hist[252 - 4 * lane];  // digits 252 - 4 l .. 255 - 4 l
+          *(int4*)&hist[252 - 4 * lane] = make_int4(0, 0, 0, 0);
           const int c[4] = {h4.w, h4.z, h4.y, h4.x};            // descending digits
           const int run = c[0] + c[1] + c[2] + c[3];
           int incl = run;
