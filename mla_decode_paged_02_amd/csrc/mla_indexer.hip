@@ -25,9 +25,9 @@
 //           threshold's top digit directly; the runs above it are listed and the runs of
 //           it are loaded into LDS (the runs below are never read).  A radix select over
 //           those keys (8-bit digits, histograms in LDS) follows until all keys of the
-//           threshold's bin are needed.  The listed keys are
-//           then ordered without a sort network: kIdxBuckets buckets of equal key width
-//           between the threshold and the largest key, a scan of the bucket counts, and
+//           threshold's bin are needed.  The listed keys are then ordered without a sort
+//           network: kIdxBuckets buckets of equal key width between the threshold and
+//           the top of the highest non-empty digit, a scan of the bucket counts, and
 //           within a bucket a count of the larger keys give each key its output slot.
 #include <stdint.h>
 
@@ -38,8 +38,8 @@ namespace mla {
 
 constexpr int kIdxThreads = 256;      // scoring work-group
 constexpr int kIdxSelThreads = 1024;  // selection work-group
-constexpr int kIdxHistCopies = 4;    // copies of each digit counter in the scoring kernel
-constexpr int kFoldHeads = 8;        // heads per fold thread whose q loads go out before the rows
+constexpr int kIdxHistCopies = 4;     // copies of each digit counter in the scoring kernel
+constexpr int kFoldHeads = 8;         // heads per fold thread whose q loads go out before the rows
 constexpr int kIdxBucketBits = 11;    // buckets of the listing order
 constexpr int kIdxBuckets = 1 << kIdxBucketBits;
 static_assert(kIdxBuckets % kIdxSelThreads == 0 && kIdxMaxTopK <= kIdxMaxKeys && kIdxMaxTopK % kIdxSelThreads == 0,
