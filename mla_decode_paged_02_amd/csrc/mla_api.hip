@@ -329,7 +329,7 @@ struct IndexerLayout {
 };
 static IndexerLayout indexer_layout(int64_t T, int64_t max_pages, int64_t PS) {
   IndexerLayout L;
-  L.keys_row = max_pages * PS;
+  L.keys_row = (max_pages * PS + 1) & ~(int64_t)1;  // even: every key slice starts 16-byte aligned
   L.hist_row = 512 * ((L.keys_row + mla::kIdxSlice - 1) / mla::kIdxSlice);
   L.key_bytes = (size_t)(T * L.keys_row) * sizeof(uint64_t);
   L.total = L.key_bytes + (size_t)(T * L.hist_row) * sizeof(uint32_t);

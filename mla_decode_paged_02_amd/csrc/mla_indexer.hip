@@ -470,20 +470,27 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
         oe += slice_equal[w];
       }
       const int na = slice_above[wave], n = na + slice_equal[wave];
+      // two keys per lane and load (slices start 16-byte aligned: the key row has an even
+      // length); a pair past the runs' end re-reads the last even pair, whose second key
+      // is still inside the token's key row
       const uint64_t* sk = krow + wave * kIdxSlice;
-      uint64_t v[kIdxSlice / 64];
+      ulonglong2 v[kIdxSlice / 128];
 #pragma unroll
-      for (int u = 0; u < kIdxSlice / 64; ++u)  // all loads in flight
-        if (u * 64 < n) v[u] = sk[min(u * 64 + lane, n - 1)];
+      for (int u = 0; u < kIdxSlice / 128; ++u)  // all loads in flight
+        if (u * 128 < n) v[u] = *(const ulonglong2*)(sk + min(2 * (u * 64 + lane), (n - 1) & ~1));
 #pragma unroll
-      for (int u = 0; u < kIdxSlice / 64; ++u) {
-        const int j = u * 64 + lane;
-        if (u * 64 < n) {
-          if (j < na) {
-            keys[oa + j] = v[u];
-          } else if (j < n) {
-            keys[oe + j - na] = v[u];
-            atomicAdd(&hist[(int)((v[u] >> 48) & 0xFF)], 1);
+      for (int u = 0; u < kIdxSlice / 128; ++u) {
+        if (u * 128 < n) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int j = 2 * (u * 64 + lane) + e;
+            const uint64_t k = e ? v[u].y : v[u].x;
+            if (j < na) {
+              keys[oa + j] = k;
+            } else if (j < n) {
+              keys[oe + j - na] = k;
+              atomicAdd(&hist[(int)((k >> 48) & 0xFF)], 1);
+            }
           }
         }
       }
