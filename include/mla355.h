@@ -340,9 +340,9 @@ size_t mla_decode_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t nu
 
 /* Workspace bytes an indexer call needs (host only, no device access): total_q query
  * tokens over a page table of max_pages pages of page_size rows.  The call keeps each
- * token's scored keys (8 bytes per row of the table) and, per 1,024-row slice of it, the
- * size and start of each top-digit run (2 KiB).  Reserve this on a stream before capturing
- * an indexer call on it. */
+ * token's scored keys (8 bytes per row of the table, the row count rounded up to even)
+ * and, per 1,024-row slice of it, the size and start of each top-digit run (2 KiB).
+ * Reserve this on a stream before capturing an indexer call on it. */
 size_t mla_indexer_workspace_bytes(int64_t total_q, int32_t max_pages, int32_t page_size);
 
 /* Grow the workspace of (device, stream) to at least `bytes` (allocates and clears it;
