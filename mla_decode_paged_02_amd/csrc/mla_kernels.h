@@ -148,7 +148,7 @@ struct IndexerArgs {
   int32_t* out;               // [T, top_k] physical rows, -1 filled
   int64_t out_row;
   uint64_t* keys;             // workspace [T, keys_row]: the scored rows' sort keys
-  int64_t keys_row;           // max_pages * PS
+  int64_t keys_row;           // max_pages * PS rounded up to even (slices 16-byte aligned)
   uint32_t* slice_hist;       // workspace [T, hist_row]: per key slice, the size and start
                               // of each top digit's run of keys
   int64_t hist_row;           // 512 * slices, slices = ceil(keys_row / kIdxSlice)
