@@ -581,8 +581,14 @@ __global__ __launch_bounds__(kIdxSelThreads) void mla_indexer_select_kernel(cons
     }
     if (lane == 63) wave_tot[wave] = (int)incl;
     __syncthreads();
-    uint32_t first = incl - run;
-    for (int w = 0; w < wave; ++w) first += (uint32_t)wave_tot[w];
+    // the waves before this one: an exclusive scan of the 16 wave totals over lanes 0..15
+    uint32_t wt = lane < kIdxSelThreads / 64 ? (uint32_t)wave_tot[lane] : 0u, wincl = wt;
+#pragma unroll
+    for (int off = 1; off < kIdxSelThreads / 64; off <<= 1) {
+      const uint32_t up = __shfl_up(wincl, off);
+      if (lane >= off) wincl += up;
+    }
+    uint32_t first = incl - run + (uint32_t)__builtin_amdgcn_readlane((int)(wincl - wt), wave);
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
       bfirst[kIdxBuckets - 1 - BPT * tid - u] = first;
