@@ -166,6 +166,29 @@ def test_indexer_widths(num_heads, depth):
     assert differ <= max(total // 100, 8)
 
 
+def test_indexer_malformed_offsets_are_flagged():
+    """Offsets that decrease set bit 2 of the device error word; a token no sequence's
+    offsets cover gets an empty list (-1), every entry is still -1 or a row of the pool,
+    and a token past the malformed entry gets the same list as with valid offsets."""
+    m = need_gpu()
+    c = make_indexer_case(48, [500, 700, 900, 1100], 8, 128, 64, 256, q_per_seq=1, name="idx-off")
+    good = run_indexer(m, c)
+    m.check_device_errors()  # clear
+    bad_off = c.input_row_offsets.copy()
+    bad_off[2] = 0  # [0, 1, 0, 3, 4]: sequence 1 would end before it starts
+    import torch
+    out = m.indexer_paged_fp8(u8_dev(c.q8), f32_dev(c.q_s), i32_dev(bad_off), i32_dev(c.page_table),
+                              i32_dev(c.cache_lens), u8_dev(c.k8), f32_dev(c.k_scale), c.top_k, mask=c.mask,
+                              local_window_size=c.window)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.int64)
+    assert m.check_device_errors() & 4
+    pool_rows = c.k8.shape[0] * c.page_size
+    assert np.all((got == -1) | ((got >= 0) & (got < pool_rows)))
+    assert np.all(got[0] == -1)  # token 0: no offsets pair covers it
+    assert np.array_equal(got[3], good[3])
+
+
 def test_indexer_unaligned_q():
     """q as a view into rows one byte wider (head stride D + 1, not a multiple of 4 bytes):
     the head fold reads it a byte at a time instead of a dword; the result meets the same
